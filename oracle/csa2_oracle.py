@@ -1,0 +1,470 @@
+"""Plain CPU oracle of the CSA2 layer hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+shares no code, table or constant generator with the HIP library; the two meet
+only through the seeded inputs of ``synth``.
+
+Arithmetic is float64 (numpy) everywhere except the FP4/FP8 encoder, which works
+in float32 on purpose: the stored format is defined by float32 divisions and
+round-to-nearest-even, and the GPU must reproduce those bytes exactly.
+
+Pages cited (titles as published):
+  [P1] "DeepSeek-V4.1 模型结构（2）：序列维度（中），CSA2 的三种模式" (blog.javazero.top)
+  [P2] "DeepSeek v4.1 Flash技术剖析——架构篇" (myhz0606.com)
+  [P3] "DeepSeek-V4.1-Flash：把百万 Token 的记忆，压缩成一套分级缓存" (junki.cn)
+  [P4] "CSA2 — l'attention creuse compressée de seconde génération" (mkdocs.reaper.mx)
+
+Readings taken where the pages are silent or garbled (each one is listed with its
+reason in the design notes of the repository):
+  * score has no 1/sqrt(d_I) factor (a positive global factor changes no selection);
+  * an entry g is visible to a query at position p iff its whole group ends at or
+    before p, i.e. g < floor((p+1)/m);
+  * RoPE uses interleaved pairs (2i, 2i+1) of the rotated slice with
+    theta_i = base^(-2i/n_rope);                          -- parity unpinned (convention)
+  * FP4 = E2M1 codes, one E4M3FN scale per 32 dims, scale = RNE(amax/6), codes =
+    RNE(u/scale) saturating at 6, sign kept (a negative value rounding to zero is
+    code 0x8), even dimension in the low nibble;          -- parity unpinned (convention)
+  * top-k ties go to the smaller entry index, -0 counts as +0, the output is
+    ascending and padded with -1;
+  * the HSI block holding the newest visible entry gets score +inf;
+  * the sliding window of a query at position p is the positions
+    [max(0, p-W+1, swa_pos0), p]; the current token is included;
+  * attention scale is 1/sqrt(d) with d = 512; no attention sink.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+LATENT_DIM = 512  # [P1] section on the KV size: one 512-d latent, K and V are the same vector
+ROPE_DIMS = 64    # [P1] compressor section: RoPE on the last 64 dims
+INDEX_DIM = 128   # [P1] indexer-K section: W^IK is 512 x 128
+FP4_BLOCK = 32    # [P1] indexer-K section: FP4 with one scale per 32 dims
+
+# ---------------------------------------------------------------------------
+# FP4 (E2M1) and FP8 (E4M3FN) codecs.  The formats themselves come from the OCP
+# Microscaling / OCP FP8 definitions; [P1] (indexer-K section) fixes "FP4, one
+# scale per 32 dims" and [P3] (section six, the 890 B budget) fixes 68 B per
+# index-K entry = 64 B of codes + 4 scale bytes.
+# ---------------------------------------------------------------------------
+
+# magnitudes of the 8 E2M1 codes 0..7 (sign is bit 3)
+E2M1_MAGNITUDE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each 4-bit E2M1 code (bit 3 = sign, bits 0-2 index the magnitude)."""
+    codes = np.asarray(codes).astype(np.int64)
+    mag = E2M1_MAGNITUDE[codes & 7]
+    return np.where((codes >> 3) & 1, -mag, mag)
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest E2M1 code, ties to the even code,
+    saturating at +-6; the sign bit is kept even when the magnitude rounds to 0."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    mids = (E2M1_MAGNITUDE[:-1] + E2M1_MAGNITUDE[1:]) / 2.0  # 0.25 0.75 1.25 1.75 2.5 3.5 5
+    idx = np.searchsorted(mids, a, side="left")  # number of midpoints strictly below a
+    at_mid = np.zeros(a.shape, dtype=bool)
+    inb = idx < len(mids)
+    at_mid[inb] = a[inb] == mids[idx[inb]]
+    # at a midpoint idx is the lower neighbour; move up when the lower one is odd
+    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    sign = np.signbit(v).astype(np.int64)
+    return (idx.astype(np.int64) | (sign << 3)).astype(np.uint8)
+
+
+def e4m3_decode(b: np.ndarray) -> np.ndarray:
+    """Value of each E4M3FN byte (bias 7, no infinities, S.1111.111 is NaN)."""
+    b = np.asarray(b).astype(np.int64)
+    s = (b >> 7) & 1
+    e = (b >> 3) & 15
+    mnt = b & 7
+    sub = mnt / 8.0 * 2.0 ** -6
+    nrm = (1.0 + mnt / 8.0) * np.power(2.0, e - 7)
+    val = np.where(e == 0, sub, nrm)
+    val = np.where((e == 15) & (mnt == 7), np.nan, val)
+    return np.where(s == 1, -val, val)
+
+
+_E4M3_POS_VALUES = e4m3_decode(np.arange(0x7F))  # bytes 0x00..0x7E, strictly increasing
+
+
+def e4m3_encode_nonneg(v: np.ndarray) -> np.ndarray:
+    """Round non-negative float32 values to the nearest E4M3FN byte, ties to the
+    even byte, saturating at 448 (byte 0x7E)."""
+    a = np.asarray(v, dtype=np.float32).astype(np.float64)
+    assert np.all(a >= 0.0), "scale encoder is only used on amax/6 >= 0"
+    mids = (_E4M3_POS_VALUES[:-1] + _E4M3_POS_VALUES[1:]) / 2.0
+    idx = np.searchsorted(mids, a, side="left")
+    at_mid = np.zeros(a.shape, dtype=bool)
+    inb = idx < len(mids)
+    at_mid[inb] = a[inb] == mids[idx[inb]]
+    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    idx = np.minimum(idx, 0x7E)
+    return idx.astype(np.uint8)
+
+
+def fp4_pack(u: np.ndarray):
+    """Quantise rows of 128 values to FP4 index-K storage.
+
+    [P1] indexer-K section: FP4, one scale per 32 dims; [P3] section six: 68 B per
+    entry.  Per 32-dim block: amax in float32, sigma = amax / 6 as a float32 division,
+    scale byte = E4M3(sigma), s = its value; code_i = E2M1(u_i / s) (float32
+    division), or 0 for the whole block when s == 0.  Code of dim 2j goes to the low
+    nibble of byte j.  Returns (codes uint8 [rows, 64], scales uint8 [rows, 4]).
+    """
+    u = np.asarray(u, dtype=np.float32)
+    rows, d = u.shape
+    assert d % FP4_BLOCK == 0
+    nb = d // FP4_BLOCK
+    blocks = u.reshape(rows, nb, FP4_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2).astype(np.float32)
+    sigma = (amax / np.float32(6.0)).astype(np.float32)
+    sbytes = e4m3_encode_nonneg(sigma)
+    s = e4m3_decode(sbytes).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (blocks / s[:, :, None]).astype(np.float32)
+    codes = e2m1_encode(ratio)
+    codes = np.where((s == 0)[:, :, None], np.uint8(0), codes).reshape(rows, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sbytes.reshape(rows, nb)
+
+
+def fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise index-K storage: value(code) * value(scale), float64 [rows, 128]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows = codes.shape[0]
+    lo = codes & 0x0F
+    hi = codes >> 4
+    c = np.empty((rows, codes.shape[1] * 2), dtype=np.uint8)
+    c[:, 0::2] = lo
+    c[:, 1::2] = hi
+    vals = e2m1_decode(c)
+    s = e4m3_decode(np.asarray(scales))
+    return vals * np.repeat(s, FP4_BLOCK, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# RoPE on the trailing slice ([P1] compressor section: RoPE on the last 64
+# dims at the group's first-token position; indexer-K section: index K gets its
+# own RoPE on its last 64 dims).
+# ---------------------------------------------------------------------------
+
+def rope_last(x: np.ndarray, pos, base: float = 10000.0, n_rope: int = ROPE_DIMS) -> np.ndarray:
+    """Rotate the last ``n_rope`` dims of each row of ``x`` at position ``pos``.
+
+    Pairs (2i, 2i+1) of the slice turn by pos * base^(-2i/n_rope).  ``pos`` is a
+    scalar or one position per row.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    d = x.shape[-1]
+    pos = np.asarray(pos, dtype=np.float64)
+    i = np.arange(n_rope // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * i / n_rope)
+    ang = pos[..., None] * theta if pos.ndim else pos * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x0 = x[..., d - n_rope::2].copy()
+    x1 = x[..., d - n_rope + 1::2].copy()
+    x[..., d - n_rope::2] = x0 * c - x1 * s
+    x[..., d - n_rope + 1::2] = x0 * s + x1 * c
+    return x
+
+
+def rms_norm(e: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis ([P1] compressor code and text: the pooled entry is normalised)."""
+    e = np.asarray(e, dtype=np.float64)
+    return e / np.sqrt(np.mean(e * e, axis=-1, keepdims=True) + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# (a) Compressor: [P1] section "压缩算子去掉了重叠和位置偏置" (code excerpt and
+# text), [P2] section CSA2-FULL, [P4] "Ce qui change par rapport à V4" (table):
+# disjoint groups of m tokens, per-channel softmax of the gate over the group,
+# no position bias, then RMSNorm, then RoPE on the last 64 dims at the position
+# of the group's first token.  m == 1 is a projection plus norm, no gate.
+# ---------------------------------------------------------------------------
+
+def compress(x, w_kv, w_gate, gamma, m: int, start_pos: int = 0, eps: float = 1e-6,
+             rope_base: float = 10000.0):
+    """One sequence.  x [T, D]; w_kv, w_gate [512, D] (output x input); T and
+    start_pos multiples of m.  Returns (latent_pre [T/m, 512], kv [T/m, 512],
+    entry_ids [T/m]); latent_pre is the normalised entry before RoPE."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    assert T % m == 0 and start_pos % m == 0
+    n = T // m
+    C = x @ np.asarray(w_kv, dtype=np.float64).T  # C_t: [T, 512]
+    if m == 1:
+        if w_gate is not None:
+            raise ValueError("m == 1 has no gate projection")
+        e = C
+    else:
+        Z = x @ np.asarray(w_gate, dtype=np.float64).T  # Z_t
+        Cg = C.reshape(n, m, -1)
+        Zg = Z.reshape(n, m, -1)
+        Zmax = Zg.max(axis=1, keepdims=True)
+        ez = np.exp(Zg - Zmax)
+        a = ez / ez.sum(axis=1, keepdims=True)  # softmax over the m tokens, per channel
+        e = (a * Cg).sum(axis=1)
+    latent_pre = rms_norm(e, gamma, eps)
+    entry_ids = start_pos // m + np.arange(n)
+    kv = rope_last(latent_pre, entry_ids * m, rope_base)
+    return latent_pre, kv, entry_ids
+
+
+# ---------------------------------------------------------------------------
+# (b) Index K: [P1] section "indexer K 改由 main KV 投影": projected from the
+# main-KV entry BEFORE its RoPE, 512 -> 128, RoPE on its own last 64 dims, FP4
+# with one scale per 32 dims, no Hadamard rotation.
+# ---------------------------------------------------------------------------
+
+def index_k(latent_pre, w_ik, entry_pos, rope_base: float = 10000.0):
+    """latent_pre [N, 512], w_ik [128, 512] (output x input), entry_pos [N] (= g*m).
+    Returns (u float64 [N, 128] before quantisation, codes [N, 64], scales [N, 4])."""
+    u = np.asarray(latent_pre, dtype=np.float64) @ np.asarray(w_ik, dtype=np.float64).T
+    u = rope_last(u, np.asarray(entry_pos), rope_base)
+    codes, scales = fp4_pack(u.astype(np.float32))
+    return u, codes, scales
+
+
+# ---------------------------------------------------------------------------
+# (c) Indexer score: [P1] indexer-K section (score unchanged from V4: per-head
+# weight w, ReLU of the q^I . k^I dot product, summed over H^I = 32 heads of
+# 128 dims), [P2] CSA2-FULL (causally visible set).
+# ---------------------------------------------------------------------------
+
+def visible_entries(p: int, m: int) -> int:
+    """Entries visible at query position p: groups that end at or before p."""
+    return (int(p) + 1) // m
+
+
+def index_scores(q_idx, w, k_deq, n_vis: int) -> np.ndarray:
+    """q_idx [H_I, 128], w [H_I], k_deq [N, 128]; scores of entries 0..n_vis-1."""
+    q = np.asarray(q_idx, dtype=np.float64)
+    k = np.asarray(k_deq, dtype=np.float64)[:n_vis]
+    dots = k @ q.T  # [n_vis, H_I]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# (d) Causal top-k: [P1] "一层全局注意力算四样东西" (top-k positions, recomputed
+# per query, never cached), [P2] CSA2-FULL / CSA2-ReIndex.
+# ---------------------------------------------------------------------------
+
+def topk_select(scores, k: int, candidates=None) -> np.ndarray:
+    """Indices of the k largest scores (ties -> smaller index; -0 == +0), returned
+    ascending and padded with -1 to length k.  ``candidates`` restricts the choice
+    to the given entry ids (default: all of range(len(scores)))."""
+    scores = np.asarray(scores, dtype=np.float64) + 0.0  # -0.0 + 0.0 == +0.0
+    if candidates is None:
+        candidates = np.arange(scores.shape[0])
+    candidates = np.asarray(candidates, dtype=np.int64)
+    if candidates.size <= k:
+        chosen = candidates
+    else:
+        s = scores[candidates]
+        order = np.lexsort((candidates, -s))  # primary: score descending, then index ascending
+        chosen = candidates[order[:k]]
+    out = np.full(k, -1, dtype=np.int64)
+    chosen = np.sort(chosen)
+    out[: chosen.size] = chosen
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (c') Hierarchical candidate pool (HSI): [P2] CSA2-ReIndex (blocks of s entry
+# positions, block score = max index score inside it, keep the best n_b blocks,
+# the block of the newest visible entry is forced in, Reindex masks scores outside
+# the pool to -inf), [P3] section five (the Full layer scans everything and forms
+# the pool; later Reindex layers choose their own top-512 inside it).
+# ---------------------------------------------------------------------------
+
+def hsi_pool(full_scores, n_vis: int, s: int, n_b: int) -> np.ndarray:
+    """Block ids of the candidate pool for one query, ascending, padded with -1 to n_b."""
+    full_scores = np.asarray(full_scores, dtype=np.float64)[:n_vis] + 0.0
+    nblk = (n_vis + s - 1) // s
+    out = np.full(n_b, -1, dtype=np.int64)
+    if nblk == 0:
+        return out
+    beta = np.array([full_scores[i * s: min((i + 1) * s, n_vis)].max() for i in range(nblk)])
+    beta[nblk - 1] = np.inf  # block holding the newest visible entry is always kept
+    if nblk <= n_b:
+        keep = np.arange(nblk)
+    else:
+        order = np.lexsort((np.arange(nblk), -beta))
+        keep = np.sort(order[:n_b])
+    out[: keep.size] = keep
+    return out
+
+
+def pool_entries(blocks, n_vis: int, s: int) -> np.ndarray:
+    """Entry ids covered by the pool blocks (clipped to the visible range)."""
+    ids = [np.arange(b * s, min((b + 1) * s, n_vis)) for b in np.asarray(blocks) if b >= 0]
+    return np.concatenate(ids) if ids else np.zeros(0, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# (e) Sparse attention: [P1] "一层全局注意力算四样东西" (attention reads the k
+# selected entries plus the 128-entry sliding window of the layer), [P2]
+# CSA2-FULL (shared key-value: one vector is both key and value; rows are the
+# window plus the selected entries), [P3] section four (p_j and o(q) equations,
+# o in the convex hull of the selected contents).
+# ---------------------------------------------------------------------------
+
+def window_positions(p: int, W: int, swa_pos0: int = 0) -> np.ndarray:
+    """Positions of the sliding window of a query at position p (current token included)."""
+    lo = max(0, int(p) - W + 1, int(swa_pos0))
+    return np.arange(lo, int(p) + 1)
+
+
+def sparse_attention(q, kv, sel, swa_kv, swa_pos0: int, p: int, W: int,
+                     scale: Optional[float] = None):
+    """One query token.  q [H, d]; kv [N, d]; sel [k] (entry ids, -1 = empty);
+    swa_kv [L_w, d] holding positions swa_pos0.. .  Returns (o [H, d], probs [H, R],
+    rows [R, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sel = np.asarray(sel, dtype=np.int64)
+    sel = sel[sel >= 0]
+    win = window_positions(p, W, swa_pos0)
+    rows = np.concatenate([kv[sel], np.asarray(swa_kv, dtype=np.float64)[win - swa_pos0]], axis=0)
+    logits = (q @ rows.T) * scale
+    logits = logits - logits.max(axis=1, keepdims=True)
+    ez = np.exp(logits)
+    probs = ez / ez.sum(axis=1, keepdims=True)
+    return probs @ rows, probs, rows
+
+
+# ---------------------------------------------------------------------------
+# Modes and the shared runtime: [P1] section "共享池里有四样东西" (four slots,
+# one position each, no per-layer numbering; the two mode tests in the
+# attention-layer excerpt), [P2] mode tables, [P4] "Les trois modes".
+# ---------------------------------------------------------------------------
+
+FULL, REINDEX, REUSE = "full", "reindex", "reuse"
+
+
+class SlotEmpty(RuntimeError):
+    pass
+
+
+@dataclass
+class Runtime:
+    """The four single-occupancy slots.  A slot holds a reference (not a copy)."""
+    compress_kv: Optional[np.ndarray] = None   # [B, N, 512]
+    index_k: Optional[tuple] = None            # (codes [B, N, 64], scales [B, N, 4])
+    topk_idxs: Optional[np.ndarray] = None     # [B, T, k]
+    candidates: Optional[np.ndarray] = None    # [B, T, n_b] block ids (+ block size)
+    candidates_s: int = 0
+    writes: list = field(default_factory=list)
+
+    def get(self, name):
+        v = getattr(self, name)
+        if v is None:
+            raise SlotEmpty(name)
+        return v
+
+
+@dataclass
+class LayerInputs:
+    """Per-layer inputs of one call: batch of B sequences, T query tokens each."""
+    q: np.ndarray                       # [B, T, H, 512] attention queries (RoPE applied)
+    swa_kv: np.ndarray                  # [B, L_w, 512] this layer's window KV
+    q_pos: np.ndarray                   # [B, T] absolute positions of the queries
+    swa_pos0: np.ndarray                # [B] position of swa_kv[:, 0]
+    q_idx: Optional[np.ndarray] = None  # [B, T, H_I, 128] indexer queries (Full / Reindex)
+    w: Optional[np.ndarray] = None      # [B, T, H_I] per-head indexer weights
+    x: Optional[np.ndarray] = None      # [B, L, D] hidden states (Full only)
+    start_pos: int = 0
+
+
+@dataclass
+class LayerConfig:
+    mode: str
+    m: int = 1
+    k: int = 512
+    W: int = 128
+    w_kv: Optional[np.ndarray] = None
+    w_gate: Optional[np.ndarray] = None
+    gamma: Optional[np.ndarray] = None
+    w_ik: Optional[np.ndarray] = None
+    eps: float = 1e-6
+    rope_base: float = 10000.0
+    hsi: str = "none"   # none | build (Full) | use (Reindex)
+    hsi_s: int = 64
+    hsi_nb: int = 256
+    scale: Optional[float] = None
+
+
+def _score_and_select(rt: Runtime, cfg: LayerConfig, inp: LayerInputs, codes, scales):
+    B, T = inp.q_pos.shape
+    topk = np.full((B, T, cfg.k), -1, dtype=np.int64)
+    cands = np.full((B, T, cfg.hsi_nb), -1, dtype=np.int64) if cfg.hsi == "build" else None
+    for b in range(B):
+        kdeq = fp4_unpack(codes[b], scales[b])
+        for t in range(T):
+            n_vis = visible_entries(inp.q_pos[b, t], cfg.m)
+            sc = index_scores(inp.q_idx[b, t], inp.w[b, t], kdeq, n_vis)
+            if cfg.hsi == "use":
+                pool = rt.get("candidates")[b, t]
+                if rt.candidates_s != cfg.hsi_s:
+                    raise ValueError("candidate pool block size mismatch")
+                topk[b, t] = topk_select(sc, cfg.k, pool_entries(pool, n_vis, cfg.hsi_s))
+            else:
+                topk[b, t] = topk_select(sc, cfg.k)
+                if cfg.hsi == "build":
+                    cands[b, t] = hsi_pool(sc, n_vis, cfg.hsi_s, cfg.hsi_nb)
+    return topk, cands
+
+
+def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
+    """One CSA2 layer in the configured mode; returns o [B, T, H, 512]."""
+    if cfg.mode == FULL:
+        B = inp.x.shape[0]
+        lat, kvs, cs, ss = [], [], [], []
+        for b in range(B):
+            latent_pre, kv, ids = compress(inp.x[b], cfg.w_kv, cfg.w_gate, cfg.gamma, cfg.m,
+                                           inp.start_pos, cfg.eps, cfg.rope_base)
+            _, codes, scales = index_k(latent_pre, cfg.w_ik, ids * cfg.m, cfg.rope_base)
+            kvs.append(kv), cs.append(codes), ss.append(scales), lat.append(latent_pre)
+        rt.compress_kv = np.stack(kvs)
+        rt.index_k = (np.stack(cs), np.stack(ss))
+        rt.writes += ["compress_kv", "index_k"]
+        topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k)
+        rt.topk_idxs = topk
+        rt.writes.append("topk_idxs")
+        if cands is not None:
+            rt.candidates, rt.candidates_s = cands, cfg.hsi_s
+            rt.writes.append("candidates")
+    elif cfg.mode == REINDEX:
+        codes, scales = rt.get("index_k")
+        kv_src = rt.get("compress_kv")
+        if cfg.hsi == "build":
+            raise ValueError("only a Full layer builds the candidate pool")
+        topk, _ = _score_and_select(rt, cfg, inp, codes, scales)
+        rt.topk_idxs = topk
+        rt.writes.append("topk_idxs")
+    elif cfg.mode == REUSE:
+        rt.get("compress_kv")
+        rt.get("topk_idxs")
+    else:
+        raise ValueError(cfg.mode)
+    kv = rt.compress_kv
+    topk = rt.topk_idxs
+    B, T = inp.q_pos.shape
+    o = np.zeros(inp.q.shape, dtype=np.float64)
+    for b in range(B):
+        for t in range(T):
+            o[b, t] = sparse_attention(inp.q[b, t], kv[b], topk[b, t], inp.swa_kv[b],
+                                       int(inp.swa_pos0[b]), int(inp.q_pos[b, t]), cfg.W,
+                                       cfg.scale)[0]
+    return o

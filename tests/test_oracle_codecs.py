@@ -1,0 +1,157 @@
+"""Pins of the oracle's FP4/FP8 codecs and FP4 index-K packing (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa2_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _e2m1_table():
+    rows = []
+    with open(os.path.join(GOLD, "e2m1_codes.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def test_e2m1_decode_matches_ocp_table():
+    rows = _e2m1_table()
+    assert len(rows) == 16
+    for code, val in rows:
+        got = O.e2m1_decode(np.array([code]))[0]
+        assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+
+
+def test_e2m1_encode_exact_values_roundtrip():
+    for code, val in _e2m1_table():
+        enc = O.e2m1_encode(np.array([val], dtype=np.float32))[0]
+        assert enc == code, (code, val, enc)
+
+
+@pytest.mark.parametrize("v,code", [
+    (0.25, 0x0), (0.75, 0x2), (1.25, 0x2), (1.75, 0x4), (2.5, 0x4), (3.5, 0x6), (5.0, 0x6),
+    (-0.25, 0x8), (-0.75, 0xA), (-5.0, 0xE), (0.2499, 0x0), (0.2501, 0x1), (7.0, 0x7),
+    (1e9, 0x7), (-1e9, 0xF), (-1e-7, 0x8),
+])
+def test_e2m1_encode_ties_to_even_and_saturates(v, code):
+    assert O.e2m1_encode(np.array([v], dtype=np.float32))[0] == code
+
+
+def test_e2m1_encode_is_nearest_brute_force():
+    # brute force over the 16 code values: nearest, ties to the even code
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.uniform(-7, 7, 4000), np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])])
+    v = v.astype(np.float32)
+    enc = O.e2m1_encode(v)
+    table = _e2m1_table()
+    for x, c in zip(v, enc):
+        best = None
+        for code, val in table[:8]:
+            dist = abs(abs(float(x)) - val)
+            key = (dist, code % 2)  # smaller distance, then even code
+            if best is None or key < best[0]:
+                best = (key, code)
+        expect = best[1] | (8 if np.signbit(x) else 0)
+        assert c == expect, (x, c, expect)
+
+
+def test_e4m3_decode_matches_torch_for_all_bytes():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = O.e4m3_decode(b)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+    assert O.e4m3_decode(np.array([0x7E]))[0] == 448.0
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(2)
+    grid = O.e4m3_decode(np.arange(0x7F))
+    mids = (grid[:-1] + grid[1:]) / 2
+    v = np.concatenate([
+        rng.uniform(0, 460, 3000), np.exp(rng.uniform(-14, 6, 3000)), grid, mids,
+        np.array([0.0, 2.0 ** -10, 1.5 * 2.0 ** -10, 447.9, 449.0, 463.9]),
+    ]).astype(np.float32)
+    v = v[v < 464]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode_nonneg(v)
+    assert np.array_equal(ref, got)
+    # saturation above the largest finite value
+    assert O.e4m3_encode_nonneg(np.array([500.0, 1e6], dtype=np.float32)).tolist() == [0x7E, 0x7E]
+
+
+def test_fp4_entry_size_matches_page():
+    facts = json.load(open(os.path.join(GOLD, "page_facts.json")))
+    u = np.random.default_rng(3).standard_normal((5, 128)).astype(np.float32)
+    codes, scales = O.fp4_pack(u)
+    assert codes.shape == (5, 64) and scales.shape == (5, 4)
+    assert codes.dtype == np.uint8 and scales.dtype == np.uint8
+    assert codes.shape[1] + scales.shape[1] == facts["index_k_entry_bytes"]["value"]
+
+
+def test_fp4_pack_roundtrip_error_bound():
+    rng = np.random.default_rng(4)
+    u = (rng.standard_normal((300, 128)) * np.exp(rng.uniform(-6, 4, (300, 1)))).astype(np.float32)
+    codes, scales = O.fp4_pack(u)
+    back = O.fp4_unpack(codes, scales)
+    s = np.repeat(O.e4m3_decode(scales), 32, axis=1)
+    amax = np.repeat(np.abs(u.reshape(300, 4, 32)).max(axis=2), 32, axis=1)
+    # inside the grid the error is at most one grid step (<= s); beyond 6 s the value clips
+    err = np.abs(back - u.astype(np.float64))
+    assert np.all(err <= s * 1.0 + np.maximum(0.0, amax - 6 * s) + 1e-12)
+    # where the scale is non-zero, the largest element of a block keeps at least half
+    # its magnitude (the scale is chosen from amax); a zero scale zeroes the block
+    sb = O.e4m3_decode(scales)
+    bmax = np.abs(back).reshape(300, 4, 32).max(axis=2)
+    umax = np.abs(u).reshape(300, 4, 32).max(axis=2)
+    assert np.all(bmax[sb > 0] >= 0.5 * umax[sb > 0])
+    assert np.all(bmax[sb == 0] == 0) and np.all(umax[sb == 0] <= 6 * 2.0 ** -10)
+
+
+def test_fp4_pack_special_blocks():
+    u = np.zeros((1, 128), dtype=np.float32)
+    u[0, 32:64] = -1.0
+    u[0, 64] = 6.0
+    u[0, 65] = -3.0
+    u[0, 66] = -0.1
+    codes, scales = O.fp4_pack(u)
+    assert scales[0, 0] == 0 and np.all(codes[0, :16] == 0)          # all-zero block
+    # block 1: all equal negatives -> each is -6 * s exactly (code 0xF)
+    assert np.all(codes[0, 16:32] == 0xFF)
+    # block 2: amax 6 -> sigma = 1 -> s = 1; 6 -> 0x7, -3 -> 0xD; -0.1 -> -0 (0x8)
+    assert scales[0, 2] == 0x38
+    assert codes[0, 32] == (0x7 | (0xD << 4))
+    assert (codes[0, 33] & 0xF) == 0x8
+    # even dimension in the low nibble
+    assert O.fp4_unpack(codes, scales)[0, 64] == 6.0 and O.fp4_unpack(codes, scales)[0, 65] == -3.0
+
+
+def test_fp4_pack_is_elementwise_brute_force():
+    # independent loop implementation of the per-block rule on a few rows
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal((6, 128)).astype(np.float32)
+    codes, scales = O.fp4_pack(u)
+    grid = O.e4m3_decode(np.arange(0x7F))
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for r in range(6):
+        for b in range(4):
+            blk = u[r, 32 * b: 32 * b + 32]
+            sigma = np.float32(np.max(np.abs(blk))) / np.float32(6)
+            # nearest e4m3 byte (ties even)
+            best = min(range(0x7F), key=lambda i: (abs(grid[i] - float(sigma)), i % 2))
+            assert scales[r, b] == best
+            s = np.float32(grid[best])
+            for i in range(32):
+                x = np.float32(blk[i]) / s
+                c = min(range(8), key=lambda j: (abs(vals[j] - abs(float(x))), j % 2)) | (8 if x < 0 or np.signbit(x) else 0)
+                byte = codes[r, 16 * b + i // 2]
+                got = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
+                assert got == c, (r, b, i, blk[i], got, c)
