@@ -1,0 +1,285 @@
+"""Thin ctypes binding of libcsa2.so (the CSA2 C ABI declared in include/csa2.h).
+
+Argument marshalling only: torch tensors are passed as device pointers together
+with the current HIP stream; every step of the path runs in the library's HIP
+kernels.  If the library is missing this module raises on first use; there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libcsa2.so")
+
+CSA2_F32, CSA2_BF16 = 0, 1
+FULL, REINDEX, REUSE = 0, 1, 2
+HSI_NONE, HSI_BUILD, HSI_USE = 0, 1, 2
+SLOT_COMPRESS_KV, SLOT_INDEX_K, SLOT_TOPK_IDXS, SLOT_CANDIDATES = 0, 1, 2, 3
+OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER = 0, 1, 2
+
+STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_DTYPE",
+          4: "CSA2_ERR_SLOT_EMPTY", 5: "CSA2_ERR_SLOT_MISMATCH", 6: "CSA2_ERR_WORKSPACE",
+          7: "CSA2_ERR_HIP", 8: "CSA2_ERR_UNSUPPORTED"}
+
+
+class CSA2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+vp = C.c_void_p
+i32 = C.c_int32
+
+
+class CompressArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("D", i32), ("m", i32), ("start_pos", i32),
+                ("N_cap", i32), ("eps", C.c_float), ("rope_base", C.c_float), ("x", vp), ("w_kv", vp),
+                ("w_gate", vp), ("gamma", vp), ("latent_pre", vp), ("kv_cache", vp)]
+
+
+class IndexKArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("N", i32), ("m", i32), ("entry0", i32), ("N_cap", i32),
+                ("rope_base", C.c_float), ("latent_pre", vp), ("w_ik", vp), ("codes", vp), ("scales", vp)]
+
+
+class ScoreTopkArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H_I", i32), ("N_cap", i32), ("n_entries", i32),
+                ("m", i32), ("k", i32), ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("q_idx", vp), ("w", vp),
+                ("codes", vp), ("scales", vp), ("q_pos", vp), ("topk", vp), ("candidates", vp),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class SparseAttnArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H", i32), ("N_cap", i32), ("k", i32), ("L_w", i32),
+                ("W", i32), ("scale", C.c_float), ("q", vp), ("kv", vp), ("topk", vp), ("swa_kv", vp),
+                ("swa_pos0", vp), ("q_pos", vp), ("o", vp), ("lse", vp), ("workspace", vp),
+                ("workspace_bytes", C.c_size_t)]
+
+
+class LayerCfg(C.Structure):
+    _fields_ = [("mode", i32), ("dtype", i32), ("m", i32), ("k", i32), ("W", i32), ("H_I", i32), ("H", i32),
+                ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("rope_base", C.c_float), ("eps", C.c_float),
+                ("scale", C.c_float)]
+
+
+class LayerIO(C.Structure):
+    _fields_ = [("B", i32), ("T", i32), ("D", i32), ("start_pos", i32), ("N_cap", i32),
+                ("x", vp), ("w_kv", vp), ("w_gate", vp), ("gamma", vp), ("w_ik", vp),
+                ("latent_pre", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
+                ("q_idx", vp), ("w", vp), ("topk", vp), ("candidates", vp),
+                ("q_pos", vp), ("q", vp), ("swa_kv", vp), ("L_w", i32), ("swa_pos0", vp),
+                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class SlotInfo(C.Structure):
+    _fields_ = [("filled", i32), ("generation", C.c_uint64), ("ptr", vp), ("ptr2", vp), ("dtype", i32),
+                ("B", i32), ("rows", i32), ("cols", i32), ("extra", i32)]
+
+
+EXPORTS = {
+    "csa2_runtime_create": ([C.POINTER(vp)], i32),
+    "csa2_runtime_destroy": ([vp], i32),
+    "csa2_runtime_reset": ([vp], i32),
+    "csa2_runtime_slot": ([vp, i32, C.POINTER(SlotInfo)], i32),
+    "csa2_compress": ([vp, C.POINTER(CompressArgs), vp], i32),
+    "csa2_index_k": ([vp, C.POINTER(IndexKArgs), vp], i32),
+    "csa2_score_topk": ([vp, C.POINTER(ScoreTopkArgs), vp], i32),
+    "csa2_sparse_attn": ([vp, C.POINTER(SparseAttnArgs), vp], i32),
+    "csa2_layer_forward": ([vp, C.POINTER(LayerCfg), C.POINTER(LayerIO), vp], i32),
+    "csa2_workspace_size": ([i32, vp, C.POINTER(LayerCfg), C.POINTER(C.c_size_t)], i32),
+    "csa2_fp4_pack": ([vp, C.c_int64, vp, vp, vp], i32),
+    "csa2_status_string": ([i32], C.c_char_p),
+    "csa2_last_error": ([], C.c_char_p),
+    "csa2_version": ([], C.c_char_p),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libcsa2.so not built ({LIB_PATH}); run "
+                               "python -m compressed_sparse_attention_compress_amd.build_lib")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise CSA2Error(status, lib().csa2_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA2_BF16
+    if t.dtype == torch.float32:
+        return CSA2_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+class Runtime:
+    """Owner of a csa2_runtime (the four shared slots)."""
+
+    def __init__(self):
+        h = vp()
+        _check(lib().csa2_runtime_create(C.byref(h)))
+        self.handle = h
+
+    def reset(self):
+        _check(lib().csa2_runtime_reset(self.handle))
+
+    def slot(self, which: int) -> SlotInfo:
+        info = SlotInfo()
+        _check(lib().csa2_runtime_slot(self.handle, which, C.byref(info)))
+        return info
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            lib().csa2_runtime_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _rt(rt):
+    return None if rt is None else rt.handle
+
+
+def csa2_compress(rt, x, w_kv, w_gate, gamma, latent_pre, kv_cache, m: int, start_pos: int = 0,
+                  eps: float = 1e-6, rope_base: float = 10000.0, stream=None):
+    B, T, D = x.shape
+    a = CompressArgs(dtype=_dtype(x), B=B, T=T, D=D, m=m, start_pos=start_pos, N_cap=kv_cache.shape[1],
+                     eps=eps, rope_base=rope_base, x=_ptr(x), w_kv=_ptr(w_kv), w_gate=_ptr(w_gate),
+                     gamma=_ptr(gamma), latent_pre=_ptr(latent_pre), kv_cache=_ptr(kv_cache))
+    _check(lib().csa2_compress(_rt(rt), C.byref(a), _stream(stream)))
+
+
+def csa2_index_k(rt, latent_pre, w_ik, codes, scales, m: int, entry0: int = 0, rope_base: float = 10000.0,
+                 stream=None):
+    B, N, _ = latent_pre.shape
+    a = IndexKArgs(dtype=_dtype(w_ik), B=B, N=N, m=m, entry0=entry0, N_cap=codes.shape[1], rope_base=rope_base,
+                   latent_pre=_ptr(latent_pre), w_ik=_ptr(w_ik), codes=_ptr(codes), scales=_ptr(scales))
+    _check(lib().csa2_index_k(_rt(rt), C.byref(a), _stream(stream)))
+
+
+def score_topk_args(q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int, N_cap: int,
+                    hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0, candidates=None, workspace=None):
+    B, T, H_I, _ = q_idx.shape
+    return ScoreTopkArgs(dtype=_dtype(q_idx), B=B, T=T, H_I=H_I, N_cap=N_cap, n_entries=n_entries, m=m, k=k,
+                         hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, q_idx=_ptr(q_idx), w=_ptr(w), codes=_ptr(codes),
+                         scales=_ptr(scales), q_pos=_ptr(q_pos), topk=_ptr(topk), candidates=_ptr(candidates),
+                         workspace=_ptr(workspace),
+                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def score_topk_workspace_bytes(**kw) -> int:
+    a = score_topk_args(**kw)
+    n = C.c_size_t()
+    _check(lib().csa2_workspace_size(OP_SCORE_TOPK, C.cast(C.byref(a), vp), None, C.byref(n)))
+    return n.value
+
+
+def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int,
+                    N_cap: Optional[int] = None, hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0,
+                    candidates=None, workspace=None, stream=None):
+    """Score and select; codes/scales None -> the runtime's index_k slot."""
+    if N_cap is None:
+        N_cap = codes.shape[1]
+    kw = dict(q_idx=q_idx, w=w, codes=codes, scales=scales, q_pos=q_pos, topk=topk, n_entries=n_entries, m=m,
+              k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates)
+    if workspace is None:
+        nbytes = score_topk_workspace_bytes(**kw)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q_idx.device)
+    a = score_topk_args(workspace=workspace, **kw)
+    _check(lib().csa2_score_topk(_rt(rt), C.byref(a), _stream(stream)))
+    return workspace
+
+
+def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Optional[int] = None,
+                     N_cap: Optional[int] = None, scale: float = 0.0, lse=None, stream=None):
+    """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots."""
+    B, T, H, _ = q.shape
+    if k is None:
+        k = topk.shape[-1]
+    if N_cap is None:
+        N_cap = kv.shape[1] if kv is not None else 0
+    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, N_cap=N_cap, k=k, L_w=swa_kv.shape[1], W=W, scale=scale,
+                       q=_ptr(q), kv=_ptr(kv), topk=_ptr(topk), swa_kv=_ptr(swa_kv), swa_pos0=_ptr(swa_pos0),
+                       q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=None, workspace_bytes=0)
+    _check(lib().csa2_sparse_attn(_rt(rt), C.byref(a), _stream(stream)))
+
+
+def csa2_fp4_pack(rows, codes, scales, stream=None):
+    n = rows.shape[0] if rows.dim() == 2 else rows.numel() // 128
+    _check(lib().csa2_fp4_pack(_ptr(rows), n, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, hsi: int = HSI_NONE,
+              hsi_s: int = 0, hsi_nb: int = 0, rope_base: float = 10000.0, eps: float = 1e-6,
+              scale: float = 0.0) -> LayerCfg:
+    return LayerCfg(mode=mode, dtype=dtype, m=m, k=k, W=W, H_I=H_I, H=H, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb,
+                    rope_base=rope_base, eps=eps, scale=scale)
+
+
+def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,
+             gamma=None, w_ik=None, latent_pre=None, kv_cache=None, ik_codes=None, ik_scales=None, q_idx=None,
+             w=None, topk=None, candidates=None, workspace=None) -> LayerIO:
+    return LayerIO(B=B, T=T, D=D, start_pos=start_pos, N_cap=N_cap, x=_ptr(x), w_kv=_ptr(w_kv),
+                   w_gate=_ptr(w_gate), gamma=_ptr(gamma), w_ik=_ptr(w_ik), latent_pre=_ptr(latent_pre),
+                   kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes), ik_scales=_ptr(ik_scales),
+                   q_idx=_ptr(q_idx), w=_ptr(w), topk=_ptr(topk), candidates=_ptr(candidates), q_pos=_ptr(q_pos),
+                   q=_ptr(q), swa_kv=_ptr(swa_kv), L_w=swa_kv.shape[1], swa_pos0=_ptr(swa_pos0), o=_ptr(o),
+                   workspace=_ptr(workspace),
+                   workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def layer_workspace_bytes(cfg: LayerCfg, io: LayerIO) -> int:
+    n = C.c_size_t()
+    _check(lib().csa2_workspace_size(OP_LAYER, C.cast(C.byref(io), vp), C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def csa2_layer_forward(rt: Runtime, cfg: LayerCfg, io: LayerIO, stream=None):
+    _check(lib().csa2_layer_forward(rt.handle, C.byref(cfg), C.byref(io), _stream(stream)))
+
+
+def version() -> str:
+    return lib().csa2_version().decode()
+
+
+def default_scale() -> float:
+    return 1.0 / math.sqrt(512.0)

@@ -1,0 +1,45 @@
+// Internal launcher interface between the host API (csa2_api.cpp) and the HIP
+// kernel translation units.  Every launcher assumes its arguments were validated
+// by the caller and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// ---- compressor (k_compress.hip)
+hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const void* w_gate,
+                           const float* gamma, float* latent_pre, void* kv_cache, int B, int T,
+                           int D, int m, int start_pos, int N_cap, float eps, float rope_base,
+                           hipStream_t stream);
+
+// ---- index K and FP4 packing (k_index_k.hip)
+hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes,
+                          uint8_t* scales, int B, int N, int m, int entry0, int N_cap,
+                          float rope_base, hipStream_t stream);
+hipError_t launch_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream);
+
+// ---- indexer score + top-k (k_score.hip)
+struct ScorePlan {
+  int chunk;        // entries per chunk (power of two)
+  int n_chunks;     // chunks per query
+  int k_chunk;      // candidates kept per chunk = min(k, chunk)
+  size_t cand_bytes, blk_bytes, total_bytes;
+};
+ScorePlan plan_score(int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb);
+hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
+                             const uint8_t* scales, const int32_t* q_pos, int32_t* topk,
+                             int32_t* candidates, int B, int T, int H_I, int N_cap, int n_entries,
+                             int m, int k, int hsi, int hsi_s, int hsi_nb, void* workspace,
+                             const ScorePlan& plan, hipStream_t stream);
+
+// ---- sparse attention (k_attn.hip)
+size_t attn_workspace_bytes(int B, int T, int H);
+hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk,
+                              const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos,
+                              void* o, float* lse, int B, int T, int H, int N_cap, int k, int L_w,
+                              int W, float scale, void* workspace, hipStream_t stream);
+
+}  // namespace csa2

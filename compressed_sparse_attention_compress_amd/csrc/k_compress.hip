@@ -1,0 +1,246 @@
+// (a) Compressor: projection GEMM with a fused per-channel group softmax-pool
+// epilogue, then RMSNorm + RoPE.
+//
+// Method ([P1] "DeepSeek-V4.1 模型结构（2）…CSA2 的三种模式", section on the
+// compressor without overlap or position bias; [P4] "CSA2 — l'attention creuse
+// compressée…", table in "Ce qui change par rapport à V4"): C = x W_kv and
+// Z = x W_gate per token; each disjoint group of m tokens is pooled as
+// sum_i softmax_i(Z[:, c]) * C[i, c] per channel c, with no position bias; the
+// entry is RMS-normalised and the last 64 dims are rotated at the position of the
+// group's first token.  m == 1 is the plain projection plus norm.
+//
+// Kernel 1 (compress_gemm_pool): a 128-token x 128-column tile per workgroup,
+// 4 waves of 64x64, MFMA 16x16x32 bf16 (or 8x 16x16x4 fp32), K staged through LDS
+// with a register prefetch of the next K tile.  The 128 columns of a gated tile
+// are 64 channels of C followed, per wave, by the same channels of Z, so each
+// lane holds C and Z of one channel for 4 consecutive tokens and pools groups of
+// 2 or 4 tokens entirely in registers.  Output: the pooled entry in float32.
+// Kernel 2 (compress_finalize): one wave per entry: RMSNorm in float32, write the
+// pre-RoPE latent (float32, in place) and the cache row with RoPE applied.
+#include "csa2_internal.h"
+#include "device_common.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int BM = 128;     // tokens per workgroup tile
+constexpr int BN = 128;     // output columns per workgroup tile
+constexpr int ROWB = 128;   // bytes of K per LDS row per stage
+constexpr int PADB = 16;    // LDS row padding (bytes)
+
+template <typename T>
+struct Tile {
+  static constexpr int BK = ROWB / (int)sizeof(T);               // elements per stage
+  static constexpr int LDK = (ROWB + PADB) / (int)sizeof(T);     // LDS row stride (elements)
+  static constexpr int CHUNK = 16 / (int)sizeof(T);              // elements per 16-B chunk
+  static constexpr int KSTEPS = BK / 32;
+};
+
+template <typename T, int M_RATIO>
+__global__ __launch_bounds__(256) void compress_gemm_pool(
+    const T* __restrict__ x, const T* __restrict__ w_kv, const T* __restrict__ w_gate,
+    float* __restrict__ e_out, int T_len, int D) {
+  typedef Tile<T> TL;
+  typedef typename Frag<T>::type FragT;
+  __shared__ __attribute__((aligned(16))) T As[BM * TL::LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[BN * TL::LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int b = blockIdx.z;
+  const int row0 = blockIdx.x * BM;
+  constexpr bool gated = M_RATIO > 1;
+  constexpr int CH_PER_WG = gated ? 64 : 128;
+  const int ch0 = blockIdx.y * CH_PER_WG;
+
+  const T* xb = x + (size_t)b * T_len * D;
+
+  // source row of B-tile row j (0..127)
+  auto wrow = [&](int j) -> const T* {
+    if (gated) {
+      int wj = j >> 6, jj = j & 63;
+      int ch = ch0 + 32 * wj + (jj & 31);
+      return (jj < 32 ? w_kv : w_gate) + (size_t)ch * D;
+    }
+    return w_kv + (size_t)(ch0 + j) * D;
+  };
+
+  // global -> register staging: 4 A chunks and 4 B chunks of 16 B per thread
+  uint4 ra[4], rb[4];
+  auto load_tiles = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int c = tid + 256 * j;
+      int r = c >> 3, cc = c & 7;
+      int tok = row0 + r;
+      if (tok < T_len)
+        ra[j] = *reinterpret_cast<const uint4*>(xb + (size_t)tok * D + k0 + cc * TL::CHUNK);
+      else
+        ra[j] = make_uint4(0, 0, 0, 0);
+      rb[j] = *reinterpret_cast<const uint4*>(wrow(r) + k0 + cc * TL::CHUNK);
+    }
+  };
+  auto store_tiles = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int c = tid + 256 * j;
+      int r = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&As[r * TL::LDK + cc * TL::CHUNK]) = ra[j];
+      *reinterpret_cast<uint4*>(&Bs[r * TL::LDK + cc * TL::CHUNK]) = rb[j];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = D / TL::BK;
+  load_tiles(0);
+  store_tiles();
+  __syncthreads();
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_tiles((kt + 1) * TL::BK);
+#pragma unroll
+    for (int ks = 0; ks < TL::KSTEPS; ++ks) {
+      FragT a[4], bb[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        a[mt] = load_frag(&As[(wm * 64 + mt * 16 + lr) * TL::LDK + ks * 32 + 8 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bb[nt] = load_frag(&Bs[(wn * 64 + nt * 16 + lr) * TL::LDK + ks * 32 + 8 * lg]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma16(a[mt], bb[nt], acc[mt][nt]);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      store_tiles();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds tokens row0 + wm*64 + mt*16 + 4*lg + i, column l%16 of n-tile nt
+  const int n_entries = T_len / M_RATIO;
+  float* eb = e_out + (size_t)b * n_entries * 512;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int tok0 = row0 + wm * 64 + mt * 16 + 4 * lg;  // first of the lane's 4 tokens
+    if (gated) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int ch = ch0 + 32 * wn + 16 * nt + lr;
+        const f32x4 c = acc[mt][nt], z = acc[mt][nt + 2];
+#pragma unroll
+        for (int g0 = 0; g0 < 4; g0 += M_RATIO) {
+          if (tok0 + g0 >= T_len) continue;
+          float zmax = z[g0];
+#pragma unroll
+          for (int i = 1; i < M_RATIO; ++i) zmax = fmaxf(zmax, z[g0 + i]);
+          float num = 0.f, den = 0.f;
+#pragma unroll
+          for (int i = 0; i < M_RATIO; ++i) {
+            float p = __expf(z[g0 + i] - zmax);
+            den += p;
+            num += p * c[g0 + i];
+          }
+          eb[(size_t)((tok0 + g0) / M_RATIO) * 512 + ch] = num / den;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int ch = ch0 + 64 * wn + 16 * nt + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + i < T_len) eb[(size_t)(tok0 + i) * 512 + ch] = acc[mt][nt][i];
+      }
+    }
+  }
+}
+
+// One wave per entry: RMSNorm, RoPE on dims 448..511, write latent (fp32, in
+// place over the pooled values) and the cache row.
+template <typename T>
+__global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat, const float* __restrict__ gamma,
+                                                         T* __restrict__ kv_cache, int n_entries, int entry0,
+                                                         int m, int N_cap, float eps, double base) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (e >= n_entries) return;
+  float* row = lat + ((size_t)b * n_entries + e) * 512;
+  float v[8];
+  const float4* r4 = reinterpret_cast<const float4*>(row + lane * 8);
+  float4 p0 = r4[0], p1 = r4[1];
+  v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w; v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+  ss = wave_sum_xor(ss, 63);
+  const float rinv = 1.0f / sqrtf(ss * (1.0f / 512.0f) + eps);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma + lane * 8);
+  float4 g0 = g4[0], g1 = g4[1];
+  float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = v[i] * rinv * g[i];
+  float4* w4 = reinterpret_cast<float4*>(row + lane * 8);
+  w4[0] = make_float4(v[0], v[1], v[2], v[3]);
+  w4[1] = make_float4(v[4], v[5], v[6], v[7]);
+  if (lane >= 56) {  // dims 448..511: 4 rotary pairs per lane
+    const int64_t pos = (int64_t)(entry0 + e) * m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pair = (lane - 56) * 4 + j;
+      float c, s;
+      rope_cos_sin(pos, pair, 64, base, c, s);
+      float x0 = v[2 * j], x1 = v[2 * j + 1];
+      v[2 * j] = x0 * c - x1 * s;
+      v[2 * j + 1] = x0 * s + x1 * c;
+    }
+  }
+  T* out = kv_cache + ((size_t)b * N_cap + entry0 + e) * 512 + lane * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = from_f32<T>(v[i]);
+}
+
+template <typename T>
+hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const float* gamma, float* lat,
+                    void* kv, int B, int T_len, int D, int m, int start_pos, int N_cap, float eps,
+                    float base, hipStream_t st) {
+  const int n_entries = T_len / m;
+  if (n_entries == 0 || B == 0) return hipSuccess;
+  dim3 blk(256);
+  dim3 grid((T_len + BM - 1) / BM, m > 1 ? 512 / 64 : 512 / 128, B);
+  const T* xx = static_cast<const T*>(x);
+  const T* wk = static_cast<const T*>(w_kv);
+  const T* wg = static_cast<const T*>(w_gate);
+  if (m == 1) hipLaunchKernelGGL((compress_gemm_pool<T, 1>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+  else if (m == 2) hipLaunchKernelGGL((compress_gemm_pool<T, 2>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+  else hipLaunchKernelGGL((compress_gemm_pool<T, 4>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 g2((n_entries + 3) / 4, B);
+  hipLaunchKernelGGL((compress_finalize<T>), g2, blk, 0, st, lat, gamma, static_cast<T*>(kv), n_entries,
+                     start_pos / m, m, N_cap, eps, (double)base);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const void* w_gate, const float* gamma,
+                           float* latent_pre, void* kv_cache, int B, int T, int D, int m, int start_pos,
+                           int N_cap, float eps, float rope_base, hipStream_t stream) {
+  if (dtype == 1)
+    return launch_t<bf16>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, B, T, D, m, start_pos, N_cap, eps,
+                          rope_base, stream);
+  return launch_t<float>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, B, T, D, m, start_pos, N_cap, eps,
+                         rope_base, stream);
+}
+
+}  // namespace csa2

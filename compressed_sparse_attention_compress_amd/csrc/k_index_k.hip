@@ -1,0 +1,157 @@
+// (b) Index K: 512 -> 128 projection of the pre-RoPE latent, RoPE on its last 64
+// dims at the entry position, FP4 (E2M1) codes with one E4M3 scale per 32 dims.
+//
+// Method ([P1] "DeepSeek-V4.1 模型结构（2）…", section "indexer K 改由 main KV
+// 投影": the projection reads the main-KV entry before its RoPE, index K then gets
+// its own RoPE on the last 64 dims, no Hadamard rotation, FP4 with one scale per
+// 32 dims; [P3] "DeepSeek-V4.1-Flash：把百万 Token 的记忆…", section six: 68 B per
+// entry).  Quantisation of a 32-dim block: scale = E4M3(amax / 6) (round to
+// nearest even, saturating), code_i = E2M1(u_i / scale) (nearest even, saturating,
+// sign kept), all divisions float32 round-to-nearest; a zero scale zeroes the
+// block.  The code of dim 2j is the low nibble of byte j.
+//
+// Kernel: one wave per 16 entries, no LDS.  MFMA with the 16 entries as rows and
+// the 128 output dims as 8 column tiles; the float32 latent is split into a bf16
+// high part and a bf16 remainder (two MFMAs) so bf16 weights lose nothing beyond
+// ~2^-17 relative; fp32 weights use the fp32 MFMA.  The accumulator layout puts
+// the 32 dims of a quantisation block in one 16-lane group (two column tiles),
+// so amax, RoPE pairs and nibble packing are lane shuffles.
+#include "csa2_internal.h"
+#include "device_common.h"
+
+namespace csa2 {
+
+namespace {
+
+__device__ __forceinline__ void split_hi_lo(const f32x8& a, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16 h = (bf16)a.v[i];
+    hi[i] = h;
+    lo[i] = (bf16)(a.v[i] - (float)h);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                      int N, int m, int entry0, int N_cap, double base) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int e0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+  const int b = blockIdx.y;
+  if (e0 >= N) return;
+  const float* lb = lat + (size_t)b * N * 512;
+  const int arow = e0 + lr;
+  f32x4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks = 0; ks < 16; ++ks) {
+    f32x8 a;
+    if (arow < N) a = load_frag(lb + (size_t)arow * 512 + ks * 32 + 8 * lg);
+    else zero_frag(a);
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 hi, lo;
+      split_hi_lo(a, hi, lo);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        bf16x8 bw = load_frag(reinterpret_cast<const bf16*>(w_ik) + (size_t)(nt * 16 + lr) * 512 + ks * 32 + 8 * lg);
+        acc[nt] = mma16(hi, bw, acc[nt]);
+        acc[nt] = mma16(lo, bw, acc[nt]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        f32x8 bw = load_frag(reinterpret_cast<const float*>(w_ik) + (size_t)(nt * 16 + lr) * 512 + ks * 32 + 8 * lg);
+        acc[nt] = mma16(a, bw, acc[nt]);
+      }
+    }
+  }
+
+  // RoPE on dims 64..127 (column tiles 4..7): pair (64+2p, 65+2p) lives in lanes l, l^1
+#pragma unroll
+  for (int nt = 4; nt < 8; ++nt) {
+    const int pair = (nt - 4) * 8 + (lr >> 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * lg + i;
+      float c, s;
+      rope_cos_sin((int64_t)(entry0 + e) * m, pair, 64, base, c, s);
+      float mine = acc[nt][i];
+      float other = __shfl_xor(mine, 1, 64);
+      acc[nt][i] = (lr & 1) ? (other * s + mine * c) : (mine * c - other * s);
+    }
+  }
+
+  // quantise: block q = column tiles 2q, 2q+1; entry 4*lg+i lives in the lane's 16-lane group
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * lg + i;
+      float v0 = acc[2 * q][i], v1 = acc[2 * q + 1][i];
+      float amax = fmaxf(fabsf(v0), fabsf(v1));
+      amax = wave_max_xor(amax, 15);  // within the 16-lane group
+      const uint32_t sb = fp4_scale_byte(amax);
+      const float s = e4m3_decode(sb);
+      const uint32_t c0 = fp4_code(v0, s), c1 = fp4_code(v1, s);
+      const uint32_t o0 = __shfl_xor((int)c0, 1, 64), o1 = __shfl_xor((int)c1, 1, 64);
+      if (e < N) {
+        uint8_t* crow = codes + ((size_t)b * N_cap + entry0 + e) * 64 + 16 * q;
+        if ((lr & 1) == 0) {
+          crow[lr >> 1] = (uint8_t)(c0 | (o0 << 4));
+          crow[8 + (lr >> 1)] = (uint8_t)(c1 | (o1 << 4));
+        }
+        if (lr == 0) scales[((size_t)b * N_cap + entry0 + e) * 4 + q] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// Stand-alone packer: one thread per 32-value block.
+__global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__ rows, int64_t n_blocks,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_blocks) return;
+  const float* src = rows + t * 32;
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    float4 p = *reinterpret_cast<const float4*>(src + i);
+    v[i] = p.x; v[i + 1] = p.y; v[i + 2] = p.z; v[i + 3] = p.w;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(p.x), fabsf(p.y)), fmaxf(fabsf(p.z), fabsf(p.w))));
+  }
+  const uint32_t sb = fp4_scale_byte(amax);
+  const float s = e4m3_decode(sb);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= fp4_code(v[i], s) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(codes + t * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[t] = (uint8_t)sb;
+}
+
+}  // namespace
+
+hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes, uint8_t* scales,
+                          int B, int N, int m, int entry0, int N_cap, float rope_base, hipStream_t stream) {
+  if (N == 0 || B == 0) return hipSuccess;
+  dim3 grid((N + 63) / 64, B), blk(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL((index_k_kernel<bf16>), grid, blk, 0, stream, latent_pre, static_cast<const bf16*>(w_ik),
+                       codes, scales, N, m, entry0, N_cap, (double)rope_base);
+  else
+    hipLaunchKernelGGL((index_k_kernel<float>), grid, blk, 0, stream, latent_pre, static_cast<const float*>(w_ik),
+                       codes, scales, N, m, entry0, N_cap, (double)rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t nb = n_rows * 4;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp4_pack_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, rows, nb, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,147 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+host-side validation rejects bad calls before anything is enqueued (no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_compress_amd import csa2 as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = K.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) <= set(K.EXPORTS), set(names) - set(K.EXPORTS)
+    assert K.version().startswith("csa2-mi355x")
+
+
+def test_status_strings():
+    L = K.lib()
+    for s in range(9):
+        assert L.csa2_status_string(s)
+
+
+def test_runtime_slots_start_empty_and_reset():
+    rt = K.Runtime()
+    for s in range(4):
+        info = rt.slot(s)
+        assert info.filled == 0 and info.generation == 0
+    rt.reset()
+    with pytest.raises(K.CSA2Error) as e:
+        rt.slot(7)
+    assert e.value.name == "CSA2_ERR_INVALID_ARG"
+    rt.close()
+
+
+def _fake(addr=0x1000):
+    class P:  # stands in for a tensor in pointer-only argument structs
+        pass
+    return addr
+
+
+def test_reuse_before_full_is_slot_empty():
+    rt = K.Runtime()
+    cfg = K.layer_cfg(K.REUSE, K.CSA2_BF16, m=2, k=512, W=128, H_I=32, H=64)
+    io = K.LayerIO(B=1, T=1, L_w=128, q_pos=0x1000, q=0x1000, swa_kv=0x1000, swa_pos0=0x1000, o=0x1000)
+    st = K.lib().csa2_layer_forward(rt.handle, C.byref(cfg), C.byref(io), None)
+    assert K.STATUS[st] == "CSA2_ERR_SLOT_EMPTY"
+    assert b"compress_kv" in K.lib().csa2_last_error()
+    cfg.mode = K.REINDEX
+    st = K.lib().csa2_layer_forward(rt.handle, C.byref(cfg), C.byref(io), None)
+    assert K.STATUS[st] == "CSA2_ERR_SLOT_EMPTY"
+
+
+def test_score_reindex_without_index_slot():
+    rt = K.Runtime()
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=10, n_entries=10, m=1, k=4, q_idx=0x1000, w=0x1000,
+                        q_pos=0x1000, topk=0x1000, workspace=0x1000, workspace_bytes=1 << 20)
+    st = K.lib().csa2_score_topk(rt.handle, C.byref(a), None)
+    assert K.STATUS[st] == "CSA2_ERR_SLOT_EMPTY"
+    st = K.lib().csa2_score_topk(None, C.byref(a), None)
+    assert K.STATUS[st] == "CSA2_ERR_INVALID_ARG"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("m", 3, "CSA2_ERR_INVALID_ARG"),
+    ("w_gate", 0x1000, "CSA2_ERR_INVALID_ARG"),    # m == 1 must not have a gate
+    ("T", 7, "CSA2_ERR_SHAPE"),
+    ("D", 100, "CSA2_ERR_SHAPE"),
+    ("N_cap", 3, "CSA2_ERR_SHAPE"),
+    ("dtype", 9, "CSA2_ERR_DTYPE"),
+    ("x", None, "CSA2_ERR_INVALID_ARG"),
+])
+def test_compress_validation(field, value, status):
+    a = K.CompressArgs(dtype=1, B=1, T=8, D=64, m=1, start_pos=0, N_cap=8, eps=1e-6, rope_base=1e4, x=0x1000,
+                       w_kv=0x1000, w_gate=None, gamma=0x1000, latent_pre=0x1000, kv_cache=0x1000)
+    if field == "T":
+        a.m, a.w_gate = 2, 0x1000
+    setattr(a, field, value)
+    st = K.lib().csa2_compress(None, C.byref(a), None)
+    assert K.STATUS[st] == status, K.lib().csa2_last_error()
+
+
+def test_compress_gated_needs_gate():
+    a = K.CompressArgs(dtype=1, B=1, T=8, D=64, m=2, start_pos=0, N_cap=8, eps=1e-6, rope_base=1e4, x=0x1000,
+                       w_kv=0x1000, w_gate=None, gamma=0x1000, latent_pre=0x1000, kv_cache=0x1000)
+    assert K.STATUS[K.lib().csa2_compress(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"
+
+
+def test_score_workspace_too_small():
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, q_idx=0x1000,
+                        w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1000,
+                        workspace_bytes=16)
+    st = K.lib().csa2_score_topk(None, C.byref(a), None)
+    assert K.STATUS[st] == "CSA2_ERR_WORKSPACE"
+    n = C.c_size_t()
+    assert K.lib().csa2_workspace_size(K.OP_SCORE_TOPK, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
+    assert n.value > 512 * 8
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("H_I", 33, "CSA2_ERR_SHAPE"), ("k", 0, "CSA2_ERR_SHAPE"), ("k", 2000, "CSA2_ERR_SHAPE"),
+    ("n_entries", 5000, "CSA2_ERR_SHAPE"), ("hsi", 5, "CSA2_ERR_INVALID_ARG"),
+])
+def test_score_validation(field, value, status):
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, q_idx=0x1000,
+                        w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1000,
+                        workspace_bytes=1 << 30)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_score_topk(None, C.byref(a), None)] == status
+
+
+def test_hsi_use_needs_candidates():
+    rt = K.Runtime()
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, hsi=K.HSI_USE,
+                        hsi_s=64, hsi_nb=256, q_idx=0x1000, w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000,
+                        topk=0x1000, workspace=0x1000, workspace_bytes=1 << 30)
+    assert K.STATUS[K.lib().csa2_score_topk(rt.handle, C.byref(a), None)] == "CSA2_ERR_SLOT_EMPTY"
+    a.hsi_s = 48
+    assert K.STATUS[K.lib().csa2_score_topk(rt.handle, C.byref(a), None)] == "CSA2_ERR_SHAPE"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("H", 65, "CSA2_ERR_SHAPE"), ("W", 0, "CSA2_ERR_SHAPE"), ("k", 1100, "CSA2_ERR_SHAPE"),
+    ("q", None, "CSA2_ERR_INVALID_ARG"), ("kv", None, "CSA2_ERR_INVALID_ARG"),
+])
+def test_attn_validation(field, value, status):
+    a = K.SparseAttnArgs(dtype=1, B=1, T=1, H=64, N_cap=100, k=512, L_w=128, W=128, q=0x1000, kv=0x1000,
+                         topk=0x1000, swa_kv=0x1000, swa_pos0=0x1000, q_pos=0x1000, o=0x1000)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_sparse_attn(None, C.byref(a), None)] == status
+
+
+def test_fp4_pack_zero_rows_is_noop():
+    assert K.lib().csa2_fp4_pack(None, 0, None, None, None) == 0
+    assert K.STATUS[K.lib().csa2_fp4_pack(None, 5, None, None, None)] == "CSA2_ERR_INVALID_ARG"
