@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 layer hot path on one MI355X.
+
+Headline (the `value` of the JSON line): encoder Full-layer prefill throughput in
+tokens/s -- one step = compressor + index K + score/top-k + sparse attention over
+one batch (B=1, L=8192, hidden 4096, m=2, 32x128 FP4 indexer heads, top-512, window
+128, 64 heads, bf16 in / fp32 accumulate).  A second record ("decode") times the
+batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries).
+
+Every input is seeded synthetic data already resident in HBM when timing starts.
+Per-kernel times come from HIP events recorded on the stream the library launches
+on (torch's current stream).  The CPU oracle is timed on a bounded sample of the
+same workload on this host (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+
+METRIC = "CSA2 layer prefill tokens/s + decode µs/step; % HBM/MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- C2
+
+class PrefillBench:
+    """Encoder Full-layer prefill (B=1, L=8192, D=4096, m=2)."""
+
+    def __init__(self, torch, K, synth, L=8192, D=4096, m=2, H_I=32, k=512, W=128, H=64, B=1):
+        self.t, self.K = torch, K
+        self.shape = synth.LayerShape(B=B, L=L, D=D, m=m, H_I=H_I, k=k, W=W, H=H)
+        s = self.shape
+        dev = "cuda"
+        self.inp = synth.full_layer_inputs(s, seed=0, dtype=torch.bfloat16, device=dev, layer=0,
+                                           w_from_linear=True)
+        self.N = L // m
+        self.lat = torch.empty(B, self.N, 512, dtype=torch.float32, device=dev)
+        self.kv = torch.empty(B, self.N, 512, dtype=torch.bfloat16, device=dev)
+        self.codes = torch.empty(B, self.N, 64, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(B, self.N, 4, dtype=torch.uint8, device=dev)
+        self.topk = torch.empty(B, L, k, dtype=torch.int32, device=dev)
+        self.o = torch.empty_like(self.inp["q"])
+        nb = K.score_topk_workspace_bytes(q_idx=self.inp["q_idx"], w=self.inp["w"], codes=self.codes,
+                                          scales=self.scales, q_pos=self.inp["q_pos"], topk=self.topk,
+                                          n_entries=self.N, m=m, k=k, N_cap=self.N)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.ev = None
+
+    def step(self, events=None):
+        K, i, s = self.K, self.inp, self.shape
+        if events is not None:
+            events[0].record()
+        K.csa2_compress(None, i["x"], i["w_kv"], i["w_gate"], i["gamma"], self.lat, self.kv, m=s.m)
+        if events is not None:
+            events[1].record()
+        K.csa2_index_k(None, self.lat, i["w_ik"], self.codes, self.scales, m=s.m)
+        if events is not None:
+            events[2].record()
+        K.csa2_score_topk(None, i["q_idx"], i["w"], self.codes, self.scales, i["q_pos"], self.topk,
+                          n_entries=self.N, m=s.m, k=s.k, workspace=self.ws)
+        if events is not None:
+            events[3].record()
+        K.csa2_sparse_attn(None, i["q"], self.kv, self.topk, i["swa_kv"], i["swa_pos0"], i["q_pos"], self.o, W=s.W)
+        if events is not None:
+            events[4].record()
+
+    # algorithmic work of each stage for this workload
+    def work(self):
+        s = self.shape
+        L, m, k, W, H = s.L, s.m, s.k, s.W, s.H
+        n_t = [(t + 1) // m for t in range(L)]
+        pairs = sum(n_t)
+        rows = sum(min(k, n) + min(W, t + 1) for t, n in enumerate(n_t))
+        g = 1 if m == 1 else 2
+        return {
+            "compress": {"flop": 2.0 * s.B * L * s.D * 512 * g},
+            "index_k": {"flop": 2.0 * s.B * self.N * 512 * 128},
+            "score_topk": {"flop": 2.0 * s.B * pairs * s.H_I * 128, "pairs": s.B * pairs},
+            "sparse_attn": {"flop": 4.0 * s.B * rows * H * 512, "rows": s.B * rows},
+        }
+
+
+# --------------------------------------------------------------------------- C4
+
+class DecodeBench:
+    """Batched decode step, Reindex + Reuse: 64 sequences x 131072 m=2 entries."""
+
+    def __init__(self, torch, K, synth, B=64, n_entries=131072, m=2, H_I=32, k=512, W=128, H=64):
+        self.t, self.K = torch, K
+        dev = "cuda"
+        self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        self.codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
+        for b in range(B):  # index K: N(0,1) rows packed by the (bit-exact) FP4 packer
+            u = torch.randn(n_entries, 128, generator=g, device=dev, dtype=torch.float32)
+            K.csa2_fp4_pack(u, self.codes[b], self.scales[b])
+        del u
+        p = n_entries * m - 1  # newest token; all entries visible
+        self.q_pos = torch.full((B, 1), p, dtype=torch.int32, device=dev)
+        self.swa_pos0 = torch.full((B,), p - W + 1, dtype=torch.int32, device=dev)
+        self.layers = [synth.decode_query_inputs(B, H, H_I, W, seed=0, layer=l, dtype=torch.bfloat16, device=dev)
+                       for l in range(2)]
+        self.topk = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+        self.o = [torch.empty_like(self.layers[l]["q"]) for l in range(2)]
+        nb = K.score_topk_workspace_bytes(q_idx=self.layers[0]["q_idx"], w=self.layers[0]["w"], codes=self.codes,
+                                          scales=self.scales, q_pos=self.q_pos, topk=self.topk, n_entries=n_entries,
+                                          m=m, k=k, N_cap=n_entries)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        K = self.K
+        r, u = self.layers
+        if events is not None:
+            events[0].record()
+        K.csa2_score_topk(None, r["q_idx"], r["w"], self.codes, self.scales, self.q_pos, self.topk,
+                          n_entries=self.N, m=self.m, k=self.k, workspace=self.ws)
+        if events is not None:
+            events[1].record()
+        K.csa2_sparse_attn(None, r["q"], self.kv, self.topk, r["swa_kv"], self.swa_pos0, self.q_pos, self.o[0],
+                           W=self.W)
+        if events is not None:
+            events[2].record()
+        K.csa2_sparse_attn(None, u["q"], self.kv, self.topk, u["swa_kv"], self.swa_pos0, self.q_pos, self.o[1],
+                           W=self.W)
+        if events is not None:
+            events[3].record()
+
+    def work(self):
+        B, N = self.B, self.N
+        rows = B * (min(self.k, N) + self.W)
+        return {
+            "score_topk": {"bytes": 68.0 * B * N + B * self.H_I * (128 * 2 + 4) + B * self.k * 4,
+                           "flop": 2.0 * B * N * self.H_I * 128},
+            "sparse_attn": {"bytes": rows * 1024.0 + 2.0 * B * self.H * 512 * 2,
+                            "flop": 4.0 * rows * self.H * 512},
+        }
+
+
+def time_steps(torch, bench, n_stages, steps, warmup):
+    for _ in range(warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stages + 1)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        bench.step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    per_stage = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)) / steps for j in range(n_stages)]
+    return total_ms / steps, per_stage
+
+
+def kernel_src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        p = os.path.join(ROOT, "compressed_sparse_attention_compress_amd", "csrc", n)
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, src_files):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, or None when
+    the kernel source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d.get(kernel)
+        if not e or e.get("src_hash") != kernel_src_hash(src_files):
+            return None
+        return e.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+# -------------------------------------------------------------- CPU baseline
+
+def cpu_baseline_prefill(bench, sample_every=32):
+    """Oracle on this host: compressor + index K over all tokens, score/top-k and
+    attention on every `sample_every`-th query; extrapolated work-proportionally."""
+    import numpy as np
+    from oracle import csa2_oracle as O
+    t = bench.t
+    s, i = bench.shape, bench.inp
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count() or 1
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    x = f64(i["x"][0])
+    w_kv, w_gate, gamma, w_ik = f64(i["w_kv"]), f64(i["w_gate"]), f64(i["gamma"]), f64(i["w_ik"])
+    t0 = time.perf_counter()
+    lat, kv, ids = O.compress(x, w_kv, w_gate, gamma, s.m, 0)
+    _, codes, scales = O.index_k(lat, w_ik, ids * s.m)
+    t_build = time.perf_counter() - t0
+    sample = list(range(sample_every - 1, s.L, sample_every))
+    kd = O.fp4_unpack(codes, scales)
+    qi = f64(i["q_idx"][0, sample])
+    ww = f64(i["w"][0, sample])
+    qq = f64(i["q"][0, sample])
+    sw = f64(i["swa_kv"][0])
+    t1 = time.perf_counter()
+    for j, tok in enumerate(sample):
+        nv = O.visible_entries(tok, s.m)
+        sc = O.index_scores(qi[j], ww[j], kd, nv)
+        sel = O.topk_select(sc, s.k)
+        O.sparse_attention(qq[j], kv, sel, sw, 0, tok, s.W)
+    t_q = time.perf_counter() - t1
+    total = t_build + t_q * (s.L / len(sample))
+    return {"value": s.B * s.L / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"compressor + index K on all {s.L} tokens ({t_build:.1f} s), score + top-k + attention on "
+                       f"every {sample_every}th query ({len(sample)} queries, {t_q:.1f} s) extrapolated x"
+                       f"{s.L / len(sample):.0f}; numpy float64, BLAS threads = {cores}"),
+            "measured_s": round(t_build + t_q, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode record")
+    ap.add_argument("--decode-seqs", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path shards by sequence; see DESIGN.md); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from compressed_sparse_attention_compress_amd import csa2 as K
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    K.lib()
+
+    log("prefill: building inputs")
+    pb = PrefillBench(torch, K, synth)
+    log("prefill: timing")
+    ms, stages = time_steps(torch, pb, 4, args.steps, args.warmup)
+    work = pb.work()
+    names = ["compress", "index_k", "score_topk", "sparse_attn"]
+    stage_rec = {}
+    for n, t_ms in zip(names, stages):
+        w = work[n]
+        rec = {"ms": round(t_ms, 4), "tflops": round(w["flop"] / (t_ms * 1e-3) / 1e12, 2),
+               "mfma_frac": round(w["flop"] / (t_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        stage_rec[n] = rec
+    dom = max(names, key=lambda n: stage_rec[n]["ms"])
+    dom_files = {"compress": ["k_compress.hip"], "index_k": ["k_index_k.hip"], "score_topk": ["k_score.hip"],
+                 "sparse_attn": ["k_attn.hip"]}[dom]
+    achieved = work[dom]["flop"] / (stage_rec[dom]["ms"] * 1e-3) / 1e12
+    tokens = pb.shape.B * pb.shape.L
+    value = tokens / (ms * 1e-3)
+    total_flop = sum(w["flop"] for w in work.values())
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "encoder Full-layer prefill: B=1, L=8192, hidden 4096, m=2 (4096 entries), latent 512, "
+                               "indexer 32x128 FP4 (E4M3 scale / 32 dims), top-512, SWA 128, 64 heads x 512",
+                   "global_batch": tokens, "seq_len": pb.shape.L, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for(dom, dom_files)},
+        "stages": stage_rec,
+        "step_tflops": round(total_flop / (ms * 1e-3) / 1e12, 2),
+    }
+    if not args.no_decode:
+        del pb
+        torch.cuda.empty_cache()
+        log("decode: building caches")
+        db = DecodeBench(torch, K, synth, B=args.decode_seqs)
+        log("decode: timing")
+        dms, dst = time_steps(torch, db, 3, max(args.steps, 20), args.warmup)
+        dw = db.work()
+        sc_gbs = dw["score_topk"]["bytes"] / (dst[0] * 1e-3) / 1e9
+        attn_gbs = (dw["sparse_attn"]["bytes"] * 2) / ((dst[1] + dst[2]) * 1e-3) / 1e9
+        step_bytes = dw["score_topk"]["bytes"] + 2 * dw["sparse_attn"]["bytes"]
+        out["decode"] = {
+            "workload": f"batched decode, Reindex + Reuse: {db.B} sequences x {db.N} m=2 entries (262144-token "
+                        f"context), bf16 latent, FP4 index K, 32x128 indexer heads, top-512, SWA 128, 64 heads",
+            "us_per_step": round(dms * 1e3, 2),
+            "stages_us": {"score_topk": round(dst[0] * 1e3, 2), "attn_reindex": round(dst[1] * 1e3, 2),
+                          "attn_reuse": round(dst[2] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "kernel": "score_topk", "achieved": round(sc_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(sc_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for("score_topk_decode", ["k_score.hip"])},
+            "attn_GBps": round(attn_gbs, 1),
+            "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (dms * 1e-3), 4),
+        }
+        del db
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("cpu baseline: oracle on a bounded sample")
+        pb2 = PrefillBench(torch, K, synth)
+        out["cpu_baseline"] = cpu_baseline_prefill(pb2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
