@@ -123,6 +123,8 @@ class DecodeBench:
                                           scales=self.scales, q_pos=self.q_pos, topk=self.topk, n_entries=n_entries,
                                           m=m, k=k, N_cap=n_entries)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W)
+        self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def step(self, events=None):
@@ -135,11 +137,11 @@ class DecodeBench:
         if events is not None:
             events[1].record()
         K.csa2_sparse_attn(None, r["q"], self.kv, self.topk, r["swa_kv"], self.swa_pos0, self.q_pos, self.o[0],
-                           W=self.W)
+                           W=self.W, workspace=self.ws_attn)
         if events is not None:
             events[2].record()
         K.csa2_sparse_attn(None, u["q"], self.kv, self.topk, u["swa_kv"], self.swa_pos0, self.q_pos, self.o[1],
-                           W=self.W)
+                           W=self.W, workspace=self.ws_attn)
         if events is not None:
             events[3].record()
 

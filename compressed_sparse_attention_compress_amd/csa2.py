@@ -229,18 +229,39 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
     return workspace
 
 
-def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Optional[int] = None,
-                     N_cap: Optional[int] = None, scale: float = 0.0, lse=None, stream=None):
-    """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots."""
+def sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: int, N_cap: int, scale: float = 0.0,
+                     lse=None, workspace=None):
     B, T, H, _ = q.shape
+    return SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, N_cap=N_cap, k=k, L_w=swa_kv.shape[1], W=W, scale=scale,
+                          q=_ptr(q), kv=_ptr(kv), topk=_ptr(topk), swa_kv=_ptr(swa_kv), swa_pos0=_ptr(swa_pos0),
+                          q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=_ptr(workspace),
+                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def sparse_attn_workspace_bytes(q, k: int, W: int) -> int:
+    B, T, H, _ = q.shape
+    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, k=k, W=W)
+    n = C.c_size_t()
+    _check(lib().csa2_workspace_size(OP_SPARSE_ATTN, C.cast(C.byref(a), vp), None, C.byref(n)))
+    return n.value
+
+
+def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Optional[int] = None,
+                     N_cap: Optional[int] = None, scale: float = 0.0, lse=None, workspace=None, stream=None):
+    """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots.  A
+    workspace (row-split partials for few-query calls) is allocated when needed
+    and none is given."""
     if k is None:
         k = topk.shape[-1]
     if N_cap is None:
         N_cap = kv.shape[1] if kv is not None else 0
-    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, N_cap=N_cap, k=k, L_w=swa_kv.shape[1], W=W, scale=scale,
-                       q=_ptr(q), kv=_ptr(kv), topk=_ptr(topk), swa_kv=_ptr(swa_kv), swa_pos0=_ptr(swa_pos0),
-                       q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=None, workspace_bytes=0)
+    if workspace is None:
+        nbytes = sparse_attn_workspace_bytes(q, k, W)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace)
     _check(lib().csa2_sparse_attn(_rt(rt), C.byref(a), _stream(stream)))
+    return workspace
 
 
 def csa2_fp4_pack(rows, codes, scales, stream=None):

@@ -275,8 +275,11 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
   csa2_status s = resolve_attn(rt, a);
   if (s != CSA2_OK) return s;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / std::sqrt(512.0f);
+  const csa2::AttnPlan plan = csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W);
+  REQ(plan.ws_bytes == 0 || (a.workspace != nullptr && a.workspace_bytes >= plan.ws_bytes), CSA2_ERR_WORKSPACE,
+      "csa2_sparse_attn: workspace of %zu bytes needed (got %zu)", plan.ws_bytes, a.workspace_bytes);
   hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse, a.B,
-                                          a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, st(stream));
+                                          a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan, st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_sparse_attn launch");
   return ok();
 }
@@ -290,13 +293,13 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
     const csa2_sparse_attn_args* a = static_cast<const csa2_sparse_attn_args*>(args);
-    *bytes = csa2::attn_workspace_bytes(a->B, a->T, a->H);
+    *bytes = csa2::plan_attn(a->dtype, a->B, a->T, a->H, a->k, a->W).ws_bytes;
     return ok();
   }
   if (op == CSA2_OP_LAYER) {
     REQ(cfg, CSA2_ERR_INVALID_ARG, "csa2_workspace_size: layer op needs cfg");
     const csa2_layer_io* io = static_cast<const csa2_layer_io*>(args);
-    size_t need = csa2::attn_workspace_bytes(io->B, io->T, cfg->H);
+    size_t need = csa2::plan_attn(cfg->dtype, io->B, io->T, cfg->H, cfg->k, cfg->W).ws_bytes;
     if (cfg->mode != CSA2_REUSE) {
       const int n_entries = io->N_cap;  // upper bound
       const int scan = cfg->hsi == CSA2_HSI_USE ? cfg->hsi_nb * cfg->hsi_s : n_entries;

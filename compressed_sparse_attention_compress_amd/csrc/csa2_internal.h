@@ -36,10 +36,15 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
                              const ScorePlan& plan, hipStream_t stream);
 
 // ---- sparse attention (k_attn.hip)
-size_t attn_workspace_bytes(int B, int T, int H);
+struct AttnPlan {
+  bool decode;      // few queries: workgroup per (query, split, head group)
+  int n_splits;     // row splits per query (decode only)
+  size_t ws_bytes;  // float32 partials when n_splits > 1
+};
+AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W);
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk,
                               const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos,
                               void* o, float* lse, int B, int T, int H, int N_cap, int k, int L_w,
-                              int W, float scale, void* workspace, hipStream_t stream);
+                              int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream);
 
 }  // namespace csa2
