@@ -14,7 +14,7 @@
 #include <cstring>
 #include <new>
 
-#include "../../include/csa2.h"
+#include "csa2.h"
 #include "csa2_internal.h"
 
 struct csa2_runtime {

@@ -57,6 +57,15 @@ __device__ __forceinline__ v4s tr_read(const lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
 }
 
+// Rows live in LDS as 64 units of 16 B with the unit index XOR-swizzled by
+// swz(row & 15), a bijection on 4 bits chosen so that both read patterns are
+// free of bank conflicts: 16 lanes reading one 16-B unit of 16 consecutive rows
+// (ds_read_b128) hit 16 different units, and the transposed reads (4 rows x two
+// 16-B units per 16-lane group, two groups at a time) hit 16 different units.
+// The DMA writes lane i's 16 B to unit i, so lane i fetches logical unit
+// i ^ swz(row) from global memory.
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 3) | ((r & 3) << 1) | ((r >> 3) & 1); }
+
 // Row list of one query: valid selected ids (order kept), then window rows
 // encoded as -(j+1) for swa row j.  Returns the number of rows.  Needs a
 // __syncthreads() before use by other waves (done by the callers).
@@ -97,7 +106,8 @@ __device__ __forceinline__ const T* row_ptr(int id, const T* kvb, const T* swb) 
 // ----------------------------------------------------------------- prefill
 
 constexpr int PRC = 32;                 // rows per chunk
-constexpr int PRS = 1024 + 16;          // LDS row stride (bytes) for bf16 rows
+constexpr int PRS = 1024;               // LDS row stride (bytes) for bf16 rows (swizzled, no padding)
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind before rescaling
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
@@ -132,6 +142,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
   for (int dt = 0; dt < 32; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // per-lane swizzled byte offsets (within a 256-B group of 16 units)
+  int soff[4], toff[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) soff[b] = ((4 * b + lg) ^ swz(lr)) << 4;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) toff[b] = ((2 * b + ((lr & 3) >> 1)) ^ swz(4 * lg + (lr >> 2))) << 4;
+
   const int nch = (n_rows + PRC - 1) / PRC;
   const int rows_per_wave = PRC / nw;   // nw in {1, 2, 4}: 32, 16, 8 loads per wave per chunk
   // every wave issues exactly rows_per_wave loads per chunk; rows past the end
@@ -142,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
       const int r = c * PRC + rr;
       const int id = rowlist[r < n_rows ? r : 0];
       const bf16* src = row_ptr(id, kvb, swb);
-      dma16(reinterpret_cast<const unsigned char*>(src) + lane * 16, (lds_u8*)(buf + rr * PRS));
+      dma16(reinterpret_cast<const unsigned char*>(src) + ((lane ^ swz(rr & 15)) << 4), (lds_u8*)(buf + rr * PRS));
     }
   };
   auto step = [&](int c, unsigned char* cur, unsigned char* nxt) {
@@ -157,18 +174,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
     __builtin_amdgcn_s_barrier();
     const lds_u8* lcur = (const lds_u8*)cur;
 
-    // ---- S^T = R Q^T
+    // ---- S^T = R Q^T; k-step ks = 4a + b reads unit 16a + ((4b + lg) ^ swz(lr))
     f32x4 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const unsigned char* srow = cur + (mt * 16 + lr) * PRS;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + (mt * 16 + lr) * PRS + (ks * 32 + 8 * lg) * 2);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(srow + soff[ks & 3] + (ks >> 2) * 256);
         s[mt] = mma16(a, qf[ks], s[mt]);
       }
     }
-    // ---- online softmax
+    // ---- online softmax; the running max is only moved (and the output
+    // rescaled) when it would grow by more than RESCALE_SLACK, so exp2 values stay
+    // below 2^RESCALE_SLACK and most chunks skip the rescale
     float x[8];
     float cmax = -INFINITY;
 #pragma unroll
@@ -182,28 +202,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
       }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = exp2f(m_run - m_new);
+    const bool grow = cmax > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? cmax : m_run;
+      const float alpha = grow ? exp2f(m_run - m_new) : 1.0f;  // 0 on the first chunk
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     bf16x8 pf;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pv = exp2f(x[i] - m_new);
+      const float pv = exp2f(x[i] - m_run);
       psum += pv;
       pf[i] = (bf16)pv;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
     // ---- O^T += R^T P^T: A operand via transposed reads of rows 4g.. and 16+4g..
-    const lds_u8* tb = lcur + (4 * lg + (lr >> 2)) * PRS + 4 * (lr & 3) * 2;
+    // lane's rows 4g + lr/4 (and +16; same swizzle); dim tile dt = 8a + b reads
+    // unit 16a + ((2b + (lr&3)/2) ^ swz(row)), half lr&1
+    const lds_u8* tb = lcur + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const v4s lo = tr_read(tb + dt * 32);
-      const v4s hi = tr_read(tb + 16 * PRS + dt * 32);
+      const int unit = toff[dt & 7] + (dt >> 3) * 256;
+      const v4s lo = tr_read(tb + unit);
+      const v4s hi = tr_read(tb + 16 * PRS + unit);
       bf16x8 a;
       __builtin_memcpy(&a, &lo, 8);
       __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
-      oacc[dt] = mma16(a, pf, oacc[dt] * alpha);
+      oacc[dt] = mma16(a, pf, oacc[dt]);
     }
     WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
@@ -238,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
 // ----------------------------------------------------------------- decode
 
 constexpr int DRC = 16;                 // rows per chunk (per wave)
-constexpr int DRS = 1024 + 16;
+constexpr int DRS = 1024;               // swizzled rows, no padding
 
 // grid.x = 32 * ceil(groups / 8), group = (query, split); block id ->
 // (group, head group) so that the 4 head groups of a group share block id mod 8.
@@ -280,6 +309,11 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
   for (int dt = 0; dt < 32; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  int soff[4], toff[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) soff[b] = ((4 * b + lg) ^ swz(lr)) << 4;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) toff[b] = ((2 * b + ((lr & 3) >> 1)) ^ swz(4 * lg + (lr >> 2))) << 4;
   // this split's range of 64-row chunks; wave w owns rows 16w..16w+15 of each
   const int nch_all = (n_rows + 4 * DRC - 1) / (4 * DRC);
   const int c0 = (int)(((long long)nch_all * split) / n_splits);
@@ -293,7 +327,8 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
     for (int rr = 0; rr < drc_rt; ++rr) {
       const int r = c * 4 * DRC + wave * DRC + rr;
       const int rid = rowlist[r < n_rows ? r : 0];
-      dma16(reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb)) + lane * 16, (lds_u8*)(buf + rr * DRS));
+      dma16(reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb)) + ((lane ^ swz(rr)) << 4),
+            (lds_u8*)(buf + rr * DRS));
     }
   };
   auto step = [&](int c, unsigned char* cur, unsigned char* nxt) {
@@ -308,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + lr * DRS + (ks * 32 + 8 * lg) * 2);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + lr * DRS + soff[ks & 3] + (ks >> 2) * 256);
       s = mma16(a, qf[ks], s);
     }
     float x[4];
@@ -321,9 +356,16 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const bool grow = cmax > m_run + RESCALE_SLACK;   // false while cmax = -inf
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? cmax : m_run;
+      const float alpha = grow ? exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
     float psum = 0.f;
     v4s pf;
 #pragma unroll
@@ -333,13 +375,12 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
       bf16 hb = (bf16)pv;
       __builtin_memcpy(reinterpret_cast<char*>(&pf) + 2 * i, &hb, 2);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const lds_u8* tb = (const lds_u8*)cur + (4 * lg + (lr >> 2)) * DRS + 4 * (lr & 3) * 2;
+    l_run += psum;
+    const lds_u8* tb = (const lds_u8*)cur + (4 * lg + (lr >> 2)) * DRS + 8 * (lr & 1);
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const v4s a = tr_read(tb + dt * 32);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pf, oacc[dt] * alpha, 0, 0, 0);
+      const v4s a = tr_read(tb + toff[dt & 7] + (dt >> 3) * 256);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pf, oacc[dt], 0, 0, 0);
     }
     WAIT_LGKM0();
   };
