@@ -37,9 +37,14 @@ def _hipcc():
     return h
 
 
+# per-source extra flags: the scorer post-processes every MFMA result with VALU
+# code, so its accumulators are kept in VGPRs instead of AGPRs
+EXTRA = {"k_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

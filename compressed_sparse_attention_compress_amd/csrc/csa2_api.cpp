@@ -104,6 +104,7 @@ csa2_status resolve_score(const csa2_runtime* rt, csa2_score_topk_args& a) {
   REQ(a.B >= 0 && a.T >= 0, CSA2_ERR_SHAPE, "csa2_score_topk: bad B/T");
   REQ(a.H_I >= 1 && a.H_I <= 32, CSA2_ERR_SHAPE, "csa2_score_topk: H_I must be in [1, 32] (got %d)", a.H_I);
   REQ(a.m >= 1, CSA2_ERR_INVALID_ARG, "csa2_score_topk: m must be >= 1");
+  REQ(a.N_cap >= 1, CSA2_ERR_SHAPE, "csa2_score_topk: N_cap must be >= 1");
   REQ(a.k >= 1 && a.k <= CSA2_MAX_TOPK, CSA2_ERR_SHAPE, "csa2_score_topk: k must be in [1, %d]", CSA2_MAX_TOPK);
   REQ(a.hsi >= CSA2_HSI_NONE && a.hsi <= CSA2_HSI_USE, CSA2_ERR_INVALID_ARG, "csa2_score_topk: bad hsi mode");
   if (a.hsi != CSA2_HSI_NONE) {

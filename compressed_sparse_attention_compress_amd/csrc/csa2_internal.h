@@ -26,7 +26,7 @@ struct ScorePlan {
   int chunk;        // entries per chunk (power of two)
   int n_chunks;     // chunks per query
   int k_chunk;      // candidates kept per chunk = min(k, chunk)
-  size_t cand_bytes, blk_bytes, total_bytes;
+  size_t cand_bytes, lb_bytes, blk_bytes, total_bytes;
 };
 ScorePlan plan_score(int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb);
 hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
