@@ -249,9 +249,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode record")
     ap.add_argument("--decode-seqs", type=int, default=64)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB device-to-device once (a plain copy "
+                         "kernel of known size, used to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the path shards by sequence; see DESIGN.md); got --gpus "
+        print(f"bench.py measures one GPU only (the path shards by sequence across GPUs, with no cross-GPU traffic on the hot path); got --gpus "
               f"{args.gpus}", file=sys.stderr)
         sys.exit(2)
 
@@ -262,6 +265,15 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     K.lib()
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
+        del src, dst
 
     log("prefill: building inputs")
     pb = PrefillBench(torch, K, synth)
