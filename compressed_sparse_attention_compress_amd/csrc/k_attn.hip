@@ -7,20 +7,21 @@
 // serves as key and value; [P3] "…分级缓存", section four: p_j proportional to
 // exp(c_j . q / sqrt(d)), o = sum_j p_j c_j).
 //
-// Both kernels list the token's rows once (selected entries, then window
-// positions) and stream them through LDS with direct global->LDS loads
-// (global_load_lds_dwordx4: one wave instruction moves one 1 KB bf16 row),
-// double-buffered so the next chunk is in flight while the current one is used.
-// S^T = R Q^T has cache rows as MFMA rows and 16 heads as columns; its
-// accumulator already is the P^T operand of O^T = R^T P^T once the k-slots of
-// the PV step are numbered (row 4g+i of tile 0, row 4g+i of tile 1) for lane
-// group g.  The R^T operand is read from the row-major LDS copy with
-// ds_read_b64_tr_b16 (each 16-lane group transposes 4 rows x 16 dims), so no
-// transposed copy is stored.  Online softmax in base 2, float32 throughout; each
-// lane owns one head, so running max, sum and rescale are per-lane scalars.
+// The rows of a token (selected entries, then window positions) are streamed
+// through LDS with direct global->LDS loads (global_load_lds_dwordx4: one wave
+// instruction moves one 1 KB bf16 row), double-buffered so the next chunk is in
+// flight while the current one is used.  S^T = R Q^T has cache rows as MFMA rows
+// and 16 heads as columns; its accumulator already is the P^T operand of
+// O^T = R^T P^T once the k-slots of the PV step are numbered (row 4g+i of tile 0,
+// row 4g+i of tile 1) for lane group g.  The R^T operand is read from the
+// row-major LDS copy with ds_read_b64_tr_b16 (each 16-lane group transposes 4 rows
+// x 16 dims), so no transposed copy is stored.  Online softmax in base 2, float32
+// throughout; each lane owns one head of a tile, so running max, sum and rescale
+// are per-lane scalars.
 //
-// attn_prefill: one workgroup per token, wave w = heads 16w..16w+15, 32-row
-//   chunks shared by the waves.
+// attn_prefill: one workgroup per token; wave (hp, dh) owns heads 32hp..32hp+31
+//   and latent dims 256dh..256dh+255 (split-K: the two half-dim score partials are
+//   swapped through LDS), 32-row chunks, two workgroups per CU.
 // attn_decode: one workgroup per (token, row split, head group); its 4 waves take
 //   interleaved 16-row chunks with private double buffers and are merged through
 //   LDS at the end.  The 4 head-group workgroups of a token are numbered so they
@@ -48,6 +49,33 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 __device__ __forceinline__ void dma16(const void* gsrc, lds_u8* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)ldst, 16, 0, 0);
+}
+
+// The same gather written as inline assembly.  The compiler cannot tell which LDS
+// buffer the builtin form writes, so before reads of the other buffer it waits for
+// every gather in flight (vmcnt(0)), which serialises the double buffering.  This
+// form is invisible to that analysis: the caller orders it with explicit
+// s_waitcnt vmcnt and barriers.  The compiler still waits correctly for its own
+// loads (it may wait longer than needed, never shorter, since it undercounts the
+// operations in flight).  M0 is set here on every call.
+__device__ __forceinline__ void dma16_asm(const void* gsrc, const lds_u8* ldst) {
+  const uint32_t base = (uint32_t)(uintptr_t)ldst;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(gsrc) : "memory");
+}
+// Same, with the row base in an SGPR pair and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_asm_s(uint64_t sbase, uint32_t voff, const lds_u8* ldst) {
+  const uint32_t base = (uint32_t)(uintptr_t)ldst;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbase)
+               : "memory");
+}
+#define COMPILER_FENCE() __asm__ volatile("" ::: "memory")
+
+// Max over lanes l and l^16, then l^32, with the gfx950 permlane swaps (VALU, no LDS).
+__device__ __forceinline__ float max_lane_groups(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
 }
 
 // Transposed read: lane i of each 16-lane group receives 4 consecutive rows
@@ -109,158 +137,296 @@ constexpr int PRC = 32;                 // rows per chunk
 constexpr int PRS = 1024;               // LDS row stride (bytes) for bf16 rows (swizzled, no padding)
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind before rescaling
 
-__global__ __launch_bounds__(256, 2) void attn_prefill_bf16(
+// Prefill: a workgroup of 2 x NW/2 waves per token; wave (hp, dh) owns heads
+// 32hp..32hp+31 and the 256 latent dims 256dh..256dh+255.  S^T for its 32 heads is
+// the sum of two half-dim products: each wave computes its half, the halves are
+// swapped through LDS and added (a + b == b + a, so both waves hold bit-identical
+// scores and run the same softmax), and PV covers the wave's own 256 dims.  Per
+// 32-row chunk a wave reads 16 KB of rows for S and 16 KB for PV (half of what a
+// 16-heads x 512-dims wave reads), two chunk buffers + the exchange area take 80 KB
+// of LDS, so two workgroups share a CU.  Row ids come from the top-k row itself:
+// lanes 0..31 hold the 32 ids of a chunk (read one chunk ahead), readlane gives
+// each gather its row, and a ballot gives the chunk's validity mask.  The selected
+// part spans the slots up to the last valid id; invalid ids inside it load row 0
+// and are masked to probability 0.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
     bf16* __restrict__ o, float* __restrict__ lse, int T_len, int H, int N_cap, int k, int L_w, int W,
     float scale_log2) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[PRC * PRS];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[PRC * PRS];
-  __shared__ int rowlist[MAX_ROWS];
-  __shared__ int n_sel_s;
+  __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
+  constexpr int RPW = PRC / NW;          // rows gathered per wave per chunk
 
   const int t = blockIdx.x, b = blockIdx.y;
   const int bt = b * T_len + t;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int nw = blockDim.x >> 6;
-  const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
-                                   L_w, W);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hp = wave >> 1, dh = wave & 1;
+  const int32_t* tk = topk + (size_t)bt * k;
   const bf16* kvb = kv + (size_t)b * N_cap * 512;
   const bf16* swb = swa + (size_t)b * L_w * 512;
 
-  const int head = wave * 16 + lr;
-  bf16x8 qf[16];
-  const bf16* qrow = q + ((size_t)bt * H + head) * 512;
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    if (head < H) qf[ks] = load_frag(qrow + ks * 32 + 8 * lg);
-    else zero_frag(qf[ks]);
+  // rows: selected slots [0, k_eff) (k_eff = one past the last valid id), then the window
+  int k_eff = 0;
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    const int j = j0 + lane;
+    const int g = j < k ? tk[j] : -1;
+    const unsigned long long bal = __ballot(g >= 0 && g < N_cap);
+    if (bal) k_eff = j0 + 64 - __clzll(bal);
   }
-  f32x4 oacc[32];
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  const int p = q_pos[bt], pos0 = swa_pos0[b];
+  int lo = p - W + 1;
+  if (lo < 0) lo = 0;
+  if (lo < pos0) lo = pos0;
+  int hi = p;
+  if (hi > pos0 + L_w - 1) hi = pos0 + L_w - 1;
+  const int n_win = hi >= lo ? hi - lo + 1 : 0;
+  const int n_rows = k_eff + n_win;
+  const bf16* dummy = n_win > 0 ? swb + (size_t)(lo - pos0) * 512 : kvb;
 
-  // per-lane swizzled byte offsets (within a 256-B group of 16 units)
-  int soff[4], toff[8];
+  bf16x8 qf[2][8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) soff[b] = ((4 * b + lg) ^ swz(lr)) << 4;
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head = hp * 32 + ht * 16 + lr;
+    const bf16* qrow = q + ((size_t)bt * H + head) * 512 + dh * 256;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) toff[b] = ((2 * b + ((lr & 3) >> 1)) ^ swz(4 * lg + (lr >> 2))) << 4;
+    for (int ks = 0; ks < 8; ++ks) {
+      if (head < H) qf[ht][ks] = load_frag(qrow + ks * 32 + 8 * lg);
+      else zero_frag(qf[ht][ks]);
+    }
+  }
+  f32x4 oacc[16][2];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    oacc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    oacc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // the query fragments are complete before any gather is issued, so no wait in
+  // the chunk loop has to cover them (which would also wait for the gathers)
+  WAIT_VMCNT(0);
+
+  f32x4* xown = xbuf[wave];
+  const f32x4* xpart = xbuf[wave ^ 1];
 
   const int nch = (n_rows + PRC - 1) / PRC;
-  const int rows_per_wave = PRC / nw;   // nw in {1, 2, 4}: 32, 16, 8 loads per wave per chunk
-  // every wave issues exactly rows_per_wave loads per chunk; rows past the end
-  // repeat row 0 (finite data, masked to probability 0)
-  auto issue = [&](int c, unsigned char* buf) {
-    for (int j = 0; j < rows_per_wave; ++j) {
-      const int rr = wave + j * nw;
-      const int r = c * PRC + rr;
-      const int id = rowlist[r < n_rows ? r : 0];
-      const bf16* src = row_ptr(id, kvb, swb);
-      dma16(reinterpret_cast<const unsigned char*>(src) + ((lane ^ swz(rr & 15)) << 4), (lds_u8*)(buf + rr * PRS));
-    }
+  // lane l (mod 32) holds the id slot of row 32c + l (selected part only)
+  auto load_ids = [&](int c) -> int {
+    const int r = c * PRC + (lane & 31);
+    return tk[r < k_eff ? r : 0];
   };
+  // gathers chunk c's rows of this wave into buf; returns the chunk's validity mask
+  auto issue = [&](int c, unsigned char* buf, int ids) -> uint32_t {
+    // lane l (mod 32) works out the source of row 32c + l without branches; each
+    // gather instruction then takes its row's address with two readlanes.  The
+    // opaque lane copy keeps the per-row offsets from being hoisted out of the loop
+    // (they would not fit beside the accumulators).
+    int lv = lane;
+    __asm__ volatile("" : "+v"(lv));
+    const int r_l = c * PRC + (lv & 31);
+    const bool in_sel = r_l < k_eff;
+    const bool ok_sel = ids >= 0 && ids < N_cap;
+    const int jw = r_l - k_eff;
+    const bool ok_win = !in_sel && jw < n_win;
+    const uint32_t mask = (uint32_t)__ballot(in_sel ? ok_sel : ok_win);
+    const bf16* src_l = in_sel ? kvb + (size_t)(ok_sel ? ids : 0) * 512
+                               : (ok_win ? swb + (size_t)(lo - pos0 + jw) * 512 : dummy);
+    const uint64_t a_l = reinterpret_cast<uint64_t>(src_l);
+    const uint32_t lane16 = (uint32_t)lv << 4;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int rr = wave * RPW + j;
+      const uint32_t alo = __builtin_amdgcn_readlane((uint32_t)a_l, rr);
+      const uint32_t ahi = __builtin_amdgcn_readlane((uint32_t)(a_l >> 32), rr);
+      dma16_asm_s(((uint64_t)ahi << 32) | alo, lane16 ^ ((uint32_t)swz(rr & 15) << 4), (const lds_u8*)(buf + rr * PRS));
+    }
+    return mask;
+  };
+  int ids_next = 0;
+  uint32_t mask_cur = 0, mask_next = 0;
   auto step = [&](int c, unsigned char* cur, unsigned char* nxt) {
+    // The id loads are ordinary loads: before ids(c+1) is used the compiler waits
+    // for it and everything older, i.e. also chunk c's gathers, which are needed
+    // now anyway.  Chunk c+1's gathers and ids(c+2) then stay in flight while
+    // chunk c is computed; the explicit waits restate that chunk c is complete.
     if (c + 1 < nch) {
-      issue(c + 1, nxt);
-      if (rows_per_wave == 8) WAIT_VMCNT(8);
-      else if (rows_per_wave == 16) WAIT_VMCNT(16);
-      else WAIT_VMCNT(32);
+      mask_next = issue(c + 1, nxt, ids_next);
+      if (c + 2 < nch) {
+        ids_next = load_ids(c + 2);
+        WAIT_VMCNT(RPW + 1);
+      } else {
+        WAIT_VMCNT(RPW);
+      }
     } else {
       WAIT_VMCNT(0);
     }
     __builtin_amdgcn_s_barrier();
+    COMPILER_FENCE();
     const lds_u8* lcur = (const lds_u8*)cur;
+    // swizzled unit offsets, recomputed per chunk (an opaque copy of the lane id
+    // keeps them from being held live across the loop, where they would spill)
+    int lv = lane;
+    __asm__ volatile("" : "+v"(lv));
+    const int vlr = lv & 15, vlg = (lv >> 4) & 3;
+    int soff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) soff[i] = ((4 * i + vlg) ^ swz(vlr)) << 4;
 
-    // ---- S^T = R Q^T; k-step ks = 4a + b reads unit 16a + ((4b + lg) ^ swz(lr))
-    f32x4 s[2];
+    // ---- this wave's half of S^T = R Q^T (k-steps 8dh .. 8dh+7 of the row)
+    // fragment f = (mt, ks) = (f / 8, f % 8); the next one is read while the
+    // current one feeds its two MFMAs
+    f32x4 s[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* srow = cur + (mt * 16 + lr) * PRS;
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(srow + soff[ks & 3] + (ks >> 2) * 256);
-        s[mt] = mma16(a, qf[ks], s[mt]);
-      }
+      s[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // ---- online softmax; the running max is only moved (and the output
-    // rescaled) when it would grow by more than RESCALE_SLACK, so exp2 values stay
-    // below 2^RESCALE_SLACK and most chunks skip the rescale
-    float x[8];
-    float cmax = -INFINITY;
+    const unsigned char* sbase = cur + vlr * PRS + dh * 512;
+    auto rd = [&](int f) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(sbase + (f >> 3) * 16 * PRS + soff[f & 3] + ((f & 7) >> 2) * 256);
+    };
+    bf16x8 a0 = rd(0), a1 = rd(1);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      bf16x8 a2;
+      if (f + 2 < 16) a2 = rd(f + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int mt = f >> 3, ks = f & 7;
+      s[mt][0] = mma16(a0, qf[0][ks], s[mt][0]);
+      s[mt][1] = mma16(a0, qf[1][ks], s[mt][1]);
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = a1;
+      if (f + 2 < 16) a1 = a2;
+    }
+    // ---- swap halves with the partner wave
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = c * PRC + mt * 16 + 4 * lg + i;
-        const float v = row < n_rows ? s[mt][i] * scale_log2 : -INFINITY;
-        x[mt * 4 + i] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const bool grow = cmax > m_run + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? cmax : m_run;
-      const float alpha = grow ? exp2f(m_run - m_new) : 1.0f;  // 0 on the first chunk
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
-    float psum = 0.f;
-    bf16x8 pf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pv = exp2f(x[i] - m_run);
-      psum += pv;
-      pf[i] = (bf16)pv;
-    }
-    l_run += psum;
-    // ---- O^T += R^T P^T: A operand via transposed reads of rows 4g.. and 16+4g..
-    // lane's rows 4g + lr/4 (and +16; same swizzle); dim tile dt = 8a + b reads
-    // unit 16a + ((2b + (lr&3)/2) ^ swz(row)), half lr&1
-    const lds_u8* tb = lcur + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const int unit = toff[dt & 7] + (dt >> 3) * 256;
-      const v4s lo = tr_read(tb + unit);
-      const v4s hi = tr_read(tb + 16 * PRS + unit);
-      bf16x8 a;
-      __builtin_memcpy(&a, &lo, 8);
-      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
-      oacc[dt] = mma16(a, pf, oacc[dt]);
-    }
+      for (int ht = 0; ht < 2; ++ht) xown[(mt * 2 + ht) * 64 + lane] = s[mt][ht];
     WAIT_LGKM0();
+    COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
+    COMPILER_FENCE();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) s[mt][ht] += xpart[(mt * 2 + ht) * 64 + lane];
+
+    // ---- online softmax with lazy rescale, per head tile.  A chunk without a
+    // valid row is skipped, so every head sees a finite chunk maximum and exp2 of
+    // (-inf - finite) gives the 0 of a masked row.
+    if (mask_cur != 0u) {
+    float cmax[2];
+    bool grow[2];
+    if (mask_cur != 0xFFFFFFFFu) {
+      const uint32_t m4 = mask_cur >> (4 * vlg);   // bit mt*16+i: row mt*16 + 4*lg + i
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((m4 >> (mt * 16 + i)) & 1u)) {
+            s[mt][0][i] = -INFINITY;
+            s[mt][1][i] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      // raw scores; the scale is positive, so the scaled maximum is the scaled raw one
+      cmax[ht] = fmaxf(fmaxf(fmaxf(s[0][ht][0], s[0][ht][1]), fmaxf(s[0][ht][2], s[0][ht][3])),
+                       fmaxf(fmaxf(s[1][ht][0], s[1][ht][1]), fmaxf(s[1][ht][2], s[1][ht][3])));
+      cmax[ht] = max_lane_groups(cmax[ht]) * scale_log2;
+      grow[ht] = cmax[ht] > m_run[ht] + RESCALE_SLACK;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1])) {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float m_new = grow[ht] ? cmax[ht] : m_run[ht];
+        const float alpha = grow[ht] ? __builtin_amdgcn_exp2f(m_run[ht] - m_new) : 1.0f;  // 0 on the first rows
+        l_run[ht] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) oacc[dt][ht] *= alpha;
+        m_run[ht] = m_new;
+      }
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i >> 2][ht][i & 3], scale_log2, -m_run[ht]));
+        psum += pv;
+        pf[ht][i] = (bf16)pv;
+      }
+      l_run[ht] += psum;
+    }
+    // ---- O^T += R^T P^T over this wave's 256 dims
+    const lds_u8* tb = lcur + (4 * vlg + (vlr >> 2)) * PRS + 8 * (vlr & 1) + dh * 512;
+    const int tsw = swz(4 * vlg + (vlr >> 2)), th = (vlr & 3) >> 1;
+    const lds_u8* tpa[8];
+#pragma unroll
+    for (int d8 = 0; d8 < 8; ++d8) tpa[d8] = tb + (((2 * d8 + th) ^ tsw) << 4);
+    auto rdt = [&](int dt) -> bf16x8 {
+      const v4s lo4 = tr_read(tpa[dt & 7] + (dt >> 3) * 256);
+      const v4s hi4 = tr_read(tpa[dt & 7] + (dt >> 3) * 256 + 16 * PRS);
+      bf16x8 a;
+      __builtin_memcpy(&a, &lo4, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi4, 8);
+      return a;
+    };
+    bf16x8 v0 = rdt(0), v1 = rdt(1);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      bf16x8 v2;
+      if (dt + 2 < 16) v2 = rdt(dt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[dt][0] = mma16(v0, pf[0], oacc[dt][0]);
+      oacc[dt][1] = mma16(v0, pf[1], oacc[dt][1]);
+      __builtin_amdgcn_sched_barrier(0);
+      v0 = v1;
+      if (dt + 2 < 16) v1 = v2;
+    }
+    }   // mask_cur != 0
+    WAIT_LGKM0();
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();
+    mask_cur = mask_next;
   };
-  if (nch > 0) issue(0, buf0);
+  if (nch > 0) {
+    const int ids0 = load_ids(0);
+    ids_next = nch > 1 ? load_ids(1) : 0;
+    mask_cur = issue(0, buf0, ids0);
+  }
   for (int c = 0; c < nch; c += 2) {
     step(c, buf0, buf1);
     if (c + 1 < nch) step(c + 1, buf1, buf0);
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (head < H) {
-    bf16* orow = o + ((size_t)bt * H + head) * 512;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const int d = dt * 16 + 4 * lg;
-      bf16x2 p0, p1;
-      p0[0] = (bf16)(oacc[dt][0] * inv); p0[1] = (bf16)(oacc[dt][1] * inv);
-      p1[0] = (bf16)(oacc[dt][2] * inv); p1[1] = (bf16)(oacc[dt][3] * inv);
-      uint2 u;
-      __builtin_memcpy(&u.x, &p0, 4);
-      __builtin_memcpy(&u.y, &p1, 4);
-      *reinterpret_cast<uint2*>(orow + d) = u;
+  for (int ht = 0; ht < 2; ++ht) {
+    float l_tot = l_run[ht] + __shfl_xor(l_run[ht], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int head = hp * 32 + ht * 16 + lr;
+    if (head < H) {
+      bf16* orow = o + ((size_t)bt * H + head) * 512 + dh * 256;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const int d = dt * 16 + 4 * lg;
+        bf16x2 p0, p1;
+        p0[0] = (bf16)(oacc[dt][ht][0] * inv); p0[1] = (bf16)(oacc[dt][ht][1] * inv);
+        p1[0] = (bf16)(oacc[dt][ht][2] * inv); p1[1] = (bf16)(oacc[dt][ht][3] * inv);
+        uint2 u;
+        __builtin_memcpy(&u.x, &p0, 4);
+        __builtin_memcpy(&u.y, &p1, 4);
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+      if (lse != nullptr && lg == 0 && dh == 0)
+        lse[(size_t)bt * H + head] = (l_tot > 0.f) ? (m_run[ht] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
-    if (lse != nullptr && lg == 0)
-      lse[(size_t)bt * H + head] = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -619,9 +785,13 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   const bf16* ss = static_cast<const bf16*>(swa_kv);
   bf16* oo = static_cast<bf16*>(o);
   if (!p.decode) {
-    const int nwp = nw == 3 ? 4 : nw;   // 1, 2 or 4 waves (32 rows split evenly)
-    hipLaunchKernelGGL(attn_prefill_bf16, dim3(T, B), dim3(64 * nwp), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, T, H, N_cap, k, L_w, W, sl2);
+    // head pairs of 32 heads; two waves (dim halves) each
+    if (H > 32)
+      hipLaunchKernelGGL(attn_prefill_bf16<4>, dim3(T, B), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+                         oo, lse, T, H, N_cap, k, L_w, W, sl2);
+    else
+      hipLaunchKernelGGL(attn_prefill_bf16<2>, dim3(T, B), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+                         oo, lse, T, H, N_cap, k, L_w, W, sl2);
     return hipGetLastError();
   }
   const int Q = B * T;

@@ -10,12 +10,13 @@
 // sign kept), all divisions float32 round-to-nearest; a zero scale zeroes the
 // block.  The code of dim 2j is the low nibble of byte j.
 //
-// Kernel: one wave per 16 entries, no LDS.  MFMA with the 16 entries as rows and
-// the 128 output dims as 8 column tiles; the float32 latent is split into a bf16
-// high part and a bf16 remainder (two MFMAs) so bf16 weights lose nothing beyond
-// ~2^-17 relative; fp32 weights use the fp32 MFMA.  The accumulator layout puts
-// the 32 dims of a quantisation block in one 16-lane group (two column tiles),
-// so amax, RoPE pairs and nibble packing are lane shuffles.
+// Kernel: a workgroup of 4 waves per 16 entries, no LDS; wave q computes the 32
+// output dims of quantisation block q.  MFMA with the 16 entries as rows and the
+// block's 32 dims as 2 column tiles; the float32 latent is split into a bf16 high
+// part and a bf16 remainder (two MFMAs) so bf16 weights lose nothing beyond ~2^-17
+// relative; fp32 weights use the fp32 MFMA.  The accumulator layout puts the 32
+// dims of the block in one 16-lane group, so amax, RoPE pairs and nibble packing
+// are lane shuffles.
 #include "csa2_internal.h"
 #include "device_common.h"
 
@@ -37,14 +38,14 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                       int N, int m, int entry0, int N_cap, double base) {
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int e0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // quantisation block of this wave
+  const int e0 = blockIdx.x * 16;
   const int b = blockIdx.y;
-  if (e0 >= N) return;
   const float* lb = lat + (size_t)b * N * 512;
   const int arow = e0 + lr;
-  f32x4 acc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2];
+  acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int ks = 0; ks < 16; ++ks) {
     f32x8 a;
@@ -54,56 +55,55 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
       bf16x8 hi, lo;
       split_hi_lo(a, hi, lo);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        bf16x8 bw = load_frag(reinterpret_cast<const bf16*>(w_ik) + (size_t)(nt * 16 + lr) * 512 + ks * 32 + 8 * lg);
-        acc[nt] = mma16(hi, bw, acc[nt]);
-        acc[nt] = mma16(lo, bw, acc[nt]);
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 bw = load_frag(reinterpret_cast<const bf16*>(w_ik) + (size_t)((2 * q + j) * 16 + lr) * 512 + ks * 32 + 8 * lg);
+        acc[j] = mma16(hi, bw, acc[j]);
+        acc[j] = mma16(lo, bw, acc[j]);
       }
     } else {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        f32x8 bw = load_frag(reinterpret_cast<const float*>(w_ik) + (size_t)(nt * 16 + lr) * 512 + ks * 32 + 8 * lg);
-        acc[nt] = mma16(a, bw, acc[nt]);
+      for (int j = 0; j < 2; ++j) {
+        f32x8 bw = load_frag(reinterpret_cast<const float*>(w_ik) + (size_t)((2 * q + j) * 16 + lr) * 512 + ks * 32 + 8 * lg);
+        acc[j] = mma16(a, bw, acc[j]);
       }
     }
   }
 
-  // RoPE on dims 64..127 (column tiles 4..7): pair (64+2p, 65+2p) lives in lanes l, l^1
+  // RoPE on dims 64..127 (blocks 2 and 3): pair (64+2p, 65+2p) lives in lanes l, l^1
+  if (q >= 2) {
 #pragma unroll
-  for (int nt = 4; nt < 8; ++nt) {
-    const int pair = (nt - 4) * 8 + (lr >> 1);
+    for (int j = 0; j < 2; ++j) {
+      const int pair = (2 * q + j - 4) * 8 + (lr >> 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 4 * lg + i;
-      float c, s;
-      rope_cos_sin((int64_t)(entry0 + e) * m, pair, 64, base, c, s);
-      float mine = acc[nt][i];
-      float other = __shfl_xor(mine, 1, 64);
-      acc[nt][i] = (lr & 1) ? (other * s + mine * c) : (mine * c - other * s);
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 4 * lg + i;
+        float c, s;
+        rope_cos_sin((int64_t)(entry0 + e) * m, pair, 64, base, c, s);
+        float mine = acc[j][i];
+        float other = __shfl_xor(mine, 1, 64);
+        acc[j][i] = (lr & 1) ? (other * s + mine * c) : (mine * c - other * s);
+      }
     }
   }
 
-  // quantise: block q = column tiles 2q, 2q+1; entry 4*lg+i lives in the lane's 16-lane group
+  // quantise block q; entry 4*lg+i lives in the lane's 16-lane group
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 4 * lg + i;
-      float v0 = acc[2 * q][i], v1 = acc[2 * q + 1][i];
-      float amax = fmaxf(fabsf(v0), fabsf(v1));
-      amax = wave_max_xor(amax, 15);  // within the 16-lane group
-      const uint32_t sb = fp4_scale_byte(amax);
-      const float s = e4m3_decode(sb);
-      const uint32_t c0 = fp4_code(v0, s), c1 = fp4_code(v1, s);
-      const uint32_t o0 = __shfl_xor((int)c0, 1, 64), o1 = __shfl_xor((int)c1, 1, 64);
-      if (e < N) {
-        uint8_t* crow = codes + ((size_t)b * N_cap + entry0 + e) * 64 + 16 * q;
-        if ((lr & 1) == 0) {
-          crow[lr >> 1] = (uint8_t)(c0 | (o0 << 4));
-          crow[8 + (lr >> 1)] = (uint8_t)(c1 | (o1 << 4));
-        }
-        if (lr == 0) scales[((size_t)b * N_cap + entry0 + e) * 4 + q] = (uint8_t)sb;
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 4 * lg + i;
+    float v0 = acc[0][i], v1 = acc[1][i];
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    amax = wave_max_xor(amax, 15);  // within the 16-lane group
+    const uint32_t sb = fp4_scale_byte(amax);
+    const float s = e4m3_decode(sb);
+    const uint32_t c0 = fp4_code(v0, s), c1 = fp4_code(v1, s);
+    const uint32_t o0 = __shfl_xor((int)c0, 1, 64), o1 = __shfl_xor((int)c1, 1, 64);
+    if (e < N) {
+      uint8_t* crow = codes + ((size_t)b * N_cap + entry0 + e) * 64 + 16 * q;
+      if ((lr & 1) == 0) {
+        crow[lr >> 1] = (uint8_t)(c0 | (o0 << 4));
+        crow[8 + (lr >> 1)] = (uint8_t)(c1 | (o1 << 4));
       }
+      if (lr == 0) scales[((size_t)b * N_cap + entry0 + e) * 4 + q] = (uint8_t)sb;
     }
   }
 }
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__
 hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes, uint8_t* scales,
                           int B, int N, int m, int entry0, int N_cap, float rope_base, hipStream_t stream) {
   if (N == 0 || B == 0) return hipSuccess;
-  dim3 grid((N + 63) / 64, B), blk(256);
+  dim3 grid((N + 15) / 16, B), blk(256);
   if (dtype == 1)
     hipLaunchKernelGGL((index_k_kernel<bf16>), grid, blk, 0, stream, latent_pre, static_cast<const bf16*>(w_ik),
                        codes, scales, N, m, entry0, N_cap, (double)rope_base);

@@ -30,85 +30,119 @@ namespace csa2 {
 
 namespace {
 
-constexpr int SEL_BINS = 2048;   // 11-bit digits
-constexpr int SEL_BITS = 11;
+constexpr int NBINS = 2048;   // radix digit of 11 bits
 
+// Shared memory of the block-wide selection helpers below.
 template <int NT>
 struct SelSmem {
-  uint32_t hist[SEL_BINS];
-  uint32_t wtot[NT / 64];
-  uint32_t digit, above, n_valid, done;
-  uint32_t count;
+  uint32_t hist[NBINS];
+  uint32_t wsum[NT / 64];
+  uint32_t red[3][NT / 64];
+  uint32_t digit, above, done, lb;
 };
 
-// Exclusive suffix sum over the threads of a block (thread t gets the sum of the
-// values of threads > t).
+// Exclusive prefix sum over the threads of a block; `total` gets the block sum.
 template <int NT>
-__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, SelSmem<NT>& sm) {
+__device__ __forceinline__ uint32_t block_prefix_excl(uint32_t v, SelSmem<NT>& sm, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    uint32_t u = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += u;
+    const uint32_t u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
   }
-  if (lane == 0) sm.wtot[wave] = x;  // inclusive suffix of lane 0 = wave total
+  if (lane == 63) sm.wsum[wave] = x;
   __syncthreads();
-  uint32_t higher = 0;
-  for (int w = wave + 1; w < NT / 64; ++w) higher += sm.wtot[w];
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t s = sm.wsum[w];
+    if (w < wave) before += s;
+    tot += s;
+  }
   __syncthreads();
-  return x - v + higher;
+  total = tot;
+  return x - v + before;
 }
 
-// Block-wide selection of the R largest non-zero 64-bit composites (R = min(k,
-// number of non-zero items)).  On return every thread has (prefix, mask): item c
-// is selected iff c != 0 and (c & mask) >= prefix.  R == 0 gives mask = 0,
-// prefix = ~0 (selects nothing).
+// Minimum, maximum and number of the non-zero keys key_at(0..n).
 template <int NT, typename Get>
-__device__ void block_select(Get get, int n, uint32_t k, int total_bits, SelSmem<NT>& sm, uint64_t& prefix,
-                             uint64_t& mask) {
-  prefix = 0;
-  mask = 0;
-  uint32_t need = 0;
-  constexpr int BPT = SEL_BINS / NT;
-  for (int pass = 0;; ++pass) {
-    int shift = total_bits - SEL_BITS * (pass + 1);
-    int width = SEL_BITS;
-    if (shift < 0) {
-      width += shift;
-      shift = 0;
+__device__ void key_stats(Get key_at, int n, SelSmem<NT>& sm, uint32_t& mn, uint32_t& mx, uint32_t& nv) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  nv = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t kk = key_at(i);
+    if (kk) {
+      mn = min(mn, kk);
+      mx = max(mx, kk);
+      ++nv;
     }
-    const uint64_t dmask = (width >= 64) ? ~0ull : ((1ull << width) - 1);
-    for (int i = threadIdx.x; i < SEL_BINS; i += NT) sm.hist[i] = 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    nv += (uint32_t)__shfl_xor((int)nv, off, 64);
+  }
+  if (lane == 0) {
+    sm.red[0][wave] = mn;
+    sm.red[1][wave] = mx;
+    sm.red[2][wave] = nv;
+  }
+  __syncthreads();
+  mn = sm.red[0][0];
+  mx = sm.red[1][0];
+  nv = sm.red[2][0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) {
+    mn = min(mn, sm.red[0][w]);
+    mx = max(mx, sm.red[1][w]);
+    nv += sm.red[2][w];
+  }
+  __syncthreads();
+}
+
+// Result of a selection: a key is chosen iff it is non-zero and either greater than
+// `thresh`, or equal to it and among the first `eq_take` keys equal to it in
+// position order.  `lb` is a lower bound of the rank-r0 largest key (0 when there
+// are fewer than r0 keys or no bound was asked for).
+struct SelOut {
+  uint32_t thresh, eq_take, lb;
+};
+
+// Radix select of the `need` (<= number of non-zero keys) largest non-zero keys,
+// ties resolved in position order.  The digit of each pass covers the live key
+// range [lo, hi] (starting from the keys' [min, max]) with 2048 bins, so a pass
+// usually shrinks the range by ~2^11 and the loop ends when the count at the
+// boundary bin is exact or the bin holds a single value.
+template <int NT, typename Get>
+__device__ SelOut select_threshold(Get key_at, int n, uint32_t need, uint32_t mn, uint32_t mx, uint32_t r0,
+                                   SelSmem<NT>& sm) {
+  if (need == 0) return SelOut{0xFFFFFFFFu, 0u, 0u};
+  if (threadIdx.x == 0) sm.lb = 0;
+  uint32_t lo = mn, hi = mx;
+  constexpr int BPT = NBINS / NT;
+  for (int pass = 0;; ++pass) {
+    const uint32_t R = hi - lo;
+    const int shift = (R >> 11) == 0 ? 0 : 32 - __clz((int)(R >> 11));
+    for (int i = threadIdx.x; i < NBINS; i += NT) sm.hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += NT) {
-      uint64_t c = get(i);
-      if (c != 0 && (c & mask) == prefix) atomicAdd(&sm.hist[(uint32_t)((c >> shift) & dmask)], 1u);
+      const uint32_t kk = key_at(i);
+      if (kk && kk >= lo && kk <= hi) atomicAdd(&sm.hist[(kk - lo) >> shift], 1u);
     }
     __syncthreads();
-    uint32_t own[BPT];
-    uint32_t tot = 0;
+    uint32_t own[BPT], tot = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       own[j] = sm.hist[threadIdx.x * BPT + j];
       tot += own[j];
     }
-    if (pass == 0) {
-      // total number of valid items
-      uint32_t above_all = block_suffix_excl<NT>(tot, sm);
-      if (threadIdx.x == 0) sm.n_valid = above_all + tot;
-      __syncthreads();
-      uint32_t nv = sm.n_valid;
-      need = nv < k ? nv : k;
-      if (need == 0) {
-        prefix = ~0ull;
-        mask = 0;
-        __syncthreads();
-        return;
-      }
-    }
-    uint32_t above = block_suffix_excl<NT>(tot, sm);
-    uint32_t cum = above;
+    uint32_t total;
+    const uint32_t pre = block_prefix_excl<NT>(tot, sm, total);
+    uint32_t cum = total - pre - tot;   // keys in higher bins
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j) {
       if (cum < need && cum + own[j] >= need) {
@@ -116,37 +150,71 @@ __device__ void block_select(Get get, int n, uint32_t k, int total_bits, SelSmem
         sm.above = cum;
         sm.done = (cum + own[j] == need) ? 1u : 0u;
       }
+      if (pass == 0 && r0 != 0 && cum < r0 && cum + own[j] >= r0) sm.lb = lo + ((uint32_t)(threadIdx.x * BPT + j) << shift);
       cum += own[j];
     }
     __syncthreads();
     const uint32_t d = sm.digit;
     need -= sm.above;
-    prefix |= (uint64_t)d << shift;
-    mask |= dmask << shift;
-    const uint32_t done = sm.done;
+    const uint32_t new_lo = lo + (d << shift);
+    const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
+    const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+    const uint32_t done = sm.done, lb = sm.lb;
     __syncthreads();
-    if (done || shift == 0) return;
+    if (done) return SelOut{new_lo, 0xFFFFFFFFu, lb};   // every key >= new_lo
+    if (shift == 0) return SelOut{new_lo, need, lb};    // keys > new_lo and the first `need` equal to it
+    lo = new_lo;
+    hi = new_hi;
   }
 }
 
-// Bitonic sort (ascending) of n_pow2 ints in LDS, n_pow2 <= 2 * NT * 4.
-template <int NT>
-__device__ void block_bitonic_sort(int* a, int n_pow2) {
-  for (int size = 2; size <= n_pow2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < n_pow2 / 2; t += NT) {
-        int lo = 2 * t - (t & (stride - 1));
-        int hi = lo + stride;
-        bool up = ((lo & size) == 0);
-        int x = a[lo], y = a[hi];
-        if ((x > y) == up) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
+// Calls emit(i, slot) for every chosen position i in increasing i, with slot =
+// the number of chosen positions before i; returns the number chosen.  Wave w owns
+// a contiguous range of positions and walks it 64 at a time, so the reads are
+// unit-stride and one block-wide exchange of per-wave counts orders the output.
+template <int NT, typename Get, typename Emit>
+__device__ uint32_t emit_ordered(Get key_at, int n, const SelOut& s, SelSmem<NT>& sm, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per_w = (((n + NW - 1) / NW) + 63) & ~63;
+  const int w0 = wave * per_w, w1 = min(n, w0 + per_w);
+  uint32_t g = 0, e = 0;
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t kk = i < w1 ? key_at(i) : 0u;
+    g += __popcll(__ballot(kk != 0 && kk > s.thresh));
+    e += __popcll(__ballot(kk != 0 && kk == s.thresh));
   }
+  if (lane == 0) {
+    sm.red[0][wave] = g;
+    sm.red[1][wave] = e;
+  }
+  __syncthreads();
+  uint32_t G = 0, E = 0, GT = 0, ET = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t gw = sm.red[0][w], ew = sm.red[1][w];
+    if (w < wave) {
+      G += gw;
+      E += ew;
+    }
+    GT += gw;
+    ET += ew;
+  }
+  __syncthreads();
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t kk = i < w1 ? key_at(i) : 0u;
+    const bool is_gt = kk != 0 && kk > s.thresh, is_eq = kk != 0 && kk == s.thresh;
+    const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+    const uint32_t gl = G + __popcll(mg & lt), el = E + __popcll(me & lt);
+    if (is_gt) emit(i, gl + min(el, s.eq_take));
+    else if (is_eq && el < s.eq_take) emit(i, gl + el);
+    G += __popcll(mg);
+    E += __popcll(me);
+  }
+  return GT + min(ET, s.eq_take);
 }
 
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w) {
@@ -175,7 +243,6 @@ template <> struct Fp4<float> { static __device__ __forceinline__ f32x8 cvt(uint
 
 constexpr int MAX_CHUNK = 4096;
 constexpr int SC_THREADS = 256;
-constexpr int NBINS = 2048;
 constexpr int SPT = 4;                          // tiles (of 16 entries) per super-tile
 constexpr int ST_BYTES = SPT * 1024 + 256;      // one super-tile in LDS: codes + scales
 
@@ -205,46 +272,22 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
-struct ChunkSmem {
-  uint32_t keys[MAX_CHUNK];
-  uint32_t hist[NBINS];
-  uint32_t wtot[SC_THREADS / 64];
-  uint32_t red[3][SC_THREADS / 64];
-  uint32_t digit, above, done, lb, count, running;
-};
-
-__device__ __forceinline__ uint32_t suffix_excl(uint32_t v, ChunkSmem& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t u = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += u;
-  }
-  if (lane == 0) sm.wtot[wave] = x;
-  __syncthreads();
-  uint32_t higher = 0;
-#pragma unroll
-  for (int w = 0; w < SC_THREADS / 64; ++w)
-    if (w > wave) higher += sm.wtot[w];
-  __syncthreads();
-  return x - v + higher;
-}
-
-// Number of chunks a query scans, and the rank whose per-chunk lower bounds the
-// merge combines: r0 = ceil(k / chunks), so chunks x r0 >= k entries lie at or
-// above the smallest of those bounds, which therefore bounds the k-th best key.
-__device__ __forceinline__ int rank_for_bound(int k, int nc) { return nc > 0 ? (k + nc - 1) / nc : k; }
+// Lower bound for the merge.  In a scan over nc chunks every chunk but the last
+// is full, so with r0 = ceil(k / (nc - 1)) the first nc - 1 chunks hold at least
+// k entries at or above the smallest of their rank-r0 keys: that smallest value
+// bounds the k-th best key from below and the merge drops every candidate under it.
+__device__ __forceinline__ uint32_t rank_for_bound(int k, int nc) { return nc > 1 ? (uint32_t)((k + nc - 2) / (nc - 1)) : 0u; }
 
 template <typename T, bool POOL, bool BUILD>
 __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ cands,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb,
-    uint32_t* __restrict__ blkmax, int T_len, int H_I, int N_cap, int n_entries, int m, int C, int k_chunk,
-    int n_chunks, int k, int hsi_s, int hsi_nb, int nblk_max) {
+    uint32_t* __restrict__ blkmax, int32_t* __restrict__ topk, int T_len, int H_I, int N_cap, int n_entries, int m,
+    int C, int k_chunk, int n_chunks, int k, int hsi_s, int hsi_nb, int nblk_max) {
   typedef typename Frag<T>::type FragT;
-  __shared__ ChunkSmem sm;
+  __shared__ SelSmem<SC_THREADS> sm;
+  __shared__ uint32_t keys[MAX_CHUNK];
   __shared__ __attribute__((aligned(16))) unsigned char ring0[4 * ST_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char ring1[4 * ST_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[4 * ST_BYTES];
@@ -255,8 +298,19 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int base = c * C;
-  if (!POOL && base >= n_t) return;  // chunk beyond the visible range: never read by the merge
   const int nc_q = POOL ? n_chunks : (n_t + C - 1) / C;
+  // a query whose candidates fit one chunk gets its top-k written here; the merge skips it
+  const bool direct = !BUILD && nc_q <= 1;
+  if (!POOL && base >= n_t) {
+    if (direct && c == 0)   // nothing visible
+      for (int i = threadIdx.x; i < k; i += SC_THREADS) topk[(size_t)bt * k + i] = -1;
+    return;   // chunk beyond the visible range: never read by the merge
+  }
+  // positions of this chunk that hold visible entries, rounded up to whole super-tiles
+  // (and whole HSI blocks); keys past them are never read
+  const int gran = BUILD ? (hsi_s > 64 ? hsi_s : 64) : 64;
+  const int n_here = POOL ? C : min(C, n_t - base);
+  const int Ce = min(C, (n_here + gran - 1) / gran * gran);
 
   // indexer query fragments: row tile mt = heads 16mt.., k-step kb = dims 32kb + 8lg ..
   FragT qf[2][4];
@@ -285,7 +339,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   // per tile moves its 1 KB of codes (16-B piece i of the tile lands in unit i,
   // piece = (entry e, block b) with unit 4e + ((b + e/4) & 3), which makes the
   // MFMA-pattern dword reads below conflict-free) and one moves the 64 scale words.
-  const int n_st = C / 64;
+  const int n_st = Ce / 64;
   const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave
   auto entry_at = [&](int j, bool& valid) -> int {   // chunk position -> entry id
     if (POOL) {
@@ -351,7 +405,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
       const int j = st * 64 + tt * 16 + lr;
       bool valid;
       entry_at(j, valid);
-      if (lg == 0) sm.keys[j] = valid ? score_key(part) : 0u;
+      if (lg == 0) keys[j] = valid ? score_key(part) : 0u;
     }
   };
   // 3-slot ring, unrolled so that each slot is a distinct LDS object
@@ -378,112 +432,26 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
 
   if (BUILD) {
     // block maxima of this chunk (C is a multiple of hsi_s)
-    const int nb_chunk = C / hsi_s;
+    const int nb_chunk = Ce / hsi_s;
     const int nvis_blk = (n_t + hsi_s - 1) / hsi_s;
     for (int jb = threadIdx.x; jb < nb_chunk; jb += SC_THREADS) {
       const int gblk = base / hsi_s + jb;
       if (gblk >= nvis_blk) break;
       uint32_t mx = 0;
-      for (int e = 0; e < hsi_s; ++e) mx = max(mx, sm.keys[jb * hsi_s + e]);
+      for (int e = 0; e < hsi_s; ++e) mx = max(mx, keys[jb * hsi_s + e]);
       blkmax[(size_t)bt * nblk_max + gblk] = mx;
     }
   }
 
-  // ---- adaptive radix select of the chunk's best min(k_chunk, valid) keys
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
-  for (int i = threadIdx.x; i < C; i += SC_THREADS) {
-    const uint32_t kk = sm.keys[i];
-    if (kk) {
-      mn = min(mn, kk);
-      mx = max(mx, kk);
-      ++nv;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    nv += (uint32_t)__shfl_xor((int)nv, off, 64);
-  }
-  if (lane == 0) {
-    sm.red[0][wave] = mn;
-    sm.red[1][wave] = mx;
-    sm.red[2][wave] = nv;
-  }
-  __syncthreads();
-  mn = sm.red[0][0]; mx = sm.red[1][0]; nv = sm.red[2][0];
-#pragma unroll
-  for (int w2 = 1; w2 < SC_THREADS / 64; ++w2) {
-    mn = min(mn, sm.red[0][w2]);
-    mx = max(mx, sm.red[1][w2]);
-    nv += sm.red[2][w2];
-  }
-  const int r0 = rank_for_bound(k, nc_q);
-  uint32_t need = nv < (uint32_t)k_chunk ? nv : (uint32_t)k_chunk;
-  const size_t obase = ((size_t)bt * n_chunks + c) * k_chunk;
-  uint32_t thresh = 0;
-  bool eq_mode = false;
-  if (threadIdx.x == 0) sm.lb = 0;
-  const bool have = nv > 0;
-  if (have) {
-    uint32_t lo = mn, hi = mx;
-    for (int pass = 0;; ++pass) {
-      const uint32_t R = hi - lo;
-      const int shift = (R >> 11) == 0 ? 0 : 32 - __clz((int)(R >> 11));
-      for (int i = threadIdx.x; i < NBINS; i += SC_THREADS) sm.hist[i] = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < C; i += SC_THREADS) {
-        const uint32_t kk = sm.keys[i];
-        if (kk && kk >= lo && kk <= hi) atomicAdd(&sm.hist[(kk - lo) >> shift], 1u);
-      }
-      __syncthreads();
-      constexpr int BPT = NBINS / SC_THREADS;
-      uint32_t own[BPT], tot = 0;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) {
-        own[j] = sm.hist[threadIdx.x * BPT + j];
-        tot += own[j];
-      }
-      const uint32_t above = suffix_excl(tot, sm);
-      uint32_t cum = above;
-#pragma unroll
-      for (int j = BPT - 1; j >= 0; --j) {
-        if (cum < need && cum + own[j] >= need) {
-          sm.digit = threadIdx.x * BPT + j;
-          sm.above = cum;
-          sm.done = (cum + own[j] == need) ? 1u : 0u;
-        }
-        if (pass == 0 && nv >= (uint32_t)r0 && cum < (uint32_t)r0 && cum + own[j] >= (uint32_t)r0)
-          sm.lb = lo + ((uint32_t)(threadIdx.x * BPT + j) << shift);
-        cum += own[j];
-      }
-      __syncthreads();
-      const uint32_t d = sm.digit;
-      need -= sm.above;
-      const uint32_t new_lo = lo + (d << shift);
-      const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
-      const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
-      const uint32_t done = sm.done;
-      __syncthreads();
-      if (done) {
-        thresh = new_lo;   // every key >= new_lo is taken
-        break;
-      }
-      if (shift == 0) {
-        thresh = new_lo;   // keys > thresh, and the first `need` keys == thresh in index order
-        eq_mode = true;
-        break;
-      }
-      lo = new_lo;
-      hi = new_hi;
-    }
-  }
-  if (threadIdx.x == 0) {
-    sm.count = 0;
-    sm.running = 0;
-    chunk_lb[(size_t)bt * n_chunks + c] = sm.lb;
-  }
-  __syncthreads();
+  // ---- the chunk's best min(k_chunk, valid) keys, emitted in entry order
+  auto key_at = [&](int i) -> uint32_t { return keys[i]; };
+  uint32_t mn, mx, nv;
+  key_stats<SC_THREADS>(key_at, Ce, sm, mn, mx, nv);
+  const uint32_t need = nv < (uint32_t)k_chunk ? nv : (uint32_t)k_chunk;
+  const uint32_t r0 = (direct || c == nc_q - 1) ? 0u : rank_for_bound(k, nc_q);
+  SelOut sel;
+  if (need == nv && r0 == 0) sel = SelOut{mn, 0xFFFFFFFFu, 0u};   // every valid key
+  else sel = select_threshold<SC_THREADS>(key_at, Ce, need, mn, mx, r0, sm);
   auto entry_of = [&](int i) -> int {
     if (POOL) {
       const int vj = base + i;
@@ -491,61 +459,32 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     }
     return base + i;
   };
-  if (have) {
-    for (int i = threadIdx.x; i < C; i += SC_THREADS) {
-      const uint32_t kk = sm.keys[i];
-      if (kk && (eq_mode ? kk > thresh : kk >= thresh)) {
-        const uint32_t slot = atomicAdd(&sm.count, 1u);
-        if (slot < (uint32_t)k_chunk) {
-          cand_key[obase + slot] = kk;
-          cand_idx[obase + slot] = entry_of(i);
-        }
-      }
+  if (direct) {
+    int32_t* out = topk + (size_t)bt * k;
+    const uint32_t cnt = emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) { out[slot] = entry_of(i); });
+    for (int i = (int)cnt + threadIdx.x; i < k; i += SC_THREADS) out[i] = -1;
+  } else {
+    const size_t obase = ((size_t)bt * n_chunks + c) * k_chunk;
+    if (threadIdx.x == 0) chunk_lb[(size_t)bt * n_chunks + c] = sel.lb;
+    const uint32_t cnt = emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) {
+      cand_key[obase + slot] = keys[i];
+      cand_idx[obase + slot] = entry_of(i);
+    });
+    for (int i = (int)cnt + threadIdx.x; i < k_chunk; i += SC_THREADS) {
+      cand_key[obase + i] = 0u;
+      cand_idx[obase + i] = -1;
     }
-    if (eq_mode) {
-      // ties at the threshold: the smallest positions (= smallest entry ids) first
-      for (int i0 = 0; i0 < C; i0 += SC_THREADS) {
-        const int i = i0 + threadIdx.x;
-        const bool eq = sm.keys[i] == thresh;
-        const unsigned long long bal = __ballot(eq);
-        const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) sm.wtot[wave] = __popcll(bal);
-        __syncthreads();
-        uint32_t wbase = sm.running;
-        for (int w2 = 0; w2 < wave; ++w2) wbase += sm.wtot[w2];
-        const uint32_t rank = wbase + before;
-        if (eq && rank < need) {
-          const uint32_t slot = atomicAdd(&sm.count, 1u);
-          if (slot < (uint32_t)k_chunk) {
-            cand_key[obase + slot] = thresh;
-            cand_idx[obase + slot] = entry_of(i);
-          }
-        }
-        __syncthreads();
-        if (threadIdx.x == 0)
-          for (int w2 = 0; w2 < SC_THREADS / 64; ++w2) sm.running += sm.wtot[w2];
-        __syncthreads();
-        if (sm.running >= need) break;
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = (int)min(sm.count, (uint32_t)k_chunk) + threadIdx.x; i < k_chunk; i += SC_THREADS) {
-    cand_key[obase + i] = 0u;
-    cand_idx[obase + i] = -1;
   }
 }
 
 constexpr int MG_THREADS = 512;
-constexpr int MAX_SORT = 1024;   // >= k and >= n_b (checked by the host)
-constexpr int MG_CAP = 12288;    // candidates staged in LDS
+constexpr int MG_TILE = 4096;    // candidate keys read into LDS per round
+constexpr int MG_CAP = 4096;     // staged candidates kept in LDS
 
-struct MergeSmem {
-  int list[MAX_SORT];
-  uint32_t count;
-  uint32_t tlb;
-};
-
+// One workgroup per query: candidates of all chunks at or above the bound are
+// staged in LDS in entry order, then the same radix select picks the k best and
+// emits their ids ascending.  With HSI BUILD the n_b best blocks (newest forced)
+// are chosen the same way from the block maxima.
 template <bool POOL, bool BUILD>
 __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restrict__ cand_key,
                                                          const int32_t* __restrict__ cand_idx,
@@ -554,94 +493,104 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                                          const int32_t* __restrict__ q_pos, int32_t* __restrict__ topk,
                                                          int32_t* __restrict__ cands_out, int T_len, int n_entries,
                                                          int m, int k, int C, int k_chunk, int n_chunks, int hsi_s,
-                                                         int hsi_nb, int nblk_max, int cap) {
+                                                         int hsi_nb, int nblk_max) {
   __shared__ SelSmem<MG_THREADS> sel;
-  __shared__ MergeSmem sm;
-  extern __shared__ uint64_t comp_dyn[];   // staged candidates, `cap` of them (dynamic LDS)
+  __shared__ uint32_t tile[MG_TILE];
+  __shared__ int32_t tile_idx[MG_TILE];
+  __shared__ uint32_t skey[MG_CAP];
+  __shared__ int32_t sidx[MG_CAP];
+  __shared__ uint32_t s_bound;
   const int t = blockIdx.x, b = blockIdx.y;
   const int bt = b * T_len + t;
   const int n_t = visible(q_pos, bt, m, n_entries);
   const int nc = POOL ? n_chunks : (n_t + C - 1) / C;
-  const int n_items = nc * k_chunk;
-  const uint32_t* kb = cand_key + (size_t)bt * n_chunks * k_chunk;
-  const int32_t* ib = cand_idx + (size_t)bt * n_chunks * k_chunk;
 
-  auto emit_sorted = [&](int32_t* out, int kk, uint32_t cnt) {
-    int np2 = 1;
-    while (np2 < kk) np2 <<= 1;
-    for (int i = cnt + threadIdx.x; i < np2; i += MG_THREADS) sm.list[i] = 0x7FFFFFFF;
-    __syncthreads();
-    block_bitonic_sort<MG_THREADS>(sm.list, np2);
-    for (int i = threadIdx.x; i < kk; i += MG_THREADS) out[i] = (i < (int)cnt) ? sm.list[i] : -1;
-    __syncthreads();
-  };
-  // select from `n` composites produced by get(i), emit the low 32 bits' entry ids sorted
-  auto select_emit = [&](auto get, int n, uint32_t kk, int32_t* out, auto id_of) {
-    uint64_t prefix, mask;
-    block_select<MG_THREADS>(get, n, kk, 64, sel, prefix, mask);
-    if (threadIdx.x == 0) sm.count = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += MG_THREADS) {
-      const uint64_t cc = get(i);
-      if (cc != 0 && (cc & mask) >= prefix) {
-        const uint32_t slot = atomicAdd(&sm.count, 1u);
-        if (slot < kk) sm.list[slot] = id_of(i, cc);
-      }
-    }
-    __syncthreads();
-    const uint32_t cnt = min(sm.count, kk);
-    __syncthreads();
-    emit_sorted(out, (int)kk, cnt);
-  };
-
-  {
-    // lower bound of the k-th best key: min over chunks of their rank-r0 bounds
-    if (threadIdx.x == 0) {
-      sm.count = 0;
+  if (BUILD || nc > 1) {
+    const int n_items = nc * k_chunk;
+    const uint32_t* kb = cand_key + (size_t)bt * n_chunks * k_chunk;
+    const int32_t* ib = cand_idx + (size_t)bt * n_chunks * k_chunk;
+    int32_t* out = topk + (size_t)bt * k;
+    // bound: smallest rank-r0 key over the full chunks (0 = none)
+    uint32_t bound = 0;
+    if (nc > 1) {
       uint32_t tl = 0xFFFFFFFFu;
-      for (int c = 0; c < nc; ++c) tl = min(tl, chunk_lb[(size_t)bt * n_chunks + c]);
-      sm.tlb = nc > 0 ? tl : 0u;
+      for (int cc = threadIdx.x; cc < nc - 1; cc += MG_THREADS) tl = min(tl, chunk_lb[(size_t)bt * n_chunks + cc]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) tl = min(tl, (uint32_t)__shfl_xor((int)tl, off, 64));
+      if (threadIdx.x == 0) s_bound = 0xFFFFFFFFu;
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) atomicMin(&s_bound, tl);
+      __syncthreads();
+      bound = s_bound;
     }
-    __syncthreads();
-    const uint32_t tlb = sm.tlb;
-    for (int i = threadIdx.x; i < n_items; i += MG_THREADS) {
-      const uint32_t kk = kb[i];
-      if (kk != 0 && kk >= tlb) {
-        const uint32_t slot = atomicAdd(&sm.count, 1u);
-        if (slot < (uint32_t)cap) comp_dyn[slot] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ib[i]);
+    // stage candidates >= bound in entry order
+    uint32_t staged = 0;
+    const SelOut keep{bound, 0xFFFFFFFFu, 0u};
+    for (int r = 0; r < n_items; r += MG_TILE) {
+      const int len = min(MG_TILE, n_items - r);
+      for (int i = threadIdx.x; i < len; i += MG_THREADS) {
+        tile[i] = kb[r + i];
+        tile_idx[i] = ib[r + i];
       }
+      __syncthreads();
+      const uint32_t base_slot = staged;
+      staged += emit_ordered<MG_THREADS>([&](int i) -> uint32_t { return tile[i]; }, len, keep, sel,
+                                         [&](int i, uint32_t slot) {
+                                           slot += base_slot;
+                                           if (slot < (uint32_t)MG_CAP) {
+                                             skey[slot] = tile[i];
+                                             sidx[slot] = tile_idx[i];
+                                           }
+                                         });
+      __syncthreads();
     }
-    __syncthreads();
-    const uint32_t staged = sm.count;
-    __syncthreads();
-    auto id_of = [&](int, uint64_t cc) -> int { return (int)(0xFFFFFFFFu - (uint32_t)(cc & 0xFFFFFFFFu)); };
-    if (staged <= (uint32_t)cap) {
-      auto get = [&](int i) -> uint64_t { return comp_dyn[i]; };
-      select_emit(get, (int)staged, (uint32_t)k, topk + (size_t)bt * k, id_of);
+    uint32_t cnt;
+    if (staged <= (uint32_t)MG_CAP) {
+      auto key_at = [&](int i) -> uint32_t { return skey[i]; };
+      uint32_t mn, mx, nv;
+      key_stats<MG_THREADS>(key_at, (int)staged, sel, mn, mx, nv);
+      const uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
+      const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                  : select_threshold<MG_THREADS>(key_at, (int)staged, need, mn, mx, 0u, sel);
+      cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel, [&](int i, uint32_t slot) { out[slot] = sidx[i]; });
     } else {
-      auto get = [&](int i) -> uint64_t {
-        const uint32_t kk = kb[i];
-        return (kk == 0 || kk < tlb) ? 0ull : (((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)ib[i]));
-      };
-      select_emit(get, n_items, (uint32_t)k, topk + (size_t)bt * k, id_of);
+      // more candidates than LDS holds: select straight from the workspace
+      auto key_at = [&](int i) -> uint32_t { const uint32_t kk = kb[i]; return kk >= bound ? kk : 0u; };
+      uint32_t mn, mx, nv;
+      key_stats<MG_THREADS>(key_at, n_items, sel, mn, mx, nv);
+      const uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
+      const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                  : select_threshold<MG_THREADS>(key_at, n_items, need, mn, mx, 0u, sel);
+      cnt = emit_ordered<MG_THREADS>(key_at, n_items, s, sel, [&](int i, uint32_t slot) { out[slot] = ib[i]; });
     }
+    for (int i = (int)cnt + threadIdx.x; i < k; i += MG_THREADS) out[i] = -1;
   }
   if (BUILD) {
+    __syncthreads();
     const int nblk = (n_t + hsi_s - 1) / hsi_s;
     const uint32_t* bm = blkmax + (size_t)bt * nblk_max;
-    auto bget = [&](int i) -> uint64_t {
-      const uint32_t kk = (i == nblk - 1) ? 0xFFFFFFFFu : bm[i];  // newest block forced in
-      return kk == 0 ? 0ull : (((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i));
-    };
-    auto id_of = [&](int i, uint64_t) -> int { return i; };
-    if (nblk <= cap) {
-      for (int i = threadIdx.x; i < nblk; i += MG_THREADS) comp_dyn[i] = bget(i);
+    int32_t* out = cands_out + (size_t)bt * hsi_nb;
+    auto bkey = [&](int i) -> uint32_t { return (i == nblk - 1) ? 0xFFFFFFFFu : bm[i]; };  // newest block forced in
+    uint32_t cnt;
+    if (nblk <= MG_CAP) {
+      for (int i = threadIdx.x; i < nblk; i += MG_THREADS) skey[i] = bkey(i);
       __syncthreads();
-      auto get = [&](int i) -> uint64_t { return comp_dyn[i]; };
-      select_emit(get, nblk, (uint32_t)hsi_nb, cands_out + (size_t)bt * hsi_nb, id_of);
+      auto key_at = [&](int i) -> uint32_t { return skey[i]; };
+      uint32_t mn, mx, nv;
+      key_stats<MG_THREADS>(key_at, nblk, sel, mn, mx, nv);
+      const uint32_t need = nv < (uint32_t)hsi_nb ? nv : (uint32_t)hsi_nb;
+      const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                  : select_threshold<MG_THREADS>(key_at, nblk, need, mn, mx, 0u, sel);
+      cnt = emit_ordered<MG_THREADS>(key_at, nblk, s, sel, [&](int i, uint32_t slot) { out[slot] = i; });
     } else {
-      select_emit(bget, nblk, (uint32_t)hsi_nb, cands_out + (size_t)bt * hsi_nb, id_of);
+      uint32_t mn, mx, nv;
+      key_stats<MG_THREADS>(bkey, nblk, sel, mn, mx, nv);
+      const uint32_t need = nv < (uint32_t)hsi_nb ? nv : (uint32_t)hsi_nb;
+      const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                  : select_threshold<MG_THREADS>(bkey, nblk, need, mn, mx, 0u, sel);
+      cnt = emit_ordered<MG_THREADS>(bkey, nblk, s, sel, [&](int i, uint32_t slot) { out[slot] = i; });
     }
+    for (int i = (int)cnt + threadIdx.x; i < hsi_nb; i += MG_THREADS) out[i] = -1;
   }
 }
 
@@ -659,25 +608,15 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   const int nblk_max = BUILD ? (n_entries + hsi_s - 1) / hsi_s : 0;
   dim3 g1(p.n_chunks, T_len, B);
   hipLaunchKernelGGL((score_chunk<T, POOL, BUILD>), g1, dim3(SC_THREADS), 0, st, static_cast<const T*>(q_idx), w,
-                     codes, scales, q_pos, cands, cand_key, cand_idx, chunk_lb, blkmax, T_len, H_I, N_cap, n_entries, m,
-                     p.chunk, p.k_chunk, p.n_chunks, k, hsi_s, hsi_nb, nblk_max);
+                     codes, scales, q_pos, cands, cand_key, cand_idx, chunk_lb, blkmax, topk, T_len, H_I, N_cap,
+                     n_entries, m, p.chunk, p.k_chunk, p.n_chunks, k, hsi_s, hsi_nb, nblk_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // LDS for staged candidates: enough for all of them (or all block maxima) up to MG_CAP
-  long long want = (long long)p.n_chunks * p.k_chunk;
-  if (nblk_max > want) want = nblk_max;
-  const int cap = (int)(want < MG_CAP ? want : MG_CAP);
-  const size_t dyn = (size_t)cap * 8;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge<POOL, BUILD>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, MG_CAP * 8);
-    attr_set = true;
-  }
+  if (!BUILD && p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single chunk
   dim3 g2(T_len, B);
-  hipLaunchKernelGGL((topk_merge<POOL, BUILD>), g2, dim3(MG_THREADS), dyn, st, cand_key, cand_idx, chunk_lb, blkmax,
+  hipLaunchKernelGGL((topk_merge<POOL, BUILD>), g2, dim3(MG_THREADS), 0, st, cand_key, cand_idx, chunk_lb, blkmax,
                      q_pos, topk, cands, T_len, n_entries, m, k, p.chunk, p.k_chunk, p.n_chunks, hsi_s, hsi_nb,
-                     nblk_max, cap);
+                     nblk_max);
   return hipGetLastError();
 }
 

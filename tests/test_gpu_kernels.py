@@ -197,6 +197,58 @@ def test_score_topk_hsi_build_and_use():
 
 # ------------------------------------------------------------ attention ----
 
+@pytest.mark.parametrize("H,k,W", [(64, 512, 128), (20, 77, 5), (64, 96, 40)])
+def test_sparse_attn_prefill_path_vs_oracle(H, k, W):
+    """Many query tokens (the prefill kernel): selected rows with holes (-1 and
+    out-of-range ids inside the list, a run of more than one 32-row chunk of holes),
+    rows with nothing selected, windows clipped by swa_pos0 and by 0 (a token with
+    neither rows nor window gets 0 and lse -inf); two sequences.  Every 13th token
+    is checked row by row against the oracle."""
+    B, T, N_cap, L_w = 2, 600, 700, 620
+    say(f"case: sparse_attn prefill path bf16 H={H} k={k} W={W} T={T}")
+    gen = np.random.default_rng(37)
+    q = synth.gaussian((B, T, H, 512), 1.0, 37, "q", 0, torch.bfloat16, DEV)
+    kv = synth.gaussian((B, N_cap, 512), 1.0, 37, "kv_cache", 0, torch.bfloat16, DEV)
+    swa = synth.gaussian((B, L_w, 512), 1.0, 37, "swa_kv", 0, torch.bfloat16, DEV)
+    pos0 = np.array([30, 0], np.int32)
+    pos = np.stack([np.arange(T) + 25, np.arange(T)]).astype(np.int32)  # b=0: early windows clipped by pos0
+    tk = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(gen.integers(0, k + 1)) if t % 7 else (0 if t % 14 == 0 else k)
+            ids = np.sort(gen.choice(N_cap, size=n, replace=False)).astype(np.int32)
+            tk[b, t, :n] = ids
+            if n > 3 and t % 3 == 0:
+                tk[b, t, n // 2] = -1                # hole inside the list
+                tk[b, t, n // 3] = N_cap + 9         # out-of-range id inside the list
+            if n >= 80 and t % 5 == 0:
+                tk[b, t, 5:45] = -1                  # a run of holes longer than one chunk
+    o = torch.empty_like(q)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=DEV)
+    K.csa2_sparse_attn(None, q, kv, torch.from_numpy(tk).to(DEV), swa, torch.from_numpy(pos0).to(DEV),
+                       torch.from_numpy(pos).to(DEV), o, W=W, lse=lse)
+    torch.cuda.synchronize()
+    og, lg = npy(o), lse.cpu().numpy()
+    kvn, swn, qn = npy(kv), npy(swa), npy(q)
+    worst, n_checked = 0.0, 0
+    for b in range(B):
+        for t in list(range(0, T, 13)) + [T - 3, T - 2, T - 1]:
+            sel = tk[b, t]
+            sel = sel[(sel >= 0) & (sel < N_cap)]
+            if len(sel) + len(O.window_positions(int(pos[b, t]), W, int(pos0[b]))) == 0:
+                assert np.all(og[b, t] == 0) and np.all(np.isneginf(lg[b, t])), (b, t)
+                continue
+            ref, p, rows = O.sparse_attention(qn[b, t], kvn[b], sel, swn[b], int(pos0[b]), int(pos[b, t]), W)
+            worst = max(worst, row_rel_err(og[b, t], ref))
+            logits = (qn[b, t] @ rows.T) / math.sqrt(512)
+            mx = logits.max(1)
+            lse_ref = mx + np.log(np.exp(logits - mx[:, None]).sum(1))
+            assert np.allclose(lg[b, t], lse_ref, rtol=1e-4, atol=1e-3), (b, t)
+            n_checked += 1
+    say(f"  {n_checked} tokens checked, worst row rel err {worst:.2e}")
+    assert worst <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype,H,k,W", [(torch.float32, 8, 32, 16), (torch.bfloat16, 64, 512, 128),
                                          (torch.bfloat16, 20, 77, 5)])
 def test_sparse_attn_vs_oracle(dtype, H, k, W):
