@@ -30,6 +30,7 @@
 //   (normalised output + log-sum-exp) that attn_combine merges.
 #include "csa2_internal.h"
 #include "device_common.h"
+#include "lds_dma.h"
 
 namespace csa2 {
 
@@ -40,35 +41,11 @@ constexpr int MAX_ROWS = 2048;   // selected + window rows per query (host-check
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory ops
-// of this wave are outstanding / until all LDS ops are done.
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-#define WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 __device__ __forceinline__ void dma16(const void* gsrc, lds_u8* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)ldst, 16, 0, 0);
 }
-
-// The same gather written as inline assembly.  The compiler cannot tell which LDS
-// buffer the builtin form writes, so before reads of the other buffer it waits for
-// every gather in flight (vmcnt(0)), which serialises the double buffering.  This
-// form is invisible to that analysis: the caller orders it with explicit
-// s_waitcnt vmcnt and barriers.  The compiler still waits correctly for its own
-// loads (it may wait longer than needed, never shorter, since it undercounts the
-// operations in flight).  M0 is set here on every call.
-__device__ __forceinline__ void dma16_asm(const void* gsrc, const lds_u8* ldst) {
-  const uint32_t base = (uint32_t)(uintptr_t)ldst;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(gsrc) : "memory");
-}
-// Same, with the row base in an SGPR pair and a 32-bit per-lane byte offset.
-__device__ __forceinline__ void dma16_asm_s(uint64_t sbase, uint32_t voff, const lds_u8* ldst) {
-  const uint32_t base = (uint32_t)(uintptr_t)ldst;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbase)
-               : "memory");
-}
-#define COMPILER_FENCE() __asm__ volatile("" ::: "memory")
 
 // Max over lanes l and l^16, then l^32, with the gfx950 permlane swaps (VALU, no LDS).
 __device__ __forceinline__ float max_lane_groups(float x) {

@@ -19,6 +19,7 @@
 // pre-RoPE latent (float32, in place) and the cache row with RoPE applied.
 #include "csa2_internal.h"
 #include "device_common.h"
+#include "lds_dma.h"
 
 namespace csa2 {
 
@@ -164,6 +165,144 @@ __global__ __launch_bounds__(256) void compress_gemm_pool(
   }
 }
 
+// ---- bf16 projection: 256-token x 128-column tiles, 8 waves of 64 x 64, operands
+// gathered straight into LDS (3-stage ring of 48 KB stages, one barrier per
+// 64-wide k step).  LDS rows are 128 B = 8 units of 16 B; unit u of row r is
+// stored in slot u ^ (r & 7), so the 8 lanes that share an LDS cycle in a
+// fragment read hit 8 different slots.  The gather makes this layout by letting
+// lane i (which the load instruction writes to slot i & 7 of row i >> 3) fetch
+// unit (i & 7) ^ (row & 7) of its row.
+constexpr int G_BM = 256;
+constexpr int G_BN = 128;
+constexpr int G_A_BYTES = G_BM * 128;
+constexpr int G_STAGE = G_A_BYTES + G_BN * 128;   // 48 KB
+
+template <int M_RATIO>
+__global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __restrict__ x,
+                                                               const bf16* __restrict__ w_kv,
+                                                               const bf16* __restrict__ w_gate,
+                                                               float* __restrict__ e_out, int T_len, int D) {
+  __shared__ __attribute__((aligned(16))) unsigned char st0[G_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[G_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[G_STAGE];
+
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int b = blockIdx.z;
+  const int row0 = blockIdx.x * G_BM;
+  constexpr bool gated = M_RATIO > 1;
+  const int ch0 = blockIdx.y * (gated ? 64 : 128);
+  const bf16* xb = x + (size_t)b * T_len * D;
+
+  // this lane's 6 source rows (4 of the token tile, 2 of the weight tile), with
+  // its swizzled 16-B unit folded in; the k offset is added per stage
+  const unsigned char* gsrc[6];
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    const int j = wave + 8 * q;             // gather instruction: stage rows 8j .. 8j+7
+    const int r = 8 * (j & 31) + (lane >> 3);
+    const int unit = (lane & 7) ^ (r & 7);
+    const bf16* rowp;
+    if (q < 4) {
+      const int tok = min(row0 + r, T_len - 1);   // rows past the end repeat the last token (discarded)
+      rowp = xb + (size_t)tok * D;
+    } else if (gated) {
+      const int ch = ch0 + 32 * (r >> 6) + (r & 31);
+      rowp = ((r & 63) < 32 ? w_kv : w_gate) + (size_t)ch * D;
+    } else {
+      rowp = w_kv + (size_t)(ch0 + r) * D;
+    }
+    gsrc[q] = reinterpret_cast<const unsigned char*>(rowp) + unit * 16;
+  }
+  auto issue = [&](int kt, unsigned char* st) {
+#pragma unroll
+    for (int q = 0; q < 6; ++q) dma16_asm(gsrc[q] + (size_t)kt * 128, (const lds_u8*)(st + (wave + 8 * q) * 1024));
+  };
+
+  // fragment offsets: row (tile row) * 128 + slot * 16; r & 7 == lr & 7 for every fragment row
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int slot = (ks * 4 + lg) ^ (lr & 7);
+    aoff[ks] = (wm * 64 + lr) * 128 + slot * 16;
+    boff[ks] = G_A_BYTES + (wn * 64 + lr) * 128 + slot * 16;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = D / 64;
+  auto step = [&](int kt, const unsigned char* cur, unsigned char* nxt2) {
+    if (kt + 1 < nk) WAIT_VMCNT(6);   // this wave's gathers of stage kt are in (kt+1's may fly)
+    else WAIT_VMCNT(0);
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();
+    COMPILER_FENCE();
+    // every wave is past stage kt-1, whose buffer takes stage kt+2
+    if (kt + 2 < nk) issue(kt + 2, nxt2);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[4], bb[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(cur + aoff[ks] + mt * 16 * 128);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bb[nt] = *reinterpret_cast<const bf16x8*>(cur + boff[ks] + nt * 16 * 128);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma16(a[mt], bb[nt], acc[mt][nt]);
+    }
+  };
+  issue(0, st0);
+  if (nk > 1) issue(1, st1);
+  for (int kt = 0; kt < nk; kt += 3) {
+    step(kt, st0, st2);
+    if (kt + 1 < nk) step(kt + 1, st1, st0);
+    if (kt + 2 < nk) step(kt + 2, st2, st1);
+  }
+
+  // epilogue: lane holds tokens row0 + wm*64 + mt*16 + 4*lg + i, column l%16 of n-tile nt
+  const int n_entries = T_len / M_RATIO;
+  float* eb = e_out + (size_t)b * n_entries * 512;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int tok0 = row0 + wm * 64 + mt * 16 + 4 * lg;
+    if (gated) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int ch = ch0 + 32 * wn + 16 * nt + lr;
+        const f32x4 c = acc[mt][nt], z = acc[mt][nt + 2];
+#pragma unroll
+        for (int g0 = 0; g0 < 4; g0 += M_RATIO) {
+          if (tok0 + g0 >= T_len) continue;
+          float zmax = z[g0];
+#pragma unroll
+          for (int i = 1; i < M_RATIO; ++i) zmax = fmaxf(zmax, z[g0 + i]);
+          float num = 0.f, den = 0.f;
+#pragma unroll
+          for (int i = 0; i < M_RATIO; ++i) {
+            const float p = __expf(z[g0 + i] - zmax);
+            den += p;
+            num += p * c[g0 + i];
+          }
+          eb[(size_t)((tok0 + g0) / M_RATIO) * 512 + ch] = num / den;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int ch = ch0 + 64 * wn + 16 * nt + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + i < T_len) eb[(size_t)(tok0 + i) * 512 + ch] = acc[mt][nt][i];
+      }
+    }
+  }
+}
+
 // One wave per entry: RMSNorm, RoPE on dims 448..511, write latent (fp32, in
 // place over the pooled values) and the cache row.
 template <typename T>
@@ -220,9 +359,16 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
   const T* xx = static_cast<const T*>(x);
   const T* wk = static_cast<const T*>(w_kv);
   const T* wg = static_cast<const T*>(w_gate);
-  if (m == 1) hipLaunchKernelGGL((compress_gemm_pool<T, 1>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
-  else if (m == 2) hipLaunchKernelGGL((compress_gemm_pool<T, 2>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
-  else hipLaunchKernelGGL((compress_gemm_pool<T, 4>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+  if constexpr (sizeof(T) == 2) {
+    dim3 gb((T_len + G_BM - 1) / G_BM, m > 1 ? 512 / 64 : 512 / 128, B);
+    if (m == 1) hipLaunchKernelGGL((compress_gemm_pool_bf16<1>), gb, dim3(512), 0, st, xx, wk, wg, lat, T_len, D);
+    else if (m == 2) hipLaunchKernelGGL((compress_gemm_pool_bf16<2>), gb, dim3(512), 0, st, xx, wk, wg, lat, T_len, D);
+    else hipLaunchKernelGGL((compress_gemm_pool_bf16<4>), gb, dim3(512), 0, st, xx, wk, wg, lat, T_len, D);
+  } else {
+    if (m == 1) hipLaunchKernelGGL((compress_gemm_pool<T, 1>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+    else if (m == 2) hipLaunchKernelGGL((compress_gemm_pool<T, 2>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+    else hipLaunchKernelGGL((compress_gemm_pool<T, 4>), grid, blk, 0, st, xx, wk, wg, lat, T_len, D);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 g2((n_entries + 3) / 4, B);
