@@ -137,7 +137,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
   constexpr int RPW = PRC / NW;          // rows gathered per wave per chunk
 
-  const int t = blockIdx.x, b = blockIdx.y;
+  // workgroups are dealt to the 8 XCDs round-robin by id; give each XCD one
+  // contiguous run of tokens, so the window rows (shared by neighbouring tokens)
+  // stay in that XCD's L2
+  const int per_xcd = (T_len + 7) >> 3;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3), b = blockIdx.y;
+  if (t >= T_len) return;
   const int bt = b * T_len + t;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,11 +153,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
 
   // rows: selected slots [0, k_eff) (k_eff = one past the last valid id), then the window
   int k_eff = 0;
-  for (int j0 = 0; j0 < k; j0 += 64) {
-    const int j = j0 + lane;
-    const int g = j < k ? tk[j] : -1;
-    const unsigned long long bal = __ballot(g >= 0 && g < N_cap);
-    if (bal) k_eff = j0 + 64 - __clzll(bal);
+  for (int j0 = 0; j0 < k; j0 += 512) {   // 8 loads per lane in flight, then the ballots
+    int g[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + 64 * u + lane;
+      g[u] = j < k ? tk[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const unsigned long long bal = __ballot(g[u] >= 0 && g[u] < N_cap);
+      if (bal) k_eff = j0 + 64 * u + 64 - __clzll(bal);
+    }
   }
   const int p = q_pos[bt], pos0 = swa_pos0[b];
   int lo = p - W + 1;
@@ -764,10 +776,10 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   if (!p.decode) {
     // head pairs of 32 heads; two waves (dim halves) each
     if (H > 32)
-      hipLaunchKernelGGL(attn_prefill_bf16<4>, dim3(T, B), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+      hipLaunchKernelGGL(attn_prefill_bf16<4>, dim3(8 * ((T + 7) / 8), B), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
                          oo, lse, T, H, N_cap, k, L_w, W, sl2);
     else
-      hipLaunchKernelGGL(attn_prefill_bf16<2>, dim3(T, B), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+      hipLaunchKernelGGL(attn_prefill_bf16<2>, dim3(8 * ((T + 7) / 8), B), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
                          oo, lse, T, H, N_cap, k, L_w, W, sl2);
     return hipGetLastError();
   }
