@@ -258,7 +258,7 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* in, cs
   csa2_score_topk_args a = *in;
   csa2_status s = resolve_score(rt, a);
   if (s != CSA2_OK) return s;
-  const csa2::ScorePlan plan = csa2::plan_score(a.B, a.T, score_scan(a), a.k, a.hsi, a.hsi_s, a.hsi_nb);
+  const csa2::ScorePlan plan = csa2::plan_score(a.dtype, a.B, a.T, score_scan(a), a.k, a.hsi, a.hsi_s, a.hsi_nb);
   REQ(a.workspace != nullptr && a.workspace_bytes >= plan.total_bytes, CSA2_ERR_WORKSPACE,
       "csa2_score_topk: workspace of %zu bytes needed (got %zu)", plan.total_bytes, a.workspace_bytes);
   hipError_t e = csa2::launch_score_topk(a.dtype, a.q_idx, a.w, a.codes, a.scales, a.q_pos, a.topk, a.candidates, a.B,
@@ -289,7 +289,7 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   REQ(bytes && args, CSA2_ERR_INVALID_ARG, "csa2_workspace_size: NULL argument");
   if (op == CSA2_OP_SCORE_TOPK) {
     const csa2_score_topk_args* a = static_cast<const csa2_score_topk_args*>(args);
-    *bytes = csa2::plan_score(a->B, a->T, score_scan(*a), a->k, a->hsi, a->hsi_s, a->hsi_nb).total_bytes;
+    *bytes = csa2::plan_score(a->dtype, a->B, a->T, score_scan(*a), a->k, a->hsi, a->hsi_s, a->hsi_nb).total_bytes;
     return ok();
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
@@ -304,7 +304,7 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
     if (cfg->mode != CSA2_REUSE) {
       const int n_entries = io->N_cap;  // upper bound
       const int scan = cfg->hsi == CSA2_HSI_USE ? cfg->hsi_nb * cfg->hsi_s : n_entries;
-      const size_t sb = csa2::plan_score(io->B, io->T, scan, cfg->k, cfg->hsi, cfg->hsi_s, cfg->hsi_nb).total_bytes;
+      const size_t sb = csa2::plan_score(cfg->dtype, io->B, io->T, scan, cfg->k, cfg->hsi, cfg->hsi_s, cfg->hsi_nb).total_bytes;
       if (sb > need) need = sb;
     }
     *bytes = need;
@@ -357,7 +357,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     }
     s = resolve_score(rt, sa);
     if (s != CSA2_OK) return s;
-    const csa2::ScorePlan plan = csa2::plan_score(sa.B, sa.T, score_scan(sa), sa.k, sa.hsi, sa.hsi_s, sa.hsi_nb);
+    const csa2::ScorePlan plan = csa2::plan_score(sa.dtype, sa.B, sa.T, score_scan(sa), sa.k, sa.hsi, sa.hsi_s, sa.hsi_nb);
     REQ(sa.workspace != nullptr && sa.workspace_bytes >= plan.total_bytes, CSA2_ERR_WORKSPACE,
         "csa2_layer_forward: workspace of %zu bytes needed (got %zu)", plan.total_bytes, sa.workspace_bytes);
   }

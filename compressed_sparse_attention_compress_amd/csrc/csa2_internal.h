@@ -23,12 +23,13 @@ hipError_t launch_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, ui
 
 // ---- indexer score + top-k (k_score.hip)
 struct ScorePlan {
+  bool tiled;       // two-phase path: query-tiled scoring into a key matrix, then one select per query
   int chunk;        // entries per chunk (power of two)
   int n_chunks;     // chunks per query
   int k_chunk;      // candidates kept per chunk = min(k, chunk)
-  size_t cand_bytes, lb_bytes, blk_bytes, total_bytes;
+  size_t cand_bytes, lb_bytes, blk_bytes, key_bytes, total_bytes;
 };
-ScorePlan plan_score(int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb);
+ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb);
 hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
                              const uint8_t* scales, const int32_t* q_pos, int32_t* topk,
                              int32_t* candidates, int B, int T, int H_I, int N_cap, int n_entries,

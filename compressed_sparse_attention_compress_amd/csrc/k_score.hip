@@ -528,9 +528,23 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     const SelOut keep{bound, 0xFFFFFFFFu, 0u};
     for (int r = 0; r < n_items; r += MG_TILE) {
       const int len = min(MG_TILE, n_items - r);
-      for (int i = threadIdx.x; i < len; i += MG_THREADS) {
-        tile[i] = kb[r + i];
-        tile_idx[i] = ib[r + i];
+      for (int i0 = 0; i0 < len; i0 += 4 * MG_THREADS) {   // all loads of a round in flight together
+        uint32_t kk[4];
+        int32_t ii[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * MG_THREADS + threadIdx.x;
+          kk[u] = i < len ? kb[r + i] : 0u;
+          ii[u] = i < len ? ib[r + i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * MG_THREADS + threadIdx.x;
+          if (i < len) {
+            tile[i] = kk[u];
+            tile_idx[i] = ii[u];
+          }
+        }
       }
       __syncthreads();
       const uint32_t base_slot = staged;
@@ -594,6 +608,324 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-phase path for many queries over one cache (prefill, bf16, flat selection):
+// score_qtile scores QT = 4 consecutive queries per workgroup, so each staged and
+// dequantised K tile feeds 4 queries x 2 head tiles = 8 MFMAs; the key of every
+// visible (query, entry) pair goes to a key matrix in the workspace, and
+// select_rows then picks each query's top-k from its row.
+//
+// The FP4 codes are dequantised with the block scale applied before the MFMA:
+// code value (at most 2 significant bits) x E4M3 scale (4 significant bits) is
+// exact in bf16, so one MFMA chain covers all 4 blocks of the 128 dims.
+constexpr int QT = 4;                 // queries per workgroup
+constexpr int QT_CE = 4096;           // entries per workgroup (64 super-tiles of 64)
+constexpr int SEL_MAX = 8192;         // keys per query row held in LDS by select_rows
+
+__device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t w, float s) {
+  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  bf16x8 r;
+  r[0] = (bf16)(p0[0] * s); r[1] = (bf16)(p0[1] * s); r[2] = (bf16)(p1[0] * s); r[3] = (bf16)(p1[1] * s);
+  r[4] = (bf16)(p2[0] * s); r[5] = (bf16)(p2[1] * s); r[6] = (bf16)(p3[0] * s); r[7] = (bf16)(p3[1] * s);
+  return r;
+}
+
+__global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
+    const bf16* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ keys,
+    int T_len, int H_I, int N_cap, int n_entries, int m, int n_scan) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[4 * ST_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[4 * ST_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[4 * ST_BYTES];
+  const int c = blockIdx.x, t0 = blockIdx.y * QT, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int n_q[QT];
+  int n_max = 0;
+#pragma unroll
+  for (int qi = 0; qi < QT; ++qi) {
+    n_q[qi] = t0 + qi < T_len ? visible(q_pos, b * T_len + t0 + qi, m, n_entries) : 0;
+    n_max = max(n_max, n_q[qi]);
+  }
+  const int base = c * QT_CE;
+  if (base >= n_max) return;
+  const int n_here = min(QT_CE, n_max - base);
+  const int n_st = (n_here + 63) / 64;
+  const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave: wave, wave + 4, ...
+
+  bf16x8 qf[QT][2][4];
+  float wv[QT][2][4];
+#pragma unroll
+  for (int qi = 0; qi < QT; ++qi) {
+    const int bt = b * T_len + min(t0 + qi, T_len - 1);
+    const bf16* qb = q_idx + (size_t)bt * H_I * 128;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int h = mt * 16 + lr;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (h < H_I) qf[qi][mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
+        else zero_frag(qf[qi][mt][kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        wv[qi][mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
+      }
+    }
+  }
+  const uint8_t* cb = codes + (size_t)b * N_cap * 64;
+  const uint8_t* sb = scales + (size_t)b * N_cap * 4;
+  // staging as in score_chunk: one DMA per 16-entry tile (swizzled 16-B pieces) and one for the scales
+  const int dma_e = lane >> 2, dma_b = ((lane & 3) - (dma_e >> 2)) & 3;
+  auto issue = [&](int i, unsigned char* ring) {
+    const int st = wave + 4 * i;
+    unsigned char* dst = ring + wave * ST_BYTES;
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const int ent = min(base + st * 64 + tt * 16 + dma_e, n_entries - 1);
+      dma16(cb + (size_t)ent * 64 + 16 * dma_b, (lds_u8*)(dst + tt * 1024));
+    }
+    const int ent = min(base + st * 64 + lane, n_entries - 1);
+    dma4(sb + (size_t)ent * 4, (lds_u8*)(dst + SPT * 1024));
+  };
+  uint32_t* krow[QT];
+#pragma unroll
+  for (int qi = 0; qi < QT; ++qi) krow[qi] = keys + (size_t)(b * T_len + min(t0 + qi, T_len - 1)) * n_scan;
+  auto compute = [&](int i, const unsigned char* ring) {
+    const int st = wave + 4 * i;
+    const unsigned char* src = ring + wave * ST_BYTES;
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const unsigned char* tb = src + tt * 1024;
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
+      const float scv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sw, 0), __builtin_amdgcn_cvt_f32_fp8((int)sw, 1),
+                            __builtin_amdgcn_cvt_f32_fp8((int)sw, 2), __builtin_amdgcn_cvt_f32_fp8((int)sw, 3)};
+      f32x4 acc[QT][2];
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) {
+        acc[qi][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[qi][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
+        const bf16x8 kf = fp4x8_scaled_bf16(cw, scv[kb]);
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) {
+          acc[qi][0] = mma16(qf[qi][0][kb], kf, acc[qi][0]);
+          acc[qi][1] = mma16(qf[qi][1][kb], kf, acc[qi][1]);
+        }
+      }
+      const int e = base + st * 64 + tt * 16 + lr;
+#pragma unroll
+      for (int qi = 0; qi < QT; ++qi) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) part += wv[qi][mt][ii] * fmaxf(acc[qi][mt][ii], 0.0f);
+        part = sum_lane_groups(part);
+        if (lg == 0 && e < n_q[qi]) krow[qi][e] = score_key(part);
+      }
+    }
+  };
+  if (st_w > 0) issue(0, ring0);
+  if (st_w > 1) issue(1, ring1);
+  auto step = [&](int i, const unsigned char* cur, unsigned char* nxt) {
+    if (i + 2 < st_w) {
+      issue(i + 2, nxt);
+      WAIT_VMCNT(2 * (SPT + 1));
+    } else if (i + 1 < st_w) {
+      WAIT_VMCNT(SPT + 1);
+    } else {
+      WAIT_VMCNT(0);
+    }
+    compute(i, cur);
+    WAIT_LGKM0();
+  };
+  for (int i = 0; i < st_w; i += 3) {
+    step(i, ring0, ring2);
+    if (i + 1 < st_w) step(i + 1, ring1, ring0);
+    if (i + 2 < st_w) step(i + 2, ring2, ring1);
+  }
+}
+
+// One workgroup per query, its visible keys held in registers: thread t owns the
+// SEL_KPT consecutive positions t*SEL_KPT.., so the chosen ids come out in
+// position order from one block-wide prefix sum.  Radix select as in
+// select_threshold (2048 bins over the live key range, ties in position order).
+constexpr int SEL_KPT = SEL_MAX / SC_THREADS;   // 32
+
+__global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __restrict__ keys,
+                                                          const int32_t* __restrict__ q_pos,
+                                                          int32_t* __restrict__ topk, int T_len, int n_entries,
+                                                          int m, int n_scan, int k) {
+  __shared__ SelSmem<SC_THREADS> sm;
+  __shared__ __attribute__((aligned(16))) uint32_t kl[SEL_MAX];
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int bt = b * T_len + t;
+  const int n_t = min(visible(q_pos, bt, m, n_entries), n_scan);
+  const uint32_t* row = keys + (size_t)bt * n_scan;
+  // coalesced row read into LDS, then each thread takes its contiguous segment
+  const int n_pad = (n_t + 3) & ~3;
+  for (int i0 = 0; i0 < n_pad; i0 += 8 * SC_THREADS) {   // 8 loads per thread in flight
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * SC_THREADS + threadIdx.x;
+      v[u] = i < n_t ? row[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * SC_THREADS + threadIdx.x;
+      if (i < n_pad) kl[i] = v[u];
+    }
+  }
+  __syncthreads();
+  const int p0 = threadIdx.x * SEL_KPT;
+  uint32_t kv[SEL_KPT];
+#pragma unroll
+  for (int i = 0; i < SEL_KPT; i += 4) {
+    if (p0 + i < n_pad) {
+      const uint4 v4 = *reinterpret_cast<const uint4*>(&kl[p0 + i]);
+      kv[i] = v4.x; kv[i + 1] = v4.y; kv[i + 2] = v4.z; kv[i + 3] = v4.w;
+    } else {
+      kv[i] = kv[i + 1] = kv[i + 2] = kv[i + 3] = 0u;
+    }
+  }
+
+  // non-zero count, min and max
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
+#pragma unroll
+  for (int i = 0; i < SEL_KPT; ++i)
+    if (kv[i]) {
+      mn = min(mn, kv[i]);
+      mx = max(mx, kv[i]);
+      ++nv;
+    }
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+      nv += (uint32_t)__shfl_xor((int)nv, off, 64);
+    }
+    if (lane == 0) {
+      sm.red[0][wave] = mn;
+      sm.red[1][wave] = mx;
+      sm.red[2][wave] = nv;
+    }
+    __syncthreads();
+    mn = sm.red[0][0]; mx = sm.red[1][0]; nv = sm.red[2][0];
+#pragma unroll
+    for (int w = 1; w < SC_THREADS / 64; ++w) {
+      mn = min(mn, sm.red[0][w]);
+      mx = max(mx, sm.red[1][w]);
+      nv += sm.red[2][w];
+    }
+  }
+  uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
+  const uint32_t want = need;
+  uint32_t thresh = mn, eq_take = 0xFFFFFFFFu;   // need == nv: every non-zero key
+  if (need == 0) {
+    thresh = 0xFFFFFFFFu;
+    eq_take = 0;
+  } else if (need < nv) {
+    uint32_t lo = mn, hi = mx;
+    constexpr int BPT = NBINS / SC_THREADS;
+    for (;;) {
+      const uint32_t R = hi - lo;
+      const int shift = (R >> 11) == 0 ? 0 : 32 - __clz((int)(R >> 11));
+      for (int i = threadIdx.x; i < NBINS; i += SC_THREADS) sm.hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < SEL_KPT; ++i)
+        if (kv[i] && kv[i] >= lo && kv[i] <= hi) atomicAdd(&sm.hist[(kv[i] - lo) >> shift], 1u);
+      __syncthreads();
+      uint32_t own[BPT], tot = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        own[j] = sm.hist[threadIdx.x * BPT + j];
+        tot += own[j];
+      }
+      uint32_t total;
+      const uint32_t pre = block_prefix_excl<SC_THREADS>(tot, sm, total);
+      uint32_t cum = total - pre - tot;
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (cum < need && cum + own[j] >= need) {
+          sm.digit = threadIdx.x * BPT + j;
+          sm.above = cum;
+          sm.done = (cum + own[j] == need) ? 1u : 0u;
+        }
+        cum += own[j];
+      }
+      __syncthreads();
+      const uint32_t d = sm.digit;
+      need -= sm.above;
+      const uint32_t new_lo = lo + (d << shift);
+      const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
+      const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+      const uint32_t done = sm.done;
+      __syncthreads();
+      if (done) {
+        thresh = new_lo;
+        break;
+      }
+      if (shift == 0) {
+        thresh = new_lo;
+        eq_take = need;
+        break;
+      }
+      lo = new_lo;
+      hi = new_hi;
+    }
+  }
+  // ordered emission: counts of this thread's keys above / at the threshold, one
+  // packed prefix sum (each count < 2^16), then the thread's chosen ids in order
+  uint32_t g = 0, e = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_KPT; ++i) {
+    g += (kv[i] != 0u && kv[i] > thresh) ? 1u : 0u;
+    e += (kv[i] != 0u && kv[i] == thresh) ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t pre = block_prefix_excl<SC_THREADS>((g << 16) | e, sm, total);
+  uint32_t G = pre >> 16, E = pre & 0xFFFFu;
+  int32_t* out = topk + (size_t)bt * k;
+#pragma unroll
+  for (int i = 0; i < SEL_KPT; ++i) {
+    if (kv[i] == 0u) continue;
+    if (kv[i] > thresh) {
+      out[G + min(E, eq_take)] = p0 + i;
+      ++G;
+    } else if (kv[i] == thresh) {
+      if (E < eq_take) out[G + E] = p0 + i;
+      ++E;
+    }
+  }
+  for (int i = (int)want + threadIdx.x; i < k; i += SC_THREADS) out[i] = -1;
+}
+
+hipError_t launch_tiled(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
+                        const int32_t* q_pos, int32_t* topk, int B, int T_len, int H_I, int N_cap, int n_entries,
+                        int m, int k, int n_scan, void* ws, const ScorePlan& p, hipStream_t st) {
+  uint32_t* keys = static_cast<uint32_t*>(ws);
+  dim3 g1((n_scan + QT_CE - 1) / QT_CE, (T_len + QT - 1) / QT, B);
+  hipLaunchKernelGGL(score_qtile_bf16, g1, dim3(SC_THREADS), 0, st, static_cast<const bf16*>(q_idx), w, codes,
+                     scales, q_pos, keys, T_len, H_I, N_cap, n_entries, m, n_scan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_rows, dim3(T_len, B), dim3(SC_THREADS), 0, st, keys, q_pos, topk, T_len, n_entries, m,
+                     n_scan, k);
+  return hipGetLastError();
+}
+
 template <typename T, bool POOL, bool BUILD>
 hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
@@ -637,9 +969,19 @@ hipError_t launch_mode(int hsi, const void* q_idx, const float* w, const uint8_t
 
 }  // namespace
 
-ScorePlan plan_score(int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb) {
+ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb) {
   ScorePlan p{};
   const long long Q = (long long)B * T;
+  // many queries over a cache of at most SEL_MAX entries: two-phase path
+  if (dtype == 1 && hsi == 0 && Q >= 256 && n_scan >= 1 && n_scan <= SEL_MAX) {
+    p.tiled = true;
+    p.chunk = n_scan;
+    p.n_chunks = 1;
+    p.k_chunk = k;
+    p.key_bytes = (size_t)Q * n_scan * 4;
+    p.total_bytes = p.key_bytes + 256;
+    return p;
+  }
   int C = MAX_CHUNK;
   while (C > 256 && C / 2 >= n_scan) C /= 2;                       // no chunk much larger than the scan
   while (C > 1024 && Q * ((n_scan + C - 1) / C) < 1024) C /= 2;   // enough workgroups to fill the GPU
@@ -660,6 +1002,9 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
                              int T, int H_I, int N_cap, int n_entries, int m, int k, int hsi, int hsi_s, int hsi_nb,
                              void* workspace, const ScorePlan& plan, hipStream_t stream) {
   if (B == 0 || T == 0) return hipSuccess;
+  if (plan.tiled)
+    return launch_tiled(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k, plan.chunk,
+                        workspace, plan, stream);
   if (dtype == 1)
     return launch_mode<bf16>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
                              k, hsi_s, hsi_nb, workspace, plan, stream);

@@ -141,6 +141,38 @@ def test_score_topk_vs_oracle(dtype, m, k, H_I):
     assert exact >= B * T - 1
 
 
+@pytest.mark.parametrize("m,k,H_I", [(2, 512, 32), (1, 64, 7)])
+def test_score_topk_many_queries_vs_oracle(m, k, H_I):
+    """Many bf16 queries over one cache (the query-tiled scorer + per-query select):
+    a query count that is not a multiple of the 4-query tile, several 1024-entry
+    workgroup chunks, positions before the first entry, inside and past the filled
+    cache; every 5th query checked against the oracle."""
+    B, T, N_cap, n_fill = 2, 301, 3000, 2900
+    say(f"case: score_topk many queries m={m} k={k} H_I={H_I}")
+    gen = np.random.default_rng(29)
+    pos = gen.integers(-3, n_fill * m + 200, size=(B, T)).astype(np.int32)
+    pos[0, :4] = [-1, 0, m - 1, m]
+    codes, scales = _index_cache(B, N_cap, n_fill, 29)
+    q_idx = synth.gaussian((B, T, H_I, 128), 1.0, 29, "q_idx", 0, torch.bfloat16, DEV)
+    w = synth.gaussian((B, T, H_I), 1.0, 29, "w", 0, torch.float32, DEV)
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    topk = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    K.csa2_score_topk(None, q_idx, w, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), q_pos, topk,
+                      n_entries=n_fill, m=m, k=k)
+    torch.cuda.synchronize()
+    tg = topk.cpu().numpy()
+    exact, n = 0, 0
+    for b in range(B):
+        kd = O.fp4_unpack(codes[b], scales[b])
+        for t in list(range(0, T, 5)) + [T - 1]:
+            nv = min(n_fill, O.visible_entries(pos[b, t], m)) if pos[b, t] >= 0 else 0
+            sc = O.index_scores(npy(q_idx[b, t]), npy(w[b, t]), kd, nv)
+            exact += check_topk_row(sc, np.arange(nv), tg[b, t], k, f"b{b} t{t} n_t={nv}")
+            n += 1
+    say(f"  exact set equality on {exact}/{n} queries")
+    assert exact >= n - 1
+
+
 def test_score_topk_hsi_build_and_use():
     B, N_cap, m, k, s, nb = 2, 4096, 1, 64, 16, 20
     pos = np.array([[4095, 100, 10, 2000], [3000, 319, 4095, 17]])
