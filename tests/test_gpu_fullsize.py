@@ -1,0 +1,245 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark
+times: every stage runs on the whole workload on the GPU and a sample of its
+outputs (entries, queries, rows) is recomputed one by one by the CPU oracle.
+
+* encoder Full-layer prefill, B=1, L=8192, hidden 4096, m=2 (the benchmark's
+  PrefillBench itself);
+* decoder macro-block, m=1, L=32768: Full (from one hidden tensor), Reindex, Reuse,
+  Reuse;
+* batched decode, 64 sequences x 131072 m=2 entries, Reindex + Reuse (the
+  benchmark's DecodeBench itself);
+* 1M-context decode with the HSI candidate pool: 4 sequences x 524288 entries,
+  Full layer (flat top-512 + 256 blocks of 64) then Reindex within the pool.
+
+Comparison rules as in parity_utils; FP4 codes are checked against the oracle's
+quantisation of the GPU's own float32 pre-quantisation values where those are
+available, so only rounding-band flips are allowed.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import csa2_oracle as O
+from parity_utils import check_fp4, check_topk_row, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def K():
+    from compressed_sparse_attention_compress_amd import csa2 as lib
+    lib.lib()
+    return lib
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_attn(tag, q_tok, kv_seq, sel_row, swa_seq, pos0, p, W, o_tok):
+    """swa_seq: the layer's window KV (torch, [L_w, 512], row j = position pos0 + j)."""
+    sel = sel_row[sel_row >= 0]
+    lo = max(0, p - W + 1, pos0)
+    swa_rows = f64(swa_seq[lo - pos0:p - pos0 + 1])
+    ref, probs, rows = O.sparse_attention(q_tok, kv_seq, sel, swa_rows, lo, p, W)
+    err = row_rel_err(o_tok, ref)
+    assert err <= TOL, f"{tag}: attention row rel err {err:.3e}"
+    return err
+
+
+# ---------------------------------------------------------------- prefill C2
+
+def test_encoder_prefill_full_size(K):
+    import bench
+    say("case: encoder Full-layer prefill B=1 L=8192 D=4096 m=2 (benchmark launch configuration)")
+    pb = bench.PrefillBench(torch, K, synth)
+    pb.step()
+    torch.cuda.synchronize()
+    s, i = pb.shape, pb.inp
+    N = pb.N
+    w_kv, w_gate, gamma, w_ik = f64(i["w_kv"]), f64(i["w_gate"]), f64(i["gamma"]), f64(i["w_ik"])
+    lat = pb.lat[0].cpu().numpy().astype(np.float64)            # GPU pre-RoPE latent (float32)
+    codes, scales = pb.codes[0].cpu().numpy(), pb.scales[0].cpu().numpy()
+    kv = f64(pb.kv[0])
+    # compressor, on sampled groups (first, last, spread)
+    groups = [0, 1, 777, 2048, N - 2, N - 1]
+    for g in groups:
+        x = f64(i["x"][0, g * s.m:(g + 1) * s.m])
+        lat_o, kv_o, _ = O.compress(x, w_kv, w_gate, gamma, s.m, g * s.m)
+        assert row_rel_err(kv[g:g + 1], kv_o) <= TOL, f"entry {g}: cache row"
+        assert row_rel_err(lat[g:g + 1], lat_o) <= TOL, f"entry {g}: pre-RoPE latent"
+    # index K of sampled entries, from the GPU's float32 latent
+    ents = np.array([0, 5, 1000, 2047, 3000, N - 1])
+    u, _, _ = O.index_k(lat[ents], w_ik, ents * s.m)
+    nc, ns = check_fp4(u, codes[ents], scales[ents], "prefill index K")
+    say(f"  FP4 code flips inside the rounding band: {nc} codes, {ns} scales")
+    # score + top-k and attention of sampled queries
+    kd = O.fp4_unpack(codes, scales)
+    topk = pb.topk[0].cpu().numpy()
+    qi, ww = i["q_idx"][0], i["w"][0]
+    worst = 0.0
+    for t in [0, 1, 2, 700, 1023, 1024, 4097, 6000, s.L - 1]:
+        nv = O.visible_entries(t, s.m)
+        sc = O.index_scores(f64(qi[t]), f64(ww[t]), kd, nv)
+        check_topk_row(sc, np.arange(nv), topk[t], s.k, f"prefill t{t}")
+        worst = max(worst, _check_attn(f"prefill t{t}", f64(i["q"][0, t]), kv, topk[t], i["swa_kv"][0],
+                                       0, t, s.W, f64(pb.o[0, t])))
+    say(f"  worst attention row rel err {worst:.2e}")
+
+
+# ---------------------------------------------------------- decoder block C3
+
+def test_decoder_macro_block_full_size(K):
+    L, D, m, H_I, k, W, H = 32768, 4096, 1, 32, 512, 128, 64
+    say(f"case: decoder macro-block Full/Reindex/Reuse/Reuse L={L} m={m}")
+    shape = synth.LayerShape(B=1, L=L, D=D, m=m, H_I=H_I, k=k, W=W, H=H)
+    bf = torch.bfloat16
+    full = synth.full_layer_inputs(shape, 5, bf, DEV, layer=0)
+    lay = [full] + [synth.full_layer_inputs(shape, 5, bf, DEV, layer=l, with_x=False) for l in (1, 2, 3)]
+    N = L // m
+    lat = torch.empty(1, N, 512, dtype=torch.float32, device=DEV)
+    kvc = torch.empty(1, N, 512, dtype=bf, device=DEV)
+    codes = torch.empty(1, N, 64, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(1, N, 4, dtype=torch.uint8, device=DEV)
+    rt = K.Runtime()
+    modes = [K.FULL, K.REINDEX, K.REUSE, K.REUSE]
+    outs, tks = [], []
+    for li, mode in enumerate(modes):
+        inp = lay[li]
+        cfg = K.layer_cfg(mode, K.CSA2_BF16, m=m, k=k, W=W, H_I=H_I, H=H)
+        topk = torch.empty(1, L, k, dtype=torch.int32, device=DEV)
+        o = torch.empty_like(inp["q"])
+        kw = dict(B=1, T=L, q_pos=inp["q_pos"], q=inp["q"], swa_kv=inp["swa_kv"], swa_pos0=inp["swa_pos0"], o=o,
+                  N_cap=N)
+        if mode == K.FULL:
+            kw.update(D=D, x=inp["x"], w_kv=inp["w_kv"], w_gate=None, gamma=inp["gamma"], w_ik=inp["w_ik"],
+                      latent_pre=lat, kv_cache=kvc, ik_codes=codes, ik_scales=scales)
+        if mode != K.REUSE:
+            kw.update(q_idx=inp["q_idx"], w=inp["w"], topk=topk)
+        io = K.layer_io(**kw)
+        ws = torch.empty(max(K.layer_workspace_bytes(cfg, io), 16), dtype=torch.uint8, device=DEV)
+        K.csa2_layer_forward(rt, cfg, K.layer_io(workspace=ws, **kw))
+        torch.cuda.synchronize()
+        outs.append(o)
+        tks.append(topk if mode != K.REUSE else tks[-1])
+        del ws
+    kv = f64(kvc[0])
+    latn = lat[0].cpu().numpy().astype(np.float64)
+    w_kv, gamma, w_ik = f64(full["w_kv"]), f64(full["gamma"]), f64(full["w_ik"])
+    for g in [0, 1, 9999, N - 1]:
+        lat_o, kv_o, _ = O.compress(f64(full["x"][0, g:g + 1]), w_kv, None, gamma, m, g)
+        assert row_rel_err(kv[g:g + 1], kv_o) <= TOL, f"entry {g}: cache row"
+    cd, sd = codes[0].cpu().numpy(), scales[0].cpu().numpy()
+    ents = np.array([0, 3, 16384, N - 1])
+    u, _, _ = O.index_k(latn[ents], w_ik, ents * m)
+    check_fp4(u, cd[ents], sd[ents], "decoder index K")
+    kd = O.fp4_unpack(cd, sd)
+    t_full, t_re = tks[0][0].cpu().numpy(), tks[1][0].cpu().numpy()
+    # the Reuse layers attend over the Reindex layer's selection (checked below)
+    worst = 0.0
+    for t in [0, 511, 512, 20000, L - 1]:
+        nv = O.visible_entries(t, m)
+        for li, tk_row in ((0, t_full[t]), (1, t_re[t])):
+            inp = lay[li]
+            sc = O.index_scores(f64(inp["q_idx"][0, t]), f64(inp["w"][0, t]), kd, nv)
+            check_topk_row(sc, np.arange(nv), tk_row, k, f"decoder layer{li} t{t}")
+        for li in range(4):
+            sel = t_full[t] if li == 0 else t_re[t]
+            worst = max(worst, _check_attn(f"decoder layer{li} t{t}", f64(lay[li]["q"][0, t]), kv, sel,
+                                           lay[li]["swa_kv"][0], 0, t, W, f64(outs[li][0, t])))
+    say(f"  worst attention row rel err {worst:.2e}")
+
+
+# -------------------------------------------------------------- decode C4
+
+def test_batched_decode_full_size(K):
+    import bench
+    say("case: batched decode 64 x 131072 entries, Reindex + Reuse (benchmark launch configuration)")
+    db = bench.DecodeBench(torch, K, synth)
+    db.step()
+    torch.cuda.synchronize()
+    topk = db.topk.cpu().numpy()
+    p = int(db.q_pos[0, 0].item())
+    pos0 = int(db.swa_pos0[0].item())
+    worst = 0.0
+    for b in [0, 31, 63]:
+        kd = O.fp4_unpack(db.codes[b].cpu().numpy(), db.scales[b].cpu().numpy())
+        r = db.layers[0]
+        sc = O.index_scores(f64(r["q_idx"][b, 0]), f64(r["w"][b, 0]), kd, db.N)
+        check_topk_row(sc, np.arange(db.N), topk[b, 0], db.k, f"decode b{b}")
+        del kd
+        sel = topk[b, 0]
+        rows = f64(db.kv[b][torch.from_numpy(sel[sel >= 0].astype(np.int64)).to(DEV)])
+        for li in range(2):
+            lay = db.layers[li]
+            ref, _, _ = O.sparse_attention(f64(lay["q"][b, 0]), rows, np.arange(rows.shape[0]), f64(lay["swa_kv"][b]),
+                                           pos0, p, db.W)
+            err = row_rel_err(f64(db.o[li][b, 0]), ref)
+            assert err <= TOL, f"decode b{b} layer{li}: {err:.3e}"
+            worst = max(worst, err)
+    say(f"  worst attention row rel err {worst:.2e}")
+
+
+# ----------------------------------------------------- 1M decode with HSI C5
+
+def test_million_context_hsi_decode_full_size(K):
+    B, N, m, H_I, k, W, H, s_blk, nb = 4, 524288, 2, 32, 512, 128, 64, 64, 256
+    say(f"case: 1M-context decode with HSI, {B} x {N} entries, s={s_blk}, n_b={nb}")
+    bf = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    kv = torch.randn(B, N, 512, generator=g, device=DEV, dtype=torch.float32).to(bf)
+    codes = torch.empty(B, N, 64, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(B, N, 4, dtype=torch.uint8, device=DEV)
+    for b in range(B):
+        u = torch.randn(N, 128, generator=g, device=DEV, dtype=torch.float32)
+        K.csa2_fp4_pack(u, codes[b], scales[b])
+        del u
+    p = N * m - 1
+    q_pos = torch.full((B, 1), p, dtype=torch.int32, device=DEV)
+    pos0 = torch.full((B,), p - W + 1, dtype=torch.int32, device=DEV)
+    lay = [synth.decode_query_inputs(B, H, H_I, W, seed=3, layer=l, dtype=bf, device=DEV) for l in range(2)]
+    tk_full = torch.empty(B, 1, k, dtype=torch.int32, device=DEV)
+    cand = torch.empty(B, 1, nb, dtype=torch.int32, device=DEV)
+    tk_re = torch.empty(B, 1, k, dtype=torch.int32, device=DEV)
+    K.csa2_score_topk(None, lay[0]["q_idx"], lay[0]["w"], codes, scales, q_pos, tk_full, n_entries=N, m=m, k=k,
+                      hsi=K.HSI_BUILD, hsi_s=s_blk, hsi_nb=nb, candidates=cand)
+    K.csa2_score_topk(None, lay[1]["q_idx"], lay[1]["w"], codes, scales, q_pos, tk_re, n_entries=N, m=m, k=k,
+                      hsi=K.HSI_USE, hsi_s=s_blk, hsi_nb=nb, candidates=cand)
+    o = [torch.empty_like(lay[l]["q"]) for l in range(2)]
+    K.csa2_sparse_attn(None, lay[0]["q"], kv, tk_full, lay[0]["swa_kv"], pos0, q_pos, o[0], W=W)
+    K.csa2_sparse_attn(None, lay[1]["q"], kv, tk_re, lay[1]["swa_kv"], pos0, q_pos, o[1], W=W)
+    torch.cuda.synchronize()
+    tf, tr, cg = tk_full.cpu().numpy(), tk_re.cpu().numpy(), cand.cpu().numpy()
+    worst = 0.0
+    for b in [0, 3]:
+        kd = O.fp4_unpack(codes[b].cpu().numpy(), scales[b].cpu().numpy())
+        sc = O.index_scores(f64(lay[0]["q_idx"][b, 0]), f64(lay[0]["w"][b, 0]), kd, N)
+        check_topk_row(sc, np.arange(N), tf[b, 0], k, f"hsi full b{b}")
+        nblk = N // s_blk
+        beta = sc.reshape(nblk, s_blk).max(1)
+        beta[-1] = np.inf
+        beta_f = np.where(np.isinf(beta), np.max(np.abs(beta[:-1])) * 10 + 1, beta)
+        check_topk_row(beta_f, np.arange(nblk), cg[b, 0], nb, f"hsi pool b{b}")
+        assert (nblk - 1) in cg[b, 0]
+        # Reindex: its own scores, restricted to the GPU's pool
+        sc2 = O.index_scores(f64(lay[1]["q_idx"][b, 0]), f64(lay[1]["w"][b, 0]), kd, N)
+        ent = O.pool_entries(cg[b, 0], N, s_blk)
+        check_topk_row(sc2[ent], ent, tr[b, 0], k, f"hsi reindex b{b}")
+        del kd
+        for li, tk in ((0, tf), (1, tr)):
+            sel = tk[b, 0]
+            rows = f64(kv[b][torch.from_numpy(sel[sel >= 0].astype(np.int64)).to(DEV)])
+            ref, _, _ = O.sparse_attention(f64(lay[li]["q"][b, 0]), rows, np.arange(rows.shape[0]),
+                                           f64(lay[li]["swa_kv"][b]), p - W + 1, p, W)
+            err = row_rel_err(f64(o[li][b, 0]), ref)
+            assert err <= TOL, f"hsi b{b} layer{li}: {err:.3e}"
+            worst = max(worst, err)
+    say(f"  worst attention row rel err {worst:.2e}")
