@@ -620,7 +620,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
 // exact in bf16, so one MFMA chain covers all 4 blocks of the 128 dims.
 constexpr int QT = 4;                 // queries per workgroup
 constexpr int QT_CE = 4096;           // entries per workgroup (64 super-tiles of 64)
-constexpr int SEL_MAX = 8192;         // keys per query row held in LDS by select_rows
+constexpr int SEL_MAX = 8192;         // keys per query row held in registers by select_rows
 
 __device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t w, float s) {
   const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
@@ -754,80 +754,104 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
   }
 }
 
-// One workgroup per query, its visible keys held in registers: thread t owns the
-// SEL_KPT consecutive positions t*SEL_KPT.., so the chosen ids come out in
-// position order from one block-wide prefix sum.  Radix select as in
-// select_threshold (2048 bins over the live key range, ties in position order).
-constexpr int SEL_KPT = SEL_MAX / SC_THREADS;   // 32
+// One wave per query (4 per workgroup, no block-wide barriers): lane l holds the
+// keys of positions 64j + l in registers (coalesced row reads).
+//  1. One histogram pass over score values: bin = floor((v - vmin) * 255.99 /
+//     (vmax - vmin)) is monotone in the key, so the boundary bin (where the count
+//     of better keys reaches k) holds a contiguous key range.
+//  2. The keys of that bin are compacted into the wave's LDS list and split
+//     exactly by radix passes over their key range (8-bit digits; a pass stops once
+//     the count at the boundary bin is exact or the bin holds a single value).
+//     When more keys share the bin than the list holds, the passes run over the
+//     registers instead.
+//  3. Emission: ballots give, for each register column j, the 64-bit masks of
+//     chosen keys among positions 64j..64j+63; lane j keeps column j's masks, so
+//     after the loop each lane owns 64 consecutive positions and writes its ids
+//     in order after a wave prefix sum.  Ties at the threshold go to the smaller
+//     position.
+constexpr int SW_BINS = 256;
+constexpr int SW_CAP = 256;   // boundary-bin keys held in the wave's LDS list
 
+__device__ __forceinline__ uint32_t wave_excl_prefix(uint32_t v, int lane) {
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
+  }
+  return x - v;
+}
+
+// Boundary bin of a 256-bin histogram held 4 bins per lane: the bin where the
+// count of keys in higher bins first reaches `need`.  Returns the bin, sets
+// `above` (keys in higher bins) and `exact` (above + bin count == need).
+__device__ __forceinline__ int wave_boundary_bin(const uint32_t* hist, uint32_t need, int lane, uint32_t& above,
+                                                 uint32_t& exact) {
+  uint32_t own[SW_BINS / 64], tot = 0;
+#pragma unroll
+  for (int i = 0; i < SW_BINS / 64; ++i) {
+    own[i] = hist[lane * (SW_BINS / 64) + i];
+    tot += own[i];
+  }
+  uint32_t x = tot;   // inclusive suffix sum over lanes >= lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += u;
+  }
+  uint32_t cum = x - tot;
+  int hit = -1;
+  uint32_t ha = 0, he = 0;
+#pragma unroll
+  for (int i = SW_BINS / 64 - 1; i >= 0; --i) {
+    if (cum < need && cum + own[i] >= need) {
+      hit = lane * (SW_BINS / 64) + i;
+      ha = cum;
+      he = (cum + own[i] == need) ? 1u : 0u;
+    }
+    cum += own[i];
+  }
+  const int src = __ffsll((long long)__ballot(hit >= 0)) - 1;   // exactly one lane
+  above = (uint32_t)__shfl((int)ha, src, 64);
+  exact = (uint32_t)__shfl((int)he, src, 64);
+  return __shfl(hit, src, 64);
+}
+
+template <int KPT>
 __global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __restrict__ keys,
                                                           const int32_t* __restrict__ q_pos,
                                                           int32_t* __restrict__ topk, int T_len, int n_entries,
                                                           int m, int n_scan, int k) {
-  __shared__ SelSmem<SC_THREADS> sm;
-  __shared__ __attribute__((aligned(16))) uint32_t kl[SEL_MAX];
-  const int t = blockIdx.x, b = blockIdx.y;
+  __shared__ uint32_t hist_all[SC_THREADS / 64][SW_BINS];
+  __shared__ uint32_t cand_all[SC_THREADS / 64][SW_CAP];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * (SC_THREADS / 64) + wave, b = blockIdx.y;
+  if (t >= T_len) return;
+  uint32_t* hist = hist_all[wave];
+  uint32_t* cand = cand_all[wave];
   const int bt = b * T_len + t;
   const int n_t = min(visible(q_pos, bt, m, n_entries), n_scan);
   const uint32_t* row = keys + (size_t)bt * n_scan;
-  // coalesced row read into LDS, then each thread takes its contiguous segment
-  const int n_pad = (n_t + 3) & ~3;
-  for (int i0 = 0; i0 < n_pad; i0 += 8 * SC_THREADS) {   // 8 loads per thread in flight
-    uint32_t v[8];
+  uint32_t kv[KPT];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * SC_THREADS + threadIdx.x;
-      v[u] = i < n_t ? row[i] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * SC_THREADS + threadIdx.x;
-      if (i < n_pad) kl[i] = v[u];
-    }
+  for (int j = 0; j < KPT; ++j) {
+    const int p = 64 * j + lane;
+    kv[j] = p < n_t ? row[p] : 0u;
   }
-  __syncthreads();
-  const int p0 = threadIdx.x * SEL_KPT;
-  uint32_t kv[SEL_KPT];
-#pragma unroll
-  for (int i = 0; i < SEL_KPT; i += 4) {
-    if (p0 + i < n_pad) {
-      const uint4 v4 = *reinterpret_cast<const uint4*>(&kl[p0 + i]);
-      kv[i] = v4.x; kv[i + 1] = v4.y; kv[i + 2] = v4.z; kv[i + 3] = v4.w;
-    } else {
-      kv[i] = kv[i + 1] = kv[i + 2] = kv[i + 3] = 0u;
-    }
-  }
-
-  // non-zero count, min and max
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
 #pragma unroll
-  for (int i = 0; i < SEL_KPT; ++i)
-    if (kv[i]) {
-      mn = min(mn, kv[i]);
-      mx = max(mx, kv[i]);
+  for (int j = 0; j < KPT; ++j)
+    if (kv[j]) {
+      mn = min(mn, kv[j]);
+      mx = max(mx, kv[j]);
       ++nv;
     }
-  {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-      nv += (uint32_t)__shfl_xor((int)nv, off, 64);
-    }
-    if (lane == 0) {
-      sm.red[0][wave] = mn;
-      sm.red[1][wave] = mx;
-      sm.red[2][wave] = nv;
-    }
-    __syncthreads();
-    mn = sm.red[0][0]; mx = sm.red[1][0]; nv = sm.red[2][0];
-#pragma unroll
-    for (int w = 1; w < SC_THREADS / 64; ++w) {
-      mn = min(mn, sm.red[0][w]);
-      mx = max(mx, sm.red[1][w]);
-      nv += sm.red[2][w];
-    }
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    nv += (uint32_t)__shfl_xor((int)nv, off, 64);
   }
   uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
   const uint32_t want = need;
@@ -836,80 +860,129 @@ __global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __rest
     thresh = 0xFFFFFFFFu;
     eq_take = 0;
   } else if (need < nv) {
-    uint32_t lo = mn, hi = mx;
-    constexpr int BPT = NBINS / SC_THREADS;
-    for (;;) {
-      const uint32_t R = hi - lo;
-      const int shift = (R >> 11) == 0 ? 0 : 32 - __clz((int)(R >> 11));
-      for (int i = threadIdx.x; i < NBINS; i += SC_THREADS) sm.hist[i] = 0;
-      __syncthreads();
+    // ---- 1. value pass
+    const float vmin = key_score(mn), vmax = key_score(mx);
+    // (a span too small to scale puts every key in bin 0; the key passes then split it)
+    const float span = vmax - vmin;
+    const float sc = span > 1e-30f ? 255.99f / span : 0.0f;
+    auto vbin = [&](uint32_t kk) -> int { return min(SW_BINS - 1, (int)((key_score(kk) - vmin) * sc)); };
 #pragma unroll
-      for (int i = 0; i < SEL_KPT; ++i)
-        if (kv[i] && kv[i] >= lo && kv[i] <= hi) atomicAdd(&sm.hist[(kv[i] - lo) >> shift], 1u);
-      __syncthreads();
-      uint32_t own[BPT], tot = 0;
+    for (int i = 0; i < SW_BINS / 64; ++i) hist[lane * (SW_BINS / 64) + i] = 0;
 #pragma unroll
-      for (int j = 0; j < BPT; ++j) {
-        own[j] = sm.hist[threadIdx.x * BPT + j];
-        tot += own[j];
+    for (int j = 0; j < KPT; ++j)
+      if (kv[j]) atomicAdd(&hist[vbin(kv[j])], 1u);
+    uint32_t above, exact;
+    const int d = wave_boundary_bin(hist, need, lane, above, exact);
+    need -= above;
+    // ---- 2. keys of the boundary bin: their range, and a compact list when it fits
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, nb = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = kv[j] != 0u && vbin(kv[j]) == d;
+      const uint64_t mk = __ballot(in);
+      if (in) {
+        lo = min(lo, kv[j]);
+        hi = max(hi, kv[j]);
+        const uint32_t slot = nb + __popcll(mk & ((1ull << lane) - 1ull));
+        if (slot < (uint32_t)SW_CAP) cand[slot] = kv[j];
       }
-      uint32_t total;
-      const uint32_t pre = block_prefix_excl<SC_THREADS>(tot, sm, total);
-      uint32_t cum = total - pre - tot;
+      nb += __popcll(mk);
+    }
 #pragma unroll
-      for (int j = BPT - 1; j >= 0; --j) {
-        if (cum < need && cum + own[j] >= need) {
-          sm.digit = threadIdx.x * BPT + j;
-          sm.above = cum;
-          sm.done = (cum + own[j] == need) ? 1u : 0u;
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+    }
+    if (exact) {
+      thresh = lo;   // every key of the bin and above
+    } else {
+      const bool listed = nb <= (uint32_t)SW_CAP;
+      uint32_t cl[SW_CAP / 64];   // the list, 4 per lane (0 = empty slot)
+#pragma unroll
+      for (int i = 0; i < SW_CAP / 64; ++i) cl[i] = (uint32_t)(64 * i + lane) < nb ? cand[64 * i + lane] : 0u;
+      for (;;) {
+        const uint32_t R = hi - lo;
+        const int shift = (R >> 8) == 0 ? 0 : 32 - __clz((int)(R >> 8));
+#pragma unroll
+        for (int i = 0; i < SW_BINS / 64; ++i) hist[lane * (SW_BINS / 64) + i] = 0;
+        if (listed) {
+#pragma unroll
+          for (int i = 0; i < SW_CAP / 64; ++i)
+            if (cl[i] && cl[i] >= lo && cl[i] <= hi) atomicAdd(&hist[(cl[i] - lo) >> shift], 1u);
+        } else {
+#pragma unroll
+          for (int j = 0; j < KPT; ++j)
+            if (kv[j] && kv[j] >= lo && kv[j] <= hi) atomicAdd(&hist[(kv[j] - lo) >> shift], 1u);
         }
-        cum += own[j];
+        const int dd = wave_boundary_bin(hist, need, lane, above, exact);
+        need -= above;
+        const uint32_t new_lo = lo + ((uint32_t)dd << shift);
+        const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
+        const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
+        if (exact) {
+          thresh = new_lo;
+          break;
+        }
+        if (shift == 0) {
+          thresh = new_lo;
+          eq_take = need;
+          break;
+        }
+        lo = new_lo;
+        hi = new_hi;
       }
-      __syncthreads();
-      const uint32_t d = sm.digit;
-      need -= sm.above;
-      const uint32_t new_lo = lo + (d << shift);
-      const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
-      const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
-      const uint32_t done = sm.done;
-      __syncthreads();
-      if (done) {
-        thresh = new_lo;
-        break;
-      }
-      if (shift == 0) {
-        thresh = new_lo;
-        eq_take = need;
-        break;
-      }
-      lo = new_lo;
-      hi = new_hi;
     }
   }
-  // ordered emission: counts of this thread's keys above / at the threshold, one
-  // packed prefix sum (each count < 2^16), then the thread's chosen ids in order
-  uint32_t g = 0, e = 0;
+  // ---- 3. ordered emission
+  uint64_t my_gt = 0, my_eq = 0;   // lane j: masks of register column j (positions 64j..64j+63)
 #pragma unroll
-  for (int i = 0; i < SEL_KPT; ++i) {
-    g += (kv[i] != 0u && kv[i] > thresh) ? 1u : 0u;
-    e += (kv[i] != 0u && kv[i] == thresh) ? 1u : 0u;
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t mg = __ballot(kv[j] != 0u && kv[j] > thresh);
+    const uint64_t me = __ballot(kv[j] != 0u && kv[j] == thresh);
+    if (lane == j) {
+      my_gt = mg;
+      my_eq = me;
+    }
   }
-  uint32_t total;
-  const uint32_t pre = block_prefix_excl<SC_THREADS>((g << 16) | e, sm, total);
-  uint32_t G = pre >> 16, E = pre & 0xFFFFu;
   int32_t* out = topk + (size_t)bt * k;
+  if (KPT <= 64) {
+    const uint32_t eq_before = wave_excl_prefix((uint32_t)__popcll(my_eq), lane);
+    // keep the first (eq_take - eq_before) ties of this lane's 64 positions
+    uint64_t keep_eq = my_eq;
+    const uint32_t room = eq_take > eq_before ? eq_take - eq_before : 0u;
+    if ((uint32_t)__popcll(keep_eq) > room) {
+      uint64_t x = keep_eq, r = 0;
+      for (uint32_t n = 0; n < room; ++n) {
+        const uint64_t low = x & (~x + 1ull);
+        r |= low;
+        x ^= low;
+      }
+      keep_eq = r;
+    }
+    uint64_t sel = my_gt | keep_eq;
+    uint32_t pos = wave_excl_prefix((uint32_t)__popcll(sel), lane);
+    while (sel) {
+      const int bit = __ffsll((long long)sel) - 1;
+      out[pos++] = 64 * lane + bit;
+      sel &= sel - 1ull;
+    }
+  } else {
+    // more register columns than lanes: emit column by column
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t G = 0, E = 0;
 #pragma unroll
-  for (int i = 0; i < SEL_KPT; ++i) {
-    if (kv[i] == 0u) continue;
-    if (kv[i] > thresh) {
-      out[G + min(E, eq_take)] = p0 + i;
-      ++G;
-    } else if (kv[i] == thresh) {
-      if (E < eq_take) out[G + E] = p0 + i;
-      ++E;
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t kk = kv[j];
+      const bool is_gt = kk != 0u && kk > thresh, is_eq = kk != 0u && kk == thresh;
+      const uint64_t mg = __ballot(is_gt), me = __ballot(is_eq);
+      const uint32_t gl = G + __popcll(mg & lt), el = E + __popcll(me & lt);
+      if (is_gt) out[gl + min(el, eq_take)] = 64 * j + lane;
+      else if (is_eq && el < eq_take) out[gl + el] = 64 * j + lane;
+      G += __popcll(mg);
+      E += __popcll(me);
     }
   }
-  for (int i = (int)want + threadIdx.x; i < k; i += SC_THREADS) out[i] = -1;
+  for (int i = (int)want + lane; i < k; i += 64) out[i] = -1;
 }
 
 hipError_t launch_tiled(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
@@ -921,8 +994,12 @@ hipError_t launch_tiled(const void* q_idx, const float* w, const uint8_t* codes,
                      scales, q_pos, keys, T_len, H_I, N_cap, n_entries, m, n_scan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_rows, dim3(T_len, B), dim3(SC_THREADS), 0, st, keys, q_pos, topk, T_len, n_entries, m,
-                     n_scan, k);
+  const dim3 g2((T_len + SC_THREADS / 64 - 1) / (SC_THREADS / 64), B);
+  if (n_scan <= 64 * 64)
+    hipLaunchKernelGGL(select_rows<64>, g2, dim3(SC_THREADS), 0, st, keys, q_pos, topk, T_len, n_entries, m, n_scan, k);
+  else
+    hipLaunchKernelGGL(select_rows<SEL_MAX / 64>, g2, dim3(SC_THREADS), 0, st, keys, q_pos, topk, T_len, n_entries, m,
+                       n_scan, k);
   return hipGetLastError();
 }
 
