@@ -272,6 +272,53 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
+// ---- fp16 scoring of bf16 queries against FP4 keys.
+// A key element is code x E4M3 scale: at most 2 + 4 significant bits with an
+// exponent in [-10, 12], so it is exact in fp16.  The convert instruction applies
+// the scale's power of two (it takes only the exponent of its f32 scale operand);
+// one packed fp16 multiply applies the scale's sign and 1.mmm significand.  A bf16
+// query has 8 significant bits, so it is exact in fp16 once each head is moved by
+// a power of two 2^-s into fp16's range; the head's weight takes the 2^s back
+// (ReLU commutes with a positive factor).  With the block scale inside the
+// operand, the four 32-dim blocks of a key chain into one MFMA accumulator.
+typedef _Float16 f16;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+template <typename T> struct ScoreQ;
+template <> struct ScoreQ<bf16> { typedef f16x8 type; };
+template <> struct ScoreQ<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ f32x4 mma16h(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 8 FP4 codes (dim 2t in the low nibble of byte t) times the scale whose power of
+// two is p2 and whose signed significand is mm.
+__device__ __forceinline__ f16x8 fp4x8_scaled_f16(uint32_t w, float p2, f16x2 mm) {
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * mm;
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * mm;
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * mm;
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * mm;
+  f16x8 r;
+  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
+  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
+  return r;
+}
+// Power of two and signed significand of an E4M3 scale byte (exact split of its
+// f32 value; a zero scale gives the power 0, whose products flush to 0).
+__device__ __forceinline__ void split_e4m3(uint32_t byte, float& p2, f16x2& mm) {
+  const uint32_t bits = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)byte, 0));
+  p2 = __uint_as_float(bits & 0x7F800000u);
+  const f16 m = (f16)__uint_as_float((bits & 0x807FFFFFu) | 0x3F800000u);
+  mm = f16x2{m, m};
+}
+// Max over lanes l, l^16, l^32, l^48 with the gfx950 permlane swaps.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+
 // Lower bound for the merge.  In a scan over nc chunks every chunk but the last
 // is full, so with r0 = ceil(k / (nc - 1)) the first nc - 1 chunks hold at least
 // k entries at or above the smallest of their rank-r0 keys: that smallest value
@@ -288,9 +335,6 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   typedef typename Frag<T>::type FragT;
   __shared__ SelSmem<SC_THREADS> sm;
   __shared__ uint32_t keys[MAX_CHUNK];
-  __shared__ __attribute__((aligned(16))) unsigned char ring0[4 * ST_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[4 * ST_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char ring2[4 * ST_BYTES];
 
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int bt = b * T_len + t;
@@ -313,21 +357,49 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   const int Ce = min(C, (n_here + gran - 1) / gran * gran);
 
   // indexer query fragments: row tile mt = heads 16mt.., k-step kb = dims 32kb + 8lg ..
-  FragT qf[2][4];
+  // bf16: k-step j of lane group g holds dims 32g + 8j .. +7 (block g), fp16 as
+  // described above; fp32: k-step kb holds block kb (dims 32kb + 8g .. +7)
+  typename ScoreQ<T>::type qf[2][4];
   float wv[2][4];
   const T* qb = q_idx + (size_t)bt * H_I * 128;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int h = mt * 16 + lr;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 raw[4];
+      float amax = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (h < H_I) qf[mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
-      else zero_frag(qf[mt][kb]);
-    }
+      for (int j = 0; j < 4; ++j) {
+        if (h < H_I) raw[j] = load_frag(qb + (size_t)h * 128 + 32 * lg + 8 * j);
+        else zero_frag(raw[j]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = mt * 16 + 4 * lg + i;
-      wv[mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)raw[j][i]));
+      }
+      amax = max_lane_groups(amax);
+      int ex = 0;
+      frexpf(amax, &ex);                          // amax < 2^ex
+      const int s = amax > 0.0f ? min(max(ex - 15, -96), 96) : 0;   // |q| 2^-s < 2^15
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[mt][j][i] = (f16)ldexpf((float)raw[j][i], -s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        const int sh = __shfl(s, 4 * lg + i, 64);
+        wv[mt][i] = hh < H_I ? ldexpf(w[(size_t)bt * H_I + hh], sh) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (h < H_I) qf[mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
+        else zero_frag(qf[mt][kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        wv[mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
+      }
     }
   }
   const int32_t* cq = POOL ? cands + (size_t)bt * hsi_nb : nullptr;
@@ -335,10 +407,14 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   const uint8_t* sb = scales + (size_t)b * N_cap * 4;
 
   // ---- scoring.  Wave w takes super-tiles w, w+4, ... of 64 entries (4 tiles of
-  // 16).  A super-tile is staged in the wave's LDS ring by 5 DMA instructions: one
-  // per tile moves its 1 KB of codes (16-B piece i of the tile lands in unit i,
-  // piece = (entry e, block b) with unit 4e + ((b + e/4) & 3), which makes the
-  // MFMA-pattern dword reads below conflict-free) and one moves the 64 scale words.
+  // 16), straight into registers: lane (e = l % 16, g = l / 16) of a tile loads the
+  // 16 code bytes of quantisation block g of entry e (a tile of consecutive entries
+  // is one contiguous 1 KB) and the entry's 4 scale bytes.  bf16: the lane's dword
+  // j feeds k-step j, scaled by block g's scale inside the operand.  fp32: four
+  // permlane swaps transpose the 4 x 4 pattern (lane group x dword) so that dword
+  // kb of lane group g holds dims 32kb + 8g .. +7 and k-step kb covers block kb,
+  // whose per-entry scale multiplies the step's partial product.  The next
+  // super-tile's loads are in flight while one is computed.
   const int n_st = Ce / 64;
   const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave
   auto entry_at = [&](int j, bool& valid) -> int {   // chunk position -> entry id
@@ -355,45 +431,105 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     valid = ent < n_t;
     return valid ? ent : 0;
   };
-  const int dma_e = lane >> 2, dma_b = ((lane & 3) - (dma_e >> 2)) & 3;
-  auto issue = [&](int i, unsigned char* ring) {
+  struct StLoad {
+    uint4 c[SPT];
+    uint32_t s[SPT];
+  };
+  // Flat selection reads consecutive entries through buffer resources over this
+  // sequence's codes and scales: one offset per super-tile, immediate offsets per
+  // tile, and reads past the N_cap entries return 0 (their keys are masked anyway).
+  const bool use_buf = !POOL && N_cap <= (1 << 25);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)cb, (short)0, use_buf ? N_cap * 64 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sb, (short)0, use_buf ? N_cap * 4 : 0, 0x00020000);
+  auto load_st = [&](int i, StLoad& L) {
     const int st = wave + 4 * i;
-    unsigned char* dst = ring + wave * ST_BYTES;
+    if (use_buf) {
+      const int e = base + st * 64 + lr;
+#pragma unroll
+      for (int tt = 0; tt < SPT; ++tt) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, e * 64 + 16 * lg + tt * 1024, 0, 0);
+        L.c[tt] = make_uint4(v[0], v[1], v[2], v[3]);
+        L.s[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs, e * 4 + tt * 64, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int tt = 0; tt < SPT; ++tt) {
       bool v;
-      const int ent = entry_at(st * 64 + tt * 16 + dma_e, v);
-      dma16(cb + (size_t)ent * 64 + 16 * dma_b, (lds_u8*)(dst + tt * 1024));
+      const int ent = entry_at(st * 64 + tt * 16 + lr, v);
+      L.c[tt] = *reinterpret_cast<const uint4*>(cb + (size_t)ent * 64 + 16 * lg);
+      L.s[tt] = *reinterpret_cast<const uint32_t*>(sb + (size_t)ent * 4);
     }
-    bool v;
-    const int ent = entry_at(st * 64 + lane, v);
-    dma4(sb + (size_t)ent * 4, (lds_u8*)(dst + SPT * 1024));
   };
-  auto compute = [&](int i, const unsigned char* ring) {
+  auto compute = [&](int i, const StLoad& L) {
     const int st = wave + 4 * i;
-    const unsigned char* src = ring + wave * ST_BYTES;
+    if constexpr (sizeof(T) == 2) {
+      // per tile: 8 heads x 1 entry per lane; ReLU as an integer max on the float's
+      // bits (negative floats are negative integers)
+      float part[SPT];
+#pragma unroll
+      for (int tt = 0; tt < SPT; ++tt) {
+        const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
+        float p2;
+        f16x2 mm;
+        split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
+        f32x4 acc[2];
+        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
+          acc[0] = mma16h(qf[0][j], kf, acc[0]);
+          acc[1] = mma16h(qf[1][j], kf, acc[1]);
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            p = fmaf(wv[mt][ii], __int_as_float(max(__float_as_int(acc[mt][ii]), 0)), p);
+        part[tt] = p;
+      }
+      // head sums of the 4 tiles over the 4 lane groups at once: after two rounds
+      // of swaps and adds lane group g holds tile g's sums, i.e. entry st*64 + lane
+      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      const float s13 = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+      const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+      const float s = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      const int j = st * 64 + lane;
+      bool valid;
+      entry_at(j, valid);
+      keys[j] = valid ? score_key(s) : 0u;
+    } else {
 #pragma unroll
     for (int tt = 0; tt < SPT; ++tt) {
-      const unsigned char* tb = src + tt * 1024;
-      uint32_t cw[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        cw[kb] = *reinterpret_cast<const uint32_t*>(tb + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
-      const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-      const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-      const float sc2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
-      const float sc3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
-      const float scv[4] = {sc0, sc1, sc2, sc3};
+      uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
       f32x4 acc[2];
+      {
+        auto a = __builtin_amdgcn_permlane32_swap(cw[0], cw[2], false, false);
+        auto b2 = __builtin_amdgcn_permlane32_swap(cw[1], cw[3], false, false);
+        auto c0 = __builtin_amdgcn_permlane16_swap(a[0], b2[0], false, false);
+        auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
+        cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
+        const uint32_t sw = L.s[tt];
+        const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+        const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+        const float sc2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
+        const float sc3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+        const float scv[4] = {sc0, sc1, sc2, sc3};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const auto kf = Fp4<T>::cvt(cw[kb]);
+        for (int kb = 0; kb < 4; ++kb) {
+          const auto kf = Fp4<T>::cvt(cw[kb]);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const f32x4 tmp = mma16(qf[mt][kb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
-          if (kb == 0) acc[mt] = tmp * scv[0];
-          else acc[mt] += tmp * scv[kb];
+          for (int mt = 0; mt < 2; ++mt) {
+            const f32x4 tmp = mma16(qf[mt][kb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (kb == 0) acc[mt] = tmp * scv[0];
+            else acc[mt] += tmp * scv[kb];
+          }
         }
       }
       float part = 0.f;
@@ -407,26 +543,19 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
       entry_at(j, valid);
       if (lg == 0) keys[j] = valid ? score_key(part) : 0u;
     }
+    }   // fp32
   };
-  // 3-slot ring, unrolled so that each slot is a distinct LDS object
-  if (st_w > 0) issue(0, ring0);
-  if (st_w > 1) issue(1, ring1);
-  auto step = [&](int i, const unsigned char* cur, unsigned char* nxt) {
-    if (i + 2 < st_w) {
-      issue(i + 2, nxt);
-      WAIT_VMCNT(2 * (SPT + 1));
-    } else if (i + 1 < st_w) {
-      WAIT_VMCNT(SPT + 1);
-    } else {
-      WAIT_VMCNT(0);
+  {
+    StLoad L0, L1;
+    if (st_w > 0) load_st(0, L0);
+    for (int i = 0; i < st_w; i += 2) {
+      if (i + 1 < st_w) load_st(i + 1, L1);
+      compute(i, L0);
+      if (i + 1 < st_w) {
+        if (i + 2 < st_w) load_st(i + 2, L0);
+        compute(i + 1, L1);
+      }
     }
-    compute(i, cur);
-    WAIT_LGKM0();
-  };
-  for (int i = 0; i < st_w; i += 3) {
-    step(i, ring0, ring2);
-    if (i + 1 < st_w) step(i + 1, ring1, ring0);
-    if (i + 2 < st_w) step(i + 2, ring2, ring1);
   }
   __syncthreads();
 
