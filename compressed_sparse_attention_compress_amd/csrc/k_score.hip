@@ -217,6 +217,65 @@ __device__ uint32_t emit_ordered(Get key_at, int n, const SelOut& s, SelSmem<NT>
   return GT + min(ET, s.eq_take);
 }
 
+// emit_ordered for a selection without a partial tie (every non-zero key >= thresh
+// is chosen) over keys in LDS: one pass in which wave w compacts its chosen keys
+// to the front of its own range of `keys` (in place: a key is written at or
+// before the position it was read from, in the same or an earlier step) and their
+// positions to its segment of `stage`, then one block-wide copy calls
+// emit(slot, key, position) for slots 0, 1, ... in position order.  Each lane
+// reads 4 consecutive keys per step; position order is lane-major.  Needs at most
+// `seg` chosen keys (the per-wave segment of `stage`).
+template <int NT, typename Emit>
+__device__ uint32_t emit_compact(uint32_t* keys, int n, uint32_t thresh, uint32_t* stage, int seg, SelSmem<NT>& sm,
+                                 Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per_w = (((n + NW - 1) / NW) + 255) & ~255;
+  const int w0 = wave * per_w, w1 = min(n, w0 + per_w);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t cnt = 0;
+  for (int i0 = w0; i0 < w1; i0 += 256) {
+    const int i = i0 + 4 * lane;
+    const uint4 kv = i < w1 ? *reinterpret_cast<const uint4*>(keys + i) : make_uint4(0, 0, 0, 0);
+    const uint32_t kk[4] = {kv.x, kv.y, kv.z, kv.w};
+    bool s[4];
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[q] = i + q < w1 && kk[q] != 0u && kk[q] >= thresh;
+      const uint64_t m = __ballot(s[q]);
+      before += __popcll(m & lt);
+      tot += __popcll(m);
+    }
+    uint32_t slot = cnt + before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (s[q]) {
+        keys[w0 + slot] = kk[q];
+        stage[wave * seg + slot] = (uint32_t)(i + q);
+        ++slot;
+      }
+    }
+    cnt += tot;
+  }
+  if (lane == 0) sm.red[0][wave] = cnt;
+  __syncthreads();
+  uint32_t off[NW + 1];
+  off[0] = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) off[w + 1] = off[w] + sm.red[0][w];
+  const uint32_t total = off[NW];
+  for (uint32_t t = threadIdx.x; t < total; t += NT) {
+    int w = 0;
+#pragma unroll
+    for (int v = 1; v < NW; ++v) w += t >= off[v] ? 1 : 0;
+    const uint32_t j = t - off[w];
+    emit(t, keys[w * per_w + j], stage[w * seg + j]);
+  }
+  __syncthreads();
+  return total;
+}
+
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w) {
   bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
   bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
@@ -334,7 +393,7 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     int C, int k_chunk, int n_chunks, int k, int hsi_s, int hsi_nb, int nblk_max) {
   typedef typename Frag<T>::type FragT;
   __shared__ SelSmem<SC_THREADS> sm;
-  __shared__ uint32_t keys[MAX_CHUNK];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[MAX_CHUNK];
 
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int bt = b * T_len + t;
@@ -588,17 +647,30 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     }
     return base + i;
   };
+  // without a partial tie and with at most NBINS / 4 chosen keys the positions can
+  // be staged in the histogram
+  constexpr int SEG = NBINS / (SC_THREADS / 64);
+  const bool compact = sel.eq_take == 0xFFFFFFFFu && need <= (uint32_t)SEG;
   if (direct) {
     int32_t* out = topk + (size_t)bt * k;
-    const uint32_t cnt = emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) { out[slot] = entry_of(i); });
+    const uint32_t cnt =
+        compact ? emit_compact<SC_THREADS>(keys, Ce, sel.thresh, sm.hist, SEG, sm,
+                                           [&](uint32_t slot, uint32_t, uint32_t i) { out[slot] = entry_of((int)i); })
+                : emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) { out[slot] = entry_of(i); });
     for (int i = (int)cnt + threadIdx.x; i < k; i += SC_THREADS) out[i] = -1;
   } else {
     const size_t obase = ((size_t)bt * n_chunks + c) * k_chunk;
     if (threadIdx.x == 0) chunk_lb[(size_t)bt * n_chunks + c] = sel.lb;
-    const uint32_t cnt = emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) {
-      cand_key[obase + slot] = keys[i];
-      cand_idx[obase + slot] = entry_of(i);
-    });
+    const uint32_t cnt =
+        compact ? emit_compact<SC_THREADS>(keys, Ce, sel.thresh, sm.hist, SEG, sm,
+                                           [&](uint32_t slot, uint32_t key, uint32_t i) {
+                                             cand_key[obase + slot] = key;
+                                             cand_idx[obase + slot] = entry_of((int)i);
+                                           })
+                : emit_ordered<SC_THREADS>(key_at, Ce, sel, sm, [&](int i, uint32_t slot) {
+                    cand_key[obase + slot] = keys[i];
+                    cand_idx[obase + slot] = entry_of(i);
+                  });
     for (int i = (int)cnt + threadIdx.x; i < k_chunk; i += SC_THREADS) {
       cand_key[obase + i] = 0u;
       cand_idx[obase + i] = -1;
