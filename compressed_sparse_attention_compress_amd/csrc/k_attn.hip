@@ -79,14 +79,21 @@ __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const i
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     int cnt = 0;
-    for (int j0 = 0; j0 < k; j0 += 64) {
-      const int j = j0 + lane;
-      const int g = j < k ? tk[j] : -1;
-      const bool ok = g >= 0 && g < N_cap;
-      const unsigned long long bal = __ballot(ok);
-      const int before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (ok) rowlist[cnt + before] = g;
-      cnt += __popcll(bal);
+    for (int j0 = 0; j0 < k; j0 += 512) {   // 8 loads per lane in flight, then the ballots
+      int g[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + 64 * u + lane;
+        g[u] = j < k ? tk[j] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = g[u] >= 0 && g[u] < N_cap;
+        const unsigned long long bal = __ballot(ok);
+        const int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (ok) rowlist[cnt + before] = g[u];
+        cnt += __popcll(bal);
+      }
     }
     if (lane == 0) *n_sel_s = cnt;
   }
@@ -421,37 +428,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
 
 // ----------------------------------------------------------------- decode
 
-constexpr int DRC = 16;                 // rows per chunk (per wave)
-constexpr int DRS = 1024;               // swizzled rows, no padding
+constexpr int DRC = 32;                 // rows per stage
+constexpr int DNS = 4;                  // stages: three in flight while one is used
 
-// grid.x = 32 * ceil(groups / 8), group = (query, split); block id ->
-// (group, head group) so that the 4 head groups of a group share block id mod 8.
-__global__ __launch_bounds__(256, 1) void attn_decode_bf16(
+// One workgroup per (query, row split); wave w owns heads 16w..16w+15, so each
+// row is fetched once per workgroup and read from LDS by every wave.  Stage s of
+// the 4-stage ring holds chunk c (32 rows) for c = s mod 4; the gathers of chunk
+// c + 3 are issued right after the barrier that opens chunk c, into the stage
+// that chunk c - 1 used.  NW = 4, 2 or 1 waves (H > 32, > 16, <= 16); wave w
+// gathers rows w, w + NW, ... of each chunk.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Q, int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
-  __shared__ __attribute__((aligned(16))) unsigned char bufA[4 * DRC * DRS];   // per-wave buffer 0
-  __shared__ __attribute__((aligned(16))) unsigned char bufB[4 * DRC * DRS];   // per-wave buffer 1
+    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
+  constexpr int RPW = DRC / NW;   // gathers per wave per chunk
+  __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
   __shared__ int rowlist[MAX_ROWS];
   __shared__ int n_sel_s;
-  __shared__ float wm[4][16], wl[4][16];
 
-  const int id = blockIdx.x;
-  const int hg = (id >> 3) & 3;
-  const int group = (id >> 5) * 8 + (id & 7);
-  if (group >= Q * n_splits) return;
-  const int qi = group / n_splits, split = group % n_splits;
-  const int b = qi / T_len, t = qi % T_len;
+  const int qi = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
+  const int b = qi / T_len;
   const int bt = qi;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
-                                   L_w, W);
-  const bf16* kvb = kv + (size_t)b * N_cap * 512;
-  const bf16* swb = swa + (size_t)b * L_w * 512;
-
-  const int head = hg * 16 + lr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the query fragments are loaded first, so that they arrive while the row list is built
+  const int head = wave * 16 + lr;
   bf16x8 qf[16];
   const bf16* qrow = q + ((size_t)bt * H + head) * 512;
 #pragma unroll
@@ -459,152 +462,147 @@ __global__ __launch_bounds__(256, 1) void attn_decode_bf16(
     if (head < H) qf[ks] = load_frag(qrow + ks * 32 + 8 * lg);
     else zero_frag(qf[ks]);
   }
+  const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
+                                   L_w, W);
+  const bf16* kvb = kv + (size_t)b * N_cap * 512;
+  const bf16* swb = swa + (size_t)b * L_w * 512;
   f32x4 oacc[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  WAIT_VMCNT(0);   // the query is in registers; from here on only the gathers use the counter
 
-  int soff[4], toff[8];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) soff[b] = ((4 * b + lg) ^ swz(lr)) << 4;
-#pragma unroll
-  for (int b = 0; b < 8; ++b) toff[b] = ((2 * b + ((lr & 3) >> 1)) ^ swz(4 * lg + (lr >> 2))) << 4;
-  // this split's range of 64-row chunks; wave w owns rows 16w..16w+15 of each
-  const int nch_all = (n_rows + 4 * DRC - 1) / (4 * DRC);
+  const int nch_all = (n_rows + DRC - 1) / DRC;
   const int c0 = (int)(((long long)nch_all * split) / n_splits);
   const int c1 = (int)(((long long)nch_all * (split + 1)) / n_splits);
-  unsigned char* myA = bufA + wave * DRC * DRS;
-  unsigned char* myB = bufB + wave * DRC * DRS;
-  // (the trip count is read from blockDim so that the compiler leaves the
-  // vector-memory wait counts to the explicit waits below)
-  const int drc_rt = (int)(blockDim.x >> 4);   // == DRC for the 256-thread launch
-  auto issue = [&](int c, unsigned char* buf) {
-    for (int rr = 0; rr < drc_rt; ++rr) {
-      const int r = c * 4 * DRC + wave * DRC + rr;
+  auto stage = [&](int c) -> unsigned char* { return ring + (c & (DNS - 1)) * (DRC * PRS); };
+  auto issue = [&](int c) {
+    unsigned char* buf = stage(c);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int rr = wave + NW * j;
+      const int r = c * DRC + rr;
       const int rid = rowlist[r < n_rows ? r : 0];
-      dma16(reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb)) + ((lane ^ swz(rr)) << 4),
-            (lds_u8*)(buf + rr * DRS));
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb));
+      dma16_asm(src + ((lane ^ swz(rr & 15)) << 4), (const lds_u8*)(buf + rr * PRS));
     }
   };
-  auto step = [&](int c, unsigned char* cur, unsigned char* nxt) {
-    if (c + 1 < c1) {
-      issue(c + 1, nxt);
-      WAIT_VMCNT(DRC);
-    } else {
-      WAIT_VMCNT(0);
-    }
-    __builtin_amdgcn_s_barrier();
-    // S^T: 16 rows x 16 heads
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  // swizzled unit offsets of the S reads and the transposed PV reads
+  int soff[4];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + lr * DRS + soff[ks & 3] + (ks >> 2) * 256);
-      s = mma16(a, qf[ks], s);
+  for (int u = 0; u < 4; ++u) soff[u] = ((4 * u + lg) ^ swz(lr)) << 4;
+  const int tsw = swz(4 * lg + (lr >> 2)), th = (lr & 3) >> 1;
+  int toff[8];
+#pragma unroll
+  for (int d8 = 0; d8 < 8; ++d8) toff[d8] = (((2 * d8 + th) ^ tsw) << 4) + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
+
+  for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue(c);
+  for (int c = c0; c < c1; ++c) {
+    const int younger = min(c1 - 1 - c, DNS - 2);   // chunks issued after c
+    if (younger >= 2) WAIT_VMCNT(2 * RPW < 63 ? 2 * RPW : 63);
+    else if (younger == 1) WAIT_VMCNT(RPW < 63 ? RPW : 63);
+    else WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();   // chunk c is in LDS; every wave is done with chunk c - 1
+    COMPILER_FENCE();
+    if (c + DNS - 1 < c1) issue(c + DNS - 1);
+    const unsigned char* cur = stage(c);
+
+    // ---- S^T = R Q^T: 32 rows (two row tiles) x this wave's 16 heads
+    f32x4 s[2];
+    s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto rd = [&](int f) -> bf16x8 {   // fragment f = (row tile f / 16, k-step f % 16)
+      return *reinterpret_cast<const bf16x8*>(cur + ((f >> 4) * 16 + lr) * PRS + soff[f & 3] + ((f & 15) >> 2) * 256);
+    };
+    bf16x8 a0 = rd(0), a1 = rd(1);
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      bf16x8 a2;
+      if (f + 2 < 32) a2 = rd(f + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      s[f >> 4] = mma16(a0, qf[f & 15], s[f >> 4]);
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = a1;
+      if (f + 2 < 32) a1 = a2;
     }
-    float x[4];
+
+    // ---- online softmax (base 2, lazy rescale); rows past the list are masked
+    float x[8];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = c * 4 * DRC + wave * DRC + 4 * lg + i;
-      x[i] = row < n_rows ? s[i] * scale_log2 : -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      const int row = c * DRC + (i >> 2) * 16 + 4 * lg + (i & 3);
+      x[i] = row < n_rows ? s[i >> 2][i & 3] * scale_log2 : -INFINITY;
       cmax = fmaxf(cmax, x[i]);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const bool grow = cmax > m_run + RESCALE_SLACK;   // false while cmax = -inf
+    cmax = max_lane_groups(cmax);   // every chunk holds a valid row, so cmax is finite
+    const bool grow = cmax > m_run + RESCALE_SLACK;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? cmax : m_run;
-      const float alpha = grow ? exp2f(m_run - m_new) : 1.0f;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 on the first rows
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    bf16x8 pf;
     float psum = 0.f;
-    v4s pf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = exp2f(x[i] - m_use);
+    for (int i = 0; i < 8; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(x[i] - m_run);
       psum += pv;
-      bf16 hb = (bf16)pv;
-      __builtin_memcpy(reinterpret_cast<char*>(&pf) + 2 * i, &hb, 2);
+      pf[i] = (bf16)pv;
     }
     l_run += psum;
-    const lds_u8* tb = (const lds_u8*)cur + (4 * lg + (lr >> 2)) * DRS + 8 * (lr & 1);
+
+    // ---- O^T += R^T P^T over the 512 dims (k-slots: rows 4g+i of tile 0, then of tile 1)
+    const lds_u8* lcur = (const lds_u8*)cur;
+    auto rdt = [&](int dt) -> bf16x8 {
+      const v4s lo4 = tr_read(lcur + toff[dt & 7] + (dt >> 3) * 256);
+      const v4s hi4 = tr_read(lcur + toff[dt & 7] + (dt >> 3) * 256 + 16 * PRS);
+      bf16x8 a;
+      __builtin_memcpy(&a, &lo4, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi4, 8);
+      return a;
+    };
+    bf16x8 v0 = rdt(0), v1 = rdt(1);
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const v4s a = tr_read(tb + toff[dt & 7] + (dt >> 3) * 256);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pf, oacc[dt], 0, 0, 0);
+      bf16x8 v2;
+      if (dt + 2 < 32) v2 = rdt(dt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[dt] = mma16(v0, pf, oacc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+      v0 = v1;
+      if (dt + 2 < 32) v1 = v2;
     }
     WAIT_LGKM0();
-  };
-  if (c0 < c1) issue(c0, myA);
-  for (int c = c0; c < c1; c += 2) {
-    step(c, myA, myB);
-    if (c + 1 < c1) step(c + 1, myB, myA);
+    COMPILER_FENCE();
   }
 
-  // ---- merge the 4 waves through LDS (reusing the row buffers)
-  float l_w = l_run + __shfl_xor(l_run, 16, 64);
-  l_w += __shfl_xor(l_w, 32, 64);
-  __syncthreads();
-  if (lg == 0) {
-    wm[wave][lr] = m_run;
-    wl[wave][lr] = l_w;
-  }
-  // per-wave [16 heads][512] float32 blocks: waves 0,1 in bufA, waves 2,3 in bufB
-  auto wave_block = [&](int w) -> float* {
-    return reinterpret_cast<float*>((w < 2 ? bufA : bufB) + (w & 1) * (16 * 512 * 4));
-  };
-  {
-    float* mine = wave_block(wave);
+  // ---- this split's normalised output and log-sum-exp (base 2) per head
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (head < H) {
+    if (n_splits == 1) {
+      bf16* orow = o + ((size_t)bt * H + head) * 512;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(&mine[lr * 512 + dt * 16 + 4 * lg]) = oacc[dt];
-  }
-  __syncthreads();
-  {
-    const int h = threadIdx.x >> 4;          // head within the group
-    const int d0 = (threadIdx.x & 15) * 32;  // 32 dims per thread
-    float mx = -INFINITY;
+      for (int dt = 0; dt < 32; ++dt) {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        bf16x4 v;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, wm[w][h]);
-    float sc[4], den = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sc[w] = (wm[w][h] == -INFINITY) ? 0.f : exp2f(wm[w][h] - mx);
-      den += sc[w] * wl[w][h];
-    }
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
-    const int hh = hg * 16 + h;
-    if (hh < H) {
-      if (n_splits == 1) {
-        bf16* orow = o + ((size_t)bt * H + hh) * 512 + d0;
-        for (int d = 0; d < 32; d += 2) {
-          float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            v0 += sc[w] * wave_block(w)[h * 512 + d0 + d];
-            v1 += sc[w] * wave_block(w)[h * 512 + d0 + d + 1];
-          }
-          bf16x2 pr;
-          pr[0] = (bf16)(v0 * inv);
-          pr[1] = (bf16)(v1 * inv);
-          *reinterpret_cast<bf16x2*>(orow + d) = pr;
-        }
-        if (lse != nullptr && (threadIdx.x & 15) == 0)
-          lse[(size_t)bt * H + hh] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
-      } else {
-        float* prow = part_o + (((size_t)bt * n_splits + split) * H + hh) * 512 + d0;
-        for (int d = 0; d < 32; ++d) {
-          float v = 0.f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) v += sc[w] * wave_block(w)[h * 512 + d0 + d];
-          prow[d] = v * inv;
-        }
-        if ((threadIdx.x & 15) == 0)
-          part_lse[((size_t)bt * n_splits + split) * H + hh] = den > 0.f ? mx + log2f(den) : -INFINITY;
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)(oacc[dt][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * lg) = v;
       }
+      if (lse != nullptr && lg == 0)
+        lse[(size_t)bt * H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      float* prow = part_o + (((size_t)bt * n_splits + split) * H + head) * 512;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + 4 * lg) = oacc[dt] * inv;
+      if (lg == 0)
+        part_lse[((size_t)bt * n_splits + split) * H + head] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
     }
   }
 }
@@ -739,17 +737,13 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W) {
   p.decode = (dtype == 1) && Q < 512;
   p.n_splits = 1;
   if (p.decode) {
-    // Each (query, head group) workgroup streams all of the query's rows, so the
-    // time of one call is about that of one workgroup; row splits only pay for
-    // their float32 partials (128 KB per query and split) when the batch is too
-    // small to give each CU a workgroup.
-    const int max_chunks = (k + W + 4 * DRC - 1) / (4 * DRC);
-    int ns = 1;
-    if (Q * 4 < 128) {
-      ns = (int)(256 / (Q * 4));
-      if (ns > max_chunks) ns = max_chunks;
-      if (ns < 1) ns = 1;
-    }
+    // A workgroup per (query, row split) keeps three 32-row chunks in flight; the
+    // splits give the GPU about 256 workgroups (one per CU) and cost a float32
+    // partial per query, split and head, merged by attn_combine.
+    const int max_chunks = (k + W + DRC - 1) / DRC;
+    int ns = (int)((256 + Q - 1) / Q);
+    if (ns > max_chunks) ns = max_chunks;
+    if (ns < 1) ns = 1;
     p.n_splits = ns;
   }
   p.ws_bytes = (p.decode && p.n_splits > 1) ? (size_t)Q * p.n_splits * H * (512 + 1) * 4 + 256 : 0;
@@ -787,8 +781,15 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   const int groups = Q * p.n_splits;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = part_o + (size_t)Q * p.n_splits * H * 512;
-  hipLaunchKernelGGL(attn_decode_bf16, dim3(32 * ((groups + 7) / 8)), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0,
-                     q_pos, oo, lse, part_o, part_lse, Q, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+  if (H > 32)
+    hipLaunchKernelGGL(attn_decode_bf16<4>, dim3(groups), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
+                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+  else if (H > 16)
+    hipLaunchKernelGGL(attn_decode_bf16<2>, dim3(groups), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
+                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+  else
+    hipLaunchKernelGGL(attn_decode_bf16<1>, dim3(groups), dim3(64), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
+                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long total = (long long)Q * H * 64;
