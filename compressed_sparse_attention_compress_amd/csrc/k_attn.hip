@@ -137,8 +137,8 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, int T_len, int H, int N_cap, int k, int L_w, int W,
-    float scale_log2) {
+    bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[PRC * PRS];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[PRC * PRS];
   __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
@@ -147,8 +147,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   // workgroups are dealt to the 8 XCDs round-robin by id; give each XCD one
   // contiguous run of tokens, so the window rows (shared by neighbouring tokens)
   // stay in that XCD's L2
+  // With row splits (few tokens) workgroup x takes split x % n_splits of token
+  // x / n_splits instead.
   const int per_xcd = (T_len + 7) >> 3;
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3), b = blockIdx.y;
+  const int split = n_splits > 1 ? (int)(blockIdx.x % n_splits) : 0;
+  const int t = n_splits > 1 ? (int)(blockIdx.x / n_splits) : (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int b = blockIdx.y;
   if (t >= T_len) return;
   const int bt = b * T_len + t;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -209,6 +213,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   const f32x4* xpart = xbuf[wave ^ 1];
 
   const int nch = (n_rows + PRC - 1) / PRC;
+  const int c0 = (int)(((long long)nch * split) / n_splits);        // this split's chunks
+  const int c1 = (int)(((long long)nch * (split + 1)) / n_splits);
   // lane l (mod 32) holds the id slot of row 32c + l (selected part only)
   auto load_ids = [&](int c) -> int {
     const int r = c * PRC + (lane & 31);
@@ -248,9 +254,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     // for it and everything older, i.e. also chunk c's gathers, which are needed
     // now anyway.  Chunk c+1's gathers and ids(c+2) then stay in flight while
     // chunk c is computed; the explicit waits restate that chunk c is complete.
-    if (c + 1 < nch) {
+    if (c + 1 < c1) {
       mask_next = issue(c + 1, nxt, ids_next);
-      if (c + 2 < nch) {
+      if (c + 2 < c1) {
         ids_next = load_ids(c + 2);
         WAIT_VMCNT(RPW + 1);
       } else {
@@ -391,14 +397,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     __builtin_amdgcn_s_barrier();
     mask_cur = mask_next;
   };
-  if (nch > 0) {
-    const int ids0 = load_ids(0);
-    ids_next = nch > 1 ? load_ids(1) : 0;
-    mask_cur = issue(0, buf0, ids0);
+  if (c0 < c1) {
+    const int ids0 = load_ids(c0);
+    ids_next = c0 + 1 < c1 ? load_ids(c0 + 1) : 0;
+    mask_cur = issue(c0, buf0, ids0);
   }
-  for (int c = 0; c < nch; c += 2) {
+  for (int c = c0; c < c1; c += 2) {
     step(c, buf0, buf1);
-    if (c + 1 < nch) step(c + 1, buf1, buf0);
+    if (c + 1 < c1) step(c + 1, buf1, buf0);
   }
 
 #pragma unroll
@@ -407,7 +413,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     l_tot += __shfl_xor(l_tot, 32, 64);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int head = hp * 32 + ht * 16 + lr;
-    if (head < H) {
+    if (head < H && n_splits > 1) {   // normalised float32 partial and log-sum-exp (base 2)
+      float* prow = part_o + (((size_t)bt * n_splits + split) * H + head) * 512 + dh * 256;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + 4 * lg) = oacc[dt][ht] * inv;
+      if (lg == 0 && dh == 0)
+        part_lse[((size_t)bt * n_splits + split) * H + head] = l_tot > 0.f ? m_run[ht] + log2f(l_tot) : -INFINITY;
+    } else if (head < H) {
       bf16* orow = o + ((size_t)bt * H + head) * 512 + dh * 256;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
@@ -771,10 +783,10 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
     // head pairs of 32 heads; two waves (dim halves) each
     if (H > 32)
       hipLaunchKernelGGL(attn_prefill_bf16<4>, dim3(8 * ((T + 7) / 8), B), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, T, H, N_cap, k, L_w, W, sl2);
+                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1);
     else
       hipLaunchKernelGGL(attn_prefill_bf16<2>, dim3(8 * ((T + 7) / 8), B), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, T, H, N_cap, k, L_w, W, sl2);
+                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1);
     return hipGetLastError();
   }
   const int Q = B * T;

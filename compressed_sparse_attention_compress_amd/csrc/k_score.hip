@@ -816,23 +816,13 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
 // visible (query, entry) pair goes to a key matrix in the workspace, and
 // select_rows then picks each query's top-k from its row.
 //
-// The FP4 codes are dequantised with the block scale applied before the MFMA:
-// code value (at most 2 significant bits) x E4M3 scale (4 significant bits) is
-// exact in bf16, so one MFMA chain covers all 4 blocks of the 128 dims.
+// The FP4 codes are dequantised to fp16 with the block scale applied before the
+// MFMA (exact, as in score_chunk), so one MFMA chain covers all 4 blocks of the
+// 128 dims; the queries are moved into fp16 range per head as there.
 constexpr int QT = 4;                 // queries per workgroup
 constexpr int QT_CE = 4096;           // entries per workgroup (64 super-tiles of 64)
 constexpr int SEL_MAX = 8192;         // keys per query row held in registers by select_rows
 
-__device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t w, float s) {
-  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  bf16x8 r;
-  r[0] = (bf16)(p0[0] * s); r[1] = (bf16)(p0[1] * s); r[2] = (bf16)(p1[0] * s); r[3] = (bf16)(p1[1] * s);
-  r[4] = (bf16)(p2[0] * s); r[5] = (bf16)(p2[1] * s); r[6] = (bf16)(p3[0] * s); r[7] = (bf16)(p3[1] * s);
-  return r;
-}
 
 __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     const bf16* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
@@ -857,7 +847,8 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
   const int n_st = (n_here + 63) / 64;
   const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave: wave, wave + 4, ...
 
-  bf16x8 qf[QT][2][4];
+  // k-step kb of lane group g: dims 32kb + 8g .. +7 (block kb)
+  f16x8 qf[QT][2][4];
   float wv[QT][2][4];
 #pragma unroll
   for (int qi = 0; qi < QT; ++qi) {
@@ -866,15 +857,28 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int h = mt * 16 + lr;
+      bf16x8 raw[4];
+      float amax = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (h < H_I) qf[qi][mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
-        else zero_frag(qf[qi][mt][kb]);
+        if (h < H_I) raw[kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
+        else zero_frag(raw[kb]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)raw[kb][i]));
       }
+      amax = max_lane_groups(amax);
+      int ex = 0;
+      frexpf(amax, &ex);
+      const int s = amax > 0.0f ? min(max(ex - 15, -96), 96) : 0;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[qi][mt][kb][i] = (f16)ldexpf((float)raw[kb][i], -s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = mt * 16 + 4 * lg + i;
-        wv[qi][mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
+        const int sh = __shfl(s, 4 * lg + i, 64);
+        wv[qi][mt][i] = hh < H_I ? ldexpf(w[(size_t)bt * H_I + hh], sh) : 0.0f;
       }
     }
   }
@@ -893,9 +897,10 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     const int ent = min(base + st * 64 + lane, n_entries - 1);
     dma4(sb + (size_t)ent * 4, (lds_u8*)(dst + SPT * 1024));
   };
-  uint32_t* krow[QT];
-#pragma unroll
-  for (int qi = 0; qi < QT; ++qi) krow[qi] = keys + (size_t)(b * T_len + min(t0 + qi, T_len - 1)) * n_scan;
+  // lane group g writes the keys of query t0 + g
+  static_assert(QT == 4, "one query per lane group");
+  const int nq_lane = t0 + lg < T_len ? visible(q_pos, b * T_len + t0 + lg, m, n_entries) : 0;
+  uint32_t* krow_lane = keys + (size_t)(b * T_len + min(t0 + lg, T_len - 1)) * n_scan;
   auto compute = [&](int i, const unsigned char* ring) {
     const int st = wave + 4 * i;
     const unsigned char* src = ring + wave * ST_BYTES;
@@ -903,8 +908,6 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     for (int tt = 0; tt < SPT; ++tt) {
       const unsigned char* tb = src + tt * 1024;
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
-      const float scv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sw, 0), __builtin_amdgcn_cvt_f32_fp8((int)sw, 1),
-                            __builtin_amdgcn_cvt_f32_fp8((int)sw, 2), __builtin_amdgcn_cvt_f32_fp8((int)sw, 3)};
       f32x4 acc[QT][2];
 #pragma unroll
       for (int qi = 0; qi < QT; ++qi) {
@@ -914,24 +917,38 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
-        const bf16x8 kf = fp4x8_scaled_bf16(cw, scv[kb]);
+        float p2;
+        f16x2 mm;
+        split_e4m3((sw >> (8 * kb)) & 0xFFu, p2, mm);
+        const f16x8 kf = fp4x8_scaled_f16(cw, p2, mm);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
-          acc[qi][0] = mma16(qf[qi][0][kb], kf, acc[qi][0]);
-          acc[qi][1] = mma16(qf[qi][1][kb], kf, acc[qi][1]);
+          acc[qi][0] = mma16h(qf[qi][0][kb], kf, acc[qi][0]);
+          acc[qi][1] = mma16h(qf[qi][1][kb], kf, acc[qi][1]);
         }
       }
-      const int e = base + st * 64 + tt * 16 + lr;
+      // per query: weighted ReLU (integer max on the float bits) summed over the
+      // lane's 8 heads, then the 4 queries' head sums over the lane groups at once:
+      // lane group g ends up with query g's score of entry e
+      float part[QT];
 #pragma unroll
       for (int qi = 0; qi < QT; ++qi) {
-        float part = 0.f;
+        float pq = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) part += wv[qi][mt][ii] * fmaxf(acc[qi][mt][ii], 0.0f);
-        part = sum_lane_groups(part);
-        if (lg == 0 && e < n_q[qi]) krow[qi][e] = score_key(part);
+          for (int ii = 0; ii < 4; ++ii)
+            pq = fmaf(wv[qi][mt][ii], __int_as_float(max(__float_as_int(acc[qi][mt][ii]), 0)), pq);
+        part[qi] = pq;
       }
+      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      const float s13 = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+      const auto cc = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+      const float sc = __uint_as_float(cc[0]) + __uint_as_float(cc[1]);
+      const int e = base + st * 64 + tt * 16 + lr;
+      if (e < nq_lane) krow_lane[e] = score_key(sc);
     }
   };
   if (st_w > 0) issue(0, ring0);
