@@ -696,9 +696,9 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                                          int m, int k, int C, int k_chunk, int n_chunks, int hsi_s,
                                                          int hsi_nb, int nblk_max) {
   __shared__ SelSmem<MG_THREADS> sel;
-  __shared__ uint32_t tile[MG_TILE];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[MG_TILE];
   __shared__ int32_t tile_idx[MG_TILE];
-  __shared__ uint32_t skey[MG_CAP];
+  __shared__ __attribute__((aligned(16))) uint32_t skey[MG_CAP];
   __shared__ int32_t sidx[MG_CAP];
   __shared__ uint32_t s_bound;
   const int t = blockIdx.x, b = blockIdx.y;
@@ -727,7 +727,68 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     // stage candidates >= bound in entry order
     uint32_t staged = 0;
     const SelOut keep{bound, 0xFFFFFFFFu, 0u};
-    for (int r = 0; r < n_items; r += MG_TILE) {
+    constexpr int MG_NW = MG_THREADS / 64;
+    constexpr int MG_REG = 8;   // uint4 loads per lane: 32 candidates
+    const bool in_regs = (k_chunk & 3) == 0 && n_items <= MG_THREADS * 4 * MG_REG;
+    if (in_regs) {
+      // all candidates at once: wave w holds items [w * 2048, w * 2048 + 2048),
+      // lane l the 4 consecutive items 4 * (64 j + l) .. + 3 of step j, so entry
+      // order is (j, lane, u); a count pass and one exchange of the per-wave
+      // counts give each wave its first slot, a second pass over the registers
+      // writes the kept candidates in order
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      const uint64_t lt = (1ull << lane) - 1ull;
+      uint4 kv[MG_REG], iv[MG_REG];
+#pragma unroll
+      for (int j = 0; j < MG_REG; ++j) {
+        const int i = wave * (256 * MG_REG) + 256 * j + 4 * lane;
+        kv[j] = i < n_items ? *reinterpret_cast<const uint4*>(kb + i) : make_uint4(0, 0, 0, 0);
+        iv[j] = i < n_items ? *reinterpret_cast<const uint4*>(ib + i) : make_uint4(0, 0, 0, 0);
+      }
+      auto kept = [&](uint32_t kk) { return kk != 0u && kk >= bound; };
+      uint32_t wc = 0;
+#pragma unroll
+      for (int j = 0; j < MG_REG; ++j)
+        wc += __popcll(__ballot(kept(kv[j].x))) + __popcll(__ballot(kept(kv[j].y))) +
+              __popcll(__ballot(kept(kv[j].z))) + __popcll(__ballot(kept(kv[j].w)));
+      if (lane == 0) sel.red[0][wave] = wc;
+      __syncthreads();
+      uint32_t slot = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < MG_NW; ++w) {
+        const uint32_t c = sel.red[0][w];
+        slot += w < wave ? c : 0u;
+        total += c;
+      }
+      if (total <= (uint32_t)MG_CAP) {
+#pragma unroll
+        for (int j = 0; j < MG_REG; ++j) {
+          const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+          const uint32_t ii[4] = {iv[j].x, iv[j].y, iv[j].z, iv[j].w};
+          bool s[4];
+          uint32_t before = 0, tot = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            s[u] = kept(kk[u]);
+            const uint64_t msk = __ballot(s[u]);
+            before += __popcll(msk & lt);
+            tot += __popcll(msk);
+          }
+          uint32_t sl = slot + before;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (s[u]) {
+              skey[sl] = kk[u];
+              sidx[sl] = (int32_t)ii[u];
+              ++sl;
+            }
+          slot += tot;
+        }
+      }
+      staged = total;
+      __syncthreads();
+    }
+    for (int r = 0; r < (in_regs ? 0 : n_items); r += MG_TILE) {
       const int len = min(MG_TILE, n_items - r);
       for (int i0 = 0; i0 < len; i0 += 4 * MG_THREADS) {   // all loads of a round in flight together
         uint32_t kk[4];
@@ -767,7 +828,12 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
       const uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
       const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
                                   : select_threshold<MG_THREADS>(key_at, (int)staged, need, mn, mx, 0u, sel);
-      cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel, [&](int i, uint32_t slot) { out[slot] = sidx[i]; });
+      // without a partial tie the chosen positions are staged in tile[] (8 waves x 512)
+      if (s.eq_take == 0xFFFFFFFFu && need <= (uint32_t)(MG_TILE / (MG_THREADS / 64)))
+        cnt = emit_compact<MG_THREADS>(skey, (int)staged, s.thresh, tile, MG_TILE / (MG_THREADS / 64), sel,
+                                       [&](uint32_t slot, uint32_t, uint32_t i) { out[slot] = sidx[i]; });
+      else
+        cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel, [&](int i, uint32_t slot) { out[slot] = sidx[i]; });
     } else {
       // more candidates than LDS holds: select straight from the workspace
       auto key_at = [&](int i) -> uint32_t { const uint32_t kk = kb[i]; return kk >= bound ? kk : 0u; };
