@@ -304,14 +304,23 @@ __global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __res
 }
 
 // One wave per entry: RMSNorm, RoPE on dims 448..511, write latent (fp32, in
-// place over the pooled values) and the cache row.
+// place over the pooled values) and the cache row.  The 4 x 32 rotary angles of
+// the workgroup's entries are evaluated once, one per thread, into LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat, const float* __restrict__ gamma,
                                                          T* __restrict__ kv_cache, int n_entries, int entry0,
                                                          int m, int N_cap, float eps, double base) {
+  __shared__ float2 rot[4][32];
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
+  if (threadIdx.x < 128) {
+    const int ee = blockIdx.x * 4 + (threadIdx.x >> 5), pair = threadIdx.x & 31;
+    float c = 1.f, s = 0.f;
+    if (ee < n_entries) rope_cos_sin((int64_t)(entry0 + ee) * m, pair, 64, base, c, s);
+    rot[threadIdx.x >> 5][pair] = make_float2(c, s);
+  }
+  __syncthreads();
   if (e >= n_entries) return;
   float* row = lat + ((size_t)b * n_entries + e) * 512;
   float v[8];
@@ -332,12 +341,10 @@ __global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat
   w4[0] = make_float4(v[0], v[1], v[2], v[3]);
   w4[1] = make_float4(v[4], v[5], v[6], v[7]);
   if (lane >= 56) {  // dims 448..511: 4 rotary pairs per lane
-    const int64_t pos = (int64_t)(entry0 + e) * m;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int pair = (lane - 56) * 4 + j;
-      float c, s;
-      rope_cos_sin(pos, pair, 64, base, c, s);
+      const float2 cs = rot[threadIdx.x >> 6][(lane - 56) * 4 + j];
+      const float c = cs.x, s = cs.y;
       float x0 = v[2 * j], x1 = v[2 * j + 1];
       v[2 * j] = x0 * c - x1 * s;
       v[2 * j + 1] = x0 * s + x1 * c;

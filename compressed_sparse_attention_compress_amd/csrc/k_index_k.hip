@@ -10,7 +10,8 @@
 // sign kept), all divisions float32 round-to-nearest; a zero scale zeroes the
 // block.  The code of dim 2j is the low nibble of byte j.
 //
-// Kernel: a workgroup of 4 waves per 16 entries, no LDS; wave q computes the 32
+// Kernel: a workgroup of 4 waves per 16 entries; the 16 x 32 rotary angles are
+// evaluated once into LDS by all threads; wave q computes the 32
 // output dims of quantisation block q.  MFMA with the 16 entries as rows and the
 // block's 32 dims as 2 column tiles; the float32 latent is split into a bf16 high
 // part and a bf16 remainder (two MFMAs) so bf16 weights lose nothing beyond ~2^-17
@@ -34,37 +35,55 @@ __device__ __forceinline__ void split_hi_lo(const f32x8& a, bf16x8& hi, bf16x8& 
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                       int N, int m, int entry0, int N_cap, double base) {
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // quantisation block of this wave
   const int e0 = blockIdx.x * 16;
   const int b = blockIdx.y;
+  // rotary angles of the 16 entries x 32 pairs, two per thread, into LDS
+  __shared__ float2 rot[16][32];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = threadIdx.x + 256 * r, ee = idx >> 5, pair = idx & 31;
+    float c = 1.f, s = 0.f;
+    if (e0 + ee < N) rope_cos_sin((int64_t)(entry0 + e0 + ee) * m, pair, 64, base, c, s);
+    rot[ee][pair] = make_float2(c, s);
+  }
+  __syncthreads();
   const float* lb = lat + (size_t)b * N * 512;
   const int arow = e0 + lr;
+  // rows past N read row N - 1: they only feed outputs of entries that are not stored
+  const float* arow_p = lb + (size_t)min(arow, N - 1) * 512;
   f32x4 acc[2];
   acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < 16; ++ks) {
-    f32x8 a;
-    if (arow < N) a = load_frag(lb + (size_t)arow * 512 + ks * 32 + 8 * lg);
-    else zero_frag(a);
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 hi, lo;
-      split_hi_lo(a, hi, lo);
+  // eight k-steps per round: all their loads are issued before the first MFMA
+  for (int k0 = 0; k0 < 16; k0 += 8) {
+    f32x8 a[8];
+    typename Frag<T>::type bw[8][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 bw = load_frag(reinterpret_cast<const bf16*>(w_ik) + (size_t)((2 * q + j) * 16 + lr) * 512 + ks * 32 + 8 * lg);
-        acc[j] = mma16(hi, bw, acc[j]);
-        acc[j] = mma16(lo, bw, acc[j]);
-      }
-    } else {
+    for (int u = 0; u < 8; ++u) {
+      a[u] = load_frag(arow_p + (k0 + u) * 32 + 8 * lg);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x8 bw = load_frag(reinterpret_cast<const float*>(w_ik) + (size_t)((2 * q + j) * 16 + lr) * 512 + ks * 32 + 8 * lg);
-        acc[j] = mma16(a, bw, acc[j]);
+      for (int j = 0; j < 2; ++j)
+        bw[u][j] = load_frag(w_ik + (size_t)((2 * q + j) * 16 + lr) * 512 + (k0 + u) * 32 + 8 * lg);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 hi, lo;
+        split_hi_lo(a[u], hi, lo);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j] = mma16(hi, bw[u][j], acc[j]);
+          acc[j] = mma16(lo, bw[u][j], acc[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = mma16(a[u], bw[u][j], acc[j]);
       }
     }
   }
@@ -76,9 +95,8 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
       const int pair = (2 * q + j - 4) * 8 + (lr >> 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = e0 + 4 * lg + i;
-        float c, s;
-        rope_cos_sin((int64_t)(entry0 + e) * m, pair, 64, base, c, s);
+        const float2 cs = rot[4 * lg + i][pair];
+        const float c = cs.x, s = cs.y;
         float mine = acc[j][i];
         float other = __shfl_xor(mine, 1, 64);
         acc[j][i] = (lr & 1) ? (other * s + mine * c) : (mine * c - other * s);
