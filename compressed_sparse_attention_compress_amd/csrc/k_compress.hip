@@ -241,20 +241,32 @@ __global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __res
     COMPILER_FENCE();
     __builtin_amdgcn_s_barrier();
     COMPILER_FENCE();
-    // every wave is past stage kt-1, whose buffer takes stage kt+2
+    // every wave is past stage kt-1, whose buffer takes stage kt+2; its gathers
+    // are issued after the first half-step (an asm statement between the
+    // fragment reads and their MFMAs would make the compiler wait for every
+    // outstanding read)
+    // the 8 fragments of the first half-step are read up front; those of the
+    // second half are read two at a time between the first half's MFMAs, so they
+    // arrive under them (the LDS counter tracks at most 15 reads)
+    bf16x8 a[2][4], bb[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) a[0][mt] = *reinterpret_cast<const bf16x8*>(cur + aoff[0] + mt * 16 * 128);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bb[0][nt] = *reinterpret_cast<const bf16x8*>(cur + boff[0] + nt * 16 * 128);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      __builtin_amdgcn_sched_barrier(0);
+      a[1][mt] = *reinterpret_cast<const bf16x8*>(cur + aoff[1] + mt * 16 * 128);
+      bb[1][mt] = *reinterpret_cast<const bf16x8*>(cur + boff[1] + mt * 16 * 128);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma16(a[0][mt], bb[0][nt], acc[mt][nt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 2 < nk) issue(kt + 2, nxt2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 a[4], bb[4];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(cur + aoff[ks] + mt * 16 * 128);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bb[nt] = *reinterpret_cast<const bf16x8*>(cur + boff[ks] + nt * 16 * 128);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma16(a[mt], bb[nt], acc[mt][nt]);
-    }
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma16(a[1][mt], bb[1][nt], acc[mt][nt]);
   };
   issue(0, st0);
   if (nk > 1) issue(1, st1);
