@@ -173,6 +173,47 @@ def test_score_topk_many_queries_vs_oracle(m, k, H_I):
     assert exact >= n - 1
 
 
+@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 3), (torch.bfloat16, 300), (torch.float32, 3)])
+def test_score_topk_exact_ties_vs_oracle(dtype, T):
+    """An index-K cache of 50 distinct rows repeated: every score value occurs ~100
+    times, so the k-th best falls inside a group of equal scores and the selection
+    must take that group's smallest positions (ties go to the smaller entry id).
+    Equal rows give bit-identical scores on both sides, and the distinct values are
+    kept well apart, so the chosen set is unique and compared exactly: T = 3 runs
+    the chunked scorer and the merge, T = 300 the query-tiled scorer and the
+    per-query select."""
+    B, n_fill, k, H_I, m = 1, 5000, 512, 32, 1
+    say(f"case: score_topk exact ties dtype={dtype} T={T}")
+    u = synth.gaussian((50, 128), 1.0, 31, "u", 0, torch.float32, "cpu").numpy()
+    base_c, base_s = O.fp4_pack(u)
+    rep = np.random.default_rng(31).integers(0, 50, size=n_fill)
+    codes = base_c[rep][None].copy()
+    scales = base_s[rep][None].copy()
+    kd = O.fp4_unpack(codes[0], scales[0])
+    q_idx = synth.gaussian((B, T, H_I, 128), 1.0, 31, "q_idx", 0, dtype, DEV)
+    w = synth.gaussian((B, T, H_I), 1.0, 31, "w", 0, torch.float32, DEV)
+    q_pos = torch.full((B, T), n_fill * m - 1, dtype=torch.int32, device=DEV)
+    topk = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    K.csa2_score_topk(None, q_idx, w, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), q_pos, topk,
+                      n_entries=n_fill, m=m, k=k)
+    torch.cuda.synchronize()
+    tg = topk.cpu().numpy()
+    checked = ties = 0
+    for t in sorted(set([0, 1, T - 1] + list(range(0, T, 37)))):
+        sc = O.index_scores(npy(q_idx[0, t]), npy(w[0, t]), kd, n_fill)
+        vals = np.unique(sc)
+        gaps = np.diff(vals) / np.maximum(np.abs(vals[1:]), 1e-30)
+        if gaps.size and gaps.min() <= 1e-3:
+            continue   # two distinct rows score too close to order them exactly
+        order = np.lexsort((np.arange(n_fill), -sc))
+        want = np.sort(order[:k])
+        assert np.array_equal(tg[0, t], want), f"t={t}: tie-broken top-k differs from the oracle"
+        checked += 1
+        ties += int(sc[order[k]] == sc[order[k - 1]])   # the k-th best shares its score with the (k+1)-th
+    say(f"  {checked} queries compared exactly, {ties} with the boundary inside a tie group")
+    assert checked >= 2 and ties >= 1
+
+
 def test_score_topk_hsi_build_and_use():
     B, N_cap, m, k, s, nb = 2, 4096, 1, 64, 16, 20
     pos = np.array([[4095, 100, 10, 2000], [3000, 319, 4095, 17]])
