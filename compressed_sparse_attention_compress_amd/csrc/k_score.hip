@@ -72,6 +72,7 @@ __device__ void key_stats(Get key_at, int n, SelSmem<NT>& sm, uint32_t& mn, uint
   mn = 0xFFFFFFFFu;
   mx = 0u;
   nv = 0u;
+#pragma unroll 8   // several key reads in flight
   for (int i = threadIdx.x; i < n; i += NT) {
     const uint32_t kk = key_at(i);
     if (kk) {
@@ -129,6 +130,7 @@ __device__ SelOut select_threshold(Get key_at, int n, uint32_t need, uint32_t mn
     const int shift = (R >> 11) == 0 ? 0 : 32 - __clz((int)(R >> 11));
     for (int i = threadIdx.x; i < NBINS; i += NT) sm.hist[i] = 0;
     __syncthreads();
+#pragma unroll 8   // several key reads in flight
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint32_t kk = key_at(i);
       if (kk && kk >= lo && kk <= hi) atomicAdd(&sm.hist[(kk - lo) >> shift], 1u);
