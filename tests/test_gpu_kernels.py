@@ -322,6 +322,56 @@ def test_sparse_attn_prefill_path_vs_oracle(H, k, W):
     assert worst <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("H,k,W", [(64, 512, 128), (16, 96, 40)])
+def test_sparse_attn_decode_single_split_vs_oracle(H, k, W):
+    """Few-query bf16 attention with one row split per query (256..511 queries: each
+    workgroup writes its output directly, no partials), with 4 and 1 waves per
+    workgroup; rows with holes, out-of-range ids and no selected entry; every 23rd
+    query checked against the oracle."""
+    B, T, N_cap, L_w = 3, 100, 1200, 400
+    say(f"case: sparse_attn decode single split H={H} k={k} W={W}")
+    gen = np.random.default_rng(37)
+    q = synth.gaussian((B, T, H, 512), 1.0, 37, "q", 0, torch.bfloat16, DEV)
+    kv = synth.gaussian((B, N_cap, 512), 1.0, 37, "kv_cache", 0, torch.bfloat16, DEV)
+    swa = synth.gaussian((B, L_w, 512), 1.0, 37, "swa_kv", 0, torch.bfloat16, DEV)
+    pos0 = np.array([0, 50, 399], np.int32)
+    # positions up to the last row the window buffer holds (some before pos0: empty window)
+    pos = np.stack([gen.integers(0, int(pos0[b]) + L_w, size=T) for b in range(B)]).astype(np.int32)
+    tk = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(gen.integers(0, k + 1)) if t % 7 else 0
+            tk[b, t, :n] = np.sort(gen.choice(N_cap, size=n, replace=False))
+            if n > 3 and t % 3 == 0:
+                tk[b, t, 1] = -1            # a hole
+                tk[b, t, n - 1] = N_cap + 9  # out of range: skipped
+    o = torch.empty_like(q)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=DEV)
+    K.csa2_sparse_attn(None, q, kv, torch.from_numpy(tk).to(DEV), swa, torch.from_numpy(pos0).to(DEV),
+                       torch.from_numpy(pos).to(DEV), o, W=W, lse=lse)
+    torch.cuda.synchronize()
+    og, lg = npy(o), lse.cpu().numpy()
+    kvn, swn, qn = npy(kv), npy(swa), npy(q)
+    worst = 0.0
+    for b in range(B):
+        for t in list(range(0, T, 23)) + [T - 1]:
+            sel = tk[b, t]
+            sel = sel[(sel >= 0) & (sel < N_cap)]
+            p_t = int(pos[b, t])
+            n_win = max(0, min(p_t, int(pos0[b]) + L_w - 1) - max(0, p_t - W + 1, int(pos0[b])) + 1)
+            if sel.size + n_win == 0:   # nothing to attend to: zero output, log-sum-exp -inf
+                assert np.all(og[b, t] == 0) and np.all(np.isneginf(lg[b, t])), f"b{b} t{t}: empty row"
+                continue
+            ref, p, rows = O.sparse_attention(qn[b, t], kvn[b], sel, swn[b], int(pos0[b]), p_t, W)
+            worst = max(worst, row_rel_err(og[b, t], ref))
+            logits = (qn[b, t] @ rows.T) / math.sqrt(512)
+            mx = logits.max(1)
+            lse_ref = mx + np.log(np.exp(logits - mx[:, None]).sum(1))
+            assert np.allclose(lg[b, t], lse_ref, rtol=1e-4, atol=1e-3)
+    say(f"  worst row rel err {worst:.2e}")
+    assert worst <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype,H,k,W", [(torch.float32, 8, 32, 16), (torch.bfloat16, 64, 512, 128),
                                          (torch.bfloat16, 20, 77, 5)])
 def test_sparse_attn_vs_oracle(dtype, H, k, W):
