@@ -138,22 +138,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
+    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits, int tbl) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[PRC * PRS];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[PRC * PRS];
   __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
   constexpr int RPW = PRC / NW;          // rows gathered per wave per chunk
 
-  // workgroups are dealt to the 8 XCDs round-robin by id; give each XCD one
-  // contiguous run of tokens, so the window rows (shared by neighbouring tokens)
-  // stay in that XCD's L2
+  // workgroups are dealt to the 8 XCDs round-robin by id; give each XCD runs of
+  // tbl consecutive tokens, so the window rows (shared by neighbouring tokens)
+  // stay in that XCD's L2, with the runs dealt round-robin so that every XCD gets
+  // early (short, causal) and late tokens alike, and the latest tokens (the most
+  // rows) go first so that the short ones fill the tail
   // With row splits (few tokens) workgroup x takes split x % n_splits of token
   // x / n_splits instead.
-  const int per_xcd = (T_len + 7) >> 3;
+  const int jx = blockIdx.x >> 3;
   const int split = n_splits > 1 ? (int)(blockIdx.x % n_splits) : 0;
-  const int t = n_splits > 1 ? (int)(blockIdx.x / n_splits) : (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int t = n_splits > 1 ? (int)(blockIdx.x / n_splits)
+                             : T_len - 1 - (((jx / tbl) * 8 + (int)(blockIdx.x & 7)) * tbl + jx % tbl);
   const int b = blockIdx.y;
-  if (t >= T_len) return;
+  if (t < 0 || t >= T_len) return;
   const int bt = b * T_len + t;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -781,12 +784,14 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   bf16* oo = static_cast<bf16*>(o);
   if (!p.decode) {
     // head pairs of 32 heads; two waves (dim halves) each
+    const int tbl = std::max(1, std::min(128, (T + 7) / 8));   // tokens per run dealt to one XCD
+    const dim3 grid(8 * tbl * ((T + 8 * tbl - 1) / (8 * tbl)), B);
     if (H > 32)
-      hipLaunchKernelGGL(attn_prefill_bf16<4>, dim3(8 * ((T + 7) / 8), B), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1);
+      hipLaunchKernelGGL(attn_prefill_bf16<4>, grid, dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1, tbl);
     else
-      hipLaunchKernelGGL(attn_prefill_bf16<2>, dim3(8 * ((T + 7) / 8), B), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1);
+      hipLaunchKernelGGL(attn_prefill_bf16<2>, grid, dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
+                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1, tbl);
     return hipGetLastError();
   }
   const int Q = B * T;

@@ -899,7 +899,9 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
   __shared__ __attribute__((aligned(16))) unsigned char ring0[4 * ST_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char ring1[4 * ST_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[4 * ST_BYTES];
-  const int c = blockIdx.x, t0 = blockIdx.y * QT, b = blockIdx.z;
+  // query tiles in reverse order: the latest queries (most visible entries) start
+  // first and the short ones fill the tail
+  const int c = blockIdx.x, t0 = (int)(gridDim.y - 1 - blockIdx.y) * QT, b = blockIdx.z;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int n_q[QT];
@@ -1112,7 +1114,8 @@ __global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __rest
   __shared__ uint32_t cand_all[SC_THREADS / 64][SW_CAP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = blockIdx.x * (SC_THREADS / 64) + wave, b = blockIdx.y;
+  // latest queries (longest rows) first
+  const int t = (int)(gridDim.x - 1 - blockIdx.x) * (SC_THREADS / 64) + wave, b = blockIdx.y;
   if (t >= T_len) return;
   uint32_t* hist = hist_all[wave];
   uint32_t* cand = cand_all[wave];
