@@ -21,12 +21,11 @@
 //
 // attn_prefill: one workgroup per token; wave (hp, dh) owns heads 32hp..32hp+31
 //   and latent dims 256dh..256dh+255 (split-K: the two half-dim score partials are
-//   swapped through LDS), 32-row chunks, two workgroups per CU.
-// attn_decode: one workgroup per (token, row split, head group); its 4 waves take
-//   interleaved 16-row chunks with private double buffers and are merged through
-//   LDS at the end.  The 4 head-group workgroups of a token are numbered so they
-//   land on the same XCD (block id mod 8), so its rows come from HBM once and are
-//   re-read from that XCD's L2.  Row splits, when used, write float32 partials
+//   swapped through LDS), 32-row chunks, two workgroups per CU; runs of tokens
+//   are dealt to the XCDs round-robin, latest tokens first.
+// attn_decode: one workgroup per (token, row split) for all heads (wave w owns
+//   heads 16w..16w+15), rows gathered once into a 4-stage ring of 32-row chunks
+//   with three chunks in flight.  Row splits, when used, write float32 partials
 //   (normalised output + log-sum-exp) that attn_combine merges.
 #include "csa2_internal.h"
 #include "device_common.h"
@@ -137,8 +136,8 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits, int tbl) {
+    bf16* __restrict__ o, float* __restrict__ lse, int T_len, int H, int N_cap, int k, int L_w, int W,
+    float scale_log2, int tbl) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[PRC * PRS];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[PRC * PRS];
   __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
@@ -149,12 +148,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   // stay in that XCD's L2, with the runs dealt round-robin so that every XCD gets
   // early (short, causal) and late tokens alike, and the latest tokens (the most
   // rows) go first so that the short ones fill the tail
-  // With row splits (few tokens) workgroup x takes split x % n_splits of token
-  // x / n_splits instead.
   const int jx = blockIdx.x >> 3;
-  const int split = n_splits > 1 ? (int)(blockIdx.x % n_splits) : 0;
-  const int t = n_splits > 1 ? (int)(blockIdx.x / n_splits)
-                             : T_len - 1 - (((jx / tbl) * 8 + (int)(blockIdx.x & 7)) * tbl + jx % tbl);
+  const int t = T_len - 1 - (((jx / tbl) * 8 + (int)(blockIdx.x & 7)) * tbl + jx % tbl);
   const int b = blockIdx.y;
   if (t < 0 || t >= T_len) return;
   const int bt = b * T_len + t;
@@ -216,8 +211,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   const f32x4* xpart = xbuf[wave ^ 1];
 
   const int nch = (n_rows + PRC - 1) / PRC;
-  const int c0 = (int)(((long long)nch * split) / n_splits);        // this split's chunks
-  const int c1 = (int)(((long long)nch * (split + 1)) / n_splits);
   // lane l (mod 32) holds the id slot of row 32c + l (selected part only)
   auto load_ids = [&](int c) -> int {
     const int r = c * PRC + (lane & 31);
@@ -257,9 +250,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     // for it and everything older, i.e. also chunk c's gathers, which are needed
     // now anyway.  Chunk c+1's gathers and ids(c+2) then stay in flight while
     // chunk c is computed; the explicit waits restate that chunk c is complete.
-    if (c + 1 < c1) {
+    if (c + 1 < nch) {
       mask_next = issue(c + 1, nxt, ids_next);
-      if (c + 2 < c1) {
+      if (c + 2 < nch) {
         ids_next = load_ids(c + 2);
         WAIT_VMCNT(RPW + 1);
       } else {
@@ -400,14 +393,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     __builtin_amdgcn_s_barrier();
     mask_cur = mask_next;
   };
-  if (c0 < c1) {
-    const int ids0 = load_ids(c0);
-    ids_next = c0 + 1 < c1 ? load_ids(c0 + 1) : 0;
-    mask_cur = issue(c0, buf0, ids0);
+  if (nch > 0) {
+    const int ids0 = load_ids(0);
+    ids_next = nch > 1 ? load_ids(1) : 0;
+    mask_cur = issue(0, buf0, ids0);
   }
-  for (int c = c0; c < c1; c += 2) {
+  for (int c = 0; c < nch; c += 2) {
     step(c, buf0, buf1);
-    if (c + 1 < c1) step(c + 1, buf1, buf0);
+    if (c + 1 < nch) step(c + 1, buf1, buf0);
   }
 
 #pragma unroll
@@ -416,13 +409,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     l_tot += __shfl_xor(l_tot, 32, 64);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int head = hp * 32 + ht * 16 + lr;
-    if (head < H && n_splits > 1) {   // normalised float32 partial and log-sum-exp (base 2)
-      float* prow = part_o + (((size_t)bt * n_splits + split) * H + head) * 512 + dh * 256;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + 4 * lg) = oacc[dt][ht] * inv;
-      if (lg == 0 && dh == 0)
-        part_lse[((size_t)bt * n_splits + split) * H + head] = l_tot > 0.f ? m_run[ht] + log2f(l_tot) : -INFINITY;
-    } else if (head < H) {
+    if (head < H) {
       bf16* orow = o + ((size_t)bt * H + head) * 512 + dh * 256;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
@@ -788,10 +775,10 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
     const dim3 grid(8 * tbl * ((T + 8 * tbl - 1) / (8 * tbl)), B);
     if (H > 32)
       hipLaunchKernelGGL(attn_prefill_bf16<4>, grid, dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1, tbl);
+                         oo, lse, T, H, N_cap, k, L_w, W, sl2, tbl);
     else
       hipLaunchKernelGGL(attn_prefill_bf16<2>, grid, dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, nullptr, nullptr, T, H, N_cap, k, L_w, W, sl2, 1, tbl);
+                         oo, lse, T, H, N_cap, k, L_w, W, sl2, tbl);
     return hipGetLastError();
   }
   const int Q = B * T;
