@@ -499,27 +499,36 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   // Flat selection reads consecutive entries through buffer resources over this
   // sequence's codes and scales: one offset per super-tile, immediate offsets per
   // tile, and reads past the N_cap entries return 0 (their keys are masked anyway).
+  // The loads of a super-tile past the wave's last one are issued too, with an
+  // offset past the buffer (no memory access) or entry 0, so that every load is
+  // unconditional: the compiler's wait counts then let the next super-tile's loads
+  // stay in flight while one is computed (a conditional load makes it assume the
+  // shorter queue and wait for them).
   const bool use_buf = !POOL && N_cap <= (1 << 25);
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)cb, (short)0, use_buf ? N_cap * 64 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)sb, (short)0, use_buf ? N_cap * 4 : 0, 0x00020000);
-  auto load_st = [&](int i, StLoad& L) {
+  auto load_buf = [&](int i, StLoad& L) {
     const int st = wave + 4 * i;
-    if (use_buf) {
-      const int e = base + st * 64 + lr;
+    const bool live = i < st_w;
+    const int e = base + st * 64 + lr;
+    const int oc = live ? e * 64 + 16 * lg : (int)0x80000000;
+    const int os = live ? e * 4 : (int)0x80000000;
 #pragma unroll
-      for (int tt = 0; tt < SPT; ++tt) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, e * 64 + 16 * lg + tt * 1024, 0, 0);
-        L.c[tt] = make_uint4(v[0], v[1], v[2], v[3]);
-        L.s[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs, e * 4 + tt * 64, 0, 0);
-      }
-      return;
+    for (int tt = 0; tt < SPT; ++tt) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + tt * 1024, 0, 0);
+      L.c[tt] = make_uint4(v[0], v[1], v[2], v[3]);
+      L.s[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs, os + tt * 64, 0, 0);
     }
+  };
+  auto load_glob = [&](int i, StLoad& L) {
+    const int st = wave + 4 * i;
+    const bool live = i < st_w;
 #pragma unroll
     for (int tt = 0; tt < SPT; ++tt) {
       bool v;
-      const int ent = entry_at(st * 64 + tt * 16 + lr, v);
+      const int ent = live ? entry_at(st * 64 + tt * 16 + lr, v) : 0;
       L.c[tt] = *reinterpret_cast<const uint4*>(cb + (size_t)ent * 64 + 16 * lg);
       L.s[tt] = *reinterpret_cast<const uint32_t*>(sb + (size_t)ent * 4);
     }
@@ -606,18 +615,21 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     }
     }   // fp32
   };
-  {
+  // one loop per load form, so that each loop's wait counts see one kind of load
+  auto scan = [&](auto load_st) {
     StLoad L0, L1;
-    if (st_w > 0) load_st(0, L0);
+    load_st(0, L0);
     for (int i = 0; i < st_w; i += 2) {
-      if (i + 1 < st_w) load_st(i + 1, L1);
+      load_st(i + 1, L1);
+      __builtin_amdgcn_sched_barrier(0);
       compute(i, L0);
-      if (i + 1 < st_w) {
-        if (i + 2 < st_w) load_st(i + 2, L0);
-        compute(i + 1, L1);
-      }
+      load_st(i + 2, L0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < st_w) compute(i + 1, L1);
     }
-  }
+  };
+  if (use_buf) scan(load_buf);
+  else scan(load_glob);
   __syncthreads();
 
   if (BUILD) {
