@@ -39,12 +39,8 @@ constexpr int MAX_ROWS = 2048;   // selected + window rows per query (host-check
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
 
 
-__device__ __forceinline__ void dma16(const void* gsrc, lds_u8* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)ldst, 16, 0, 0);
-}
 
 // Max over lanes l and l^16, then l^32, with the gfx950 permlane swaps (VALU, no LDS).
 __device__ __forceinline__ float max_lane_groups(float x) {

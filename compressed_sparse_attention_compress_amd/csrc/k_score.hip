@@ -25,6 +25,7 @@
 // -1; with HSI BUILD also the n_b best blocks (newest block forced) as the pool.
 #include "csa2_internal.h"
 #include "device_common.h"
+#include "lds_dma.h"
 
 namespace csa2 {
 
@@ -307,16 +308,6 @@ constexpr int SC_THREADS = 256;
 constexpr int SPT = 4;                          // tiles (of 16 entries) per super-tile
 constexpr int ST_BYTES = SPT * 1024 + 256;      // one super-tile in LDS: codes + scales
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-#define WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
-__device__ __forceinline__ void dma16(const void* g, lds_u8* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, lds_u8* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 4, 0, 0);
-}
 
 // Visible entries of query (b, t).
 __device__ __forceinline__ int visible(const int32_t* q_pos, int bt, int m, int n_entries) {
@@ -974,10 +965,10 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
 #pragma unroll
     for (int tt = 0; tt < SPT; ++tt) {
       const int ent = min(base + st * 64 + tt * 16 + dma_e, n_entries - 1);
-      dma16(cb + (size_t)ent * 64 + 16 * dma_b, (lds_u8*)(dst + tt * 1024));
+      dma16_asm(cb + (size_t)ent * 64 + 16 * dma_b, (const lds_u8*)(dst + tt * 1024));
     }
     const int ent = min(base + st * 64 + lane, n_entries - 1);
-    dma4(sb + (size_t)ent * 4, (lds_u8*)(dst + SPT * 1024));
+    dma4_asm(sb + (size_t)ent * 4, (const lds_u8*)(dst + SPT * 1024));
   };
   // lane group g writes the keys of query t0 + g
   static_assert(QT == 4, "one query per lane group");
@@ -1035,6 +1026,10 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
   };
   if (st_w > 0) issue(0, ring0);
   if (st_w > 1) issue(1, ring1);
+  // Each wave reads only the super-tiles it loaded itself, so its own wait is
+  // enough: loads complete in issue order, so at most the younger stages' loads
+  // outstanding (the key stores in between may be either way) means super-tile i
+  // is in LDS.  The LDS-read wait at the end frees the buffer for the next DMA.
   auto step = [&](int i, const unsigned char* cur, unsigned char* nxt) {
     if (i + 2 < st_w) {
       issue(i + 2, nxt);
@@ -1044,8 +1039,10 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     } else {
       WAIT_VMCNT(0);
     }
+    COMPILER_FENCE();
     compute(i, cur);
     WAIT_LGKM0();
+    COMPILER_FENCE();
   };
   for (int i = 0; i < st_w; i += 3) {
     step(i, ring0, ring2);
