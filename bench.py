@@ -5,7 +5,9 @@ Headline (the `value` of the JSON line): encoder Full-layer prefill throughput i
 tokens/s -- one step = compressor + index K + score/top-k + sparse attention over
 one batch (B=1, L=8192, hidden 4096, m=2, 32x128 FP4 indexer heads, top-512, window
 128, 64 heads, bf16 in / fp32 accumulate).  A second record ("decode") times the
-batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries).
+batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries), and
+a third ("decode_hsi_1m") the 1M-context decode step with the HSI candidate pool
+(4 sequences x 524288 entries).
 
 Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
@@ -156,6 +158,83 @@ class DecodeBench:
         }
 
 
+# --------------------------------------------------------------------------- C5
+
+class HsiDecodeBench:
+    """1M-context decode with the HSI candidate pool: 4 sequences x 524288 m=2
+    entries.  The Full layer scores every entry, keeps its top-512 and the block
+    maxima (s=64) and picks the 256 best blocks (newest forced); the Reindex layer
+    scores the 16384-entry pool only; both attend.  The 142.6 MB of index K would
+    sit in the 256 MB MALL if one copy were re-read every step, so the steps rotate
+    over three copies (428 MB) and every scan comes from HBM."""
+
+    def __init__(self, torch, K, synth, B=4, n_entries=524288, m=2, H_I=32, k=512, W=128, H=64, s_blk=64, n_b=256,
+                 copies=3):
+        self.t, self.K = torch, K
+        dev = "cuda"
+        self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
+        self.s_blk, self.n_b, self.copies = s_blk, n_b, copies
+        g = torch.Generator(device=dev)
+        g.manual_seed(4321)
+        self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
+        scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
+        for b in range(B):
+            u = torch.randn(n_entries, 128, generator=g, device=dev, dtype=torch.float32)
+            K.csa2_fp4_pack(u, codes[b], scales[b])
+        del u
+        self.ik = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]
+        p = n_entries * m - 1
+        self.q_pos = torch.full((B, 1), p, dtype=torch.int32, device=dev)
+        self.swa_pos0 = torch.full((B,), p - W + 1, dtype=torch.int32, device=dev)
+        self.layers = [synth.decode_query_inputs(B, H, H_I, W, seed=5, layer=l, dtype=torch.bfloat16, device=dev)
+                       for l in range(2)]
+        self.tk = [torch.empty(B, 1, k, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.cand = torch.empty(B, 1, n_b, dtype=torch.int32, device=dev)
+        self.o = [torch.empty_like(self.layers[l]["q"]) for l in range(2)]
+        common = dict(codes=codes, scales=scales, q_pos=self.q_pos, n_entries=n_entries, m=m, k=k, N_cap=n_entries,
+                      hsi_s=s_blk, hsi_nb=n_b, candidates=self.cand)
+        nb = max(K.score_topk_workspace_bytes(q_idx=self.layers[l]["q_idx"], w=self.layers[l]["w"], topk=self.tk[l],
+                                              hsi=(K.HSI_BUILD, K.HSI_USE)[l], **common) for l in range(2))
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W)
+        self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
+        self.rep = 0
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        K = self.K
+        f, r = self.layers
+        codes, scales = self.ik[self.rep]
+        self.rep = (self.rep + 1) % self.copies
+        kw = dict(q_pos=self.q_pos, n_entries=self.N, m=self.m, k=self.k, hsi_s=self.s_blk, hsi_nb=self.n_b,
+                  candidates=self.cand, workspace=self.ws)
+        if events is not None:
+            events[0].record()
+        K.csa2_score_topk(None, f["q_idx"], f["w"], codes, scales, topk=self.tk[0], hsi=K.HSI_BUILD, **kw)
+        if events is not None:
+            events[1].record()
+        K.csa2_score_topk(None, r["q_idx"], r["w"], codes, scales, topk=self.tk[1], hsi=K.HSI_USE, **kw)
+        if events is not None:
+            events[2].record()
+        for l, lay in enumerate((f, r)):
+            K.csa2_sparse_attn(None, lay["q"], self.kv, self.tk[l], lay["swa_kv"], self.swa_pos0, self.q_pos,
+                               self.o[l], W=self.W, workspace=self.ws_attn)
+        if events is not None:
+            events[3].record()
+
+    def work(self):
+        B, N = self.B, self.N
+        pool = self.n_b * self.s_blk
+        rows = B * (self.k + self.W)
+        q_bytes = B * self.H_I * (128 * 2 + 4)
+        return {
+            "score_full": {"bytes": 68.0 * B * N + q_bytes + B * (self.k + self.n_b) * 4},
+            "score_pool": {"bytes": 68.0 * B * pool + q_bytes + B * (self.n_b + self.k) * 4},
+            "attn_2_layers": {"bytes": 2 * (rows * 1024.0 + 2.0 * B * self.H * 512 * 2)},
+        }
+
+
 def time_steps(torch, bench, n_stages, steps, warmup):
     for _ in range(warmup):
         bench.step()
@@ -173,11 +252,13 @@ def time_steps(torch, bench, n_stages, steps, warmup):
     return total_ms / steps, per_stage
 
 
-def time_graph(torch, bench, steps, warmup):
+def time_graph(torch, bench, steps, warmup, per_graph=1):
     """The step captured once as a HIP graph (stream capture of the C-ABI calls,
     which launch on torch's current stream and neither allocate nor synchronise),
     then replayed: the launch gaps and the Python/ctypes overhead between kernels
-    go away, the kernels are the same.  Returns ms per step."""
+    go away, the kernels are the same.  With per_graph > 1 the graph holds that
+    many consecutive steps (a bench that rotates input copies captures one step
+    per copy).  Returns ms per step."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -187,17 +268,19 @@ def time_graph(torch, bench, steps, warmup):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        bench.step()
+        for _ in range(per_graph):
+            bench.step()
+    reps = max(1, steps // per_graph)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(steps):
+    for _ in range(reps):
         g.replay()
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
+    ms = start.elapsed_time(stop) / (reps * per_graph)
     del g
     return ms
 
@@ -278,6 +361,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode record")
     ap.add_argument("--decode-seqs", type=int, default=64)
+    ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches instead of a HIP graph replay of the step")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -366,6 +450,32 @@ def main():
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (dms * 1e-3), 4),
         }
         del db
+        torch.cuda.empty_cache()
+    if not args.no_hsi:
+        log("hsi decode: building caches")
+        hb = HsiDecodeBench(torch, K, synth)
+        log("hsi decode: timing")
+        n_hsi = 3 * max(args.steps, 20)
+        hms_eager, hst = time_steps(torch, hb, 3, n_hsi, args.warmup)
+        hms = time_graph(torch, hb, n_hsi, args.warmup, per_graph=hb.copies) if args.graph else hms_eager
+        hw = hb.work()
+        full_gbs = hw["score_full"]["bytes"] / (hst[0] * 1e-3) / 1e9
+        step_bytes = sum(v["bytes"] for v in hw.values())
+        out["decode_hsi_1m"] = {
+            "workload": f"1M-context decode with the HSI candidate pool: {hb.B} sequences x {hb.N} m=2 entries "
+                        f"(1048576-token context), blocks of {hb.s_blk}, top-{hb.n_b} blocks (16384-entry pool), "
+                        f"Full layer (scan + pool build) + Reindex layer (pool only), top-512, SWA 128, 64 heads; "
+                        f"index K rotated over {hb.copies} copies so scans come from HBM",
+            "us_per_step": round(hms * 1e3, 2), "us_per_step_eager": round(hms_eager * 1e3, 2),
+            "stages_us": {"score_full_build": round(hst[0] * 1e3, 2), "score_reindex_pool": round(hst[1] * 1e3, 2),
+                          "attn_2_layers": round(hst[2] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "kernel": "score_full_build", "achieved": round(full_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(full_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None},
+            "step_bytes": step_bytes,
+            "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (hms * 1e-3), 4),
+        }
+        del hb
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")

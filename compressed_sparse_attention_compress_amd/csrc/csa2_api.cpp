@@ -261,6 +261,7 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* in, cs
   const csa2::ScorePlan plan = csa2::plan_score(a.dtype, a.B, a.T, score_scan(a), a.k, a.hsi, a.hsi_s, a.hsi_nb);
   REQ(a.workspace != nullptr && a.workspace_bytes >= plan.total_bytes, CSA2_ERR_WORKSPACE,
       "csa2_score_topk: workspace of %zu bytes needed (got %zu)", plan.total_bytes, a.workspace_bytes);
+  REQ(((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE, "csa2_score_topk: workspace not 16-byte aligned");
   hipError_t e = csa2::launch_score_topk(a.dtype, a.q_idx, a.w, a.codes, a.scales, a.q_pos, a.topk, a.candidates, a.B,
                                          a.T, a.H_I, a.N_cap, a.n_entries, a.m, a.k, a.hsi, a.hsi_s, a.hsi_nb,
                                          a.workspace, plan, st(stream));
@@ -279,6 +280,8 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
   const csa2::AttnPlan plan = csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W);
   REQ(plan.ws_bytes == 0 || (a.workspace != nullptr && a.workspace_bytes >= plan.ws_bytes), CSA2_ERR_WORKSPACE,
       "csa2_sparse_attn: workspace of %zu bytes needed (got %zu)", plan.ws_bytes, a.workspace_bytes);
+  REQ(plan.ws_bytes == 0 || ((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
+      "csa2_sparse_attn: workspace not 16-byte aligned");
   hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse, a.B,
                                           a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan, st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_sparse_attn launch");
@@ -360,6 +363,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     const csa2::ScorePlan plan = csa2::plan_score(sa.dtype, sa.B, sa.T, score_scan(sa), sa.k, sa.hsi, sa.hsi_s, sa.hsi_nb);
     REQ(sa.workspace != nullptr && sa.workspace_bytes >= plan.total_bytes, CSA2_ERR_WORKSPACE,
         "csa2_layer_forward: workspace of %zu bytes needed (got %zu)", plan.total_bytes, sa.workspace_bytes);
+    REQ(((uintptr_t)sa.workspace & 15u) == 0, CSA2_ERR_WORKSPACE, "csa2_layer_forward: workspace not 16-byte aligned");
   }
   csa2_sparse_attn_args aa{};
   aa.dtype = cfg->dtype; aa.B = io->B; aa.T = io->T; aa.H = cfg->H; aa.k = cfg->k; aa.L_w = io->L_w; aa.W = cfg->W;

@@ -616,17 +616,38 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict
   const long long qh = gid >> 6;
   const int h = (int)(qh % H);
   const long long qi = qh / H;
+  const float* ls_q = part_lse + qi * n_splits * H + h;                    // split s at s * H
+  const float* po_q = part_o + (qi * n_splits * H + h) * 512 + d0;         // split s at s * H * 512
   float mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[(qi * n_splits + s) * H + h]);
+#pragma unroll 8
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ls_q[(size_t)s * H]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, den = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float ls = part_lse[(qi * n_splits + s) * H + h];
-    if (ls == -INFINITY) continue;
+  // four splits' partials in flight at a time (an empty split's row is read but
+  // not used: its log-sum-exp is -inf)
+  auto add = [&](float ls, const float4& a0, const float4& a1) {
+    if (ls == -INFINITY) return;
     const float wgt = exp2f(ls - mx);
     den += wgt;
-    const float* pr = part_o + ((qi * n_splits + s) * H + h) * 512 + d0;
+    acc[0] += wgt * a0.x; acc[1] += wgt * a0.y; acc[2] += wgt * a0.z; acc[3] += wgt * a0.w;
+    acc[4] += wgt * a1.x; acc[5] += wgt * a1.y; acc[6] += wgt * a1.z; acc[7] += wgt * a1.w;
+  };
+  int s = 0;
+  for (; s + 4 <= n_splits; s += 4) {
+    float ls[4];
+    float4 a0[4], a1[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += wgt * pr[i];
+    for (int u = 0; u < 4; ++u) {
+      ls[u] = ls_q[(size_t)(s + u) * H];
+      const float4* pr = reinterpret_cast<const float4*>(po_q + (size_t)(s + u) * H * 512);
+      a0[u] = pr[0];
+      a1[u] = pr[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(ls[u], a0[u], a1[u]);
+  }
+  for (; s < n_splits; ++s) {
+    const float4* pr = reinterpret_cast<const float4*>(po_q + (size_t)s * H * 512);
+    add(ls_q[(size_t)s * H], pr[0], pr[1]);
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   bf16* orow = o + (qi * H + h) * 512 + d0;

@@ -39,7 +39,7 @@ struct SelSmem {
   uint32_t hist[NBINS];
   uint32_t wsum[NT / 64];
   uint32_t red[3][NT / 64];
-  uint32_t digit, above, done, lb;
+  uint32_t digit, above, done, lb, lb_above;
 };
 
 // Exclusive prefix sum over the threads of a block; `total` gets the block sum.
@@ -118,10 +118,12 @@ struct SelOut {
 // ties resolved in position order.  The digit of each pass covers the live key
 // range [lo, hi] (starting from the keys' [min, max]) with 2048 bins, so a pass
 // usually shrinks the range by ~2^11 and the loop ends when the count at the
-// boundary bin is exact or the bin holds a single value.
+// boundary bin is exact or the bin holds a single value.  The rank-r0 bound is
+// the lower edge of the first pass's bin that holds the rank-r0 key; with
+// `fine_lb` one more histogram over that bin makes it 2^11 times finer.
 template <int NT, typename Get>
 __device__ SelOut select_threshold(Get key_at, int n, uint32_t need, uint32_t mn, uint32_t mx, uint32_t r0,
-                                   SelSmem<NT>& sm) {
+                                   SelSmem<NT>& sm, bool fine_lb = false) {
   if (need == 0) return SelOut{0xFFFFFFFFu, 0u, 0u};
   if (threadIdx.x == 0) sm.lb = 0;
   uint32_t lo = mn, hi = mx;
@@ -153,7 +155,10 @@ __device__ SelOut select_threshold(Get key_at, int n, uint32_t need, uint32_t mn
         sm.above = cum;
         sm.done = (cum + own[j] == need) ? 1u : 0u;
       }
-      if (pass == 0 && r0 != 0 && cum < r0 && cum + own[j] >= r0) sm.lb = lo + ((uint32_t)(threadIdx.x * BPT + j) << shift);
+      if (pass == 0 && r0 != 0 && cum < r0 && cum + own[j] >= r0) {
+        sm.lb = lo + ((uint32_t)(threadIdx.x * BPT + j) << shift);
+        sm.lb_above = cum;
+      }
       cum += own[j];
     }
     __syncthreads();
@@ -162,8 +167,42 @@ __device__ SelOut select_threshold(Get key_at, int n, uint32_t need, uint32_t mn
     const uint32_t new_lo = lo + (d << shift);
     const uint64_t top = (uint64_t)new_lo + ((1ull << shift) - 1);
     const uint32_t new_hi = top < (uint64_t)hi ? (uint32_t)top : hi;
-    const uint32_t done = sm.done, lb = sm.lb;
+    const uint32_t done = sm.done;
+    uint32_t lb = sm.lb;
+    const uint32_t lb_above = sm.lb_above;
     __syncthreads();
+    if (pass == 0 && fine_lb && lb != 0 && shift > 0) {
+      // keys of the rank-r0 bin [blo, bhi] at 2^11 finer bins; lb_above keys lie above it
+      const uint32_t blo = lb;
+      const uint64_t btop = (uint64_t)blo + ((1ull << shift) - 1);
+      const uint32_t bhi = btop < (uint64_t)hi ? (uint32_t)btop : hi;
+      const int shift1 = shift > 11 ? shift - 11 : 0;
+      for (int i = threadIdx.x; i < NBINS; i += NT) sm.hist[i] = 0;
+      __syncthreads();
+#pragma unroll 8
+      for (int i = threadIdx.x; i < n; i += NT) {
+        const uint32_t kk = key_at(i);
+        if (kk && kk >= blo && kk <= bhi) atomicAdd(&sm.hist[(kk - blo) >> shift1], 1u);
+      }
+      __syncthreads();
+      uint32_t own1[BPT], tot1 = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        own1[j] = sm.hist[threadIdx.x * BPT + j];
+        tot1 += own1[j];
+      }
+      uint32_t total1;
+      const uint32_t pre1 = block_prefix_excl<NT>(tot1, sm, total1);
+      uint32_t cum1 = lb_above + (total1 - pre1 - tot1);
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (cum1 < r0 && cum1 + own1[j] >= r0) sm.lb = blo + ((uint32_t)(threadIdx.x * BPT + j) << shift1);
+        cum1 += own1[j];
+      }
+      __syncthreads();
+      lb = sm.lb;
+      __syncthreads();
+    }
     if (done) return SelOut{new_lo, 0xFFFFFFFFu, lb};   // every key >= new_lo
     if (shift == 0) return SelOut{new_lo, need, lb};    // keys > new_lo and the first `need` equal to it
     lo = new_lo;
@@ -640,11 +679,13 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   auto key_at = [&](int i) -> uint32_t { return keys[i]; };
   uint32_t mn, mx, nv;
   key_stats<SC_THREADS>(key_at, Ce, sm, mn, mx, nv);
-  const uint32_t need = nv < (uint32_t)k_chunk ? nv : (uint32_t)k_chunk;
+  // a direct query's row holds k ids; a chunk's candidate list k_chunk (>= min(k, C))
+  const uint32_t lim = direct ? (uint32_t)k : (uint32_t)k_chunk;
+  const uint32_t need = nv < lim ? nv : lim;
   const uint32_t r0 = (direct || c == nc_q - 1) ? 0u : rank_for_bound(k, nc_q);
   SelOut sel;
   if (need == nv && r0 == 0) sel = SelOut{mn, 0xFFFFFFFFu, 0u};   // every valid key
-  else sel = select_threshold<SC_THREADS>(key_at, Ce, need, mn, mx, r0, sm);
+  else sel = select_threshold<SC_THREADS>(key_at, Ce, need, mn, mx, r0, sm, nc_q > 32);
   auto entry_of = [&](int i) -> int {
     if (POOL) {
       const int vj = base + i;
@@ -684,13 +725,15 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
 }
 
 constexpr int MG_THREADS = 512;
-constexpr int MG_TILE = 4096;    // candidate keys read into LDS per round
-constexpr int MG_CAP = 4096;     // staged candidates kept in LDS
+constexpr int MG_TILE = 4096;    // candidate keys read into LDS per round (LDS-tile form)
+constexpr int MG_CAP = 4096;     // staged candidates kept in LDS (LDS-tile form)
+constexpr int MG_CAP_R = 8192;   // staged candidates kept in LDS (register form)
 
 // One workgroup per query: candidates of all chunks at or above the bound are
 // staged in LDS in entry order, then the same radix select picks the k best and
-// emits their ids ascending.  With HSI BUILD the n_b best blocks (newest forced)
-// are chosen the same way from the block maxima.
+// emits their ids ascending.  With HSI BUILD a second workgroup per query picks
+// the n_b best blocks (newest forced) the same way from the block maxima, staged
+// in the whole 80 KB candidate area (up to 20480 blocks).
 template <bool POOL, bool BUILD>
 __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restrict__ cand_key,
                                                          const int32_t* __restrict__ cand_idx,
@@ -701,17 +744,26 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                                          int m, int k, int C, int k_chunk, int n_chunks, int hsi_s,
                                                          int hsi_nb, int nblk_max) {
   __shared__ SelSmem<MG_THREADS> sel;
-  __shared__ __attribute__((aligned(16))) uint32_t tile[MG_TILE];
-  __shared__ int32_t tile_idx[MG_TILE];
-  __shared__ __attribute__((aligned(16))) uint32_t skey[MG_CAP];
-  __shared__ int32_t sidx[MG_CAP];
+  // one 80 KB area: [tile | staged keys | staged ids], with the candidate ids of
+  // an LDS tile behind the first MG_CAP staged ids (that form stages at most
+  // MG_CAP); the block selection of HSI BUILD uses all of it once the
+  // candidates are done
+  constexpr int BLK_CAP = MG_TILE + 2 * MG_CAP_R;
+  static_assert(MG_CAP + MG_TILE <= MG_CAP_R, "tile ids fit behind the staged ids");
+  __shared__ __attribute__((aligned(16))) uint32_t area[BLK_CAP];
+  uint32_t* tile = area;
+  uint32_t* skey = area + MG_TILE;
+  int32_t* sidx = reinterpret_cast<int32_t*>(area + MG_TILE + MG_CAP_R);
+  int32_t* tile_idx = sidx + MG_CAP;
   __shared__ uint32_t s_bound;
   const int t = blockIdx.x, b = blockIdx.y;
   const int bt = b * T_len + t;
   const int n_t = visible(q_pos, bt, m, n_entries);
   const int nc = POOL ? n_chunks : (n_t + C - 1) / C;
 
-  if (BUILD || nc > 1) {
+  // with HSI BUILD, blockIdx.z == 0 merges the candidates and blockIdx.z == 1
+  // selects the blocks, side by side
+  if ((BUILD || nc > 1) && blockIdx.z == 0) {
     const int n_items = nc * k_chunk;
     const uint32_t* kb = cand_key + (size_t)bt * n_chunks * k_chunk;
     const int32_t* ib = cand_idx + (size_t)bt * n_chunks * k_chunk;
@@ -731,26 +783,35 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     }
     // stage candidates >= bound in entry order
     uint32_t staged = 0;
+    const uint32_t cap = (k_chunk & 3) == 0 ? (uint32_t)MG_CAP_R : (uint32_t)MG_CAP;
     const SelOut keep{bound, 0xFFFFFFFFu, 0u};
     constexpr int MG_NW = MG_THREADS / 64;
     constexpr int MG_REG = 8;   // uint4 loads per lane: 32 candidates
-    const bool in_regs = (k_chunk & 3) == 0 && n_items <= MG_THREADS * 4 * MG_REG;
-    if (in_regs) {
-      // all candidates at once: wave w holds items [w * 2048, w * 2048 + 2048),
-      // lane l the 4 consecutive items 4 * (64 j + l) .. + 3 of step j, so entry
-      // order is (j, lane, u); a count pass and one exchange of the per-wave
-      // counts give each wave its first slot, a second pass over the registers
-      // writes the kept candidates in order
+    constexpr int MG_ROUND = MG_THREADS * 4 * MG_REG;   // 16384 candidates per register round
+    const bool in_regs = (k_chunk & 3) == 0;
+    for (int r0 = 0; r0 < (in_regs ? n_items : 0); r0 += MG_ROUND) {
+      // a round of up to 16384 candidates at once: wave w holds items
+      // [w * 2048, w * 2048 + 2048) of the round, lane l the 4 consecutive items
+      // 4 * (64 j + l) .. + 3 of step j, so entry order is (j, lane, u); a count
+      // pass and one exchange of the per-wave counts give each wave its first
+      // slot, a second pass over the registers writes the kept candidates in order
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       const uint64_t lt = (1ull << lane) - 1ull;
+      const int len = min(MG_ROUND, n_items - r0);
       uint4 kv[MG_REG], iv[MG_REG];
 #pragma unroll
       for (int j = 0; j < MG_REG; ++j) {
         const int i = wave * (256 * MG_REG) + 256 * j + 4 * lane;
-        kv[j] = i < n_items ? *reinterpret_cast<const uint4*>(kb + i) : make_uint4(0, 0, 0, 0);
-        iv[j] = i < n_items ? *reinterpret_cast<const uint4*>(ib + i) : make_uint4(0, 0, 0, 0);
+        kv[j] = i < len ? *reinterpret_cast<const uint4*>(kb + r0 + i) : make_uint4(0, 0, 0, 0);
       }
       auto kept = [&](uint32_t kk) { return kk != 0u && kk >= bound; };
+      // ids only where one of the lane's 4 keys is kept (few are, past the bound)
+#pragma unroll
+      for (int j = 0; j < MG_REG; ++j) {
+        const int i = wave * (256 * MG_REG) + 256 * j + 4 * lane;
+        const bool any = kept(kv[j].x) || kept(kv[j].y) || kept(kv[j].z) || kept(kv[j].w);
+        iv[j] = any ? *reinterpret_cast<const uint4*>(ib + r0 + i) : make_uint4(0, 0, 0, 0);
+      }
       uint32_t wc = 0;
 #pragma unroll
       for (int j = 0; j < MG_REG; ++j)
@@ -758,14 +819,14 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
               __popcll(__ballot(kept(kv[j].z))) + __popcll(__ballot(kept(kv[j].w)));
       if (lane == 0) sel.red[0][wave] = wc;
       __syncthreads();
-      uint32_t slot = 0, total = 0;
+      uint32_t slot = staged, total = 0;
 #pragma unroll
       for (int w = 0; w < MG_NW; ++w) {
         const uint32_t c = sel.red[0][w];
         slot += w < wave ? c : 0u;
         total += c;
       }
-      if (total <= (uint32_t)MG_CAP) {
+      if (staged + total <= cap) {
 #pragma unroll
         for (int j = 0; j < MG_REG; ++j) {
           const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
@@ -790,7 +851,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
           slot += tot;
         }
       }
-      staged = total;
+      staged += total;
       __syncthreads();
     }
     for (int r = 0; r < (in_regs ? 0 : n_items); r += MG_TILE) {
@@ -826,7 +887,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
       __syncthreads();
     }
     uint32_t cnt;
-    if (staged <= (uint32_t)MG_CAP) {
+    if (staged <= cap) {
       auto key_at = [&](int i) -> uint32_t { return skey[i]; };
       uint32_t mn, mx, nv;
       key_stats<MG_THREADS>(key_at, (int)staged, sel, mn, mx, nv);
@@ -851,17 +912,28 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     }
     for (int i = (int)cnt + threadIdx.x; i < k; i += MG_THREADS) out[i] = -1;
   }
-  if (BUILD) {
-    __syncthreads();
+  if (BUILD && blockIdx.z == 1) {
     const int nblk = (n_t + hsi_s - 1) / hsi_s;
     const uint32_t* bm = blkmax + (size_t)bt * nblk_max;
     int32_t* out = cands_out + (size_t)bt * hsi_nb;
     auto bkey = [&](int i) -> uint32_t { return (i == nblk - 1) ? 0xFFFFFFFFu : bm[i]; };  // newest block forced in
     uint32_t cnt;
-    if (nblk <= MG_CAP) {
-      for (int i = threadIdx.x; i < nblk; i += MG_THREADS) skey[i] = bkey(i);
+    if (nblk <= BLK_CAP) {
+      for (int i0 = 0; i0 < nblk; i0 += 4 * MG_THREADS) {   // 4 loads per thread in flight
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * MG_THREADS + threadIdx.x;
+          v[u] = i < nblk ? bkey(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * MG_THREADS + threadIdx.x;
+          if (i < nblk) area[i] = v[u];
+        }
+      }
       __syncthreads();
-      auto key_at = [&](int i) -> uint32_t { return skey[i]; };
+      auto key_at = [&](int i) -> uint32_t { return area[i]; };
       uint32_t mn, mx, nv;
       key_stats<MG_THREADS>(key_at, nblk, sel, mn, mx, nv);
       const uint32_t need = nv < (uint32_t)hsi_nb ? nv : (uint32_t)hsi_nb;
@@ -1320,7 +1392,7 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!BUILD && p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single chunk
-  dim3 g2(T_len, B);
+  dim3 g2(T_len, B, BUILD ? 2 : 1);
   hipLaunchKernelGGL((topk_merge<POOL, BUILD>), g2, dim3(MG_THREADS), 0, st, cand_key, cand_idx, chunk_lb, blkmax,
                      q_pos, topk, cands, T_len, n_entries, m, k, p.chunk, p.k_chunk, p.n_chunks, hsi_s, hsi_nb,
                      nblk_max);
@@ -1363,7 +1435,8 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
   if (hsi != 0 && C < hsi_s) C = hsi_s;                           // chunks hold whole blocks
   p.chunk = C;
   p.n_chunks = n_scan <= 0 ? 1 : (n_scan + C - 1) / C;
-  p.k_chunk = k < C ? k : C;
+  const int k4 = (k + 3) & ~3;   // candidate lists in whole uint4s (the merge reads them so)
+  p.k_chunk = k4 < C ? k4 : C;
   p.cand_bytes = (size_t)Q * p.n_chunks * p.k_chunk * 8;
   p.lb_bytes = ((size_t)Q * p.n_chunks * 4 + 255) / 256 * 256;
   const long long nblk = (hsi == 1) ? ((long long)n_scan + hsi_s - 1) / hsi_s : 0;

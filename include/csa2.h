@@ -50,7 +50,7 @@ typedef enum csa2_status {
   CSA2_ERR_DTYPE = 3,         /* dtype not supported for this argument */
   CSA2_ERR_SLOT_EMPTY = 4,    /* a runtime slot was read before any layer wrote it */
   CSA2_ERR_SLOT_MISMATCH = 5, /* a runtime slot does not fit the consumer's shapes */
-  CSA2_ERR_WORKSPACE = 6,     /* workspace missing or smaller than csa2_workspace_size() */
+  CSA2_ERR_WORKSPACE = 6,     /* workspace missing, smaller than csa2_workspace_size() or not 16-byte aligned */
   CSA2_ERR_HIP = 7,           /* a HIP launch failed */
   CSA2_ERR_UNSUPPORTED = 8    /* valid request this build does not implement */
 } csa2_status;
@@ -172,7 +172,8 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
  *   topk    [B, T, k] int32 out          chosen entry ids ascending, then -1
  *   candidates [B, T, n_b] int32         BUILD: out; USE: in (NULL -> slot);
  *                                        block ids ascending, then -1
- *   workspace  device scratch of at least csa2_workspace_size() bytes
+ *   workspace  device scratch of at least csa2_workspace_size() bytes, 16-byte
+ *              aligned (CSA2_ERR_WORKSPACE otherwise)
  * Ties in score go to the smaller entry id; -0 counts as +0.
  * With rt != NULL the topk_idxs slot (and on BUILD the candidates slot) is set. */
 typedef struct csa2_score_topk_args {
@@ -210,7 +211,9 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa
  *   max(0, p-W+1, swa_pos0) .. min(p, swa_pos0 + L_w - 1) with p = q_pos[b,t]
  *   o        [B, T, H, 512] dtype out
  *   lse      [B, T, H] float32 out (optional, natural-log sum of exp of scaled logits)
- *   scale    0 -> 1/sqrt(512)                                                 */
+ *   scale    0 -> 1/sqrt(512)
+ *   workspace  device scratch of csa2_workspace_size() bytes (may be 0 bytes:
+ *              then NULL is accepted), 16-byte aligned                        */
 typedef struct csa2_sparse_attn_args {
   int32_t dtype;            /* csa2_dtype of q, kv, swa_kv, o */
   int32_t B, T, H;
