@@ -109,6 +109,18 @@ def test_score_workspace_too_small():
     assert n.value > 512 * 8
 
 
+def test_workspace_must_be_16_byte_aligned():
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, q_idx=0x1000,
+                        w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1008,
+                        workspace_bytes=1 << 30)
+    assert K.STATUS[K.lib().csa2_score_topk(None, C.byref(a), None)] == "CSA2_ERR_WORKSPACE"
+    # a one-query attention call uses row-split partials, so it needs a workspace
+    b = K.SparseAttnArgs(dtype=1, B=1, T=1, H=64, N_cap=100, k=512, L_w=128, W=128, q=0x1000, kv=0x1000,
+                         topk=0x1000, swa_kv=0x1000, swa_pos0=0x1000, q_pos=0x1000, o=0x1000, workspace=0x1004,
+                         workspace_bytes=1 << 30)
+    assert K.STATUS[K.lib().csa2_sparse_attn(None, C.byref(b), None)] == "CSA2_ERR_WORKSPACE"
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("H_I", 33, "CSA2_ERR_SHAPE"), ("k", 0, "CSA2_ERR_SHAPE"), ("k", 2000, "CSA2_ERR_SHAPE"),
     ("n_entries", 5000, "CSA2_ERR_SHAPE"), ("hsi", 5, "CSA2_ERR_INVALID_ARG"),
