@@ -744,17 +744,13 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                                          int m, int k, int C, int k_chunk, int n_chunks, int hsi_s,
                                                          int hsi_nb, int nblk_max) {
   __shared__ SelSmem<MG_THREADS> sel;
-  // one 80 KB area: [tile | staged keys | staged ids], with the candidate ids of
-  // an LDS tile behind the first MG_CAP staged ids (that form stages at most
-  // MG_CAP); the block selection of HSI BUILD uses all of it once the
-  // candidates are done
+  // one 80 KB area: [tile | staged keys | staged candidate positions]; the block
+  // selection of HSI BUILD (a workgroup of its own) uses all of it
   constexpr int BLK_CAP = MG_TILE + 2 * MG_CAP_R;
-  static_assert(MG_CAP + MG_TILE <= MG_CAP_R, "tile ids fit behind the staged ids");
   __shared__ __attribute__((aligned(16))) uint32_t area[BLK_CAP];
   uint32_t* tile = area;
   uint32_t* skey = area + MG_TILE;
-  int32_t* sidx = reinterpret_cast<int32_t*>(area + MG_TILE + MG_CAP_R);
-  int32_t* tile_idx = sidx + MG_CAP;
+  int32_t* sidx = reinterpret_cast<int32_t*>(area + MG_TILE + MG_CAP_R);   // candidate positions
   __shared__ uint32_t s_bound;
   const int t = blockIdx.x, b = blockIdx.y;
   const int bt = b * T_len + t;
@@ -789,89 +785,93 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     constexpr int MG_REG = 8;   // uint4 loads per lane: 32 candidates
     constexpr int MG_ROUND = MG_THREADS * 4 * MG_REG;   // 16384 candidates per register round
     const bool in_regs = (k_chunk & 3) == 0;
-    for (int r0 = 0; r0 < (in_regs ? n_items : 0); r0 += MG_ROUND) {
-      // a round of up to 16384 candidates at once: wave w holds items
+    if (in_regs && n_items > 0) {
+      // rounds of up to 16384 candidates at once: wave w holds items
       // [w * 2048, w * 2048 + 2048) of the round, lane l the 4 consecutive items
       // 4 * (64 j + l) .. + 3 of step j, so entry order is (j, lane, u); a count
       // pass and one exchange of the per-wave counts give each wave its first
-      // slot, a second pass over the registers writes the kept candidates in order
+      // slot, a second pass over the registers writes the kept candidates (key and
+      // candidate position; ids are read for the chosen k only) in order.  The keys
+      // of the next round load while one is processed, through a buffer resource
+      // over the query's candidates, so reads past them return 0 without a memory
+      // access and every load is unconditional.
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       const uint64_t lt = (1ull << lane) - 1ull;
-      const int len = min(MG_ROUND, n_items - r0);
-      uint4 kv[MG_REG], iv[MG_REG];
-#pragma unroll
-      for (int j = 0; j < MG_REG; ++j) {
-        const int i = wave * (256 * MG_REG) + 256 * j + 4 * lane;
-        kv[j] = i < len ? *reinterpret_cast<const uint4*>(kb + r0 + i) : make_uint4(0, 0, 0, 0);
-      }
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, n_items * 4, 0x00020000);
       auto kept = [&](uint32_t kk) { return kk != 0u && kk >= bound; };
-      // ids only where one of the lane's 4 keys is kept (few are, past the bound)
-#pragma unroll
-      for (int j = 0; j < MG_REG; ++j) {
-        const int i = wave * (256 * MG_REG) + 256 * j + 4 * lane;
-        const bool any = kept(kv[j].x) || kept(kv[j].y) || kept(kv[j].z) || kept(kv[j].w);
-        iv[j] = any ? *reinterpret_cast<const uint4*>(ib + r0 + i) : make_uint4(0, 0, 0, 0);
-      }
-      uint32_t wc = 0;
-#pragma unroll
-      for (int j = 0; j < MG_REG; ++j)
-        wc += __popcll(__ballot(kept(kv[j].x))) + __popcll(__ballot(kept(kv[j].y))) +
-              __popcll(__ballot(kept(kv[j].z))) + __popcll(__ballot(kept(kv[j].w)));
-      if (lane == 0) sel.red[0][wave] = wc;
-      __syncthreads();
-      uint32_t slot = staged, total = 0;
-#pragma unroll
-      for (int w = 0; w < MG_NW; ++w) {
-        const uint32_t c = sel.red[0][w];
-        slot += w < wave ? c : 0u;
-        total += c;
-      }
-      if (staged + total <= cap) {
+      auto load_keys = [&](int r0, uint4* dst) {
 #pragma unroll
         for (int j = 0; j < MG_REG; ++j) {
-          const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
-          const uint32_t ii[4] = {iv[j].x, iv[j].y, iv[j].z, iv[j].w};
-          bool s[4];
-          uint32_t before = 0, tot = 0;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            s[u] = kept(kk[u]);
-            const uint64_t msk = __ballot(s[u]);
-            before += __popcll(msk & lt);
-            tot += __popcll(msk);
-          }
-          uint32_t sl = slot + before;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (s[u]) {
-              skey[sl] = kk[u];
-              sidx[sl] = (int32_t)ii[u];
-              ++sl;
-            }
-          slot += tot;
+          const int i = r0 + wave * (256 * MG_REG) + 256 * j + 4 * lane;
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, i < n_items ? i * 4 : (int)0x80000000, 0, 0);
+          dst[j] = make_uint4(v[0], v[1], v[2], v[3]);
         }
+      };
+      uint4 kn[MG_REG];
+      load_keys(0, kn);
+      for (int r0 = 0; r0 < n_items; r0 += MG_ROUND) {
+        uint4 kv[MG_REG];
+#pragma unroll
+        for (int j = 0; j < MG_REG; ++j) kv[j] = kn[j];
+        __builtin_amdgcn_sched_barrier(0);
+        load_keys(r0 + MG_ROUND, kn);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t wc = 0;
+#pragma unroll
+        for (int j = 0; j < MG_REG; ++j)
+          wc += __popcll(__ballot(kept(kv[j].x))) + __popcll(__ballot(kept(kv[j].y))) +
+                __popcll(__ballot(kept(kv[j].z))) + __popcll(__ballot(kept(kv[j].w)));
+        if (lane == 0) sel.red[0][wave] = wc;
+        __syncthreads();
+        uint32_t slot = staged, total = 0;
+#pragma unroll
+        for (int w = 0; w < MG_NW; ++w) {
+          const uint32_t c = sel.red[0][w];
+          slot += w < wave ? c : 0u;
+          total += c;
+        }
+        if (staged + total <= cap) {
+#pragma unroll
+          for (int j = 0; j < MG_REG; ++j) {
+            const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+            const int i0 = r0 + wave * (256 * MG_REG) + 256 * j + 4 * lane;
+            bool s[4];
+            uint32_t before = 0, tot = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              s[u] = kept(kk[u]);
+              const uint64_t msk = __ballot(s[u]);
+              before += __popcll(msk & lt);
+              tot += __popcll(msk);
+            }
+            uint32_t sl = slot + before;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (s[u]) {
+                skey[sl] = kk[u];
+                sidx[sl] = i0 + u;
+                ++sl;
+              }
+            slot += tot;
+          }
+        }
+        staged += total;
+        __syncthreads();
       }
-      staged += total;
-      __syncthreads();
     }
     for (int r = 0; r < (in_regs ? 0 : n_items); r += MG_TILE) {
       const int len = min(MG_TILE, n_items - r);
       for (int i0 = 0; i0 < len; i0 += 4 * MG_THREADS) {   // all loads of a round in flight together
         uint32_t kk[4];
-        int32_t ii[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = i0 + u * MG_THREADS + threadIdx.x;
           kk[u] = i < len ? kb[r + i] : 0u;
-          ii[u] = i < len ? ib[r + i] : -1;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = i0 + u * MG_THREADS + threadIdx.x;
-          if (i < len) {
-            tile[i] = kk[u];
-            tile_idx[i] = ii[u];
-          }
+          if (i < len) tile[i] = kk[u];
         }
       }
       __syncthreads();
@@ -881,7 +881,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                            slot += base_slot;
                                            if (slot < (uint32_t)MG_CAP) {
                                              skey[slot] = tile[i];
-                                             sidx[slot] = tile_idx[i];
+                                             sidx[slot] = r + i;
                                            }
                                          });
       __syncthreads();
@@ -897,9 +897,10 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
       // without a partial tie the chosen positions are staged in tile[] (8 waves x 512)
       if (s.eq_take == 0xFFFFFFFFu && need <= (uint32_t)(MG_TILE / (MG_THREADS / 64)))
         cnt = emit_compact<MG_THREADS>(skey, (int)staged, s.thresh, tile, MG_TILE / (MG_THREADS / 64), sel,
-                                       [&](uint32_t slot, uint32_t, uint32_t i) { out[slot] = sidx[i]; });
+                                       [&](uint32_t slot, uint32_t, uint32_t i) { out[slot] = ib[sidx[i]]; });
       else
-        cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel, [&](int i, uint32_t slot) { out[slot] = sidx[i]; });
+        cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel,
+                                       [&](int i, uint32_t slot) { out[slot] = ib[sidx[i]]; });
     } else {
       // more candidates than LDS holds: select straight from the workspace
       auto key_at = [&](int i) -> uint32_t { const uint32_t kk = kb[i]; return kk >= bound ? kk : 0u; };
