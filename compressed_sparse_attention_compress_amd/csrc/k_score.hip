@@ -1306,13 +1306,22 @@ __global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __rest
   }
   // ---- 3. ordered emission
   uint64_t my_gt = 0, my_eq = 0;   // lane j: masks of register column j (positions 64j..64j+63)
+  if (eq_take == 0xFFFFFFFFu) {
+    // no partial tie: every key >= thresh is chosen, one ballot per column
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint64_t mg = __ballot(kv[j] != 0u && kv[j] > thresh);
-    const uint64_t me = __ballot(kv[j] != 0u && kv[j] == thresh);
-    if (lane == j) {
-      my_gt = mg;
-      my_eq = me;
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t mg = __ballot(kv[j] != 0u && kv[j] >= thresh);
+      if (lane == j) my_gt = mg;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t mg = __ballot(kv[j] != 0u && kv[j] > thresh);
+      const uint64_t me = __ballot(kv[j] != 0u && kv[j] == thresh);
+      if (lane == j) {
+        my_gt = mg;
+        my_eq = me;
+      }
     }
   }
   int32_t* out = topk + (size_t)bt * k;
