@@ -173,16 +173,17 @@ def test_score_topk_many_queries_vs_oracle(m, k, H_I):
     assert exact >= n - 1
 
 
-@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 3), (torch.bfloat16, 300), (torch.float32, 3)])
-def test_score_topk_exact_ties_vs_oracle(dtype, T):
+@pytest.mark.parametrize("dtype,T,n_fill", [(torch.bfloat16, 3, 5000), (torch.bfloat16, 300, 5000),
+                                            (torch.bfloat16, 300, 4000), (torch.float32, 3, 5000)])
+def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill):
     """An index-K cache of 50 distinct rows repeated: every score value occurs ~100
     times, so the k-th best falls inside a group of equal scores and the selection
     must take that group's smallest positions (ties go to the smaller entry id).
     Equal rows give bit-identical scores on both sides, and the distinct values are
     kept well apart, so the chosen set is unique and compared exactly: T = 3 runs
     the chunked scorer and the merge, T = 300 the query-tiled scorer and the
-    per-query select."""
-    B, n_fill, k, H_I, m = 1, 5000, 512, 32, 1
+    per-query select (rows of up to 4096 keys held 64 per lane, longer rows 128)."""
+    B, k, H_I, m = 1, 512, 32, 1
     say(f"case: score_topk exact ties dtype={dtype} T={T}")
     u = synth.gaussian((50, 128), 1.0, 31, "u", 0, torch.float32, "cpu").numpy()
     base_c, base_s = O.fp4_pack(u)
