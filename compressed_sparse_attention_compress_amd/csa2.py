@@ -61,7 +61,7 @@ class SparseAttnArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H", i32), ("N_cap", i32), ("k", i32), ("L_w", i32),
                 ("W", i32), ("scale", C.c_float), ("q", vp), ("kv", vp), ("topk", vp), ("swa_kv", vp),
                 ("swa_pos0", vp), ("q_pos", vp), ("o", vp), ("lse", vp), ("workspace", vp),
-                ("workspace_bytes", C.c_size_t)]
+                ("workspace_bytes", C.c_size_t), ("sink", vp)]
 
 
 class LayerCfg(C.Structure):
@@ -76,7 +76,7 @@ class LayerIO(C.Structure):
                 ("latent_pre", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
                 ("q_idx", vp), ("w", vp), ("topk", vp), ("candidates", vp),
                 ("q_pos", vp), ("q", vp), ("swa_kv", vp), ("L_w", i32), ("swa_pos0", vp),
-                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("sink", vp)]
 
 
 class SlotInfo(C.Structure):
@@ -230,12 +230,13 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
 
 
 def sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: int, N_cap: int, scale: float = 0.0,
-                     lse=None, workspace=None):
+                     lse=None, workspace=None, sink=None):
     B, T, H, _ = q.shape
     return SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, N_cap=N_cap, k=k, L_w=swa_kv.shape[1], W=W, scale=scale,
                           q=_ptr(q), kv=_ptr(kv), topk=_ptr(topk), swa_kv=_ptr(swa_kv), swa_pos0=_ptr(swa_pos0),
                           q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=_ptr(workspace),
-                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          sink=_ptr(sink))
 
 
 def sparse_attn_workspace_bytes(q, k: int, W: int) -> int:
@@ -247,10 +248,11 @@ def sparse_attn_workspace_bytes(q, k: int, W: int) -> int:
 
 
 def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Optional[int] = None,
-                     N_cap: Optional[int] = None, scale: float = 0.0, lse=None, workspace=None, stream=None):
-    """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots.  A
-    workspace (row-split partials for few-query calls) is allocated when needed
-    and none is given."""
+                     N_cap: Optional[int] = None, scale: float = 0.0, lse=None, workspace=None, stream=None,
+                     sink=None):
+    """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots; sink
+    [H] float32 per-head sink logits or None.  A workspace (row-split partials for
+    few-query calls) is allocated when needed and none is given."""
     if k is None:
         k = topk.shape[-1]
     if N_cap is None:
@@ -259,7 +261,7 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
         nbytes = sparse_attn_workspace_bytes(q, k, W)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace)
+    a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace, sink)
     _check(lib().csa2_sparse_attn(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
@@ -278,14 +280,15 @@ def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, h
 
 def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,
              gamma=None, w_ik=None, latent_pre=None, kv_cache=None, ik_codes=None, ik_scales=None, q_idx=None,
-             w=None, topk=None, candidates=None, workspace=None) -> LayerIO:
+             w=None, topk=None, candidates=None, workspace=None, sink=None) -> LayerIO:
     return LayerIO(B=B, T=T, D=D, start_pos=start_pos, N_cap=N_cap, x=_ptr(x), w_kv=_ptr(w_kv),
                    w_gate=_ptr(w_gate), gamma=_ptr(gamma), w_ik=_ptr(w_ik), latent_pre=_ptr(latent_pre),
                    kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes), ik_scales=_ptr(ik_scales),
                    q_idx=_ptr(q_idx), w=_ptr(w), topk=_ptr(topk), candidates=_ptr(candidates), q_pos=_ptr(q_pos),
                    q=_ptr(q), swa_kv=_ptr(swa_kv), L_w=swa_kv.shape[1], swa_pos0=_ptr(swa_pos0), o=_ptr(o),
                    workspace=_ptr(workspace),
-                   workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+                   workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
+                   sink=_ptr(sink))
 
 
 def layer_workspace_bytes(cfg: LayerCfg, io: LayerIO) -> int:

@@ -282,8 +282,9 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
       "csa2_sparse_attn: workspace of %zu bytes needed (got %zu)", plan.ws_bytes, a.workspace_bytes);
   REQ(plan.ws_bytes == 0 || ((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
       "csa2_sparse_attn: workspace not 16-byte aligned");
-  hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse, a.B,
-                                          a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan, st(stream));
+  hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse,
+                                          a.sink, a.B, a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan,
+                                          st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_sparse_attn launch");
   return ok();
 }
@@ -368,7 +369,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
   csa2_sparse_attn_args aa{};
   aa.dtype = cfg->dtype; aa.B = io->B; aa.T = io->T; aa.H = cfg->H; aa.k = cfg->k; aa.L_w = io->L_w; aa.W = cfg->W;
   aa.scale = cfg->scale; aa.q = io->q; aa.swa_kv = io->swa_kv; aa.swa_pos0 = io->swa_pos0; aa.q_pos = io->q_pos;
-  aa.o = io->o; aa.workspace = io->workspace; aa.workspace_bytes = io->workspace_bytes;
+  aa.o = io->o; aa.workspace = io->workspace; aa.workspace_bytes = io->workspace_bytes; aa.sink = io->sink;
   if (cfg->mode == CSA2_FULL) {
     aa.kv = io->kv_cache;
     aa.N_cap = io->N_cap;

@@ -45,7 +45,7 @@ struct AttnPlan {
 AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W);
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk,
                               const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos,
-                              void* o, float* lse, int B, int T, int H, int N_cap, int k, int L_w,
-                              int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream);
+                              void* o, float* lse, const float* sink, int B, int T, int H, int N_cap, int k,
+                              int L_w, int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream);
 
 }  // namespace csa2

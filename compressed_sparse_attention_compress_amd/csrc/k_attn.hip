@@ -110,6 +110,26 @@ __device__ __forceinline__ const T* row_ptr(int id, const T* kvb, const T* swb) 
   return id >= 0 ? kvb + (size_t)id * 512 : swb + (size_t)(-id - 1) * 512;
 }
 
+// Final softmax normalisation of one head, base 2: the rows' running maximum m and
+// sum l (relative to m), and the head's sink logit s2 (log2 units; -inf without a
+// sink), which enters the denominator only.  Returns the factor that turns the
+// accumulator (weights relative to m) into the output and sets lse2 to the
+// log2-sum-exp over the rows and the sink (-inf when both are empty).
+__device__ __forceinline__ float softmax_norm(float m, float l, float s2, float& lse2) {
+  if (!(l > 0.f)) {   // no rows: zero output, the sink alone in the log-sum-exp
+    lse2 = s2;
+    return 0.f;
+  }
+  const float M = fmaxf(m, s2);
+  const float a = exp2f(m - M);
+  const float den = l * a + exp2f(s2 - M);
+  lse2 = M + log2f(den);
+  return a / den;
+}
+__device__ __forceinline__ float sink_log2(const float* sink, int head, int H) {
+  return (sink != nullptr && head < H) ? sink[head] * 1.4426950408889634f : -INFINITY;
+}
+
 // ----------------------------------------------------------------- prefill
 
 constexpr int PRC = 32;                 // rows per chunk
@@ -132,8 +152,8 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, int T_len, int H, int N_cap, int k, int L_w, int W,
-    float scale_log2, int tbl) {
+    bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink, int T_len, int H, int N_cap,
+    int k, int L_w, int W, float scale_log2, int tbl) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[PRC * PRS];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[PRC * PRS];
   __shared__ f32x4 xbuf[NW][4 * 64];    // per wave: its half-dim S partial, [tile mt*2+ht][lane]
@@ -403,8 +423,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
   for (int ht = 0; ht < 2; ++ht) {
     float l_tot = l_run[ht] + __shfl_xor(l_run[ht], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const int head = hp * 32 + ht * 16 + lr;
+    float lse2;
+    const float inv = softmax_norm(m_run[ht], l_tot, sink_log2(sink, head, H), lse2);
     if (head < H) {
       bf16* orow = o + ((size_t)bt * H + head) * 512 + dh * 256;
 #pragma unroll
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
         *reinterpret_cast<uint2*>(orow + d) = u;
       }
       if (lse != nullptr && lg == 0 && dh == 0)
-        lse[(size_t)bt * H + head] = (l_tot > 0.f) ? (m_run[ht] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        lse[(size_t)bt * H + head] = lse2 * 0.69314718055994531f;
     }
   }
 }
@@ -439,8 +460,8 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
+    bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink, float* __restrict__ part_o,
+    float* __restrict__ part_lse, int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
   constexpr int RPW = DRC / NW;   // gathers per wave per chunk
   __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
   __shared__ int rowlist[MAX_ROWS];
@@ -578,10 +599,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     COMPILER_FENCE();
   }
 
-  // ---- this split's normalised output and log-sum-exp (base 2) per head
+  // ---- this split's normalised output and log-sum-exp (base 2) per head; the
+  // sink enters once, here for a single split, else in attn_combine
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  float lse2;
+  const float inv = softmax_norm(m_run, l_tot, n_splits == 1 ? sink_log2(sink, head, H) : -INFINITY, lse2);
   if (head < H) {
     if (n_splits == 1) {
       bf16* orow = o + ((size_t)bt * H + head) * 512;
@@ -593,14 +616,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
         for (int i = 0; i < 4; ++i) v[i] = (bf16)(oacc[dt][i] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * lg) = v;
       }
-      if (lse != nullptr && lg == 0)
-        lse[(size_t)bt * H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      if (lse != nullptr && lg == 0) lse[(size_t)bt * H + head] = lse2 * 0.69314718055994531f;
     } else {
       float* prow = part_o + (((size_t)bt * n_splits + split) * H + head) * 512;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + 4 * lg) = oacc[dt] * inv;
-      if (lg == 0)
-        part_lse[((size_t)bt * n_splits + split) * H + head] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      if (lg == 0) part_lse[((size_t)bt * n_splits + split) * H + head] = lse2;
     }
   }
 }
@@ -608,7 +629,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
 // Merge of row-split partials: one thread per (query, head, 8 dims).
 __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_lse, bf16* __restrict__ o,
-                                                         float* __restrict__ lse, int Q, int H, int n_splits) {
+                                                         float* __restrict__ lse, const float* __restrict__ sink, int Q,
+                                                         int H, int n_splits) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Q * H * 64;
   if (gid >= total) return;
@@ -618,7 +640,8 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict
   const long long qi = qh / H;
   const float* ls_q = part_lse + qi * n_splits * H + h;                    // split s at s * H
   const float* po_q = part_o + (qi * n_splits * H + h) * 512 + d0;         // split s at s * H * 512
-  float mx = -INFINITY;
+  const float s2 = sink_log2(sink, h, H);   // the head's sink logit, counted once here
+  float mx = s2;
 #pragma unroll 8
   for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ls_q[(size_t)s * H]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, den = 0.f;
@@ -649,6 +672,7 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict
     const float4* pr = reinterpret_cast<const float4*>(po_q + (size_t)s * H * 512);
     add(ls_q[(size_t)s * H], pr[0], pr[1]);
   }
+  if (s2 != -INFINITY) den += exp2f(s2 - mx);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   bf16* orow = o + (qi * H + h) * 512 + d0;
 #pragma unroll
@@ -665,8 +689,9 @@ constexpr int FRC = 32;
 __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, const float* __restrict__ kv,
                                                 const int32_t* __restrict__ topk, const float* __restrict__ swa,
                                                 const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-                                                float* __restrict__ o, float* __restrict__ lse, int T_len, int H,
-                                                int N_cap, int k, int L_w, int W, float scale_log2) {
+                                                float* __restrict__ o, float* __restrict__ lse,
+                                                const float* __restrict__ sink, int T_len, int H, int N_cap, int k,
+                                                int L_w, int W, float scale_log2) {
   constexpr int RSF = 512 + 4;  // floats
   __shared__ __attribute__((aligned(16))) float buf[FRC * RSF];
   __shared__ int rowlist[MAX_ROWS];
@@ -735,7 +760,8 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  float lse2;
+  const float inv = softmax_norm(m_run, l_tot, sink_log2(sink, head, H), lse2);
   if (head < H) {
     float* orow = o + ((size_t)bt * H + head) * 512;
     for (int dt = 0; dt < 32; ++dt) {
@@ -743,8 +769,7 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
       *reinterpret_cast<float4*>(orow + d) =
           make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
     }
-    if (lse != nullptr && lg == 0)
-      lse[(size_t)bt * H + head] = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (lse != nullptr && lg == 0) lse[(size_t)bt * H + head] = lse2 * 0.69314718055994531f;
   }
 }
 
@@ -770,16 +795,16 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W) {
 }
 
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk, const void* swa_kv,
-                              const int32_t* swa_pos0, const int32_t* q_pos, void* o, float* lse, int B, int T, int H,
-                              int N_cap, int k, int L_w, int W, float scale, void* workspace, const AttnPlan& p,
-                              hipStream_t st) {
+                              const int32_t* swa_pos0, const int32_t* q_pos, void* o, float* lse, const float* sink,
+                              int B, int T, int H, int N_cap, int k, int L_w, int W, float scale, void* workspace,
+                              const AttnPlan& p, hipStream_t st) {
   if (B == 0 || T == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   const int nw = (H + 15) / 16;
   if (dtype == 0) {
     hipLaunchKernelGGL(attn_f32, dim3(T, B), dim3(64 * nw), 0, st, static_cast<const float*>(q),
                        static_cast<const float*>(kv), topk, static_cast<const float*>(swa_kv), swa_pos0, q_pos,
-                       static_cast<float*>(o), lse, T, H, N_cap, k, L_w, W, sl2);
+                       static_cast<float*>(o), lse, sink, T, H, N_cap, k, L_w, W, sl2);
     return hipGetLastError();
   }
   const bf16* qq = static_cast<const bf16*>(q);
@@ -792,10 +817,10 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
     const dim3 grid(8 * tbl * ((T + 8 * tbl - 1) / (8 * tbl)), B);
     if (H > 32)
       hipLaunchKernelGGL(attn_prefill_bf16<4>, grid, dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, T, H, N_cap, k, L_w, W, sl2, tbl);
+                         oo, lse, sink, T, H, N_cap, k, L_w, W, sl2, tbl);
     else
       hipLaunchKernelGGL(attn_prefill_bf16<2>, grid, dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos,
-                         oo, lse, T, H, N_cap, k, L_w, W, sl2, tbl);
+                         oo, lse, sink, T, H, N_cap, k, L_w, W, sl2, tbl);
     return hipGetLastError();
   }
   const int Q = B * T;
@@ -804,18 +829,18 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   float* part_lse = part_o + (size_t)Q * p.n_splits * H * 512;
   if (H > 32)
     hipLaunchKernelGGL(attn_decode_bf16<4>, dim3(groups), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
   else if (H > 16)
     hipLaunchKernelGGL(attn_decode_bf16<2>, dim3(groups), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
   else
     hipLaunchKernelGGL(attn_decode_bf16<1>, dim3(groups), dim3(64), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long total = (long long)Q * H * 64;
   hipLaunchKernelGGL(attn_combine_bf16, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part_o, part_lse, oo,
-                     lse, Q, H, p.n_splits);
+                     lse, sink, Q, H, p.n_splits);
   return hipGetLastError();
 }
 

@@ -213,7 +213,13 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa
  *   lse      [B, T, H] float32 out (optional, natural-log sum of exp of scaled logits)
  *   scale    0 -> 1/sqrt(512)
  *   workspace  device scratch of csa2_workspace_size() bytes (may be 0 bytes:
- *              then NULL is accepted), 16-byte aligned                        */
+ *              then NULL is accepted), 16-byte aligned
+ *   sink     [H] float32 or NULL.  Every layer has one attention sink per head
+ *            ([P1] sections "三种模式的参数清单" and "容易混淆的几点"); the pages
+ *            give no formula.  Read here as a logit s_h that enters only the
+ *            softmax denominator: p_r = exp(l_r) / (exp(s_h) + sum_r' exp(l_r')),
+ *            o = sum_r p_r row_r, lse = log(exp(s_h) + sum_r exp(l_r)), with
+ *            l_r = scale * q . row_r.  NULL is the plain softmax.            */
 typedef struct csa2_sparse_attn_args {
   int32_t dtype;            /* csa2_dtype of q, kv, swa_kv, o */
   int32_t B, T, H;
@@ -229,6 +235,7 @@ typedef struct csa2_sparse_attn_args {
   float* lse;
   void* workspace;
   size_t workspace_bytes;
+  const float* sink;        /* [H] float32 per-head sink logits, or NULL (no sink) */
 } csa2_sparse_attn_args;
 
 csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* a, csa2_stream stream);
@@ -261,6 +268,7 @@ typedef struct csa2_layer_io {
   const int32_t* q_pos; const void* q; const void* swa_kv; int32_t L_w; const int32_t* swa_pos0;
   void* o;
   void* workspace; size_t workspace_bytes;
+  const float* sink;        /* [H] float32 per-head attention sink, or NULL (see csa2_sparse_attn_args) */
 } csa2_layer_io;
 
 csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, const csa2_layer_io* io,

@@ -324,10 +324,17 @@ def window_positions(p: int, W: int, swa_pos0: int = 0) -> np.ndarray:
 
 
 def sparse_attention(q, kv, sel, swa_kv, swa_pos0: int, p: int, W: int,
-                     scale: Optional[float] = None):
+                     scale: Optional[float] = None, sink=None):
     """One query token.  q [H, d]; kv [N, d]; sel [k] (entry ids, -1 = empty);
     swa_kv [L_w, d] holding positions swa_pos0.. .  Returns (o [H, d], probs [H, R],
-    rows [R, d])."""
+    rows [R, d]).
+
+    sink [H] (optional): every layer has one attention sink per head ([P1]
+    sections "三种模式的参数清单" and "容易混淆的几点"), with no formula on the
+    pages.  Read as a per-head logit that joins the softmax normalisation but
+    carries no value row: p_r = exp(l_r) / (exp(sink_h) + sum_r' exp(l_r')), so
+    the probabilities of the rows sum to less than 1 and o lies in the convex
+    hull of the rows and the origin."""
     q = np.asarray(q, dtype=np.float64)
     kv = np.asarray(kv, dtype=np.float64)
     d = q.shape[-1]
@@ -338,10 +345,32 @@ def sparse_attention(q, kv, sel, swa_kv, swa_pos0: int, p: int, W: int,
     win = window_positions(p, W, swa_pos0)
     rows = np.concatenate([kv[sel], np.asarray(swa_kv, dtype=np.float64)[win - swa_pos0]], axis=0)
     logits = (q @ rows.T) * scale
-    logits = logits - logits.max(axis=1, keepdims=True)
-    ez = np.exp(logits)
-    probs = ez / ez.sum(axis=1, keepdims=True)
+    if sink is None:
+        logits = logits - logits.max(axis=1, keepdims=True)
+        ez = np.exp(logits)
+        probs = ez / ez.sum(axis=1, keepdims=True)
+        return probs @ rows, probs, rows
+    sk = np.asarray(sink, dtype=np.float64).reshape(-1, 1)
+    top = np.maximum(logits.max(axis=1, keepdims=True) if rows.shape[0] else -np.inf, sk)
+    ez = np.exp(logits - top)
+    probs = ez / (ez.sum(axis=1, keepdims=True) + np.exp(sk - top))
     return probs @ rows, probs, rows
+
+
+def attention_lse(q, rows, scale: Optional[float] = None, sink=None) -> np.ndarray:
+    """Natural-log sum of exp over the rows' scaled logits (and the sink logit when
+    given), per head: the normaliser of sparse_attention."""
+    q = np.asarray(q, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    logits = (q @ rows.T) * scale
+    if sink is not None:
+        logits = np.concatenate([logits, np.asarray(sink, dtype=np.float64).reshape(-1, 1)], axis=1)
+    if logits.shape[1] == 0:
+        return np.full(q.shape[0], -np.inf)
+    mx = logits.max(axis=1)
+    return mx + np.log(np.exp(logits - mx[:, None]).sum(axis=1))
 
 
 # ---------------------------------------------------------------------------

@@ -42,7 +42,7 @@ class GpuLayerStack:
         self.hsi, self.hsi_s, self.hsi_nb = hsi, hsi_s, hsi_nb
         self.cands = torch.full((s.B, s.L, max(hsi_nb, 1)), -3, dtype=torch.int32, device=DEV)
 
-    def run(self, mode, inp, hsi=None):
+    def run(self, mode, inp, hsi=None, sink=None):
         s = self.s
         hsi = self.hsi if hsi is None else hsi
         cfg = K.layer_cfg(mode, K.CSA2_BF16 if self.dtype == torch.bfloat16 else K.CSA2_F32, m=s.m, k=s.k, W=s.W,
@@ -50,7 +50,7 @@ class GpuLayerStack:
         topk = torch.full((s.B, s.L, s.k), -9, dtype=torch.int32, device=DEV)
         o = torch.empty_like(inp["q"])
         kw = dict(B=s.B, T=s.L, q_pos=inp["q_pos"], q=inp["q"], swa_kv=inp["swa_kv"], swa_pos0=inp["swa_pos0"], o=o,
-                  N_cap=self.N)
+                  N_cap=self.N, sink=sink)
         if mode == K.FULL:
             kw.update(D=s.D, x=inp["x"], w_kv=inp["w_kv"], w_gate=inp["w_gate"], gamma=inp["gamma"],
                       w_ik=inp["w_ik"], latent_pre=self.lat, kv_cache=self.kv, ik_codes=self.codes,

@@ -260,6 +260,39 @@ def test_attention_convex_hull_and_special_cases():
     assert np.allclose(o1b, np.repeat(swa[0][None], 4, 0))
 
 
+def test_attention_sink_special_cases():
+    """The sink logit (denominator only): a sink of -inf is the plain softmax; with
+    q = 0 every row logit is 0, so o = sum(rows) / (R + exp(sink)) in closed form;
+    probabilities stay non-negative and sum to 1 / (1 + exp(sink - lse_rows)); a
+    huge sink drives o to 0; the log-sum-exp gains the sink term."""
+    r = rng(19)
+    kv = r.standard_normal((40, 512))
+    swa = r.standard_normal((20, 512))
+    q = r.standard_normal((4, 512))
+    sel = np.array([3, 7, 11, 39, -1])
+    o_plain, p_plain, rows = O.sparse_attention(q, kv, sel, swa, 100, 110, 8)
+    o_ninf, p_ninf, _ = O.sparse_attention(q, kv, sel, swa, 100, 110, 8, sink=np.full(4, -np.inf))
+    assert np.array_equal(o_ninf, o_plain) or np.allclose(o_ninf, o_plain, rtol=0, atol=1e-15)
+    sink = np.array([-3.0, 0.0, 2.5, 7.0])
+    R = rows.shape[0]
+    o0, p0, _ = O.sparse_attention(np.zeros((4, 512)), kv, sel, swa, 100, 110, 8, sink=sink)
+    for h in range(4):
+        assert np.allclose(o0[h], rows.sum(0) / (R + math.exp(sink[h])), rtol=1e-12)
+        assert np.allclose(p0[h], 1.0 / (R + math.exp(sink[h])), rtol=1e-12)
+    o, p, _ = O.sparse_attention(q, kv, sel, swa, 100, 110, 8, sink=sink)
+    assert np.all(p >= 0)
+    lse_rows = O.attention_lse(q, rows)
+    assert np.allclose(p.sum(1), 1.0 / (1.0 + np.exp(sink - lse_rows)), rtol=1e-12)
+    assert np.allclose(o, p @ rows)
+    # o = (1 - p_sink) * o_plain: the sink only rescales
+    assert np.allclose(o, o_plain * p.sum(1, keepdims=True), rtol=1e-10, atol=1e-13)
+    big, _, _ = O.sparse_attention(q, kv, sel, swa, 100, 110, 8, sink=np.full(4, 1e3))
+    assert np.allclose(big, 0.0, atol=1e-300)
+    assert np.allclose(O.attention_lse(q, rows, sink=sink), np.logaddexp(lse_rows, sink), rtol=1e-12)
+    # no rows at all: zero output, the sink alone in the normaliser
+    assert np.allclose(O.attention_lse(q, rows[:0], sink=sink), sink)
+
+
 def test_attention_select_all_equals_torch_sdpa():
     r = rng(15)
     kv = r.standard_normal((24, 512))
