@@ -21,7 +21,7 @@ CSA2_F32, CSA2_BF16 = 0, 1
 FULL, REINDEX, REUSE = 0, 1, 2
 HSI_NONE, HSI_BUILD, HSI_USE = 0, 1, 2
 SLOT_COMPRESS_KV, SLOT_INDEX_K, SLOT_TOPK_IDXS, SLOT_CANDIDATES = 0, 1, 2, 3
-OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER = 0, 1, 2
+OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER, OP_COMPRESS_STEP = 0, 1, 2, 3
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_DTYPE",
           4: "CSA2_ERR_SLOT_EMPTY", 5: "CSA2_ERR_SLOT_MISMATCH", 6: "CSA2_ERR_WORKSPACE",
@@ -43,6 +43,13 @@ class CompressArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("D", i32), ("m", i32), ("start_pos", i32),
                 ("N_cap", i32), ("eps", C.c_float), ("rope_base", C.c_float), ("x", vp), ("w_kv", vp),
                 ("w_gate", vp), ("gamma", vp), ("latent_pre", vp), ("kv_cache", vp)]
+
+
+class CompressStepArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("D", i32), ("m", i32), ("N_cap", i32), ("eps", C.c_float),
+                ("rope_base", C.c_float), ("x", vp), ("pos", vp), ("w_kv", vp), ("w_gate", vp), ("gamma", vp),
+                ("w_ik", vp), ("state", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
+                ("latent_pre", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
 class IndexKArgs(C.Structure):
@@ -93,6 +100,7 @@ EXPORTS = {
     "csa2_index_k": ([vp, C.POINTER(IndexKArgs), vp], i32),
     "csa2_score_topk": ([vp, C.POINTER(ScoreTopkArgs), vp], i32),
     "csa2_sparse_attn": ([vp, C.POINTER(SparseAttnArgs), vp], i32),
+    "csa2_compress_step": ([vp, C.POINTER(CompressStepArgs), vp], i32),
     "csa2_layer_forward": ([vp, C.POINTER(LayerCfg), C.POINTER(LayerIO), vp], i32),
     "csa2_workspace_size": ([i32, vp, C.POINTER(LayerCfg), C.POINTER(C.c_size_t)], i32),
     "csa2_fp4_pack": ([vp, C.c_int64, vp, vp, vp], i32),
@@ -263,6 +271,22 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace, sink)
     _check(lib().csa2_sparse_attn(_rt(rt), C.byref(a), _stream(stream)))
+    return workspace
+
+
+def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, ik_codes, ik_scales, m: int,
+                       latent_pre=None, eps: float = 1e-6, rope_base: float = 10000.0, workspace=None, stream=None):
+    """Decode append: x [B, D] (one new token per sequence at positions pos [B]);
+    state [B, 3, 512] float32 (None iff m == 1).  Returns the workspace used."""
+    B, D = x.shape
+    if workspace is None and B > 0:
+        workspace = torch.empty(B * 1024 * 4, dtype=torch.uint8, device=x.device)
+    a = CompressStepArgs(dtype=_dtype(x), B=B, D=D, m=m, N_cap=kv_cache.shape[1], eps=eps, rope_base=rope_base,
+                         x=_ptr(x), pos=_ptr(pos), w_kv=_ptr(w_kv), w_gate=_ptr(w_gate), gamma=_ptr(gamma),
+                         w_ik=_ptr(w_ik), state=_ptr(state), kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes),
+                         ik_scales=_ptr(ik_scales), latent_pre=_ptr(latent_pre), workspace=_ptr(workspace),
+                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+    _check(lib().csa2_compress_step(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
 

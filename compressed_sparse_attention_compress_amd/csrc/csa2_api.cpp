@@ -86,6 +86,28 @@ csa2_status check_compress(const csa2_compress_args* a) {
   return CSA2_OK;
 }
 
+csa2_status check_compress_step(const csa2_compress_step_args* a) {
+  REQ(a, CSA2_ERR_INVALID_ARG, "csa2_compress_step: args is NULL");
+  REQ(dtype_ok(a->dtype), CSA2_ERR_DTYPE, "csa2_compress_step: unsupported dtype %d", a->dtype);
+  REQ(a->m == 1 || a->m == 2 || a->m == 4, CSA2_ERR_INVALID_ARG, "csa2_compress_step: m must be 1, 2 or 4 (got %d)",
+      a->m);
+  REQ(a->m == 1 || (a->w_gate != nullptr && a->state != nullptr), CSA2_ERR_INVALID_ARG,
+      "csa2_compress_step: m > 1 needs w_gate and state");
+  REQ(a->m > 1 || a->w_gate == nullptr, CSA2_ERR_INVALID_ARG,
+      "csa2_compress_step: m == 1 has no gate; w_gate must be NULL");
+  REQ(a->B >= 0 && a->D > 0 && a->D % 64 == 0, CSA2_ERR_SHAPE, "csa2_compress_step: bad B/D (D %% 64 == 0)");
+  REQ(a->N_cap >= 0, CSA2_ERR_SHAPE, "csa2_compress_step: bad N_cap");
+  REQ(a->x && a->pos && a->w_kv && a->gamma && a->w_ik && a->kv_cache && a->ik_codes && a->ik_scales,
+      CSA2_ERR_INVALID_ARG, "csa2_compress_step: NULL tensor");
+  REQ(a->eps >= 0.f && a->rope_base > 0.f, CSA2_ERR_INVALID_ARG, "csa2_compress_step: bad eps/rope_base");
+  const size_t need = (size_t)a->B * 1024 * 4;
+  REQ(a->B == 0 || (a->workspace != nullptr && a->workspace_bytes >= need), CSA2_ERR_WORKSPACE,
+      "csa2_compress_step: workspace of %zu bytes needed (got %zu)", need, a->workspace_bytes);
+  REQ(a->B == 0 || ((uintptr_t)a->workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
+      "csa2_compress_step: workspace not 16-byte aligned");
+  return CSA2_OK;
+}
+
 csa2_status check_index_k(const csa2_index_k_args* a) {
   REQ(a, CSA2_ERR_INVALID_ARG, "csa2_index_k: args is NULL");
   REQ(dtype_ok(a->dtype), CSA2_ERR_DTYPE, "csa2_index_k: unsupported dtype %d", a->dtype);
@@ -243,6 +265,18 @@ csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_st
   return ok();
 }
 
+csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream) {
+  (void)rt;
+  csa2_status s = check_compress_step(a);
+  if (s != CSA2_OK) return s;
+  hipError_t e = csa2::launch_compress_step(a->dtype, a->x, a->pos, a->w_kv, a->w_gate, a->gamma, a->w_ik, a->state,
+                                            a->kv_cache, a->ik_codes, a->ik_scales, a->latent_pre,
+                                            static_cast<float*>(a->workspace), a->B, a->D, a->m, a->N_cap, a->eps,
+                                            a->rope_base, st(stream));
+  if (e != hipSuccess) return hip_status(e, "csa2_compress_step launch");
+  return ok();
+}
+
 csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stream stream) {
   csa2_status s = check_index_k(a);
   if (s != CSA2_OK) return s;
@@ -299,6 +333,11 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   if (op == CSA2_OP_SPARSE_ATTN) {
     const csa2_sparse_attn_args* a = static_cast<const csa2_sparse_attn_args*>(args);
     *bytes = csa2::plan_attn(a->dtype, a->B, a->T, a->H, a->k, a->W).ws_bytes;
+    return ok();
+  }
+  if (op == CSA2_OP_COMPRESS_STEP) {
+    const csa2_compress_step_args* a = static_cast<const csa2_compress_step_args*>(args);
+    *bytes = a->B > 0 ? (size_t)a->B * 1024 * 4 : 0;
     return ok();
   }
   if (op == CSA2_OP_LAYER) {

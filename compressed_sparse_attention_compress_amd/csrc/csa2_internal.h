@@ -14,6 +14,14 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
                            int D, int m, int start_pos, int N_cap, float eps, float rope_base,
                            hipStream_t stream);
 
+// decode append: C and Z of one token per sequence into cz [B, 1024] (float32), then
+// the group pool / entry / index-K row per sequence
+hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv,
+                                const void* w_gate, const float* gamma, const void* w_ik, float* state,
+                                void* kv_cache, uint8_t* codes, uint8_t* scales, float* latent_pre,
+                                float* cz, int B, int D, int m, int N_cap, float eps, float rope_base,
+                                hipStream_t stream);
+
 // ---- index K and FP4 packing (k_index_k.hip)
 hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes,
                           uint8_t* scales, int B, int N, int m, int entry0, int N_cap,

@@ -396,6 +396,172 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- decode append
+// One new token per sequence after the prefill.  Step 1 (compress_step_proj):
+// C and Z of every sequence's token into cz[b][n] (n < 512: C channel n, else Z
+// channel n - 512).  A workgroup computes 16 output columns for all sequences
+// with MFMA (sequences as the rows of 16-row tiles, 4 tiles per pass); its 4
+// waves take the 32-wide k-steps in turn and their partial sums meet in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void compress_step_proj(const T* __restrict__ x, const T* __restrict__ w_kv,
+                                                          const T* __restrict__ w_gate, float* __restrict__ cz,
+                                                          int B, int D) {
+  typedef typename Frag<T>::type FragT;
+  __shared__ f32x4 red[3][4 * 64];
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = blockIdx.x * 16 + lr;
+  const T* wrow = n < 512 ? w_kv + (size_t)n * D : w_gate + (size_t)(n - 512) * D;
+  const int nks = D / 32;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = wave; ks < nks; ks += 4) {
+      const FragT wf = load_frag(wrow + ks * 32 + 8 * lg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int seq = min(b0 + t * 16 + lr, B - 1);   // rows past B repeat the last token (discarded)
+        const FragT xf = load_frag(x + (size_t)seq * D + ks * 32 + 8 * lg);
+        acc[t] = mma16(xf, wf, acc[t]);
+      }
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[wave - 1][t * 64 + lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 v = acc[t] + red[0][t * 64 + lane] + red[1][t * 64 + lane] + red[2][t * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int seq = b0 + t * 16 + 4 * lg + i;   // accumulator row 4*lg+i, column lr
+          if (seq < B) cz[(size_t)seq * 1024 + n] = v[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ float frag_elem(const bf16x8& f, int i) { return (float)f[i]; }
+__device__ __forceinline__ float frag_elem(const f32x8& f, int i) { return f.v[i]; }
+
+// Step 2 (compress_step_entry), one workgroup per sequence; thread t owns channels
+// t and t + 256.  The token joins its group's running softmax pool per channel
+// (maximum of Z, sum of exp(Z - max), sum of exp(Z - max) C): the exact softmax
+// pool of the group, reached one token at a time.  At the group's last token the
+// pooled vector is normalised (RMSNorm), written before RoPE to latent_pre and
+// after RoPE on dims 448..511 (at position g*m) to the cache row g; then its
+// index-K row: 512 -> 128 (thread pair per output dim, halves of the dot product
+// added by a shuffle), RoPE on dims 64..127, FP4 codes with one E4M3 scale per
+// 32 dims (wave q holds block q).
+template <typename T>
+__global__ __launch_bounds__(256) void compress_step_entry(const float* __restrict__ cz, const int32_t* __restrict__ pos_arr,
+                                                           const float* __restrict__ gamma, const T* __restrict__ w_ik,
+                                                           float* __restrict__ state, T* __restrict__ kv_cache,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                           float* __restrict__ latent_pre, int m, int N_cap, float eps,
+                                                           double base) {
+  typedef typename Frag<T>::type FragT;
+  __shared__ float lat_s[512];
+  __shared__ float red[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pos = pos_arr[b];
+  if (pos < 0) return;
+  const int gi = pos % m, g = pos / m;
+  const float* czb = cz + (size_t)b * 1024;
+  float e[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ch = tid + 256 * j;
+    const float c = czb[ch];
+    if (m == 1) {
+      e[j] = c;
+      continue;
+    }
+    float* st = state + (size_t)b * 1536;
+    const float z = czb[512 + ch];
+    float zm, den, num;
+    if (gi == 0) {
+      zm = z;
+      den = 1.f;
+      num = c;
+    } else {
+      const float zo = st[ch];
+      zm = fmaxf(zo, z);
+      const float ao = __expf(zo - zm), an = __expf(z - zm);
+      den = st[512 + ch] * ao + an;
+      num = st[1024 + ch] * ao + c * an;
+    }
+    if (gi < m - 1) {
+      st[ch] = zm;
+      st[512 + ch] = den;
+      st[1024 + ch] = num;
+    }
+    e[j] = num / den;
+  }
+  if (gi < m - 1 || g >= N_cap) return;   // the group goes on (or its row is outside the cache)
+
+  float ss = e[0] * e[0] + e[1] * e[1];
+  ss = wave_sum_xor(ss, 63);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float rinv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) * (1.0f / 512.0f) + eps);
+  float v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ch = tid + 256 * j;
+    v[j] = e[j] * rinv * gamma[ch];
+    lat_s[ch] = v[j];
+    if (latent_pre != nullptr) latent_pre[(size_t)b * 512 + ch] = v[j];
+  }
+  {
+    // RoPE pair (448 + 2p, 449 + 2p) = channels tid + 256 of threads tid, tid ^ 1
+    const float other = __shfl_xor(v[1], 1, 64);
+    const int ch = tid + 256;
+    if (ch >= 448) {
+      float c, s;
+      rope_cos_sin((int64_t)g * m, (ch - 448) >> 1, 64, base, c, s);
+      v[1] = (ch & 1) ? (other * s + v[1] * c) : (v[1] * c - other * s);
+    }
+  }
+  T* kvrow = kv_cache + ((size_t)b * N_cap + g) * 512;
+  kvrow[tid] = from_f32<T>(v[0]);
+  kvrow[tid + 256] = from_f32<T>(v[1]);
+  __syncthreads();   // lat_s complete
+
+  const int o = tid >> 1, h = tid & 1;
+  const T* wr = w_ik + (size_t)o * 512 + h * 256;
+  const float* lh = lat_s + h * 256;
+  float acc = 0.f;
+  for (int d = 0; d < 256; d += 8) {
+    const FragT wf = load_frag(wr + d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(lh[d + i], frag_elem(wf, i), acc);
+  }
+  float u = acc + __shfl_xor(acc, 1, 64);
+  {
+    // RoPE pair (64 + 2p, 65 + 2p) = outputs o, o ^ 1 = threads tid, tid ^ 2
+    const float uo = __shfl_xor(u, 2, 64);
+    if (o >= 64) {
+      float c, s;
+      rope_cos_sin((int64_t)g * m, (o - 64) >> 1, 64, base, c, s);
+      u = (o & 1) ? (uo * s + u * c) : (u * c - uo * s);
+    }
+  }
+  const float amax = wave_max_xor(fabsf(u), 63);   // block `wave` = outputs 32*wave .. +31
+  const uint32_t sb = fp4_scale_byte(amax);
+  const uint32_t code = fp4_code(u, e4m3_decode(sb));
+  const uint32_t code_next = (uint32_t)__shfl_xor((int)code, 2, 64);   // output o + 1 for even o
+  if (h == 0 && (o & 1) == 0) codes[((size_t)b * N_cap + g) * 64 + (o >> 1)] = (uint8_t)(code | (code_next << 4));
+  if (lane == 0) scales[((size_t)b * N_cap + g) * 4 + wave] = (uint8_t)sb;
+}
+
 }  // namespace
 
 hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const void* w_gate, const float* gamma,
@@ -406,6 +572,29 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
                           rope_base, stream);
   return launch_t<float>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, B, T, D, m, start_pos, N_cap, eps,
                          rope_base, stream);
+}
+
+
+hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv, const void* w_gate,
+                                const float* gamma, const void* w_ik, float* state, void* kv_cache, uint8_t* codes,
+                                uint8_t* scales, float* latent_pre, float* cz, int B, int D, int m, int N_cap,
+                                float eps, float rope_base, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const dim3 g1((m > 1 ? 1024 : 512) / 16), g2(B), blk(256);
+  if (dtype == 1) {
+    hipLaunchKernelGGL((compress_step_proj<bf16>), g1, blk, 0, stream, static_cast<const bf16*>(x),
+                       static_cast<const bf16*>(w_kv), static_cast<const bf16*>(w_gate), cz, B, D);
+    hipLaunchKernelGGL((compress_step_entry<bf16>), g2, blk, 0, stream, cz, pos, gamma,
+                       static_cast<const bf16*>(w_ik), state, static_cast<bf16*>(kv_cache), codes, scales,
+                       latent_pre, m, N_cap, eps, (double)rope_base);
+  } else {
+    hipLaunchKernelGGL((compress_step_proj<float>), g1, blk, 0, stream, static_cast<const float*>(x),
+                       static_cast<const float*>(w_kv), static_cast<const float*>(w_gate), cz, B, D);
+    hipLaunchKernelGGL((compress_step_entry<float>), g2, blk, 0, stream, cz, pos, gamma,
+                       static_cast<const float*>(w_ik), state, static_cast<float*>(kv_cache), codes, scales,
+                       latent_pre, m, N_cap, eps, (double)rope_base);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace csa2

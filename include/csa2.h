@@ -158,6 +158,54 @@ typedef struct csa2_index_k_args {
 csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* Decode append for a Full layer: the compressor (a) and index K (b) for one new
+ * token per sequence after the prefill.  Groups are disjoint runs of m tokens
+ * ([P1] section "压缩算子去掉了重叠和位置偏置"), so a token becomes part of an
+ * entry only at its group's last token; until then the group lives in a
+ * caller-owned state.  The entry is then the one csa2_compress and csa2_index_k
+ * would have written for the whole group: per-channel softmax of Z over the
+ * group, pooled C, RMSNorm, RoPE on the last 64 dims at position g*m, and its
+ * index-K row.
+ *
+ *   x        [B, D]  dtype               the new token of each sequence, D % 64 == 0
+ *   pos      [B] int32 (device)          its absolute position; < 0 = no token
+ *   w_kv, w_gate, gamma                  as csa2_compress (w_gate NULL iff m == 1)
+ *   w_ik     [128, 512] dtype            as csa2_index_k
+ *   state    [B, 3, 512] float32 (device, in/out; NULL iff m == 1): the
+ *            group's running softmax pool per channel (maximum of Z, sum of
+ *            exp(Z - max), sum of exp(Z - max) C).  A group's first token
+ *            overwrites it, so it needs no initialisation.
+ *   kv_cache [B, N_cap, 512] dtype out   row pos/m, written at a group's last token
+ *   ik_codes [B, N_cap, 64], ik_scales [B, N_cap, 4] uint8 out: the same row
+ *   latent_pre [B, 512] float32 out      that entry's latent before RoPE (NULL: not written)
+ *   workspace  csa2_workspace_size(CSA2_OP_COMPRESS_STEP) bytes (B * 1024 * 4),
+ *              16-byte aligned
+ * Rows pos/m >= N_cap are not written.  The runtime slots are not changed (after
+ * the layer's prefill they already point at these caches; consumers take the
+ * visible range from q_pos).                                                 */
+typedef struct csa2_compress_step_args {
+  int32_t dtype;            /* csa2_dtype of x, w_kv, w_gate, w_ik, kv_cache */
+  int32_t B, D, m;
+  int32_t N_cap;
+  float eps, rope_base;
+  const void* x;
+  const int32_t* pos;
+  const void* w_kv;
+  const void* w_gate;
+  const float* gamma;
+  const void* w_ik;
+  float* state;
+  void* kv_cache;
+  uint8_t* ik_codes;
+  uint8_t* ik_scales;
+  float* latent_pre;
+  void* workspace;
+  size_t workspace_bytes;
+} csa2_compress_step_args;
+
+csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* (c)+(d) Indexer score and causal top-k ([P1] indexer-K section: score =
  * sum over the H_I heads of w * ReLU(q^I . k^I); [P2] CSA2-FULL / CSA2-ReIndex:
  * the k best among the causally visible entries, or inside the candidate pool).
@@ -275,7 +323,9 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
                                csa2_stream stream);
 
 /* ------------------------------------------------------------------------ */
-typedef enum csa2_op { CSA2_OP_SCORE_TOPK = 0, CSA2_OP_SPARSE_ATTN = 1, CSA2_OP_LAYER = 2 } csa2_op;
+typedef enum csa2_op {
+  CSA2_OP_SCORE_TOPK = 0, CSA2_OP_SPARSE_ATTN = 1, CSA2_OP_LAYER = 2, CSA2_OP_COMPRESS_STEP = 3
+} csa2_op;
 
 /* Device workspace bytes the op needs for these arguments (args points to the
  * op's argument struct; for CSA2_OP_LAYER a csa2_layer_io with the cfg passed

@@ -218,6 +218,36 @@ def compress(x, w_kv, w_gate, gamma, m: int, start_pos: int = 0, eps: float = 1e
     return latent_pre, kv, entry_ids
 
 
+def compress_step(pending, x_tok, w_kv, w_gate, gamma, pos: int, m: int, eps: float = 1e-6,
+                  rope_base: float = 10000.0):
+    """Decode append for one sequence: the token at absolute position pos joins
+    its group g = pos // m ([P1] compressor section: groups of m consecutive
+    tokens, no overlap); `pending` is the list of (C_t, Z_t) rows of the group's
+    earlier tokens (the partial-group state; empty at a group's first token).
+    Returns (pending', entry) where entry is None until the group's last token
+    (pos % m == m - 1), then (g, latent_pre [512], kv [512]) computed by the same
+    steps as `compress`: softmax of Z over the group per channel, pooled C,
+    RMSNorm, RoPE on the last 64 dims at position g*m."""
+    x_tok = np.asarray(x_tok, dtype=np.float64)
+    c = x_tok @ np.asarray(w_kv, dtype=np.float64).T
+    z = None if m == 1 else x_tok @ np.asarray(w_gate, dtype=np.float64).T
+    assert len(pending) == pos % m, "the state must hold the group's earlier tokens"
+    rows = list(pending) + [(c, z)]
+    if len(rows) < m:
+        return rows, None
+    if m == 1:
+        e = c
+    else:
+        Cg = np.stack([r[0] for r in rows])
+        Zg = np.stack([r[1] for r in rows])
+        ez = np.exp(Zg - Zg.max(axis=0, keepdims=True))
+        e = ((ez / ez.sum(axis=0, keepdims=True)) * Cg).sum(axis=0)
+    g = pos // m
+    latent_pre = rms_norm(e[None], gamma, eps)[0]
+    kv = rope_last(latent_pre[None], np.array([g * m]), rope_base)[0]
+    return [], (g, latent_pre, kv)
+
+
 # ---------------------------------------------------------------------------
 # (b) Index K: [P1] section "indexer K 改由 main KV 投影": projected from the
 # main-KV entry BEFORE its RoPE, 512 -> 128, RoPE on its own last 64 dims, FP4

@@ -109,6 +109,24 @@ def test_score_workspace_too_small():
     assert n.value > 512 * 8
 
 
+@pytest.mark.parametrize("field,value,status", [
+    ("m", 3, "CSA2_ERR_INVALID_ARG"), ("state", None, "CSA2_ERR_INVALID_ARG"),
+    ("w_gate", None, "CSA2_ERR_INVALID_ARG"), ("D", 100, "CSA2_ERR_SHAPE"), ("dtype", 9, "CSA2_ERR_DTYPE"),
+    ("workspace_bytes", 1024, "CSA2_ERR_WORKSPACE"), ("workspace", 0x1008, "CSA2_ERR_WORKSPACE"),
+    ("pos", None, "CSA2_ERR_INVALID_ARG"),
+])
+def test_compress_step_validation(field, value, status):
+    a = K.CompressStepArgs(dtype=1, B=4, D=256, m=2, N_cap=100, eps=1e-6, rope_base=1e4, x=0x1000, pos=0x1000,
+                           w_kv=0x1000, w_gate=0x1000, gamma=0x1000, w_ik=0x1000, state=0x1000, kv_cache=0x1000,
+                           ik_codes=0x1000, ik_scales=0x1000, workspace=0x1000, workspace_bytes=1 << 20)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_compress_step(None, C.byref(a), None)] == status
+    n = C.c_size_t()
+    a.workspace_bytes = 0
+    assert K.lib().csa2_workspace_size(K.OP_COMPRESS_STEP, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
+    assert n.value == a.B * 1024 * 4
+
+
 def test_workspace_must_be_16_byte_aligned():
     a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, q_idx=0x1000,
                         w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1008,

@@ -260,6 +260,32 @@ def test_attention_convex_hull_and_special_cases():
     assert np.allclose(o1b, np.repeat(swa[0][None], 4, 0))
 
 
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_compress_step_streams_the_prefill_compressor(m):
+    """Appending the tokens of a sequence one at a time (the partial-group state
+    carries a group's earlier tokens) yields the rows the whole-sequence
+    compressor computes: the same group softmax, norm and RoPE at the same entry
+    positions, reached by a different route (per-group vs batched)."""
+    r = rng(24 + m)
+    T, D = 8 * m, 48
+    x = r.standard_normal((T, D))
+    w_kv = r.standard_normal((512, D)) / math.sqrt(D)
+    w_gate = r.standard_normal((512, D)) / math.sqrt(D) if m > 1 else None
+    gamma = 1.0 + 0.1 * r.standard_normal(512)
+    lat, kv, ids = O.compress(x, w_kv, w_gate, gamma, m, 0)
+    pending, got = [], []
+    for t in range(T):
+        pending, ent = O.compress_step(pending, x[t], w_kv, w_gate, gamma, t, m)
+        if t % m == m - 1:
+            assert ent is not None and ent[0] == t // m and pending == []
+            got.append(ent)
+        else:
+            assert ent is None and len(pending) == t % m + 1
+    assert [g for g, _, _ in got] == list(ids)
+    assert np.allclose(np.stack([l for _, l, _ in got]), lat, rtol=1e-12, atol=1e-12)
+    assert np.allclose(np.stack([k for _, _, k in got]), kv, rtol=1e-12, atol=1e-12)
+
+
 def test_attention_sink_special_cases():
     """The sink logit (denominator only): a sink of -inf is the plain softmax; with
     q = 0 every row logit is 0, so o = sum(rows) / (R + exp(sink)) in closed form;
