@@ -7,7 +7,8 @@ one batch (B=1, L=8192, hidden 4096, m=2, 32x128 FP4 indexer heads, top-512, win
 128, 64 heads, bf16 in / fp32 accumulate).  A second record ("decode") times the
 batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries), and
 a third ("decode_hsi_1m") the 1M-context decode step with the HSI candidate pool
-(4 sequences x 524288 entries).
+(4 sequences x 524288 entries), and a fourth ("decode_append") the Full layer's
+decode append of one token per sequence.
 
 Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
@@ -235,6 +236,49 @@ class HsiDecodeBench:
         }
 
 
+# ------------------------------------------------------------ decode append
+
+class AppendBench:
+    """Full-layer decode append: one new token per sequence per step for 64
+    sequences (hidden 4096, m=2).  A step pair covers both kinds of step: the
+    group's first token (C and Z, then the running pool), and its last (C and Z,
+    pool, norm, RoPE, cache row, index-K row)."""
+
+    def __init__(self, torch, K, synth, B=64, D=4096, m=2, N_cap=131072):
+        self.t, self.K = torch, K
+        dev = "cuda"
+        self.B, self.D, self.m = B, D, m
+        bf = torch.bfloat16
+        self.x = [synth.gaussian((B, D), 1.0, 71, "x", l, bf, dev) for l in range(m)]
+        self.w_kv = synth.linear_weight(512, D, 71, "w_kv", 0, bf, dev)
+        self.w_gate = synth.linear_weight(512, D, 71, "w_gate", 0, bf, dev)
+        self.w_ik = synth.linear_weight(128, 512, 71, "w_ik", 0, bf, dev)
+        self.gamma = torch.ones(512, dtype=torch.float32, device=dev)
+        self.state = torch.zeros(B, 3, 512, dtype=torch.float32, device=dev)
+        self.kv = torch.zeros(B, N_cap, 512, dtype=bf, device=dev)
+        self.codes = torch.zeros(B, N_cap, 64, dtype=torch.uint8, device=dev)
+        self.scales = torch.zeros(B, N_cap, 4, dtype=torch.uint8, device=dev)
+        p0 = 2 * (N_cap // 2) - 2 * m
+        self.pos = [torch.full((B,), p0 + i, dtype=torch.int32, device=dev) for i in range(m)]
+        self.ws = torch.empty(B * 1024 * 4 * 4, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        K = self.K
+        for i in range(self.m):
+            if events is not None:
+                events[i].record()
+            K.csa2_compress_step(None, self.x[i], self.pos[i], self.w_kv, self.w_gate, self.gamma, self.w_ik,
+                                 self.state, self.kv, self.codes, self.scales, m=self.m, workspace=self.ws)
+        if events is not None:
+            events[self.m].record()
+
+    def bytes_per_step(self):
+        B, D = self.B, self.D
+        w = 2 * 512 * D * 2 + 128 * 512 * 2                    # W_kv, W_gate, W_ik (bf16)
+        return w + B * D * 2 + B * 3 * 512 * 4 * 2 + B * 1024 * 4 * 4 * 2   # x, state in/out, C/Z partials
+
+
 def time_steps(torch, bench, n_stages, steps, warmup):
     for _ in range(warmup):
         bench.step()
@@ -362,6 +406,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode record")
     ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
+    ap.add_argument("--no-append", action="store_true", help="skip the decode-append record")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches instead of a HIP graph replay of the step")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -476,6 +521,25 @@ def main():
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (hms * 1e-3), 4),
         }
         del hb
+        torch.cuda.empty_cache()
+    if not args.no_append:
+        log("decode append: building inputs")
+        ab = AppendBench(torch, K, synth)
+        n_app = max(args.steps, 20)
+        ams_eager, ast = time_steps(torch, ab, ab.m, n_app, args.warmup)
+        ams = time_graph(torch, ab, n_app, args.warmup) if args.graph else ams_eager
+        per_tok = ams / ab.m                      # one append call = one new token per sequence
+        gbs = ab.bytes_per_step() / (per_tok * 1e-3) / 1e9
+        out["decode_append"] = {
+            "workload": f"Full-layer decode append: {ab.B} sequences, hidden {ab.D}, m={ab.m}; one new token per "
+                        f"sequence per call (C/Z projection, running group pool, and at a group's last token the "
+                        f"cache row and its FP4 index-K row)",
+            "us_per_token_step": round(per_tok * 1e3, 2), "us_per_token_step_eager": round(ams_eager / ab.m * 1e3, 2),
+            "stages_us": {"group_first_token": round(ast[0] * 1e3, 2), "group_last_token": round(ast[1] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "kernel": "compress_step", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        }
+        del ab
         torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")

@@ -280,7 +280,7 @@ def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, i
     state [B, 3, 512] float32 (None iff m == 1).  Returns the workspace used."""
     B, D = x.shape
     if workspace is None and B > 0:
-        workspace = torch.empty(B * 1024 * 4, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(B * 1024 * 4 * 4, dtype=torch.uint8, device=x.device)
     a = CompressStepArgs(dtype=_dtype(x), B=B, D=D, m=m, N_cap=kv_cache.shape[1], eps=eps, rope_base=rope_base,
                          x=_ptr(x), pos=_ptr(pos), w_kv=_ptr(w_kv), w_gate=_ptr(w_gate), gamma=_ptr(gamma),
                          w_ik=_ptr(w_ik), state=_ptr(state), kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes),

@@ -100,7 +100,7 @@ csa2_status check_compress_step(const csa2_compress_step_args* a) {
   REQ(a->x && a->pos && a->w_kv && a->gamma && a->w_ik && a->kv_cache && a->ik_codes && a->ik_scales,
       CSA2_ERR_INVALID_ARG, "csa2_compress_step: NULL tensor");
   REQ(a->eps >= 0.f && a->rope_base > 0.f, CSA2_ERR_INVALID_ARG, "csa2_compress_step: bad eps/rope_base");
-  const size_t need = (size_t)a->B * 1024 * 4;
+  const size_t need = (size_t)a->B * 1024 * 4 * 4;   // C and Z partials of 4 K quarters
   REQ(a->B == 0 || (a->workspace != nullptr && a->workspace_bytes >= need), CSA2_ERR_WORKSPACE,
       "csa2_compress_step: workspace of %zu bytes needed (got %zu)", need, a->workspace_bytes);
   REQ(a->B == 0 || ((uintptr_t)a->workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
@@ -337,7 +337,7 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   }
   if (op == CSA2_OP_COMPRESS_STEP) {
     const csa2_compress_step_args* a = static_cast<const csa2_compress_step_args*>(args);
-    *bytes = a->B > 0 ? (size_t)a->B * 1024 * 4 : 0;
+    *bytes = a->B > 0 ? (size_t)a->B * 1024 * 4 * 4 : 0;
     return ok();
   }
   if (op == CSA2_OP_LAYER) {

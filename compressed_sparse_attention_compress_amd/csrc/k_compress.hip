@@ -399,10 +399,16 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
 
 // ---------------------------------------------------------------- decode append
 // One new token per sequence after the prefill.  Step 1 (compress_step_proj):
-// C and Z of every sequence's token into cz[b][n] (n < 512: C channel n, else Z
-// channel n - 512).  A workgroup computes 16 output columns for all sequences
+// partial C and Z of every sequence's token, cz[q][b][n] for K quarter q of the
+// hidden dims (n < 512: C channel n, else Z channel n - 512).  Workgroup
+// (column group, q) computes 16 output columns over quarter q for all sequences
 // with MFMA (sequences as the rows of 16-row tiles, 4 tiles per pass); its 4
-// waves take the 32-wide k-steps in turn and their partial sums meet in LDS.
+// waves split the quarter's 32-wide k-steps into contiguous runs (so a wave reads
+// long pieces of each weight row), issue the loads of eight k-steps before
+// their MFMAs, and their partial sums meet in LDS.  The weights are read once;
+// the four quarters give 4x more workgroups than column groups.
+constexpr int STEP_KQ = 4;   // K quarters (partial sums summed by compress_step_entry)
+constexpr int STEP_KB = 8;   // k-steps whose loads are in flight together
 template <typename T>
 __global__ __launch_bounds__(256) void compress_step_proj(const T* __restrict__ x, const T* __restrict__ w_kv,
                                                           const T* __restrict__ w_gate, float* __restrict__ cz,
@@ -412,19 +418,33 @@ __global__ __launch_bounds__(256) void compress_step_proj(const T* __restrict__ 
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = blockIdx.x * 16 + lr;
+  const int kq = blockIdx.y;
   const T* wrow = n < 512 ? w_kv + (size_t)n * D : w_gate + (size_t)(n - 512) * D;
   const int nks = D / 32;
+  const int q0 = kq * nks / STEP_KQ, q1 = (kq + 1) * nks / STEP_KQ;
+  const int ks0 = q0 + wave * (q1 - q0) / 4, ks1 = q0 + (wave + 1) * (q1 - q0) / 4;   // this wave's k-steps
+  float* czq = cz + (size_t)kq * B * 1024;
   for (int b0 = 0; b0 < B; b0 += 64) {
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = wave; ks < nks; ks += 4) {
-      const FragT wf = load_frag(wrow + ks * 32 + 8 * lg);
+    for (int kb = ks0; kb < ks1; kb += STEP_KB) {   // k-steps kb .. kb + STEP_KB - 1
+      FragT wf[STEP_KB], xf[STEP_KB][4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int seq = min(b0 + t * 16 + lr, B - 1);   // rows past B repeat the last token (discarded)
-        const FragT xf = load_frag(x + (size_t)seq * D + ks * 32 + 8 * lg);
-        acc[t] = mma16(xf, wf, acc[t]);
+      for (int u = 0; u < STEP_KB; ++u) {
+        const int ks = min(kb + u, ks1 - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int seq = min(b0 + t * 16 + lr, B - 1);   // rows past B repeat the last token (discarded)
+          xf[u][t] = load_frag(x + (size_t)seq * D + ks * 32 + 8 * lg);
+        }
+        wf[u] = load_frag(wrow + ks * 32 + 8 * lg);
+      }
+#pragma unroll
+      for (int u = 0; u < STEP_KB; ++u) {
+        if (kb + u >= ks1) break;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = mma16(xf[u][t], wf[u], acc[t]);
       }
     }
     if (wave > 0) {
@@ -439,7 +459,7 @@ __global__ __launch_bounds__(256) void compress_step_proj(const T* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int seq = b0 + t * 16 + 4 * lg + i;   // accumulator row 4*lg+i, column lr
-          if (seq < B) cz[(size_t)seq * 1024 + n] = v[i];
+          if (seq < B) czq[(size_t)seq * 1024 + n] = v[i];
         }
       }
     }
@@ -464,28 +484,50 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
                                                            const float* __restrict__ gamma, const T* __restrict__ w_ik,
                                                            float* __restrict__ state, T* __restrict__ kv_cache,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                           float* __restrict__ latent_pre, int m, int N_cap, float eps,
-                                                           double base) {
+                                                           float* __restrict__ latent_pre, int B, int m, int N_cap,
+                                                           float eps, double base) {
   typedef typename Frag<T>::type FragT;
   __shared__ float lat_s[512];
   __shared__ float red[4];
+  __shared__ float2 rot[32];   // cos, sin of the 32 rotary pairs at position g*m (latent and index K alike)
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pos = pos_arr[b];
   if (pos < 0) return;
   const int gi = pos % m, g = pos / m;
-  const float* czb = cz + (size_t)b * 1024;
+  const bool closes = gi == m - 1 && g < N_cap;   // this token completes a group whose row is stored
+  // a closing token needs the index-K weights: their loads start now, under the pool and norm
+  const int o = tid >> 1, h = tid & 1;
+  constexpr int NPF = sizeof(T) == 2 ? 32 : 16;   // fragments of the 256 weights per load round
+  const T* wr = w_ik + (size_t)o * 512 + h * 256;
+  FragT wf[NPF];
+  if (closes) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) wf[u] = load_frag(wr + 8 * u);
+    if (tid < 32) {
+      float c, s;
+      rope_cos_sin((int64_t)g * m, tid, 64, base, c, s);
+      rot[tid] = make_float2(c, s);
+    }
+  }
+  // C and Z of the token: the sum of the projection's K-quarter partials
+  auto cz_at = [&](int col) -> float {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < STEP_KQ; ++q) v += cz[((size_t)q * B + b) * 1024 + col];
+    return v;
+  };
   float e[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int ch = tid + 256 * j;
-    const float c = czb[ch];
+    const float c = cz_at(ch);
     if (m == 1) {
       e[j] = c;
       continue;
     }
     float* st = state + (size_t)b * 1536;
-    const float z = czb[512 + ch];
+    const float z = cz_at(512 + ch);
     float zm, den, num;
     if (gi == 0) {
       zm = z;
@@ -505,7 +547,7 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
     }
     e[j] = num / den;
   }
-  if (gi < m - 1 || g >= N_cap) return;   // the group goes on (or its row is outside the cache)
+  if (!closes) return;   // the group goes on (or its row is outside the cache)
 
   float ss = e[0] * e[0] + e[1] * e[1];
   ss = wave_sum_xor(ss, 63);
@@ -525,9 +567,8 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
     const float other = __shfl_xor(v[1], 1, 64);
     const int ch = tid + 256;
     if (ch >= 448) {
-      float c, s;
-      rope_cos_sin((int64_t)g * m, (ch - 448) >> 1, 64, base, c, s);
-      v[1] = (ch & 1) ? (other * s + v[1] * c) : (v[1] * c - other * s);
+      const float2 cs = rot[(ch - 448) >> 1];
+      v[1] = (ch & 1) ? (other * cs.y + v[1] * cs.x) : (v[1] * cs.x - other * cs.y);
     }
   }
   T* kvrow = kv_cache + ((size_t)b * N_cap + g) * 512;
@@ -535,23 +576,26 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
   kvrow[tid + 256] = from_f32<T>(v[1]);
   __syncthreads();   // lat_s complete
 
-  const int o = tid >> 1, h = tid & 1;
-  const T* wr = w_ik + (size_t)o * 512 + h * 256;
   const float* lh = lat_s + h * 256;
   float acc = 0.f;
-  for (int d = 0; d < 256; d += 8) {
-    const FragT wf = load_frag(wr + d);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(lh[d + i], frag_elem(wf, i), acc);
+  for (int r = 0; r < 32 / NPF; ++r) {
+    if (r > 0) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) wf[u] = load_frag(wr + 8 * (r * NPF + u));
+    }
+#pragma unroll
+    for (int u = 0; u < NPF; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(lh[8 * (r * NPF + u) + i], frag_elem(wf[u], i), acc);
   }
   float u = acc + __shfl_xor(acc, 1, 64);
   {
     // RoPE pair (64 + 2p, 65 + 2p) = outputs o, o ^ 1 = threads tid, tid ^ 2
     const float uo = __shfl_xor(u, 2, 64);
     if (o >= 64) {
-      float c, s;
-      rope_cos_sin((int64_t)g * m, (o - 64) >> 1, 64, base, c, s);
-      u = (o & 1) ? (uo * s + u * c) : (u * c - uo * s);
+      const float2 cs = rot[(o - 64) >> 1];
+      u = (o & 1) ? (uo * cs.y + u * cs.x) : (u * cs.x - uo * cs.y);
     }
   }
   const float amax = wave_max_xor(fabsf(u), 63);   // block `wave` = outputs 32*wave .. +31
@@ -580,19 +624,19 @@ hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, co
                                 uint8_t* scales, float* latent_pre, float* cz, int B, int D, int m, int N_cap,
                                 float eps, float rope_base, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  const dim3 g1((m > 1 ? 1024 : 512) / 16), g2(B), blk(256);
+  const dim3 g1((m > 1 ? 1024 : 512) / 16, STEP_KQ), g2(B), blk(256);
   if (dtype == 1) {
     hipLaunchKernelGGL((compress_step_proj<bf16>), g1, blk, 0, stream, static_cast<const bf16*>(x),
                        static_cast<const bf16*>(w_kv), static_cast<const bf16*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<bf16>), g2, blk, 0, stream, cz, pos, gamma,
                        static_cast<const bf16*>(w_ik), state, static_cast<bf16*>(kv_cache), codes, scales,
-                       latent_pre, m, N_cap, eps, (double)rope_base);
+                       latent_pre, B, m, N_cap, eps, (double)rope_base);
   } else {
     hipLaunchKernelGGL((compress_step_proj<float>), g1, blk, 0, stream, static_cast<const float*>(x),
                        static_cast<const float*>(w_kv), static_cast<const float*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<float>), g2, blk, 0, stream, cz, pos, gamma,
                        static_cast<const float*>(w_ik), state, static_cast<float*>(kv_cache), codes, scales,
-                       latent_pre, m, N_cap, eps, (double)rope_base);
+                       latent_pre, B, m, N_cap, eps, (double)rope_base);
   }
   return hipGetLastError();
 }

@@ -178,8 +178,8 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
  *   kv_cache [B, N_cap, 512] dtype out   row pos/m, written at a group's last token
  *   ik_codes [B, N_cap, 64], ik_scales [B, N_cap, 4] uint8 out: the same row
  *   latent_pre [B, 512] float32 out      that entry's latent before RoPE (NULL: not written)
- *   workspace  csa2_workspace_size(CSA2_OP_COMPRESS_STEP) bytes (B * 1024 * 4),
- *              16-byte aligned
+ *   workspace  csa2_workspace_size(CSA2_OP_COMPRESS_STEP) bytes (B * 16384: C and
+ *              Z partial sums of 4 quarters of the hidden dims), 16-byte aligned
  * Rows pos/m >= N_cap are not written.  The runtime slots are not changed (after
  * the layer's prefill they already point at these caches; consumers take the
  * visible range from q_pos).                                                 */

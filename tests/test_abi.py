@@ -124,7 +124,7 @@ def test_compress_step_validation(field, value, status):
     n = C.c_size_t()
     a.workspace_bytes = 0
     assert K.lib().csa2_workspace_size(K.OP_COMPRESS_STEP, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
-    assert n.value == a.B * 1024 * 4
+    assert n.value == a.B * 1024 * 4 * 4
 
 
 def test_workspace_must_be_16_byte_aligned():
