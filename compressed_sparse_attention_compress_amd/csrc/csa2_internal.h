@@ -48,7 +48,7 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
 struct AttnPlan {
   bool decode;      // few queries: workgroup per (query, split, head group)
   int n_splits;     // row splits per query (decode only)
-  size_t ws_bytes;  // float32 partials when n_splits > 1
+  size_t ws_bytes;  // split partials (bf16 rows, float32 log-sum-exp) when n_splits > 1
 };
 AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W);
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk,

@@ -25,8 +25,8 @@
 //   are dealt to the XCDs round-robin, latest tokens first.
 // attn_decode: one workgroup per (token, row split) for all heads (wave w owns
 //   heads 16w..16w+15), rows gathered once into a 4-stage ring of 32-row chunks
-//   with three chunks in flight.  Row splits, when used, write float32 partials
-//   (normalised output + log-sum-exp) that attn_combine merges.
+//   with three chunks in flight.  Row splits, when used, write partials (bf16
+//   normalised output, float32 log-sum-exp) that attn_combine merges.
 #include "csa2_internal.h"
 #include "device_common.h"
 #include "lds_dma.h"
@@ -69,9 +69,12 @@ __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 3) | ((r &
 // Row list of one query: valid selected ids (order kept), then window rows
 // encoded as -(j+1) for swa row j.  Returns the number of rows.  Needs a
 // __syncthreads() before use by other waves (done by the callers).
+// after_issue() runs once in every wave: in wave 0 right after the first 512
+// ids are requested (so loads it issues queue behind them), elsewhere at once.
+template <typename F>
 __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const int32_t* tk, int k, int N_cap, int p,
-                                             int pos0, int L_w, int W) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                             int pos0, int L_w, int W, F&& after_issue) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) {
     int cnt = 0;
     for (int j0 = 0; j0 < k; j0 += 512) {   // 8 loads per lane in flight, then the ballots
@@ -81,6 +84,7 @@ __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const i
         const int j = j0 + 64 * u + lane;
         g[u] = j < k ? tk[j] : -1;
       }
+      if (j0 == 0) after_issue();
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const bool ok = g[u] >= 0 && g[u] < N_cap;
@@ -91,6 +95,8 @@ __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const i
       }
     }
     if (lane == 0) *n_sel_s = cnt;
+  } else {
+    after_issue();
   }
   __syncthreads();
   const int n_sel = *n_sel_s;
@@ -460,7 +466,7 @@ template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
     const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink, float* __restrict__ part_o,
+    bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink, bf16* __restrict__ part_o,
     float* __restrict__ part_lse, int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
   constexpr int RPW = DRC / NW;   // gathers per wave per chunk
   __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
@@ -472,17 +478,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   const int bt = qi;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the query fragments are loaded first, so that they arrive while the row list is built
+  // the query fragments are requested right after the first row ids (in wave 0,
+  // which builds the row list), so they arrive while the list is built
   const int head = wave * 16 + lr;
   bf16x8 qf[16];
   const bf16* qrow = q + ((size_t)bt * H + head) * 512;
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    if (head < H) qf[ks] = load_frag(qrow + ks * 32 + 8 * lg);
-    else zero_frag(qf[ks]);
-  }
   const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
-                                   L_w, W);
+                                   L_w, W, [&]() {
+#pragma unroll
+                                     for (int ks = 0; ks < 16; ++ks) {
+                                       if (head < H) qf[ks] = load_frag(qrow + ks * 32 + 8 * lg);
+                                       else zero_frag(qf[ks]);
+                                     }
+                                   });
   const bf16* kvb = kv + (size_t)b * N_cap * 512;
   const bf16* swb = swa + (size_t)b * L_w * 512;
   f32x4 oacc[32];
@@ -605,29 +613,47 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   l_tot += __shfl_xor(l_tot, 32, 64);
   float lse2;
   const float inv = softmax_norm(m_run, l_tot, n_splits == 1 ? sink_log2(sink, head, H) : -INFINITY, lse2);
-  if (head < H) {
-    if (n_splits == 1) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  if (n_splits == 1) {
+    if (head < H) {
       bf16* orow = o + ((size_t)bt * H + head) * 512;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
-        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         bf16x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (bf16)(oacc[dt][i] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * lg) = v;
       }
       if (lse != nullptr && lg == 0) lse[(size_t)bt * H + head] = lse2 * 0.69314718055994531f;
-    } else {
-      float* prow = part_o + (((size_t)bt * n_splits + split) * H + head) * 512;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + 4 * lg) = oacc[dt] * inv;
-      if (lg == 0) part_lse[((size_t)bt * n_splits + split) * H + head] = lse2;
     }
+    return;
   }
+  // A split's partial: the heads' bf16 rows go through LDS (the ring is free once
+  // every wave has passed the barrier) so that the workgroup stores them as one
+  // contiguous run of H KB.  Staging stride 1040 B: the 8-byte writes of a
+  // half-wave (16 heads x 2 dim quads) then fall on 64 distinct banks.
+  constexpr int OST = 1040;
+  static_assert(OST * 16 * NW <= DNS * DRC * PRS, "staging fits in the ring");
+  __syncthreads();
+  unsigned char* srow = ring + (wave * 16 + lr) * OST + 8 * lg;
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(oacc[dt][i] * inv);
+    *reinterpret_cast<bf16x4*>(srow + dt * 32) = v;
+  }
+  const size_t prow0 = ((size_t)bt * n_splits + split) * H;
+  if (head < H && lg == 0) part_lse[prow0 + head] = lse2;
+  __syncthreads();
+  const int nh = H < 16 * NW ? H : 16 * NW;
+  uint4* pdst = reinterpret_cast<uint4*>(part_o + prow0 * 512);
+  for (int u = threadIdx.x; u < nh * 64; u += 64 * NW)
+    pdst[u] = *reinterpret_cast<const uint4*>(ring + (u >> 6) * OST + (u & 63) * 16);
 }
 
 // Merge of row-split partials: one thread per (query, head, 8 dims).
-__global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_combine_bf16(const bf16* __restrict__ part_o,
                                                          const float* __restrict__ part_lse, bf16* __restrict__ o,
                                                          float* __restrict__ lse, const float* __restrict__ sink, int Q,
                                                          int H, int n_splits) {
@@ -639,7 +665,7 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict
   const int h = (int)(qh % H);
   const long long qi = qh / H;
   const float* ls_q = part_lse + qi * n_splits * H + h;                    // split s at s * H
-  const float* po_q = part_o + (qi * n_splits * H + h) * 512 + d0;         // split s at s * H * 512
+  const bf16* po_q = part_o + (qi * n_splits * H + h) * 512 + d0;          // split s at s * H * 512
   const float s2 = sink_log2(sink, h, H);   // the head's sink logit, counted once here
   float mx = s2;
 #pragma unroll 8
@@ -647,31 +673,30 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const float* __restrict
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, den = 0.f;
   // four splits' partials in flight at a time (an empty split's row is read but
   // not used: its log-sum-exp is -inf)
-  auto add = [&](float ls, const float4& a0, const float4& a1) {
+  auto add = [&](float ls, const uint4& a) {   // a: 8 bf16 dims
     if (ls == -INFINITY) return;
     const float wgt = exp2f(ls - mx);
     den += wgt;
-    acc[0] += wgt * a0.x; acc[1] += wgt * a0.y; acc[2] += wgt * a0.z; acc[3] += wgt * a0.w;
-    acc[4] += wgt * a1.x; acc[5] += wgt * a1.y; acc[6] += wgt * a1.z; acc[7] += wgt * a1.w;
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wgt * __uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += wgt * __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   };
   int s = 0;
   for (; s + 4 <= n_splits; s += 4) {
     float ls[4];
-    float4 a0[4], a1[4];
+    uint4 a[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ls[u] = ls_q[(size_t)(s + u) * H];
-      const float4* pr = reinterpret_cast<const float4*>(po_q + (size_t)(s + u) * H * 512);
-      a0[u] = pr[0];
-      a1[u] = pr[1];
+      a[u] = *reinterpret_cast<const uint4*>(po_q + (size_t)(s + u) * H * 512);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add(ls[u], a0[u], a1[u]);
+    for (int u = 0; u < 4; ++u) add(ls[u], a[u]);
   }
-  for (; s < n_splits; ++s) {
-    const float4* pr = reinterpret_cast<const float4*>(po_q + (size_t)s * H * 512);
-    add(ls_q[(size_t)s * H], pr[0], pr[1]);
-  }
+  for (; s < n_splits; ++s) add(ls_q[(size_t)s * H], *reinterpret_cast<const uint4*>(po_q + (size_t)s * H * 512));
   if (s2 != -INFINITY) den += exp2f(s2 - mx);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   bf16* orow = o + (qi * H + h) * 512 + d0;
@@ -701,7 +726,7 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
-                                   L_w, W);
+                                   L_w, W, []() {});
   const float* kvb = kv + (size_t)b * N_cap * 512;
   const float* swb = swa + (size_t)b * L_w * 512;
   const int head = wave * 16 + lr;
@@ -782,15 +807,16 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W) {
   p.n_splits = 1;
   if (p.decode) {
     // A workgroup per (query, row split) keeps three 32-row chunks in flight; the
-    // splits give the GPU about 256 workgroups (one per CU) and cost a float32
-    // partial per query, split and head, merged by attn_combine.
+    // splits give the GPU about 256 workgroups (one per CU) and cost a partial
+    // (512 bf16 + a float32 log-sum-exp) per query, split and head, merged by
+    // attn_combine.
     const int max_chunks = (k + W + DRC - 1) / DRC;
     int ns = (int)((256 + Q - 1) / Q);
     if (ns > max_chunks) ns = max_chunks;
     if (ns < 1) ns = 1;
     p.n_splits = ns;
   }
-  p.ws_bytes = (p.decode && p.n_splits > 1) ? (size_t)Q * p.n_splits * H * (512 + 1) * 4 + 256 : 0;
+  p.ws_bytes = (p.decode && p.n_splits > 1) ? (size_t)Q * p.n_splits * H * (512 * 2 + 4) + 256 : 0;
   return p;
 }
 
@@ -825,8 +851,8 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   }
   const int Q = B * T;
   const int groups = Q * p.n_splits;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = part_o + (size_t)Q * p.n_splits * H * 512;
+  bf16* part_o = static_cast<bf16*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(part_o + (size_t)Q * p.n_splits * H * 512);
   if (H > 32)
     hipLaunchKernelGGL(attn_decode_bf16<4>, dim3(groups), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
                        lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
