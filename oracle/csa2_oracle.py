@@ -22,6 +22,8 @@ reason in the design notes of the repository):
     before p, i.e. g < floor((p+1)/m);
   * RoPE uses interleaved pairs (2i, 2i+1) of the rotated slice with
     theta_i = base^(-2i/n_rope);                          -- parity unpinned (convention)
+  * FP4 main KV (optional storage of the cache rows) uses the same rule with one
+    scale per 16 dims (288 B per entry);
   * FP4 = E2M1 codes, one E4M3FN scale per 32 dims, scale = RNE(amax/6), codes =
     RNE(u/scale) saturating at 6, sign kept (a negative value rounding to zero is
     code 0x8), even dimension in the low nibble;          -- parity unpinned (convention)
@@ -44,6 +46,8 @@ LATENT_DIM = 512  # [P1] section on the KV size: one 512-d latent, K and V are t
 ROPE_DIMS = 64    # [P1] compressor section: RoPE on the last 64 dims
 INDEX_DIM = 128   # [P1] indexer-K section: W^IK is 512 x 128
 FP4_BLOCK = 32    # [P1] indexer-K section: FP4 with one scale per 32 dims
+KV_FP4_BLOCK = 16  # [P3] section six: a main-KV entry is 288 B = 256 B of E2M1 codes for
+                   # 512 dims + 32 E4M3 scale bytes, i.e. one scale per 16 dims
 
 # ---------------------------------------------------------------------------
 # FP4 (E2M1) and FP8 (E4M3FN) codecs.  The formats themselves come from the OCP
@@ -110,20 +114,21 @@ def e4m3_encode_nonneg(v: np.ndarray) -> np.ndarray:
     return idx.astype(np.uint8)
 
 
-def fp4_pack(u: np.ndarray):
-    """Quantise rows of 128 values to FP4 index-K storage.
+def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
+    """Quantise rows of 128 values to FP4 index-K storage (``block`` = 32), or
+    rows of 512 values to FP4 main-KV storage (``block`` = 16, see kv_fp4_pack).
 
     [P1] indexer-K section: FP4, one scale per 32 dims; [P3] section six: 68 B per
     entry.  Per 32-dim block: amax in float32, sigma = amax / 6 as a float32 division,
     scale byte = E4M3(sigma), s = its value; code_i = E2M1(u_i / s) (float32
     division), or 0 for the whole block when s == 0.  Code of dim 2j goes to the low
-    nibble of byte j.  Returns (codes uint8 [rows, 64], scales uint8 [rows, 4]).
+    nibble of byte j.  Returns (codes uint8 [rows, d/2], scales uint8 [rows, d/block]).
     """
     u = np.asarray(u, dtype=np.float32)
     rows, d = u.shape
-    assert d % FP4_BLOCK == 0
-    nb = d // FP4_BLOCK
-    blocks = u.reshape(rows, nb, FP4_BLOCK)
+    assert d % block == 0
+    nb = d // block
+    blocks = u.reshape(rows, nb, block)
     amax = np.max(np.abs(blocks), axis=2).astype(np.float32)
     sigma = (amax / np.float32(6.0)).astype(np.float32)
     sbytes = e4m3_encode_nonneg(sigma)
@@ -136,8 +141,9 @@ def fp4_pack(u: np.ndarray):
     return packed, sbytes.reshape(rows, nb)
 
 
-def fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Dequantise index-K storage: value(code) * value(scale), float64 [rows, 128]."""
+def fp4_unpack(codes: np.ndarray, scales: np.ndarray, block: int = FP4_BLOCK) -> np.ndarray:
+    """Dequantise FP4 storage: value(code) * value(scale of its block), float64
+    [rows, 2 * codes.shape[1]]."""
     codes = np.asarray(codes, dtype=np.uint8)
     rows = codes.shape[0]
     lo = codes & 0x0F
@@ -147,7 +153,26 @@ def fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     c[:, 1::2] = hi
     vals = e2m1_decode(c)
     s = e4m3_decode(np.asarray(scales))
-    return vals * np.repeat(s, FP4_BLOCK, axis=1)
+    return vals * np.repeat(s, block, axis=1)
+
+
+def kv_fp4_pack(rows: np.ndarray):
+    """Quantise 512-d main-KV rows (the compressor's post-RoPE latents) to FP4.
+
+    [P3] section seven, FP4 main KV: E2M1 data, one E4M3 scale shared by each group
+    of channels, dequantised to a wider type before attention; [P3] section six: 288 B
+    per entry, which fixes the group at 16 channels (256 B of codes + 32 scale bytes).
+    Same per-block rule as the index-K codec.  Returns (codes uint8 [rows, 256],
+    scales uint8 [rows, 32]).
+    """
+    rows = np.asarray(rows, dtype=np.float32)
+    assert rows.shape[1] == LATENT_DIM
+    return fp4_pack(rows, KV_FP4_BLOCK)
+
+
+def kv_fp4_unpack(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise FP4 main-KV storage to float64 [rows, 512] (attention reads these)."""
+    return fp4_unpack(codes, scales, KV_FP4_BLOCK)
 
 
 # ---------------------------------------------------------------------------
@@ -462,6 +487,7 @@ class LayerConfig:
     hsi_s: int = 64
     hsi_nb: int = 256
     scale: Optional[float] = None
+    kv_fp4: bool = False   # Full: store the main KV as FP4 (attention reads it dequantised)
 
 
 def _score_and_select(rt: Runtime, cfg: LayerConfig, inp: LayerInputs, codes, scales):
@@ -494,6 +520,10 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
             latent_pre, kv, ids = compress(inp.x[b], cfg.w_kv, cfg.w_gate, cfg.gamma, cfg.m,
                                            inp.start_pos, cfg.eps, cfg.rope_base)
             _, codes, scales = index_k(latent_pre, cfg.w_ik, ids * cfg.m, cfg.rope_base)
+            if cfg.kv_fp4:
+                # [P3] section seven: the stored main KV is FP4; attention sees its
+                # dequantised values
+                kv = kv_fp4_unpack(*kv_fp4_pack(kv.astype(np.float32)))
             kvs.append(kv), cs.append(codes), ss.append(scales), lat.append(latent_pre)
         rt.compress_kv = np.stack(kvs)
         rt.index_k = (np.stack(cs), np.stack(ss))

@@ -155,3 +155,69 @@ def test_fp4_pack_is_elementwise_brute_force():
                 byte = codes[r, 16 * b + i // 2]
                 got = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
                 assert got == c, (r, b, i, blk[i], got, c)
+
+
+# ---- FP4 main KV: same per-block rule, one scale per 16 of the 512 latent dims
+
+def test_kv_fp4_entry_size_matches_page():
+    facts = json.load(open(os.path.join(GOLD, "page_facts.json")))
+    rows = np.random.default_rng(6).standard_normal((3, 512)).astype(np.float32)
+    codes, scales = O.kv_fp4_pack(rows)
+    assert codes.shape == (3, 256) and scales.shape == (3, 32)
+    assert codes.shape[1] + scales.shape[1] == facts["main_kv_entry_bytes"]["value"]
+    assert facts["main_kv_entry_bytes"]["value"] + facts["index_k_entry_bytes"]["value"] == facts["entry_bytes"]["value"]
+    enc = facts["encoder_bytes_per_token"]
+    assert enc["layers"] * facts["entry_bytes"]["value"] / enc["m"] == enc["value"]
+
+
+def test_kv_fp4_exact_grid_roundtrip():
+    # Rows built on the FP4 grid: per 16-dim block a scale byte and 16 codes, one of
+    # them of magnitude 6 (so amax / 6 is exactly that scale).  Encoding must give
+    # back exactly those bytes; any slip in block size, nibble order or either
+    # rounding rule breaks it.
+    rng = np.random.default_rng(7)
+    n = 64
+    sb = rng.integers(1, 0x7F, (n, 32)).astype(np.uint8)
+    c = rng.integers(0, 16, (n, 512)).astype(np.uint8)
+    c[c == 8] = 0                                   # -0 and +0 decode alike; keep +0
+    c.reshape(n, 32, 16)[:, :, rng.integers(0, 16)] = 0x7 | (8 * rng.integers(0, 2))
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    val = np.where(c & 8, -1.0, 1.0) * mag[c & 7]
+    s = O.e4m3_decode(sb)
+    rows = (val * np.repeat(s, 16, axis=1)).astype(np.float32)
+    assert np.all(rows.astype(np.float64) == val * np.repeat(s, 16, axis=1))   # exact in float32
+    codes, scales = O.kv_fp4_pack(rows)
+    assert np.array_equal(scales, sb)
+    assert np.array_equal(codes, (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8))
+    assert np.array_equal(O.kv_fp4_unpack(codes, scales), rows.astype(np.float64))
+
+
+def test_kv_fp4_blocks_are_16_dims_and_local():
+    rng = np.random.default_rng(8)
+    rows = rng.standard_normal((4, 512)).astype(np.float32)
+    c0, s0 = O.kv_fp4_pack(rows)
+    for d in (0, 15, 16, 250, 511):
+        r = rows.copy()
+        r[1, d] = 40.0                               # new block maximum
+        c1, s1 = O.kv_fp4_pack(r)
+        b = d // 16
+        changed = np.nonzero(s1[1] != s0[1])[0].tolist()
+        assert changed == [b]
+        keep = np.ones(256, dtype=bool)
+        keep[8 * b: 8 * b + 8] = False
+        assert np.array_equal(c1[1, keep], c0[1, keep])
+        assert np.array_equal(np.delete(s1, 1, axis=0), np.delete(s0, 1, axis=0))
+
+
+def test_kv_fp4_roundtrip_error_bound():
+    rng = np.random.default_rng(9)
+    u = (rng.standard_normal((200, 512)) * np.exp(rng.uniform(-6, 4, (200, 1)))).astype(np.float32)
+    codes, scales = O.kv_fp4_pack(u)
+    back = O.kv_fp4_unpack(codes, scales)
+    s = np.repeat(O.e4m3_decode(scales), 16, axis=1)
+    amax = np.repeat(np.abs(u.reshape(200, 32, 16)).max(axis=2), 16, axis=1)
+    err = np.abs(back - u.astype(np.float64))
+    assert np.all(err <= s + np.maximum(0.0, amax - 6 * s) + 1e-12)
+    # a finer block never has a larger scale than the 32-dim block around it
+    _, s32 = O.fp4_pack(u, 32)
+    assert np.all(O.e4m3_decode(scales).reshape(200, 16, 2).max(axis=2) == O.e4m3_decode(s32).reshape(200, 16))
