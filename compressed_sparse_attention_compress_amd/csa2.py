@@ -22,6 +22,7 @@ FULL, REINDEX, REUSE = 0, 1, 2
 HSI_NONE, HSI_BUILD, HSI_USE = 0, 1, 2
 SLOT_COMPRESS_KV, SLOT_INDEX_K, SLOT_TOPK_IDXS, SLOT_CANDIDATES = 0, 1, 2, 3
 OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER, OP_COMPRESS_STEP = 0, 1, 2, 3
+KV_DENSE, KV_FP4 = 0, 1
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_DTYPE",
           4: "CSA2_ERR_SLOT_EMPTY", 5: "CSA2_ERR_SLOT_MISMATCH", 6: "CSA2_ERR_WORKSPACE",
@@ -42,14 +43,16 @@ i32 = C.c_int32
 class CompressArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("D", i32), ("m", i32), ("start_pos", i32),
                 ("N_cap", i32), ("eps", C.c_float), ("rope_base", C.c_float), ("x", vp), ("w_kv", vp),
-                ("w_gate", vp), ("gamma", vp), ("latent_pre", vp), ("kv_cache", vp)]
+                ("w_gate", vp), ("gamma", vp), ("latent_pre", vp), ("kv_cache", vp), ("kv_fmt", i32),
+                ("kv_scales", vp)]
 
 
 class CompressStepArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("D", i32), ("m", i32), ("N_cap", i32), ("eps", C.c_float),
                 ("rope_base", C.c_float), ("x", vp), ("pos", vp), ("w_kv", vp), ("w_gate", vp), ("gamma", vp),
                 ("w_ik", vp), ("state", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
-                ("latent_pre", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("latent_pre", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("kv_fmt", i32),
+                ("kv_scales", vp)]
 
 
 class IndexKArgs(C.Structure):
@@ -68,13 +71,13 @@ class SparseAttnArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H", i32), ("N_cap", i32), ("k", i32), ("L_w", i32),
                 ("W", i32), ("scale", C.c_float), ("q", vp), ("kv", vp), ("topk", vp), ("swa_kv", vp),
                 ("swa_pos0", vp), ("q_pos", vp), ("o", vp), ("lse", vp), ("workspace", vp),
-                ("workspace_bytes", C.c_size_t), ("sink", vp)]
+                ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_fmt", i32), ("kv_scales", vp)]
 
 
 class LayerCfg(C.Structure):
     _fields_ = [("mode", i32), ("dtype", i32), ("m", i32), ("k", i32), ("W", i32), ("H_I", i32), ("H", i32),
                 ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("rope_base", C.c_float), ("eps", C.c_float),
-                ("scale", C.c_float)]
+                ("scale", C.c_float), ("kv_fmt", i32)]
 
 
 class LayerIO(C.Structure):
@@ -83,12 +86,12 @@ class LayerIO(C.Structure):
                 ("latent_pre", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
                 ("q_idx", vp), ("w", vp), ("topk", vp), ("candidates", vp),
                 ("q_pos", vp), ("q", vp), ("swa_kv", vp), ("L_w", i32), ("swa_pos0", vp),
-                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("sink", vp)]
+                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_scales", vp)]
 
 
 class SlotInfo(C.Structure):
     _fields_ = [("filled", i32), ("generation", C.c_uint64), ("ptr", vp), ("ptr2", vp), ("dtype", i32),
-                ("B", i32), ("rows", i32), ("cols", i32), ("extra", i32)]
+                ("B", i32), ("rows", i32), ("cols", i32), ("extra", i32), ("kv_fmt", i32)]
 
 
 EXPORTS = {
@@ -104,6 +107,7 @@ EXPORTS = {
     "csa2_layer_forward": ([vp, C.POINTER(LayerCfg), C.POINTER(LayerIO), vp], i32),
     "csa2_workspace_size": ([i32, vp, C.POINTER(LayerCfg), C.POINTER(C.c_size_t)], i32),
     "csa2_fp4_pack": ([vp, C.c_int64, vp, vp, vp], i32),
+    "csa2_kv_fp4_pack": ([vp, C.c_int64, vp, vp, vp], i32),
     "csa2_status_string": ([i32], C.c_char_p),
     "csa2_last_error": ([], C.c_char_p),
     "csa2_version": ([], C.c_char_p),
@@ -188,11 +192,14 @@ def _rt(rt):
 
 
 def csa2_compress(rt, x, w_kv, w_gate, gamma, latent_pre, kv_cache, m: int, start_pos: int = 0,
-                  eps: float = 1e-6, rope_base: float = 10000.0, stream=None):
+                  eps: float = 1e-6, rope_base: float = 10000.0, stream=None, kv_scales=None):
+    """kv_scales given: FP4 main KV (kv_cache = uint8 codes [B, N_cap, 256], kv_scales
+    uint8 [B, N_cap, 32])."""
     B, T, D = x.shape
     a = CompressArgs(dtype=_dtype(x), B=B, T=T, D=D, m=m, start_pos=start_pos, N_cap=kv_cache.shape[1],
                      eps=eps, rope_base=rope_base, x=_ptr(x), w_kv=_ptr(w_kv), w_gate=_ptr(w_gate),
-                     gamma=_ptr(gamma), latent_pre=_ptr(latent_pre), kv_cache=_ptr(kv_cache))
+                     gamma=_ptr(gamma), latent_pre=_ptr(latent_pre), kv_cache=_ptr(kv_cache),
+                     kv_fmt=KV_DENSE if kv_scales is None else KV_FP4, kv_scales=_ptr(kv_scales))
     _check(lib().csa2_compress(_rt(rt), C.byref(a), _stream(stream)))
 
 
@@ -238,18 +245,19 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
 
 
 def sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: int, N_cap: int, scale: float = 0.0,
-                     lse=None, workspace=None, sink=None):
+                     lse=None, workspace=None, sink=None, kv_scales=None):
     B, T, H, _ = q.shape
     return SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, N_cap=N_cap, k=k, L_w=swa_kv.shape[1], W=W, scale=scale,
                           q=_ptr(q), kv=_ptr(kv), topk=_ptr(topk), swa_kv=_ptr(swa_kv), swa_pos0=_ptr(swa_pos0),
                           q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=_ptr(workspace),
                           workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
-                          sink=_ptr(sink))
+                          sink=_ptr(sink), kv_fmt=KV_DENSE if kv_scales is None else KV_FP4,
+                          kv_scales=_ptr(kv_scales))
 
 
-def sparse_attn_workspace_bytes(q, k: int, W: int) -> int:
+def sparse_attn_workspace_bytes(q, k: int, W: int, kv_fp4: bool = False, N_cap: int = 0) -> int:
     B, T, H, _ = q.shape
-    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, k=k, W=W)
+    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, k=k, W=W, N_cap=N_cap, kv_fmt=KV_FP4 if kv_fp4 else KV_DENSE)
     n = C.c_size_t()
     _check(lib().csa2_workspace_size(OP_SPARSE_ATTN, C.cast(C.byref(a), vp), None, C.byref(n)))
     return n.value
@@ -257,25 +265,37 @@ def sparse_attn_workspace_bytes(q, k: int, W: int) -> int:
 
 def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Optional[int] = None,
                      N_cap: Optional[int] = None, scale: float = 0.0, lse=None, workspace=None, stream=None,
-                     sink=None):
+                     sink=None, kv_scales=None):
     """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots; sink
-    [H] float32 per-head sink logits or None.  A workspace (row-split partials for
-    few-query calls) is allocated when needed and none is given."""
+    [H] float32 per-head sink logits or None; kv_scales given: kv is FP4 main KV
+    (uint8 codes [B, N_cap, 256], scales [B, N_cap, 32]).  A workspace (row-split
+    partials for few-query calls, or the dequantised cache for FP4 KV outside
+    them) is allocated when needed and none is given."""
     if k is None:
         k = topk.shape[-1]
+    fp4 = kv_scales is not None
     if N_cap is None:
-        N_cap = kv.shape[1] if kv is not None else 0
+        if kv is not None:
+            N_cap = kv.shape[1]
+        elif rt is not None:
+            N_cap = rt.slot(SLOT_COMPRESS_KV).rows
+        else:
+            N_cap = 0
+    if kv is None and rt is not None and rt.slot(SLOT_COMPRESS_KV).filled:
+        fp4 = rt.slot(SLOT_COMPRESS_KV).kv_fmt == KV_FP4
     if workspace is None:
-        nbytes = sparse_attn_workspace_bytes(q, k, W)
+        nbytes = sparse_attn_workspace_bytes(q, k, W, fp4, N_cap)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace, sink)
+    a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace, sink,
+                         kv_scales)
     _check(lib().csa2_sparse_attn(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
 
 def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, ik_codes, ik_scales, m: int,
-                       latent_pre=None, eps: float = 1e-6, rope_base: float = 10000.0, workspace=None, stream=None):
+                       latent_pre=None, eps: float = 1e-6, rope_base: float = 10000.0, workspace=None, stream=None,
+                       kv_scales=None):
     """Decode append: x [B, D] (one new token per sequence at positions pos [B]);
     state [B, 3, 512] float32 (None iff m == 1).  Returns the workspace used."""
     B, D = x.shape
@@ -285,7 +305,8 @@ def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, i
                          x=_ptr(x), pos=_ptr(pos), w_kv=_ptr(w_kv), w_gate=_ptr(w_gate), gamma=_ptr(gamma),
                          w_ik=_ptr(w_ik), state=_ptr(state), kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes),
                          ik_scales=_ptr(ik_scales), latent_pre=_ptr(latent_pre), workspace=_ptr(workspace),
-                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         kv_fmt=KV_DENSE if kv_scales is None else KV_FP4, kv_scales=_ptr(kv_scales))
     _check(lib().csa2_compress_step(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
@@ -295,16 +316,22 @@ def csa2_fp4_pack(rows, codes, scales, stream=None):
     _check(lib().csa2_fp4_pack(_ptr(rows), n, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
+def csa2_kv_fp4_pack(rows, codes, scales, stream=None):
+    """FP4 main-KV packing of float32 rows [n, 512] -> codes [n, 256], scales [n, 32]."""
+    n = rows.numel() // 512
+    _check(lib().csa2_kv_fp4_pack(_ptr(rows), n, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
 def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, hsi: int = HSI_NONE,
               hsi_s: int = 0, hsi_nb: int = 0, rope_base: float = 10000.0, eps: float = 1e-6,
-              scale: float = 0.0) -> LayerCfg:
+              scale: float = 0.0, kv_fmt: int = 0) -> LayerCfg:
     return LayerCfg(mode=mode, dtype=dtype, m=m, k=k, W=W, H_I=H_I, H=H, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb,
-                    rope_base=rope_base, eps=eps, scale=scale)
+                    rope_base=rope_base, eps=eps, scale=scale, kv_fmt=kv_fmt)
 
 
 def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,
              gamma=None, w_ik=None, latent_pre=None, kv_cache=None, ik_codes=None, ik_scales=None, q_idx=None,
-             w=None, topk=None, candidates=None, workspace=None, sink=None) -> LayerIO:
+             w=None, topk=None, candidates=None, workspace=None, sink=None, kv_scales=None) -> LayerIO:
     return LayerIO(B=B, T=T, D=D, start_pos=start_pos, N_cap=N_cap, x=_ptr(x), w_kv=_ptr(w_kv),
                    w_gate=_ptr(w_gate), gamma=_ptr(gamma), w_ik=_ptr(w_ik), latent_pre=_ptr(latent_pre),
                    kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes), ik_scales=_ptr(ik_scales),
@@ -312,7 +339,7 @@ def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=N
                    q=_ptr(q), swa_kv=_ptr(swa_kv), L_w=swa_kv.shape[1], swa_pos0=_ptr(swa_pos0), o=_ptr(o),
                    workspace=_ptr(workspace),
                    workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
-                   sink=_ptr(sink))
+                   sink=_ptr(sink), kv_scales=_ptr(kv_scales))
 
 
 def layer_workspace_bytes(cfg: LayerCfg, io: LayerIO) -> int:

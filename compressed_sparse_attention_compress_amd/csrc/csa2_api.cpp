@@ -23,7 +23,7 @@ struct csa2_runtime {
     uint64_t generation = 0;
     const void* ptr = nullptr;
     const void* ptr2 = nullptr;
-    int dtype = 0, B = 0, rows = 0, cols = 0, extra = 0;
+    int dtype = 0, B = 0, rows = 0, cols = 0, extra = 0, kv_fmt = 0;
   } slot[4];
 };
 
@@ -50,9 +50,10 @@ bool dtype_ok(int d) { return d == CSA2_F32 || d == CSA2_BF16; }
 hipStream_t st(csa2_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 void publish(csa2_runtime* rt, csa2_slot which, const void* p, const void* p2, int dtype, int B, int rows, int cols,
-             int extra) {
+             int extra, int kv_fmt = CSA2_KV_DENSE) {
   if (!rt) return;
   auto& s = rt->slot[which];
+  s.kv_fmt = kv_fmt;
   s.filled = 1;
   s.generation += 1;
   s.ptr = p;
@@ -82,6 +83,12 @@ csa2_status check_compress(const csa2_compress_args* a) {
   REQ((long long)a->start_pos / a->m + a->T / a->m <= a->N_cap, CSA2_ERR_SHAPE,
       "csa2_compress: cache too small (N_cap %d < %d)", a->N_cap, a->start_pos / a->m + a->T / a->m);
   REQ(a->x && a->w_kv && a->gamma && a->latent_pre && a->kv_cache, CSA2_ERR_INVALID_ARG, "csa2_compress: NULL tensor");
+  REQ(a->kv_fmt == CSA2_KV_DENSE || a->kv_fmt == CSA2_KV_FP4, CSA2_ERR_INVALID_ARG, "csa2_compress: bad kv_fmt %d",
+      a->kv_fmt);
+  REQ(a->kv_fmt != CSA2_KV_FP4 || a->kv_scales != nullptr, CSA2_ERR_INVALID_ARG,
+      "csa2_compress: FP4 main KV needs kv_scales");
+  REQ(a->kv_fmt != CSA2_KV_FP4 || ((uintptr_t)a->kv_cache & 15u) == 0, CSA2_ERR_INVALID_ARG,
+      "csa2_compress: FP4 codes must be 16-byte aligned");
   REQ(a->eps >= 0.f && a->rope_base > 0.f, CSA2_ERR_INVALID_ARG, "csa2_compress: bad eps/rope_base");
   return CSA2_OK;
 }
@@ -100,6 +107,10 @@ csa2_status check_compress_step(const csa2_compress_step_args* a) {
   REQ(a->x && a->pos && a->w_kv && a->gamma && a->w_ik && a->kv_cache && a->ik_codes && a->ik_scales,
       CSA2_ERR_INVALID_ARG, "csa2_compress_step: NULL tensor");
   REQ(a->eps >= 0.f && a->rope_base > 0.f, CSA2_ERR_INVALID_ARG, "csa2_compress_step: bad eps/rope_base");
+  REQ(a->kv_fmt == CSA2_KV_DENSE || a->kv_fmt == CSA2_KV_FP4, CSA2_ERR_INVALID_ARG,
+      "csa2_compress_step: bad kv_fmt %d", a->kv_fmt);
+  REQ(a->kv_fmt != CSA2_KV_FP4 || a->kv_scales != nullptr, CSA2_ERR_INVALID_ARG,
+      "csa2_compress_step: FP4 main KV needs kv_scales");
   const size_t need = (size_t)a->B * 1024 * 4 * 4;   // C and Z partials of 4 K quarters
   REQ(a->B == 0 || (a->workspace != nullptr && a->workspace_bytes >= need), CSA2_ERR_WORKSPACE,
       "csa2_compress_step: workspace of %zu bytes needed (got %zu)", need, a->workspace_bytes);
@@ -177,7 +188,15 @@ csa2_status resolve_attn(const csa2_runtime* rt, csa2_sparse_attn_args& a) {
     REQ(s.B == a.B && s.dtype == a.dtype, CSA2_ERR_SLOT_MISMATCH, "csa2_sparse_attn: compress_kv slot does not fit");
     a.kv = s.ptr;
     a.N_cap = s.rows;
+    a.kv_fmt = s.kv_fmt;
+    a.kv_scales = static_cast<const uint8_t*>(s.ptr2);
   }
+  REQ(a.kv_fmt == CSA2_KV_DENSE || a.kv_fmt == CSA2_KV_FP4, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: bad kv_fmt %d",
+      a.kv_fmt);
+  REQ(a.kv_fmt != CSA2_KV_FP4 || a.kv_scales != nullptr, CSA2_ERR_INVALID_ARG,
+      "csa2_sparse_attn: FP4 main KV needs kv_scales");
+  REQ(a.kv_fmt != CSA2_KV_FP4 || (((uintptr_t)a.kv & 15u) == 0 && ((uintptr_t)a.kv_scales & 3u) == 0),
+      CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: FP4 codes must be 16-byte and scales 4-byte aligned");
   if (a.topk == nullptr) {
     REQ(rt != nullptr, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: no topk given and no runtime");
     const auto& s = rt->slot[CSA2_SLOT_TOPK_IDXS];
@@ -251,17 +270,20 @@ csa2_status csa2_runtime_slot(const csa2_runtime* rt, csa2_slot slot, csa2_slot_
   out->rows = s.rows;
   out->cols = s.cols;
   out->extra = s.extra;
+  out->kv_fmt = s.kv_fmt;
   return ok();
 }
 
 csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_stream stream) {
   csa2_status s = check_compress(a);
   if (s != CSA2_OK) return s;
-  hipError_t e = csa2::launch_compress(a->dtype, a->x, a->w_kv, a->w_gate, a->gamma, a->latent_pre, a->kv_cache, a->B,
-                                       a->T, a->D, a->m, a->start_pos, a->N_cap, a->eps, a->rope_base, st(stream));
+  uint8_t* ksc = a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr;
+  hipError_t e = csa2::launch_compress(a->dtype, a->x, a->w_kv, a->w_gate, a->gamma, a->latent_pre, a->kv_cache, ksc,
+                                       a->B, a->T, a->D, a->m, a->start_pos, a->N_cap, a->eps, a->rope_base,
+                                       st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_compress launch");
-  publish(rt, CSA2_SLOT_COMPRESS_KV, a->kv_cache, nullptr, a->dtype, a->B, a->N_cap,
-          a->start_pos / a->m + a->T / a->m, a->m);
+  publish(rt, CSA2_SLOT_COMPRESS_KV, a->kv_cache, ksc, a->dtype, a->B, a->N_cap,
+          a->start_pos / a->m + a->T / a->m, a->m, a->kv_fmt);
   return ok();
 }
 
@@ -270,7 +292,8 @@ csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* 
   csa2_status s = check_compress_step(a);
   if (s != CSA2_OK) return s;
   hipError_t e = csa2::launch_compress_step(a->dtype, a->x, a->pos, a->w_kv, a->w_gate, a->gamma, a->w_ik, a->state,
-                                            a->kv_cache, a->ik_codes, a->ik_scales, a->latent_pre,
+                                            a->kv_cache, a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr,
+                                            a->ik_codes, a->ik_scales, a->latent_pre,
                                             static_cast<float*>(a->workspace), a->B, a->D, a->m, a->N_cap, a->eps,
                                             a->rope_base, st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_compress_step launch");
@@ -311,12 +334,14 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
   csa2_status s = resolve_attn(rt, a);
   if (s != CSA2_OK) return s;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / std::sqrt(512.0f);
-  const csa2::AttnPlan plan = csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W);
+  const csa2::AttnPlan plan =
+      csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W, a.kv_fmt == CSA2_KV_FP4, a.N_cap);
   REQ(plan.ws_bytes == 0 || (a.workspace != nullptr && a.workspace_bytes >= plan.ws_bytes), CSA2_ERR_WORKSPACE,
       "csa2_sparse_attn: workspace of %zu bytes needed (got %zu)", plan.ws_bytes, a.workspace_bytes);
   REQ(plan.ws_bytes == 0 || ((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
       "csa2_sparse_attn: workspace not 16-byte aligned");
-  hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse,
+  hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.kv_fmt == CSA2_KV_FP4 ? a.kv_scales : nullptr,
+                                          a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse,
                                           a.sink, a.B, a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan,
                                           st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_sparse_attn launch");
@@ -332,7 +357,8 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   }
   if (op == CSA2_OP_SPARSE_ATTN) {
     const csa2_sparse_attn_args* a = static_cast<const csa2_sparse_attn_args*>(args);
-    *bytes = csa2::plan_attn(a->dtype, a->B, a->T, a->H, a->k, a->W).ws_bytes;
+    // with kv NULL the slot decides the format; size for FP4 when the caller says so
+    *bytes = csa2::plan_attn(a->dtype, a->B, a->T, a->H, a->k, a->W, a->kv_fmt == CSA2_KV_FP4, a->N_cap).ws_bytes;
     return ok();
   }
   if (op == CSA2_OP_COMPRESS_STEP) {
@@ -343,7 +369,8 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   if (op == CSA2_OP_LAYER) {
     REQ(cfg, CSA2_ERR_INVALID_ARG, "csa2_workspace_size: layer op needs cfg");
     const csa2_layer_io* io = static_cast<const csa2_layer_io*>(args);
-    size_t need = csa2::plan_attn(cfg->dtype, io->B, io->T, cfg->H, cfg->k, cfg->W).ws_bytes;
+    size_t need =
+        csa2::plan_attn(cfg->dtype, io->B, io->T, cfg->H, cfg->k, cfg->W, cfg->kv_fmt == CSA2_KV_FP4, io->N_cap).ws_bytes;
     if (cfg->mode != CSA2_REUSE) {
       const int n_entries = io->N_cap;  // upper bound
       const int scan = cfg->hsi == CSA2_HSI_USE ? cfg->hsi_nb * cfg->hsi_s : n_entries;
@@ -368,6 +395,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     ca.dtype = cfg->dtype; ca.B = io->B; ca.T = io->T; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
     ca.N_cap = io->N_cap; ca.eps = cfg->eps; ca.rope_base = cfg->rope_base; ca.x = io->x; ca.w_kv = io->w_kv;
     ca.w_gate = io->w_gate; ca.gamma = io->gamma; ca.latent_pre = io->latent_pre; ca.kv_cache = io->kv_cache;
+    ca.kv_fmt = cfg->kv_fmt; ca.kv_scales = io->kv_scales;
     s = check_compress(&ca);
     if (s != CSA2_OK) return s;
     csa2_index_k_args ia{};
@@ -411,6 +439,8 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
   aa.o = io->o; aa.workspace = io->workspace; aa.workspace_bytes = io->workspace_bytes; aa.sink = io->sink;
   if (cfg->mode == CSA2_FULL) {
     aa.kv = io->kv_cache;
+    aa.kv_fmt = cfg->kv_fmt;
+    aa.kv_scales = io->kv_scales;
     aa.N_cap = io->N_cap;
     aa.topk = io->topk;
   } else if (cfg->mode == CSA2_REINDEX) {
@@ -424,6 +454,8 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
           CSA2_ERR_SLOT_MISMATCH, "csa2_layer_forward: compress_kv slot does not fit this layer");
       probe.kv = rt->slot[CSA2_SLOT_COMPRESS_KV].ptr;
       probe.N_cap = rt->slot[CSA2_SLOT_COMPRESS_KV].rows;
+      probe.kv_fmt = rt->slot[CSA2_SLOT_COMPRESS_KV].kv_fmt;
+      probe.kv_scales = static_cast<const uint8_t*>(rt->slot[CSA2_SLOT_COMPRESS_KV].ptr2);
     }
     if (probe.topk == nullptr) {
       const auto& ts = rt->slot[CSA2_SLOT_TOPK_IDXS];
@@ -441,6 +473,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     ca.dtype = cfg->dtype; ca.B = io->B; ca.T = io->T; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
     ca.N_cap = io->N_cap; ca.eps = cfg->eps; ca.rope_base = cfg->rope_base; ca.x = io->x; ca.w_kv = io->w_kv;
     ca.w_gate = io->w_gate; ca.gamma = io->gamma; ca.latent_pre = io->latent_pre; ca.kv_cache = io->kv_cache;
+    ca.kv_fmt = cfg->kv_fmt; ca.kv_scales = io->kv_scales;
     if ((s = csa2_compress(rt, &ca, stream)) != CSA2_OK) return s;
     csa2_index_k_args ia{};
     ia.dtype = cfg->dtype; ia.B = io->B; ia.N = io->T / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
@@ -452,6 +485,15 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     if ((s = csa2_score_topk(rt, &sa, stream)) != CSA2_OK) return s;
   }
   return csa2_sparse_attn(rt, &aa, stream);
+}
+
+csa2_status csa2_kv_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales, csa2_stream stream) {
+  REQ(n_rows >= 0, CSA2_ERR_SHAPE, "csa2_kv_fp4_pack: n_rows < 0");
+  REQ(n_rows == 0 || (rows && codes && scales), CSA2_ERR_INVALID_ARG, "csa2_kv_fp4_pack: NULL tensor");
+  REQ(n_rows == 0 || ((uintptr_t)rows & 15u) == 0, CSA2_ERR_INVALID_ARG, "csa2_kv_fp4_pack: rows not 16-byte aligned");
+  hipError_t e = csa2::launch_kv_fp4_pack(rows, n_rows, codes, scales, st(stream));
+  if (e != hipSuccess) return hip_status(e, "csa2_kv_fp4_pack launch");
+  return ok();
 }
 
 csa2_status csa2_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales, csa2_stream stream) {

@@ -9,8 +9,10 @@
 namespace csa2 {
 
 // ---- compressor (k_compress.hip)
+// kv_scales != nullptr: the cache is FP4 main KV (kv_cache = codes [B, N_cap, 256],
+// kv_scales = E4M3 scales [B, N_cap, 32]); otherwise rows of the dtype
 hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const void* w_gate,
-                           const float* gamma, float* latent_pre, void* kv_cache, int B, int T,
+                           const float* gamma, float* latent_pre, void* kv_cache, uint8_t* kv_scales, int B, int T,
                            int D, int m, int start_pos, int N_cap, float eps, float rope_base,
                            hipStream_t stream);
 
@@ -18,7 +20,7 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
 // the group pool / entry / index-K row per sequence
 hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv,
                                 const void* w_gate, const float* gamma, const void* w_ik, float* state,
-                                void* kv_cache, uint8_t* codes, uint8_t* scales, float* latent_pre,
+                                void* kv_cache, uint8_t* kv_scales, uint8_t* codes, uint8_t* scales, float* latent_pre,
                                 float* cz, int B, int D, int m, int N_cap, float eps, float rope_base,
                                 hipStream_t stream);
 
@@ -28,6 +30,12 @@ hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, 
                           float rope_base, hipStream_t stream);
 hipError_t launch_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream);
+// FP4 main KV: 512-d float32 rows -> codes [n, 256] + E4M3 scales [n, 32], and back
+// to dense rows of the dtype
+hipError_t launch_kv_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+hipError_t launch_kv_fp4_dequant(int dtype, const uint8_t* codes, const uint8_t* scales, int64_t n_rows, void* out,
+                                 hipStream_t stream);
 
 // ---- indexer score + top-k (k_score.hip)
 struct ScorePlan {
@@ -47,11 +55,14 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
 // ---- sparse attention (k_attn.hip)
 struct AttnPlan {
   bool decode;      // few queries: workgroup per (query, split, head group)
+  bool kv_fp4;      // main KV stored as FP4
   int n_splits;     // row splits per query (decode only)
-  size_t ws_bytes;  // split partials (bf16 rows, float32 log-sum-exp) when n_splits > 1
+  int n_fp4;        // decode with FP4 KV: the first n_fp4 splits take the selected rows, the rest the window
+  size_t ws_bytes;  // decode: split partials (bf16 rows, float32 log-sum-exp) when n_splits > 1;
+                    // FP4 KV outside decode: the dequantised cache rows [B, N_cap, 512]
 };
-AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W);
-hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk,
+AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap);
+hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const uint8_t* kv_scales, const int32_t* topk,
                               const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos,
                               void* o, float* lse, const float* sink, int B, int T, int H, int N_cap, int k,
                               int L_w, int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream);

@@ -92,6 +92,14 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x) {
   return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// Value of an E2M1 code as a float32: magnitude bits e1 e0 m give m/2 for e = 0
+// and 2^(e-1) (1 + m/2) otherwise; bit 3 is the sign.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t bits = (e == 0u) ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
 // Quantise one 32-value block held 2 values per lane by 16 lanes of a 16-lane
 // group: returns the scale byte (all 16 lanes) and the two codes of this lane.
 // `amax` must already be the maximum of |v| over the block.

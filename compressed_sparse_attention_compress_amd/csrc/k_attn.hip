@@ -455,6 +455,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_prefill_bf16(
 
 constexpr int DRC = 32;                 // rows per stage
 constexpr int DNS = 4;                  // stages: three in flight while one is used
+constexpr int RAW4 = DRC * 288;         // FP4 chunk: 32 x 256 B of codes, then 32 x 32 scale bytes
 
 // One workgroup per (query, row split); wave w owns heads 16w..16w+15, so each
 // row is fetched once per workgroup and read from LDS by every wave.  Stage s of
@@ -462,16 +463,27 @@ constexpr int DNS = 4;                  // stages: three in flight while one is 
 // c + 3 are issued right after the barrier that opens chunk c, into the stage
 // that chunk c - 1 used.  NW = 4, 2 or 1 waves (H > 32, > 16, <= 16); wave w
 // gathers rows w, w + NW, ... of each chunk.
-template <int NW>
+//
+// FP4 main KV (FP4 = true): the first n_fp4 splits of a query cover its selected
+// rows, the others its window rows (bf16, the ring as above).  A selected-row
+// chunk lands raw (288 B per row) in a 4-stage ring of 9 KiB stages; after the
+// barrier that opens it, every thread dequantises 64 dims of one row into a
+// single bf16 chunk buffer (same swizzled layout as a gathered bf16 chunk), and
+// a second barrier hands that buffer to the MFMA steps.  E2M1 x E4M3 values are
+// exact in bf16, so the MFMA inputs are exactly the dequantised cache.
+template <int NW, bool FP4>
 __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
-    const bf16* __restrict__ q, const bf16* __restrict__ kv, const int32_t* __restrict__ topk,
-    const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0, const int32_t* __restrict__ q_pos,
-    bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink, bf16* __restrict__ part_o,
-    float* __restrict__ part_lse, int T_len, int H, int N_cap, int k, int L_w, int W, float scale_log2, int n_splits) {
+    const bf16* __restrict__ q, const void* __restrict__ kv, const uint8_t* __restrict__ kv_scales,
+    const int32_t* __restrict__ topk, const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0,
+    const int32_t* __restrict__ q_pos, bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink,
+    bf16* __restrict__ part_o, float* __restrict__ part_lse, int T_len, int H, int N_cap, int k, int L_w, int W,
+    float scale_log2, int n_splits, int n_fp4) {
   constexpr int RPW = DRC / NW;   // gathers per wave per chunk
+  constexpr int DPW4 = 8 / NW + 4 / NW;   // DMA instructions per wave per FP4 chunk
   __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
   __shared__ int rowlist[MAX_ROWS];
   __shared__ int n_sel_s;
+  static_assert(!FP4 || DRC * PRS + DNS * RAW4 <= DNS * DRC * PRS, "FP4 buffers fit in the ring");
 
   const int qi = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
   const int b = qi / T_len;
@@ -491,7 +503,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
                                        else zero_frag(qf[ks]);
                                      }
                                    });
-  const bf16* kvb = kv + (size_t)b * N_cap * 512;
+  // rows [rb, rb + nr) of the row list belong to this workgroup's kind of split
+  int rb = 0, nr = n_rows, sp = split, nsp = n_splits;
+  bool fp4_rows = false;
+  if constexpr (FP4) {
+    const int n_sel = n_sel_s;
+    if (split < n_fp4) {
+      nr = n_sel; nsp = n_fp4; fp4_rows = true;
+    } else {
+      rb = n_sel; nr = n_rows - n_sel; sp = split - n_fp4; nsp = n_splits - n_fp4;
+    }
+  }
+  const bf16* kvb = static_cast<const bf16*>(kv) + (size_t)b * N_cap * 512;   // bf16 rows (not read by FP4 splits)
   const bf16* swb = swa + (size_t)b * L_w * 512;
   f32x4 oacc[32];
 #pragma unroll
@@ -499,21 +522,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   float m_run = -INFINITY, l_run = 0.f;
   WAIT_VMCNT(0);   // the query is in registers; from here on only the gathers use the counter
 
-  const int nch_all = (n_rows + DRC - 1) / DRC;
-  const int c0 = (int)(((long long)nch_all * split) / n_splits);
-  const int c1 = (int)(((long long)nch_all * (split + 1)) / n_splits);
-  auto stage = [&](int c) -> unsigned char* { return ring + (c & (DNS - 1)) * (DRC * PRS); };
-  auto issue = [&](int c) {
-    unsigned char* buf = stage(c);
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int rr = wave + NW * j;
-      const int r = c * DRC + rr;
-      const int rid = rowlist[r < n_rows ? r : 0];
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb));
-      dma16_asm(src + ((lane ^ swz(rr & 15)) << 4), (const lds_u8*)(buf + rr * PRS));
-    }
-  };
+  const int nch_all = (nr + DRC - 1) / DRC;
+  const int c0 = (int)(((long long)nch_all * sp) / nsp);
+  const int c1 = (int)(((long long)nch_all * (sp + 1)) / nsp);
+  const int* rl = rowlist + rb;
   // swizzled unit offsets of the S reads and the transposed PV reads
   int soff[4];
 #pragma unroll
@@ -523,17 +535,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
 #pragma unroll
   for (int d8 = 0; d8 < 8; ++d8) toff[d8] = (((2 * d8 + th) ^ tsw) << 4) + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
 
-  for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue(c);
-  for (int c = c0; c < c1; ++c) {
-    const int younger = min(c1 - 1 - c, DNS - 2);   // chunks issued after c
-    if (younger >= 2) WAIT_VMCNT(2 * RPW < 63 ? 2 * RPW : 63);
-    else if (younger == 1) WAIT_VMCNT(RPW < 63 ? RPW : 63);
-    else WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();   // chunk c is in LDS; every wave is done with chunk c - 1
-    COMPILER_FENCE();
-    if (c + DNS - 1 < c1) issue(c + DNS - 1);
-    const unsigned char* cur = stage(c);
-
+  // one 32-row chunk c in LDS (bf16, swizzled): scores, online softmax, PV
+  auto attend = [&](const unsigned char* cur, int c) {
     // ---- S^T = R Q^T: 32 rows (two row tiles) x this wave's 16 heads
     f32x4 s[2];
     s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = c * DRC + (i >> 2) * 16 + 4 * lg + (i & 3);
-      x[i] = row < n_rows ? s[i >> 2][i & 3] * scale_log2 : -INFINITY;
+      x[i] = row < nr ? s[i >> 2][i & 3] * scale_log2 : -INFINITY;
       cmax = fmaxf(cmax, x[i]);
     }
     cmax = max_lane_groups(cmax);   // every chunk holds a valid row, so cmax is finite
@@ -605,6 +608,95 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     }
     WAIT_LGKM0();
     COMPILER_FENCE();
+  };
+
+  if (!fp4_rows) {
+    auto stage = [&](int c) -> unsigned char* { return ring + (c & (DNS - 1)) * (DRC * PRS); };
+    auto issue = [&](int c) {
+      unsigned char* buf = stage(c);
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        const int rr = wave + NW * j;
+        const int r = c * DRC + rr;
+        const int rid = rl[r < nr ? r : 0];
+        const unsigned char* src = reinterpret_cast<const unsigned char*>(row_ptr(rid, kvb, swb));
+        dma16_asm(src + ((lane ^ swz(rr & 15)) << 4), (const lds_u8*)(buf + rr * PRS));
+      }
+    };
+    for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue(c);
+    for (int c = c0; c < c1; ++c) {
+      const int younger = min(c1 - 1 - c, DNS - 2);   // chunks issued after c
+      if (younger >= 2) WAIT_VMCNT(2 * RPW < 63 ? 2 * RPW : 63);
+      else if (younger == 1) WAIT_VMCNT(RPW < 63 ? RPW : 63);
+      else WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();   // chunk c is in LDS; every wave is done with chunk c - 1
+      COMPILER_FENCE();
+      if (c + DNS - 1 < c1) issue(c + DNS - 1);
+      attend(stage(c), c);
+    }
+  } else if constexpr (FP4) {
+    const uint8_t* codes_b = static_cast<const uint8_t*>(kv) + (size_t)b * N_cap * 256;
+    const uint8_t* scales_b = kv_scales + (size_t)b * N_cap * 32;
+    unsigned char* dq = ring;   // the dequantised chunk
+    auto raw = [&](int c) -> unsigned char* { return ring + DRC * PRS + (c & (DNS - 1)) * RAW4; };
+    auto issue4 = [&](int c) {
+      unsigned char* st = raw(c);
+#pragma unroll
+      for (int jj = 0; jj < 8 / NW; ++jj) {   // codes: one instruction moves 4 rows x 256 B
+        const int j = wave + NW * jj;
+        const int r = c * DRC + 4 * j + (lane >> 4);
+        const int rid = rl[r < nr ? r : 0];
+        dma16_asm(codes_b + (size_t)rid * 256 + (lane & 15) * 16, (const lds_u8*)(st + j * 1024));
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4 / NW; ++jj) {   // scales: one instruction moves 8 rows x 32 B
+        const int j = wave + NW * jj;
+        const int r = c * DRC + 8 * j + (lane >> 3);
+        const int rid = rl[r < nr ? r : 0];
+        dma4_asm(scales_b + (size_t)rid * 32 + (lane & 7) * 4, (const lds_u8*)(st + DRC * 256 + j * 256));
+      }
+    };
+    // thread x: row x / 8 of the chunk, dims 64 (x % 8) .. + 63 (four 16-dim scale blocks)
+    auto dequant = [&](int c) {
+      const unsigned char* st = raw(c);
+      for (int x = threadIdx.x; x < DRC * 8; x += 64 * NW) {
+        const int rr = x >> 3, part = x & 7;
+        const uint4 w0 = *reinterpret_cast<const uint4*>(st + rr * 256 + part * 32);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(st + rr * 256 + part * 32 + 16);
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + DRC * 256 + rr * 32 + part * 4);
+        const uint32_t cw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        unsigned char* drow = dq + rr * PRS;
+        const int sz = swz(rr & 15);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {   // 16-B unit: 8 dims, one word of codes
+          const float sc = e4m3_decode((sw >> (8 * (u >> 1))) & 0xFFu);
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = __float_as_uint(e2m1_value((cw[u] >> (8 * i)) & 0xFu) * sc) >> 16;
+            const uint32_t hi = __float_as_uint(e2m1_value((cw[u] >> (8 * i + 4)) & 0xFu) * sc) >> 16;
+            h[i] = lo | (hi << 16);
+          }
+          const int unit = part * 8 + u;
+          *reinterpret_cast<uint4*>(drow + ((unit ^ sz) << 4)) = make_uint4(h[0], h[1], h[2], h[3]);
+        }
+      }
+    };
+    for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue4(c);
+    for (int c = c0; c < c1; ++c) {
+      const int younger = min(c1 - 1 - c, DNS - 2);
+      if (younger >= 2) WAIT_VMCNT(2 * DPW4);
+      else if (younger == 1) WAIT_VMCNT(DPW4);
+      else WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();   // raw chunk c is in LDS; every wave is done with the bf16 buffer
+      COMPILER_FENCE();
+      if (c + DNS - 1 < c1) issue4(c + DNS - 1);
+      dequant(c);
+      WAIT_LGKM0();
+      __builtin_amdgcn_s_barrier();   // the bf16 chunk is complete
+      COMPILER_FENCE();
+      attend(dq, c);
+    }
   }
 
   // ---- this split's normalised output and log-sum-exp (base 2) per head; the
@@ -800,10 +892,11 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
 
 }  // namespace
 
-AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W) {
+AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap) {
   AttnPlan p{};
   const long long Q = (long long)B * T;
   p.decode = (dtype == 1) && Q < 512;
+  p.kv_fp4 = kv_fp4;
   p.n_splits = 1;
   if (p.decode) {
     // A workgroup per (query, row split) keeps three 32-row chunks in flight; the
@@ -814,19 +907,39 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W) {
     int ns = (int)((256 + Q - 1) / Q);
     if (ns > max_chunks) ns = max_chunks;
     if (ns < 1) ns = 1;
+    if (kv_fp4) {
+      // selected rows (FP4) and window rows (bf16) go to different splits, in
+      // proportion to their chunk counts; at least one of each
+      const int c4 = (k + DRC - 1) / DRC, cw = (W + DRC - 1) / DRC;
+      if (ns < 2) ns = 2;
+      int nw = (int)(((long long)ns * cw + (c4 + cw) / 2) / (c4 + cw));
+      if (nw < 1) nw = 1;
+      if (nw > ns - 1) nw = ns - 1;
+      p.n_fp4 = ns - nw;
+    }
     p.n_splits = ns;
   }
-  p.ws_bytes = (p.decode && p.n_splits > 1) ? (size_t)Q * p.n_splits * H * (512 * 2 + 4) + 256 : 0;
+  if (p.decode && p.n_splits > 1)
+    p.ws_bytes = (size_t)Q * p.n_splits * H * (512 * 2 + 4) + 256;
+  else if (kv_fp4 && !p.decode)
+    p.ws_bytes = (size_t)B * N_cap * 512 * (dtype == 1 ? 2 : 4) + 256;
   return p;
 }
 
-hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const int32_t* topk, const void* swa_kv,
-                              const int32_t* swa_pos0, const int32_t* q_pos, void* o, float* lse, const float* sink,
-                              int B, int T, int H, int N_cap, int k, int L_w, int W, float scale, void* workspace,
-                              const AttnPlan& p, hipStream_t st) {
+hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const uint8_t* kv_scales, const int32_t* topk,
+                              const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos, void* o, float* lse,
+                              const float* sink, int B, int T, int H, int N_cap, int k, int L_w, int W, float scale,
+                              void* workspace, const AttnPlan& p, hipStream_t st) {
   if (B == 0 || T == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   const int nw = (H + 15) / 16;
+  if (p.kv_fp4 && !p.decode) {
+    // every row is read by many queries: dequantise the cache once into the workspace
+    hipError_t e = launch_kv_fp4_dequant(dtype, static_cast<const uint8_t*>(kv), kv_scales, (int64_t)B * N_cap,
+                                         workspace, st);
+    if (e != hipSuccess) return e;
+    kv = workspace;
+  }
   if (dtype == 0) {
     hipLaunchKernelGGL(attn_f32, dim3(T, B), dim3(64 * nw), 0, st, static_cast<const float*>(q),
                        static_cast<const float*>(kv), topk, static_cast<const float*>(swa_kv), swa_pos0, q_pos,
@@ -853,15 +966,20 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const in
   const int groups = Q * p.n_splits;
   bf16* part_o = static_cast<bf16*>(workspace);
   float* part_lse = reinterpret_cast<float*>(part_o + (size_t)Q * p.n_splits * H * 512);
-  if (H > 32)
-    hipLaunchKernelGGL(attn_decode_bf16<4>, dim3(groups), dim3(256), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
-  else if (H > 16)
-    hipLaunchKernelGGL(attn_decode_bf16<2>, dim3(groups), dim3(128), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
-  else
-    hipLaunchKernelGGL(attn_decode_bf16<1>, dim3(groups), dim3(64), 0, st, qq, kk, topk, ss, swa_pos0, q_pos, oo,
-                       lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2, p.n_splits);
+#define CSA2_DECODE(NWV, F4)                                                                                   \
+  hipLaunchKernelGGL((attn_decode_bf16<NWV, F4>), dim3(groups), dim3(64 * NWV), 0, st, qq, kv, kv_scales, topk, \
+                     ss, swa_pos0, q_pos, oo, lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2,           \
+                     p.n_splits, p.n_fp4)
+  if (p.kv_fp4) {
+    if (H > 32) CSA2_DECODE(4, true);
+    else if (H > 16) CSA2_DECODE(2, true);
+    else CSA2_DECODE(1, true);
+  } else {
+    if (H > 32) CSA2_DECODE(4, false);
+    else if (H > 16) CSA2_DECODE(2, false);
+    else CSA2_DECODE(1, false);
+  }
+#undef CSA2_DECODE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long total = (long long)Q * H * 64;

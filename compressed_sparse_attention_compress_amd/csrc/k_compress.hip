@@ -320,8 +320,9 @@ __global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __res
 // the workgroup's entries are evaluated once, one per thread, into LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat, const float* __restrict__ gamma,
-                                                         T* __restrict__ kv_cache, int n_entries, int entry0,
-                                                         int m, int N_cap, float eps, double base) {
+                                                         T* __restrict__ kv_cache, uint8_t* __restrict__ kv_scales,
+                                                         int n_entries, int entry0, int m, int N_cap, float eps,
+                                                         double base) {
   __shared__ float2 rot[4][32];
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -362,14 +363,30 @@ __global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat
       v[2 * j + 1] = x0 * s + x1 * c;
     }
   }
-  T* out = kv_cache + ((size_t)b * N_cap + entry0 + e) * 512 + lane * 8;
+  const size_t er = (size_t)b * N_cap + entry0 + e;
+  if (kv_scales != nullptr) {
+    // FP4 main KV: a 16-dim block is lanes 2j, 2j + 1; even dimension in the low nibble
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    const uint32_t sb = fp4_scale_byte(amax);
+    const float sc = e4m3_decode(sb);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= fp4_code(v[i], sc) << (4 * i);
+    reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(kv_cache) + er * 256)[lane] = w;
+    if ((lane & 1) == 0) kv_scales[er * 32 + (lane >> 1)] = (uint8_t)sb;
+    return;
+  }
+  T* out = kv_cache + er * 512 + lane * 8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = from_f32<T>(v[i]);
 }
 
 template <typename T>
 hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const float* gamma, float* lat,
-                    void* kv, int B, int T_len, int D, int m, int start_pos, int N_cap, float eps,
+                    void* kv, uint8_t* kv_scales, int B, int T_len, int D, int m, int start_pos, int N_cap, float eps,
                     float base, hipStream_t st) {
   const int n_entries = T_len / m;
   if (n_entries == 0 || B == 0) return hipSuccess;
@@ -391,7 +408,7 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 g2((n_entries + 3) / 4, B);
-  hipLaunchKernelGGL((compress_finalize<T>), g2, blk, 0, st, lat, gamma, static_cast<T*>(kv), n_entries,
+  hipLaunchKernelGGL((compress_finalize<T>), g2, blk, 0, st, lat, gamma, static_cast<T*>(kv), kv_scales, n_entries,
                      start_pos / m, m, N_cap, eps, (double)base);
   return hipGetLastError();
 }
@@ -483,6 +500,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void compress_step_entry(const float* __restrict__ cz, const int32_t* __restrict__ pos_arr,
                                                            const float* __restrict__ gamma, const T* __restrict__ w_ik,
                                                            float* __restrict__ state, T* __restrict__ kv_cache,
+                                                           uint8_t* __restrict__ kv_scales,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                            float* __restrict__ latent_pre, int B, int m, int N_cap,
                                                            float eps, double base) {
@@ -571,9 +589,27 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
       v[1] = (ch & 1) ? (other * cs.y + v[1] * cs.x) : (v[1] * cs.x - other * cs.y);
     }
   }
-  T* kvrow = kv_cache + ((size_t)b * N_cap + g) * 512;
-  kvrow[tid] = from_f32<T>(v[0]);
-  kvrow[tid + 256] = from_f32<T>(v[1]);
+  if (kv_scales != nullptr) {
+    // FP4 main KV: a 16-dim block is 16 consecutive threads; the even thread of a
+    // pair writes the byte (even dimension in the low nibble)
+    uint8_t* crow = reinterpret_cast<uint8_t*>(kv_cache) + ((size_t)b * N_cap + g) * 256;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float amax = fabsf(v[j]);
+#pragma unroll
+      for (int o2 = 1; o2 < 16; o2 <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o2, 64));
+      const uint32_t sb = fp4_scale_byte(amax);
+      const uint32_t code = fp4_code(v[j], e4m3_decode(sb));
+      const uint32_t other = __shfl_xor(code, 1, 64);
+      const int ch = tid + 256 * j;
+      if ((tid & 1) == 0) crow[ch >> 1] = (uint8_t)(code | (other << 4));
+      if ((tid & 15) == 0) kv_scales[((size_t)b * N_cap + g) * 32 + (ch >> 4)] = (uint8_t)sb;
+    }
+  } else {
+    T* kvrow = kv_cache + ((size_t)b * N_cap + g) * 512;
+    kvrow[tid] = from_f32<T>(v[0]);
+    kvrow[tid + 256] = from_f32<T>(v[1]);
+  }
   __syncthreads();   // lat_s complete
 
   const float* lh = lat_s + h * 256;
@@ -609,19 +645,19 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
 }  // namespace
 
 hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const void* w_gate, const float* gamma,
-                           float* latent_pre, void* kv_cache, int B, int T, int D, int m, int start_pos,
-                           int N_cap, float eps, float rope_base, hipStream_t stream) {
+                           float* latent_pre, void* kv_cache, uint8_t* kv_scales, int B, int T, int D, int m,
+                           int start_pos, int N_cap, float eps, float rope_base, hipStream_t stream) {
   if (dtype == 1)
-    return launch_t<bf16>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, B, T, D, m, start_pos, N_cap, eps,
+    return launch_t<bf16>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, kv_scales, B, T, D, m, start_pos, N_cap, eps,
                           rope_base, stream);
-  return launch_t<float>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, B, T, D, m, start_pos, N_cap, eps,
+  return launch_t<float>(x, w_kv, w_gate, gamma, latent_pre, kv_cache, kv_scales, B, T, D, m, start_pos, N_cap, eps,
                          rope_base, stream);
 }
 
 
 hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv, const void* w_gate,
-                                const float* gamma, const void* w_ik, float* state, void* kv_cache, uint8_t* codes,
-                                uint8_t* scales, float* latent_pre, float* cz, int B, int D, int m, int N_cap,
+                                const float* gamma, const void* w_ik, float* state, void* kv_cache, uint8_t* kv_scales,
+                                uint8_t* codes, uint8_t* scales, float* latent_pre, float* cz, int B, int D, int m, int N_cap,
                                 float eps, float rope_base, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   const dim3 g1((m > 1 ? 1024 : 512) / 16, STEP_KQ), g2(B), blk(256);
@@ -629,13 +665,13 @@ hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, co
     hipLaunchKernelGGL((compress_step_proj<bf16>), g1, blk, 0, stream, static_cast<const bf16*>(x),
                        static_cast<const bf16*>(w_kv), static_cast<const bf16*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<bf16>), g2, blk, 0, stream, cz, pos, gamma,
-                       static_cast<const bf16*>(w_ik), state, static_cast<bf16*>(kv_cache), codes, scales,
+                       static_cast<const bf16*>(w_ik), state, static_cast<bf16*>(kv_cache), kv_scales, codes, scales,
                        latent_pre, B, m, N_cap, eps, (double)rope_base);
   } else {
     hipLaunchKernelGGL((compress_step_proj<float>), g1, blk, 0, stream, static_cast<const float*>(x),
                        static_cast<const float*>(w_kv), static_cast<const float*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<float>), g2, blk, 0, stream, cz, pos, gamma,
-                       static_cast<const float*>(w_ik), state, static_cast<float*>(kv_cache), codes, scales,
+                       static_cast<const float*>(w_ik), state, static_cast<float*>(kv_cache), kv_scales, codes, scales,
                        latent_pre, B, m, N_cap, eps, (double)rope_base);
   }
   return hipGetLastError();

@@ -149,7 +149,68 @@ __global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__
   scales[t] = (uint8_t)sb;
 }
 
+// FP4 main KV: one thread per 16-value block of a 512-d row (one E4M3 scale per
+// block, 8 code bytes, even dimension in the low nibble).
+__global__ __launch_bounds__(256) void kv_fp4_pack_kernel(const float* __restrict__ rows, int64_t n_blocks,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_blocks) return;
+  const float4* src = reinterpret_cast<const float4*>(rows + t * 16);
+  float v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 p = src[i];
+    v[4 * i] = p.x; v[4 * i + 1] = p.y; v[4 * i + 2] = p.z; v[4 * i + 3] = p.w;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(p.x), fabsf(p.y)), fmaxf(fabsf(p.z), fabsf(p.w))));
+  }
+  const uint32_t sb = fp4_scale_byte(amax);
+  const float s = e4m3_decode(sb);
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= fp4_code(v[i], s) << (4 * (i & 7));
+  *reinterpret_cast<uint2*>(codes + t * 8) = make_uint2(w[0], w[1]);
+  scales[t] = (uint8_t)sb;
+}
+
+// FP4 main KV -> dense rows (bf16 or float32): one thread per 16-dim block.  The
+// products are exact in both types.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_fp4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales, int64_t n_blocks,
+                                                             T* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_blocks) return;
+  const uint2 w = *reinterpret_cast<const uint2*>(codes + t * 8);
+  const float s = e4m3_decode(scales[t]);
+  T* dst = out + t * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[i] = from_f32<T>(e2m1_value(((i < 8 ? w.x : w.y) >> (4 * (i & 7))) & 0xFu) * s);
+}
+
 }  // namespace
+
+hipError_t launch_kv_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t nb = n_rows * 32;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_fp4_pack_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, rows, nb, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_fp4_dequant(int dtype, const uint8_t* codes, const uint8_t* scales, int64_t n_rows, void* out,
+                                 hipStream_t stream) {
+  const int64_t nb = n_rows * 32;
+  if (nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nb + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(kv_fp4_dequant_kernel<bf16>, grid, dim3(256), 0, stream, codes, scales, nb,
+                       static_cast<bf16*>(out));
+  else
+    hipLaunchKernelGGL(kv_fp4_dequant_kernel<float>, grid, dim3(256), 0, stream, codes, scales, nb,
+                       static_cast<float*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes, uint8_t* scales,
                           int B, int N, int m, int entry0, int N_cap, float rope_base, hipStream_t stream) {

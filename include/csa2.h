@@ -57,6 +57,17 @@ typedef enum csa2_status {
 
 typedef enum csa2_dtype { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
 
+/* Storage of the main KV cache rows.  DENSE: 512 values of the layer dtype per
+ * row.  FP4 ([P3] section seven, FP4 main KV: E2M1 data with an E4M3 scale shared
+ * by a group of channels, dequantised to a wider type before attention; [P3]
+ * section six: 288 B per entry, hence one scale per 16 channels): per row 256
+ * code bytes (E2M1, dim 2j in the low nibble of byte j) in the cache tensor and
+ * 32 E4M3FN scale bytes in a second tensor.  Each 16-dim block is quantised as
+ * the index K is: s = E4M3(amax / 6) (float32 divide, nearest-even, saturating at
+ * 448), codes E2M1(u / s) (nearest-even, saturating at 6, sign kept), all zero
+ * when s is 0.  The rows quantised are the float32 post-RoPE latents.         */
+typedef enum csa2_kv_fmt { CSA2_KV_DENSE = 0, CSA2_KV_FP4 = 1 } csa2_kv_fmt;
+
 /* Layer modes ([P1] section on the four slots and the mode excerpt; [P2] mode
  * tables; [P4] "Les trois modes"): Full computes main KV, index K and top-k;
  * Reindex borrows main KV and index K and selects anew; Reuse borrows main KV and
@@ -96,6 +107,7 @@ typedef struct csa2_slot_info {
   int32_t B, rows, cols;/* COMPRESS_KV: B, N_cap, n_entries; INDEX_K: B, N_cap, n_entries;
                            TOPK_IDXS: B, T, k; CANDIDATES: B, T, n_b */
   int32_t extra;        /* CANDIDATES: block size s; COMPRESS_KV/INDEX_K: m */
+  int32_t kv_fmt;       /* COMPRESS_KV: csa2_kv_fmt (FP4: ptr = codes, ptr2 = scales) */
 } csa2_slot_info;
 
 csa2_status csa2_runtime_slot(const csa2_runtime* rt, csa2_slot slot, csa2_slot_info* out);
@@ -113,7 +125,9 @@ csa2_status csa2_runtime_slot(const csa2_runtime* rt, csa2_slot slot, csa2_slot_
  *   latent_pre [B, T/m, 512] float32 out  normalised entries before RoPE (feeds index K)
  *   kv_cache [B, N_cap, 512] dtype out    rows start_pos/m .. start_pos/m + T/m - 1 written
  *   start_pos  absolute position of x[:, 0] (same for all sequences), multiple of m
- * With rt != NULL the compress_kv slot is set to kv_cache with
+ *   kv_fmt   CSA2_KV_FP4: kv_cache is uint8 codes [B, N_cap, 256] and kv_scales
+ *            uint8 [B, N_cap, 32] receives the scales (see csa2_kv_fmt)
+ * With rt != NULL the compress_kv slot is set to kv_cache (and kv_scales) with
  * n_entries = start_pos/m + T/m.                                              */
 typedef struct csa2_compress_args {
   int32_t dtype;            /* csa2_dtype of x, w_kv, w_gate, kv_cache */
@@ -128,6 +142,8 @@ typedef struct csa2_compress_args {
   const float* gamma;
   float* latent_pre;
   void* kv_cache;
+  int32_t kv_fmt;           /* csa2_kv_fmt */
+  uint8_t* kv_scales;       /* FP4 only: [B, N_cap, 32] */
 } csa2_compress_args;
 
 csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_stream stream);
@@ -176,6 +192,7 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
  *            exp(Z - max), sum of exp(Z - max) C).  A group's first token
  *            overwrites it, so it needs no initialisation.
  *   kv_cache [B, N_cap, 512] dtype out   row pos/m, written at a group's last token
+ *            (kv_fmt CSA2_KV_FP4: codes [B, N_cap, 256] and kv_scales [B, N_cap, 32])
  *   ik_codes [B, N_cap, 64], ik_scales [B, N_cap, 4] uint8 out: the same row
  *   latent_pre [B, 512] float32 out      that entry's latent before RoPE (NULL: not written)
  *   workspace  csa2_workspace_size(CSA2_OP_COMPRESS_STEP) bytes (B * 16384: C and
@@ -201,6 +218,8 @@ typedef struct csa2_compress_step_args {
   float* latent_pre;
   void* workspace;
   size_t workspace_bytes;
+  int32_t kv_fmt;           /* csa2_kv_fmt */
+  uint8_t* kv_scales;       /* FP4 only: [B, N_cap, 32] */
 } csa2_compress_step_args;
 
 csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream);
@@ -267,7 +286,14 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa
  *            give no formula.  Read here as a logit s_h that enters only the
  *            softmax denominator: p_r = exp(l_r) / (exp(s_h) + sum_r' exp(l_r')),
  *            o = sum_r p_r row_r, lse = log(exp(s_h) + sum_r exp(l_r)), with
- *            l_r = scale * q . row_r.  NULL is the plain softmax.            */
+ *            l_r = scale * q . row_r.  NULL is the plain softmax.
+ *   kv_fmt   CSA2_KV_FP4: kv is uint8 codes [B, N_cap, 256] (16-byte aligned)
+ *            and kv_scales uint8 [B, N_cap, 32] (4-byte aligned); the rows are
+ *            attended as their exact dequantised values (window rows stay
+ *            dense).  Few-query bf16 calls dequantise inside the row gather;
+ *            other calls dequantise the whole cache once into the workspace
+ *            (B * N_cap * 512 elements of the dtype), since there each row is
+ *            read by many queries.  With kv == NULL the slot's format is used. */
 typedef struct csa2_sparse_attn_args {
   int32_t dtype;            /* csa2_dtype of q, kv, swa_kv, o */
   int32_t B, T, H;
@@ -284,6 +310,8 @@ typedef struct csa2_sparse_attn_args {
   void* workspace;
   size_t workspace_bytes;
   const float* sink;        /* [H] float32 per-head sink logits, or NULL (no sink) */
+  int32_t kv_fmt;           /* csa2_kv_fmt of kv (ignored when kv is NULL) */
+  const uint8_t* kv_scales; /* FP4 only: [B, N_cap, 32] */
 } csa2_sparse_attn_args;
 
 csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* a, csa2_stream stream);
@@ -301,6 +329,7 @@ typedef struct csa2_layer_cfg {
   int32_t m, k, W, H_I, H;
   int32_t hsi, hsi_s, hsi_nb;
   float rope_base, eps, scale;
+  int32_t kv_fmt;           /* Full: storage of the main KV it writes (csa2_kv_fmt) */
 } csa2_layer_cfg;
 
 typedef struct csa2_layer_io {
@@ -317,6 +346,7 @@ typedef struct csa2_layer_io {
   void* o;
   void* workspace; size_t workspace_bytes;
   const float* sink;        /* [H] float32 per-head attention sink, or NULL (see csa2_sparse_attn_args) */
+  uint8_t* kv_scales;       /* Full with kv_fmt CSA2_KV_FP4: [B, N_cap, 32]; kv_cache then holds the codes */
 } csa2_layer_io;
 
 csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, const csa2_layer_io* io,
@@ -336,6 +366,12 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
  * float32 -> codes [n_rows, 64], scales [n_rows, 4], as described above. */
 csa2_status csa2_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                           csa2_stream stream);
+
+/* FP4 main-KV packing alone (test hook for bit-exactness): rows [n_rows, 512]
+ * float32 (16-byte aligned) -> codes [n_rows, 256], scales [n_rows, 32], as
+ * described at csa2_kv_fmt. */
+csa2_status csa2_kv_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                             csa2_stream stream);
 
 const char* csa2_status_string(csa2_status s);
 const char* csa2_last_error(void);

@@ -77,13 +77,15 @@ def check_topk_row(scores, cand_ids, gpu_row, k, tag="", exempt=None):
     return exact
 
 
-def check_fp4(u, codes_gpu, scales_gpu, tag=""):
-    """u: oracle float64 values before quantisation [rows, 128].  Returns
-    (#code mismatches, #scale mismatches), all of them inside the rounding bands."""
+def check_fp4(u, codes_gpu, scales_gpu, tag="", block=32):
+    """u: oracle float64 values before quantisation [rows, d] (index K: d = 128,
+    block 32; main KV: d = 512, block 16).  Returns (#code mismatches, #scale
+    mismatches), all of them inside the rounding bands."""
     u32 = np.asarray(u, dtype=np.float64).astype(np.float32)
-    codes_o, scales_o = O.fp4_pack(u32)
-    rows = u32.shape[0]
-    blocks = u32.reshape(rows, 4, 32)
+    codes_o, scales_o = O.fp4_pack(u32, block)
+    rows, d = u32.shape
+    nb = d // block
+    blocks = u32.reshape(rows, nb, block)
     sigma = (np.max(np.abs(blocks), axis=2).astype(np.float32) / np.float32(6)).astype(np.float64)
     sdiff = scales_gpu != scales_o
     assert np.all(near_any(sigma[sdiff], E4M3_MIDS)), f"{tag}: scale bytes differ away from an E4M3 midpoint"
@@ -92,13 +94,13 @@ def check_fp4(u, codes_gpu, scales_gpu, tag=""):
         ratio = blocks / s[:, :, None]
     def unpack(c):
         c = np.asarray(c, dtype=np.uint8)
-        out = np.empty((rows, 128), dtype=np.uint8)
+        out = np.empty((rows, d), dtype=np.uint8)
         out[:, 0::2] = c & 15
         out[:, 1::2] = c >> 4
-        return out.reshape(rows, 4, 32)
+        return out.reshape(rows, nb, block)
     cg, co = unpack(codes_gpu), unpack(codes_o)
     cdiff = (cg != co) & ~sdiff[:, :, None]
-    ok = near_any(ratio[cdiff], E2M1_MIDS) | (s[:, :, None].repeat(32, 2)[cdiff] == 0)
+    ok = near_any(ratio[cdiff], E2M1_MIDS) | (s[:, :, None].repeat(block, 2)[cdiff] == 0)
     assert np.all(ok), f"{tag}: {np.count_nonzero(~ok)} codes differ away from an E2M1 midpoint"
     return int(np.count_nonzero(cdiff)), int(np.count_nonzero(sdiff))
 

@@ -175,3 +175,45 @@ def test_attn_validation(field, value, status):
 def test_fp4_pack_zero_rows_is_noop():
     assert K.lib().csa2_fp4_pack(None, 0, None, None, None) == 0
     assert K.STATUS[K.lib().csa2_fp4_pack(None, 5, None, None, None)] == "CSA2_ERR_INVALID_ARG"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("kv_fmt", 2, "CSA2_ERR_INVALID_ARG"), ("kv_scales", None, "CSA2_ERR_INVALID_ARG"),
+    ("kv", 0x1008, "CSA2_ERR_INVALID_ARG"), ("kv_scales", 0x2002, "CSA2_ERR_INVALID_ARG"),
+])
+def test_attn_fp4_kv_validation(field, value, status):
+    a = K.SparseAttnArgs(dtype=1, B=1, T=1, H=64, N_cap=100, k=512, L_w=128, W=128, q=0x1000, kv=0x1000,
+                         topk=0x1000, swa_kv=0x1000, swa_pos0=0x1000, q_pos=0x1000, o=0x1000,
+                         kv_fmt=K.KV_FP4, kv_scales=0x2000)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_sparse_attn(None, C.byref(a), None)] == status
+
+
+def test_fp4_kv_workspace_sizes():
+    # few-query bf16: split partials for selected-row and window splits (at least
+    # one of each); many queries or float32: the dequantised cache
+    def ws(dtype, B, T, fp4, N_cap=1000):
+        a = K.SparseAttnArgs(dtype=dtype, B=B, T=T, H=64, k=512, W=128, N_cap=N_cap,
+                             kv_fmt=K.KV_FP4 if fp4 else K.KV_DENSE)
+        n = C.c_size_t()
+        assert K.lib().csa2_workspace_size(K.OP_SPARSE_ATTN, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
+        return n.value
+    assert ws(1, 64, 1, True) == ws(1, 64, 1, False)          # 4 splits either way
+    assert ws(1, 300, 1, False) == 0 and ws(1, 300, 1, True) == 300 * 2 * 64 * 1028 + 256
+    assert ws(1, 1, 1024, True) == 1000 * 512 * 2 + 256 and ws(1, 1, 1024, False) == 0
+    assert ws(0, 2, 8, True) == 2 * 1000 * 512 * 4 + 256
+
+
+@pytest.mark.parametrize("field,value", [("kv_fmt", 3), ("kv_scales", None)])
+def test_compress_fp4_kv_validation(field, value):
+    a = K.CompressArgs(dtype=1, B=1, T=4, D=64, m=2, start_pos=0, N_cap=8, eps=1e-6, rope_base=1e4, x=0x1000,
+                       w_kv=0x1000, w_gate=0x1000, gamma=0x1000, latent_pre=0x1000, kv_cache=0x1000,
+                       kv_fmt=K.KV_FP4, kv_scales=0x1000)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_compress(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"
+
+
+def test_kv_fp4_pack_zero_rows_is_noop():
+    assert K.lib().csa2_kv_fp4_pack(None, 0, None, None, None) == 0
+    assert K.STATUS[K.lib().csa2_kv_fp4_pack(None, 5, None, None, None)] == "CSA2_ERR_INVALID_ARG"
+    assert K.STATUS[K.lib().csa2_kv_fp4_pack(0x1008, 5, 0x1000, 0x1000, None)] == "CSA2_ERR_INVALID_ARG"

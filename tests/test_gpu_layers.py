@@ -30,13 +30,19 @@ class GpuLayerStack:
     """Device buffers of one Full layer's caches plus per-layer call helpers."""
 
     def __init__(self, shape: synth.LayerShape, dtype, hsi=K.HSI_NONE if torch.cuda.is_available() else 0,
-                 hsi_s=0, hsi_nb=0):
+                 hsi_s=0, hsi_nb=0, kv_fp4=False):
         s = shape
         self.s, self.dtype = s, dtype
         self.N = s.L // s.m
         self.rt = K.Runtime()
         self.lat = torch.empty(s.B, self.N, 512, dtype=torch.float32, device=DEV)
-        self.kv = torch.zeros(s.B, self.N, 512, dtype=dtype, device=DEV)
+        self.kv_fp4 = kv_fp4
+        if kv_fp4:   # FP4 main KV: codes in kv, E4M3 scales beside them
+            self.kv = torch.zeros(s.B, self.N, 256, dtype=torch.uint8, device=DEV)
+            self.kv_scales = torch.zeros(s.B, self.N, 32, dtype=torch.uint8, device=DEV)
+        else:
+            self.kv = torch.zeros(s.B, self.N, 512, dtype=dtype, device=DEV)
+            self.kv_scales = None
         self.codes = torch.zeros(s.B, self.N, 64, dtype=torch.uint8, device=DEV)
         self.scales = torch.zeros(s.B, self.N, 4, dtype=torch.uint8, device=DEV)
         self.hsi, self.hsi_s, self.hsi_nb = hsi, hsi_s, hsi_nb
@@ -46,7 +52,8 @@ class GpuLayerStack:
         s = self.s
         hsi = self.hsi if hsi is None else hsi
         cfg = K.layer_cfg(mode, K.CSA2_BF16 if self.dtype == torch.bfloat16 else K.CSA2_F32, m=s.m, k=s.k, W=s.W,
-                          H_I=s.H_I, H=s.H, hsi=hsi, hsi_s=self.hsi_s, hsi_nb=self.hsi_nb)
+                          H_I=s.H_I, H=s.H, hsi=hsi, hsi_s=self.hsi_s, hsi_nb=self.hsi_nb,
+                          kv_fmt=K.KV_FP4 if self.kv_fp4 else K.KV_DENSE)
         topk = torch.full((s.B, s.L, s.k), -9, dtype=torch.int32, device=DEV)
         o = torch.empty_like(inp["q"])
         kw = dict(B=s.B, T=s.L, q_pos=inp["q_pos"], q=inp["q"], swa_kv=inp["swa_kv"], swa_pos0=inp["swa_pos0"], o=o,
@@ -54,7 +61,7 @@ class GpuLayerStack:
         if mode == K.FULL:
             kw.update(D=s.D, x=inp["x"], w_kv=inp["w_kv"], w_gate=inp["w_gate"], gamma=inp["gamma"],
                       w_ik=inp["w_ik"], latent_pre=self.lat, kv_cache=self.kv, ik_codes=self.codes,
-                      ik_scales=self.scales)
+                      ik_scales=self.scales, kv_scales=self.kv_scales)
         if mode != K.REUSE:
             kw.update(q_idx=inp["q_idx"], w=inp["w"], topk=topk,
                       candidates=self.cands if hsi == K.HSI_BUILD else None)
