@@ -7,8 +7,9 @@ one batch (B=1, L=8192, hidden 4096, m=2, 32x128 FP4 indexer heads, top-512, win
 128, 64 heads, bf16 in / fp32 accumulate).  A second record ("decode") times the
 batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries), and
 a third ("decode_hsi_1m") the 1M-context decode step with the HSI candidate pool
-(4 sequences x 524288 entries), and a fourth ("decode_append") the Full layer's
-decode append of one token per sequence.
+(4 sequences x 524288 entries), a fourth ("decode_append") the Full layer's
+decode append of one token per sequence, and a fifth ("decode_fp4kv") the batched
+decode step with the main KV stored as FP4.
 
 Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
@@ -102,13 +103,23 @@ class PrefillBench:
 class DecodeBench:
     """Batched decode step, Reindex + Reuse: 64 sequences x 131072 m=2 entries."""
 
-    def __init__(self, torch, K, synth, B=64, n_entries=131072, m=2, H_I=32, k=512, W=128, H=64):
+    def __init__(self, torch, K, synth, B=64, n_entries=131072, m=2, H_I=32, k=512, W=128, H=64, kv_fp4=False):
         self.t, self.K = torch, K
         dev = "cuda"
         self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
+        self.kv_fp4 = kv_fp4
         g = torch.Generator(device=dev)
         g.manual_seed(1234)
-        self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        if kv_fp4:   # FP4 main KV: N(0,1) latent rows packed by the (bit-exact) FP4 packer
+            self.kv = torch.empty(B, n_entries, 256, dtype=torch.uint8, device=dev)
+            self.kv_scales = torch.empty(B, n_entries, 32, dtype=torch.uint8, device=dev)
+            for b in range(B):
+                r = torch.randn(n_entries, 512, generator=g, device=dev, dtype=torch.float32)
+                K.csa2_kv_fp4_pack(r, self.kv[b], self.kv_scales[b])
+            del r
+        else:
+            self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            self.kv_scales = None
         self.codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
         for b in range(B):  # index K: N(0,1) rows packed by the (bit-exact) FP4 packer
@@ -126,7 +137,7 @@ class DecodeBench:
                                           scales=self.scales, q_pos=self.q_pos, topk=self.topk, n_entries=n_entries,
                                           m=m, k=k, N_cap=n_entries)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W)
+        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W, kv_fp4, n_entries)
         self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -140,21 +151,23 @@ class DecodeBench:
         if events is not None:
             events[1].record()
         K.csa2_sparse_attn(None, r["q"], self.kv, self.topk, r["swa_kv"], self.swa_pos0, self.q_pos, self.o[0],
-                           W=self.W, workspace=self.ws_attn)
+                           W=self.W, workspace=self.ws_attn, kv_scales=self.kv_scales)
         if events is not None:
             events[2].record()
         K.csa2_sparse_attn(None, u["q"], self.kv, self.topk, u["swa_kv"], self.swa_pos0, self.q_pos, self.o[1],
-                           W=self.W, workspace=self.ws_attn)
+                           W=self.W, workspace=self.ws_attn, kv_scales=self.kv_scales)
         if events is not None:
             events[3].record()
 
     def work(self):
         B, N = self.B, self.N
         rows = B * (min(self.k, N) + self.W)
+        sel_row_bytes = 288.0 if self.kv_fp4 else 1024.0     # FP4 main KV row, or bf16 row
         return {
             "score_topk": {"bytes": 68.0 * B * N + B * self.H_I * (128 * 2 + 4) + B * self.k * 4,
                            "flop": 2.0 * B * N * self.H_I * 128},
-            "sparse_attn": {"bytes": rows * 1024.0 + 2.0 * B * self.H * 512 * 2,
+            "sparse_attn": {"bytes": B * min(self.k, N) * sel_row_bytes + B * self.W * 1024.0
+                            + 2.0 * B * self.H * 512 * 2,
                             "flop": 4.0 * rows * self.H * 512},
         }
 
@@ -407,6 +420,7 @@ def main():
     ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
     ap.add_argument("--no-append", action="store_true", help="skip the decode-append record")
+    ap.add_argument("--no-fp4kv", action="store_true", help="skip the decode record with FP4 main KV")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches instead of a HIP graph replay of the step")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -495,6 +509,30 @@ def main():
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (dms * 1e-3), 4),
         }
         del db
+        torch.cuda.empty_cache()
+    if not args.no_decode and not args.no_fp4kv:
+        log("decode (FP4 main KV): building caches")
+        fb = DecodeBench(torch, K, synth, B=args.decode_seqs, kv_fp4=True)
+        log("decode (FP4 main KV): timing")
+        fms_eager, fst = time_steps(torch, fb, 3, max(args.steps, 20), args.warmup)
+        fms = time_graph(torch, fb, max(args.steps, 20), args.warmup) if args.graph else fms_eager
+        fw = fb.work()
+        attn_gbs = fw["sparse_attn"]["bytes"] / (fst[1] * 1e-3) / 1e9
+        step_bytes = fw["score_topk"]["bytes"] + 2 * fw["sparse_attn"]["bytes"]
+        out["decode_fp4kv"] = {
+            "workload": f"batched decode, Reindex + Reuse, FP4 main KV (288 B per entry, E2M1 + E4M3 per 16 dims): "
+                        f"{fb.B} sequences x {fb.N} m=2 entries, FP4 index K, 32x128 indexer heads, top-512, "
+                        f"SWA 128 (bf16), 64 heads",
+            "us_per_step": round(fms * 1e3, 2), "us_per_step_eager": round(fms_eager * 1e3, 2),
+            "stages_us": {"score_topk": round(fst[0] * 1e3, 2), "attn_reindex": round(fst[1] * 1e3, 2),
+                          "attn_reuse": round(fst[2] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "kernel": "sparse_attn_fp4kv", "achieved": round(attn_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None},
+            "attn_bytes_per_layer": fw["sparse_attn"]["bytes"],
+            "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (fms * 1e-3), 4),
+        }
+        del fb
         torch.cuda.empty_cache()
     if not args.no_hsi:
         log("hsi decode: building caches")

@@ -483,7 +483,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
   __shared__ int rowlist[MAX_ROWS];
   __shared__ int n_sel_s;
-  static_assert(!FP4 || DRC * PRS + DNS * RAW4 <= DNS * DRC * PRS, "FP4 buffers fit in the ring");
+  static_assert(!FP4 || 2 * DRC * PRS + DNS * RAW4 <= DNS * DRC * PRS, "FP4 buffers fit in the ring");
 
   const int qi = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
   const int b = qi / T_len;
@@ -637,8 +637,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   } else if constexpr (FP4) {
     const uint8_t* codes_b = static_cast<const uint8_t*>(kv) + (size_t)b * N_cap * 256;
     const uint8_t* scales_b = kv_scales + (size_t)b * N_cap * 32;
-    unsigned char* dq = ring;   // the dequantised chunk
-    auto raw = [&](int c) -> unsigned char* { return ring + DRC * PRS + (c & (DNS - 1)) * RAW4; };
+    // two dequantised chunks (chunk c in buffer c & 1), then the raw ring
+    auto dqb = [&](int c) -> unsigned char* { return ring + (c & 1) * (DRC * PRS); };
+    auto raw = [&](int c) -> unsigned char* { return ring + 2 * DRC * PRS + (c & (DNS - 1)) * RAW4; };
     auto issue4 = [&](int c) {
       unsigned char* st = raw(c);
 #pragma unroll
@@ -656,7 +657,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
         dma4_asm(scales_b + (size_t)rid * 32 + (lane & 7) * 4, (const lds_u8*)(st + DRC * 256 + j * 256));
       }
     };
-    // thread x: row x / 8 of the chunk, dims 64 (x % 8) .. + 63 (four 16-dim scale blocks)
+    // thread x: row x / 8 of the chunk, dims 64 (x % 8) .. + 63 (four 16-dim scale blocks).
+    // A code word holds 8 dims.  Its nibbles become E4M3 bytes of the same value
+    // (E2M1 magnitude k -> byte via an 8-entry v_perm table, sign to bit 7), the
+    // hardware FP8 conversion yields float32, the block scale multiplies, and the
+    // upper halves are the exact bf16 values.
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    auto to_e4m3 = [](uint32_t nib4) -> uint32_t {   // 4 nibbles, one per byte
+      return __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, nib4 & 0x07070707u) | ((nib4 & 0x08080808u) << 4);
+    };
+    auto bf16_pair = [](float lo, float hi) -> uint32_t {
+      return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    };
     auto dequant = [&](int c) {
       const unsigned char* st = raw(c);
       for (int x = threadIdx.x; x < DRC * 8; x += 64 * NW) {
@@ -665,37 +677,47 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
         const uint4 w1 = *reinterpret_cast<const uint4*>(st + rr * 256 + part * 32 + 16);
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + DRC * 256 + rr * 32 + part * 4);
         const uint32_t cw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        unsigned char* drow = dq + rr * PRS;
+        float scl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) scl[j] = e4m3_decode((sw >> (8 * j)) & 0xFFu);
+        unsigned char* drow = dqb(c) + rr * PRS;
         const int sz = swz(rr & 15);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {   // 16-B unit: 8 dims, one word of codes
-          const float sc = e4m3_decode((sw >> (8 * (u >> 1))) & 0xFFu);
-          uint32_t h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = __float_as_uint(e2m1_value((cw[u] >> (8 * i)) & 0xFu) * sc) >> 16;
-            const uint32_t hi = __float_as_uint(e2m1_value((cw[u] >> (8 * i + 4)) & 0xFu) * sc) >> 16;
-            h[i] = lo | (hi << 16);
-          }
+          const float sc = scl[u >> 1];
+          const uint32_t ev = to_e4m3(cw[u] & 0x0F0F0F0Fu);          // dims 0, 2, 4, 6
+          const uint32_t od = to_e4m3((cw[u] >> 4) & 0x0F0F0F0Fu);   // dims 1, 3, 5, 7
+          const v2f e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false), e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);
+          const v2f o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false), o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);
+          const uint4 h = make_uint4(bf16_pair(e0.x * sc, o0.x * sc), bf16_pair(e0.y * sc, o0.y * sc),
+                                     bf16_pair(e1.x * sc, o1.x * sc), bf16_pair(e1.y * sc, o1.y * sc));
           const int unit = part * 8 + u;
-          *reinterpret_cast<uint4*>(drow + ((unit ^ sz) << 4)) = make_uint4(h[0], h[1], h[2], h[3]);
+          *reinterpret_cast<uint4*>(drow + ((unit ^ sz) << 4)) = h;
         }
       }
     };
+    // Chunk c + 1 is dequantised while chunk c is attended, so one barrier per
+    // chunk: it finds raw chunk c + 1 landed, chunk c dequantised by every wave and
+    // chunk c - 1 (whose buffer chunk c + 1 takes) no longer read.
     for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue4(c);
-    for (int c = c0; c < c1; ++c) {
-      const int younger = min(c1 - 1 - c, DNS - 2);
-      if (younger >= 2) WAIT_VMCNT(2 * DPW4);
-      else if (younger == 1) WAIT_VMCNT(DPW4);
+    if (c0 < c1) {
+      if (c1 - c0 >= 3) WAIT_VMCNT(2 * DPW4);
+      else if (c1 - c0 == 2) WAIT_VMCNT(DPW4);
       else WAIT_VMCNT(0);
-      __builtin_amdgcn_s_barrier();   // raw chunk c is in LDS; every wave is done with the bf16 buffer
+      __builtin_amdgcn_s_barrier();   // raw chunk c0 is in LDS
+      COMPILER_FENCE();
+      dequant(c0);
+    }
+    for (int c = c0; c < c1; ++c) {
+      const int younger = min(c1 - 2 - c, DNS - 3);   // chunks issued after c + 1
+      if (younger >= 1) WAIT_VMCNT(DPW4);
+      else WAIT_VMCNT(0);
+      WAIT_LGKM0();
+      __builtin_amdgcn_s_barrier();
       COMPILER_FENCE();
       if (c + DNS - 1 < c1) issue4(c + DNS - 1);
-      dequant(c);
-      WAIT_LGKM0();
-      __builtin_amdgcn_s_barrier();   // the bf16 chunk is complete
-      COMPILER_FENCE();
-      attend(dq, c);
+      if (c + 1 < c1) dequant(c + 1);
+      attend(dqb(c), c);
     }
   }
 
