@@ -528,7 +528,7 @@ def main():
                           "attn_reuse": round(fst[2] * 1e3, 2)},
             "roofline": {"bound": "hbm", "kernel": "sparse_attn_fp4kv", "achieved": round(attn_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None},
+                         "traffic": traffic_for("sparse_attn_fp4kv", ["k_attn.hip"])},
             "attn_bytes_per_layer": fw["sparse_attn"]["bytes"],
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (fms * 1e-3), 4),
         }

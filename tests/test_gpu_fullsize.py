@@ -7,7 +7,7 @@ outputs (entries, queries, rows) is recomputed one by one by the CPU oracle.
 * decoder macro-block, m=1, L=32768: Full (from one hidden tensor), Reindex, Reuse,
   Reuse;
 * batched decode, 64 sequences x 131072 m=2 entries, Reindex + Reuse (the
-  benchmark's DecodeBench itself);
+  benchmark's DecodeBench itself), with bf16 and with FP4 main KV;
 * 1M-context decode with the HSI candidate pool: 4 sequences x 524288 entries,
   Full layer (flat top-512 + 256 blocks of 64) then Reindex within the pool.
 
@@ -183,6 +183,30 @@ def test_batched_decode_full_size(K):
                                            pos0, p, db.W)
             err = row_rel_err(f64(db.o[li][b, 0]), ref)
             assert err <= TOL, f"decode b{b} layer{li}: {err:.3e}"
+            worst = max(worst, err)
+    say(f"  worst attention row rel err {worst:.2e}")
+
+
+def test_batched_decode_fp4_kv_full_size(K):
+    import bench
+    say("case: batched decode 64 x 131072 entries with FP4 main KV (benchmark launch configuration)")
+    db = bench.DecodeBench(torch, K, synth, kv_fp4=True)
+    db.step()
+    torch.cuda.synchronize()
+    topk = db.topk.cpu().numpy()
+    p = int(db.q_pos[0, 0].item())
+    pos0 = int(db.swa_pos0[0].item())
+    worst = 0.0
+    for b in [0, 40, 63]:
+        sel = topk[b, 0]
+        ids = torch.from_numpy(sel[sel >= 0].astype(np.int64)).to(DEV)
+        rows = O.kv_fp4_unpack(db.kv[b][ids].cpu().numpy(), db.kv_scales[b][ids].cpu().numpy())
+        for li in range(2):
+            lay = db.layers[li]
+            ref, _, _ = O.sparse_attention(f64(lay["q"][b, 0]), rows, np.arange(rows.shape[0]), f64(lay["swa_kv"][b]),
+                                           pos0, p, db.W)
+            err = row_rel_err(f64(db.o[li][b, 0]), ref)
+            assert err <= TOL, f"decode FP4 KV b{b} layer{li}: {err:.3e}"
             worst = max(worst, err)
     say(f"  worst attention row rel err {worst:.2e}")
 
