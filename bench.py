@@ -108,22 +108,23 @@ class DecodeBench:
         dev = "cuda"
         self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
         self.kv_fp4 = kv_fp4
-        g = torch.Generator(device=dev)
-        g.manual_seed(1234)
+        self.seed = seed = 11   # per-sequence cache rows: synth.cache_rows(n, d, seed, name, b)
         if kv_fp4:   # FP4 main KV: N(0,1) latent rows packed by the (bit-exact) FP4 packer
             self.kv = torch.empty(B, n_entries, 256, dtype=torch.uint8, device=dev)
             self.kv_scales = torch.empty(B, n_entries, 32, dtype=torch.uint8, device=dev)
             for b in range(B):
-                r = torch.randn(n_entries, 512, generator=g, device=dev, dtype=torch.float32)
+                r = synth.cache_rows(n_entries, 512, seed, "kv_cache", b, dev)
                 K.csa2_kv_fp4_pack(r, self.kv[b], self.kv_scales[b])
             del r
         else:
-            self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            self.kv = torch.empty(B, n_entries, 512, dtype=torch.bfloat16, device=dev)
+            for b in range(B):
+                self.kv[b] = synth.cache_rows(n_entries, 512, seed, "kv_cache", b, dev).to(torch.bfloat16)
             self.kv_scales = None
         self.codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
         for b in range(B):  # index K: N(0,1) rows packed by the (bit-exact) FP4 packer
-            u = torch.randn(n_entries, 128, generator=g, device=dev, dtype=torch.float32)
+            u = synth.cache_rows(n_entries, 128, seed, "u", b, dev)
             K.csa2_fp4_pack(u, self.codes[b], self.scales[b])
         del u
         p = n_entries * m - 1  # newest token; all entries visible
@@ -188,13 +189,13 @@ class HsiDecodeBench:
         dev = "cuda"
         self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
         self.s_blk, self.n_b, self.copies = s_blk, n_b, copies
-        g = torch.Generator(device=dev)
-        g.manual_seed(4321)
-        self.kv = torch.randn(B, n_entries, 512, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        seed = 12
+        self.kv = torch.empty(B, n_entries, 512, dtype=torch.bfloat16, device=dev)
         codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
         scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
         for b in range(B):
-            u = torch.randn(n_entries, 128, generator=g, device=dev, dtype=torch.float32)
+            self.kv[b] = synth.cache_rows(n_entries, 512, seed, "kv_cache", b, dev).to(torch.bfloat16)
+            u = synth.cache_rows(n_entries, 128, seed, "u", b, dev)
             K.csa2_fp4_pack(u, codes[b], scales[b])
         del u
         self.ik = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(copies - 1)]

@@ -108,6 +108,13 @@ def decode_cache_inputs(B: int, n_entries: int, seed: int = 0, dtype=torch.bfloa
     return kv, u
 
 
+def cache_rows(n: int, d: int, seed: int, name: str, seq: int, device="cpu") -> torch.Tensor:
+    """N(0, 1) float32 rows [n, d] of one sequence's pre-filled cache (latent rows,
+    or index-K values before quantisation), from a generator of its own per
+    (seed, name, sequence), so that any one sequence can be drawn again alone."""
+    return gaussian((n, d), 1.0, seed, name, seq, torch.float32, device)
+
+
 def decode_query_inputs(B: int, H: int, H_I: int, W: int, seed: int = 0, layer: int = 0,
                         dtype=torch.bfloat16, device="cpu", d: int = 512, d_I: int = 128):
     """One new query token per sequence for one layer: q [B,1,H,512],
