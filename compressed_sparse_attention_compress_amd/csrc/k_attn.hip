@@ -657,7 +657,6 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
         dma4_asm(scales_b + (size_t)rid * 32 + (lane & 7) * 4, (const lds_u8*)(st + DRC * 256 + j * 256));
       }
     };
-    // thread x: row x / 8 of the chunk, dims 64 (x % 8) .. + 63 (four 16-dim scale blocks).
     // A code word holds 8 dims.  Its nibbles become E4M3 bytes of the same value
     // (E2M1 magnitude k -> byte via an 8-entry v_perm table, sign to bit 7), the
     // hardware FP8 conversion yields float32, the block scale multiplies, and the
@@ -669,29 +668,29 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     auto bf16_pair = [](float lo, float hi) -> uint32_t {
       return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
     };
+    // 16 threads per row, thread l of a row takes units l, l + 16, l + 32, l + 48
+    // (16-B units of the bf16 row = 8 dims = one code word): the 16 stores of a row
+    // land on 16 distinct slots of the swizzled row, so they are free of bank
+    // conflicts (rows of 8 threads x 8 consecutive units conflicted 4 ways).
     auto dequant = [&](int c) {
       const unsigned char* st = raw(c);
-      for (int x = threadIdx.x; x < DRC * 8; x += 64 * NW) {
-        const int rr = x >> 3, part = x & 7;
-        const uint4 w0 = *reinterpret_cast<const uint4*>(st + rr * 256 + part * 32);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(st + rr * 256 + part * 32 + 16);
-        const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + DRC * 256 + rr * 32 + part * 4);
-        const uint32_t cw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float scl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) scl[j] = e4m3_decode((sw >> (8 * j)) & 0xFFu);
+      for (int x = threadIdx.x; x < DRC * 16; x += 64 * NW) {
+        const int rr = x >> 4, l = x & 15;
+        const uint32_t* crow = reinterpret_cast<const uint32_t*>(st + rr * 256);
+        const unsigned char* srow = st + DRC * 256 + rr * 32;
         unsigned char* drow = dqb(c) + rr * PRS;
         const int sz = swz(rr & 15);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {   // 16-B unit: 8 dims, one word of codes
-          const float sc = scl[u >> 1];
-          const uint32_t ev = to_e4m3(cw[u] & 0x0F0F0F0Fu);          // dims 0, 2, 4, 6
-          const uint32_t od = to_e4m3((cw[u] >> 4) & 0x0F0F0F0Fu);   // dims 1, 3, 5, 7
+        for (int j = 0; j < 4; ++j) {
+          const int unit = 16 * j + l;
+          const uint32_t w = crow[unit];
+          const float sc = e4m3_decode(srow[unit >> 1]);
+          const uint32_t ev = to_e4m3(w & 0x0F0F0F0Fu);          // dims 0, 2, 4, 6
+          const uint32_t od = to_e4m3((w >> 4) & 0x0F0F0F0Fu);   // dims 1, 3, 5, 7
           const v2f e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false), e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);
           const v2f o0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false), o1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);
           const uint4 h = make_uint4(bf16_pair(e0.x * sc, o0.x * sc), bf16_pair(e0.y * sc, o0.y * sc),
                                      bf16_pair(e1.x * sc, o1.x * sc), bf16_pair(e1.y * sc, o1.y * sc));
-          const int unit = part * 8 + u;
           *reinterpret_cast<uint4*>(drow + ((unit ^ sz) << 4)) = h;
         }
       }
