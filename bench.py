@@ -13,8 +13,8 @@ decode step with the main KV stored as FP4.
 
 Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
-on (torch's current stream).  The CPU oracle is timed on a bounded sample of the
-same workload on this host (`cpu_baseline`).
+on (torch's current stream).  The CPU oracle is timed on this host on the same
+workload (`cpu_baseline`): the whole prefill step, unsampled.
 """
 from __future__ import annotations
 
@@ -582,7 +582,7 @@ def main():
         del ab
         torch.cuda.empty_cache()
     if not args.no_cpu:
-        log("cpu baseline: oracle on a bounded sample")
+        log("cpu baseline: the oracle on the whole prefill step")
         pb2 = PrefillBench(torch, K, synth)
         out["cpu_baseline"] = cpu_baseline_prefill(pb2)
     print(json.dumps(out), flush=True)

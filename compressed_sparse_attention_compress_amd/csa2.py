@@ -8,7 +8,6 @@ no fallback implementation.
 from __future__ import annotations
 
 import ctypes as C
-import math
 import os
 from typing import Optional
 
@@ -52,7 +51,7 @@ class CompressStepArgs(C.Structure):
                 ("rope_base", C.c_float), ("x", vp), ("pos", vp), ("w_kv", vp), ("w_gate", vp), ("gamma", vp),
                 ("w_ik", vp), ("state", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
                 ("latent_pre", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("kv_fmt", i32),
-                ("kv_scales", vp)]
+                ("kv_scales", vp), ("n_entries", i32)]
 
 
 class IndexKArgs(C.Structure):
@@ -295,9 +294,11 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
 
 def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, ik_codes, ik_scales, m: int,
                        latent_pre=None, eps: float = 1e-6, rope_base: float = 10000.0, workspace=None, stream=None,
-                       kv_scales=None):
+                       kv_scales=None, n_entries: int = 0):
     """Decode append: x [B, D] (one new token per sequence at positions pos [B]);
-    state [B, 3, 512] float32 (None iff m == 1).  Returns the workspace used."""
+    state [B, 3, 512] float32 (None iff m == 1).  With a runtime, n_entries (the
+    longest sequence's entry count after the step) is republished in the
+    compress_kv and index_k slots.  Returns the workspace used."""
     B, D = x.shape
     if workspace is None and B > 0:
         workspace = torch.empty(B * 1024 * 4 * 4, dtype=torch.uint8, device=x.device)
@@ -306,7 +307,8 @@ def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, i
                          w_ik=_ptr(w_ik), state=_ptr(state), kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes),
                          ik_scales=_ptr(ik_scales), latent_pre=_ptr(latent_pre), workspace=_ptr(workspace),
                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
-                         kv_fmt=KV_DENSE if kv_scales is None else KV_FP4, kv_scales=_ptr(kv_scales))
+                         kv_fmt=KV_DENSE if kv_scales is None else KV_FP4, kv_scales=_ptr(kv_scales),
+                         n_entries=n_entries)
     _check(lib().csa2_compress_step(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
@@ -355,6 +357,3 @@ def csa2_layer_forward(rt: Runtime, cfg: LayerCfg, io: LayerIO, stream=None):
 def version() -> str:
     return lib().csa2_version().decode()
 
-
-def default_scale() -> float:
-    return 1.0 / math.sqrt(512.0)

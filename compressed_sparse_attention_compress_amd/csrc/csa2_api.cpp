@@ -288,15 +288,20 @@ csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_st
 }
 
 csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream) {
-  (void)rt;
   csa2_status s = check_compress_step(a);
   if (s != CSA2_OK) return s;
+  REQ(rt == nullptr || (a->n_entries >= 0 && a->n_entries <= a->N_cap), CSA2_ERR_SHAPE,
+      "csa2_compress_step: n_entries (%d) must be in [0, N_cap = %d]", a->n_entries, a->N_cap);
   hipError_t e = csa2::launch_compress_step(a->dtype, a->x, a->pos, a->w_kv, a->w_gate, a->gamma, a->w_ik, a->state,
                                             a->kv_cache, a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr,
                                             a->ik_codes, a->ik_scales, a->latent_pre,
                                             static_cast<float*>(a->workspace), a->B, a->D, a->m, a->N_cap, a->eps,
                                             a->rope_base, st(stream));
   if (e != hipSuccess) return hip_status(e, "csa2_compress_step launch");
+  // the Full layer's caches as they stand after this step, for the layers that borrow them
+  publish(rt, CSA2_SLOT_COMPRESS_KV, a->kv_cache, a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr, a->dtype, a->B,
+          a->N_cap, a->n_entries, a->m, a->kv_fmt);
+  publish(rt, CSA2_SLOT_INDEX_K, a->ik_codes, a->ik_scales, 0, a->B, a->N_cap, a->n_entries, a->m);
   return ok();
 }
 
@@ -466,6 +471,14 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     }
     s = resolve_attn(rt, probe);
     if (s != CSA2_OK) return s;
+    // the attention workspace, for the main KV actually attended (a borrowed FP4
+    // cache may be dequantised whole), before anything is enqueued
+    const csa2::AttnPlan ap = csa2::plan_attn(probe.dtype, probe.B, probe.T, probe.H, probe.k, probe.W,
+                                              probe.kv_fmt == CSA2_KV_FP4, probe.N_cap);
+    REQ(ap.ws_bytes == 0 || (io->workspace != nullptr && io->workspace_bytes >= ap.ws_bytes), CSA2_ERR_WORKSPACE,
+        "csa2_layer_forward: attention needs a workspace of %zu bytes (got %zu)", ap.ws_bytes, io->workspace_bytes);
+    REQ(ap.ws_bytes == 0 || ((uintptr_t)io->workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
+        "csa2_layer_forward: workspace not 16-byte aligned");
   }
   // ---- enqueue
   if (cfg->mode == CSA2_FULL) {

@@ -94,6 +94,7 @@ __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const i
         cnt += __popcll(bal);
       }
     }
+    if (k <= 0) after_issue();   // no id loads: the loop above did not run
     if (lane == 0) *n_sel_s = cnt;
   } else {
     after_issue();

@@ -9,20 +9,30 @@
 // scores outside it being -inf; [P3] "…分级缓存", section five).
 // Ties go to the smaller entry id; -0 and +0 are equal.
 //
-// Kernel 1 (score_chunk): one workgroup per (query, chunk of C entries).  Each
-// wave scores tiles of 16 entries with MFMA 16x16x32: rows = 16 indexer heads
-// (two row tiles for 32 heads), columns = 16 entries, one k-step per 32-dim
-// quantisation block.  The FP4 codes are expanded with v_cvt_scalef32_pk_bf16_fp4
-// (unit scale: exact) and the block's E4M3 scale, which is per entry and so per
-// accumulator column, multiplies the block's partial product afterwards.  The
-// accumulator gives each lane 8 heads of one entry, so ReLU * w and the head sum
-// are in-lane plus two cross-lane adds.  Scores go to LDS as order-preserving
-// keys; a radix select (11-bit digits over key|local-index composites, all
-// distinct so no tie pass is needed) keeps the chunk's best min(k, C), and for
-// HSI the chunk's block maxima are written too.
-// Kernel 2 (topk_merge): one workgroup per query: the same select over all chunk
-// candidates (key|entry-id composites), indices sorted ascending and padded with
-// -1; with HSI BUILD also the n_b best blocks (newest block forced) as the pool.
+// Dequantisation (every bf16 path): a key element is an E2M1 value times an E4M3
+// block scale, exact in fp16.  v_cvt_scalef32_pk_f16_fp4 expands the codes and
+// applies the power of two of the scale, one v_pk_mul_f16 applies its sign and
+// significand, so the block scale sits inside the MFMA operand and the four
+// 32-dim blocks of a key chain into one v_mfma_f32_16x16x32_f16 accumulator.  The
+// bf16 query is exact in fp16 once each head is moved into range by a power of
+// two, which the head weight takes back (it commutes with the ReLU).  The fp32
+// path expands to fp32 and multiplies the block scale into each block's partial
+// product instead.
+//
+// Kernel score_chunk: one workgroup per (query, chunk of C entries); codes and
+// scales are loaded straight into registers through buffer resources.  Each
+// 16-entry tile is one MFMA column block with the indexer heads as rows; the
+// weighted ReLU sums are head-summed with permlane swaps and written to LDS as
+// order-preserving keys; a radix select (11-bit digits) keeps the chunk's best
+// min(k, C) with a lower bound for the merge, and for HSI the chunk's block
+// maxima are written too.
+// Kernel score_qtile_bf16 + select_rows (many queries over a cache of at most
+// 8192 entries): 4 queries per workgroup share each dequantised tile; keys go to
+// a key matrix, then one wave per query selects its k best.
+// Kernel topk_merge: one workgroup per query: the select over all chunk
+// candidates at or above the merge bound, indices sorted ascending and padded
+// with -1; with HSI BUILD also the n_b best blocks (newest block forced) as the
+// pool.
 #include "csa2_internal.h"
 #include "device_common.h"
 #include "lds_dma.h"

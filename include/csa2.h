@@ -197,9 +197,15 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
  *   latent_pre [B, 512] float32 out      that entry's latent before RoPE (NULL: not written)
  *   workspace  csa2_workspace_size(CSA2_OP_COMPRESS_STEP) bytes (B * 16384: C and
  *              Z partial sums of 4 quarters of the hidden dims), 16-byte aligned
- * Rows pos/m >= N_cap are not written.  The runtime slots are not changed (after
- * the layer's prefill they already point at these caches; consumers take the
- * visible range from q_pos).                                                 */
+ *   n_entries  (host) entries of the longest sequence once this step is done, i.e.
+ *              max over b of (pos[b] + 1) / m for the positions reached so far; in
+ *              [0, N_cap].  Read only when rt != NULL.
+ * Rows pos/m >= N_cap are not written.  With rt != NULL the compress_kv slot is
+ * republished as (kv_cache, kv_scales) and the index_k slot as (ik_codes,
+ * ik_scales), both with n_entries entries, so that Reindex and Reuse layers that
+ * borrow them see the appended entries ([P1] section "共享池里有四样东西": the
+ * slot holds the Full layer's cache as it grows; a query at position p still sees
+ * only the entries whose group ended at or before p).                        */
 typedef struct csa2_compress_step_args {
   int32_t dtype;            /* csa2_dtype of x, w_kv, w_gate, w_ik, kv_cache */
   int32_t B, D, m;
@@ -220,6 +226,7 @@ typedef struct csa2_compress_step_args {
   size_t workspace_bytes;
   int32_t kv_fmt;           /* csa2_kv_fmt */
   uint8_t* kv_scales;       /* FP4 only: [B, N_cap, 32] */
+  int32_t n_entries;        /* host; see above (read only with rt != NULL) */
 } csa2_compress_step_args;
 
 csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream);
@@ -359,7 +366,9 @@ typedef enum csa2_op {
 
 /* Device workspace bytes the op needs for these arguments (args points to the
  * op's argument struct; for CSA2_OP_LAYER a csa2_layer_io with the cfg passed
- * through `cfg`, else NULL). */
+ * through `cfg`, else NULL).  For a Reindex or Reuse layer, io->N_cap and
+ * cfg->kv_fmt are read as those of the main KV the layer borrows (the Full
+ * layer's cache), since attention there may dequantise that whole cache. */
 csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_cfg* cfg, size_t* bytes);
 
 /* FP4 index-K packing alone (test hook for bit-exactness): rows [n_rows, 128]

@@ -547,6 +547,10 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
         rt.get("topk_idxs")
     else:
         raise ValueError(cfg.mode)
+    return _attend(rt, cfg, inp)
+
+
+def _attend(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
     kv = rt.compress_kv
     topk = rt.topk_idxs
     B, T = inp.q_pos.shape
@@ -557,3 +561,63 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
                                        int(inp.swa_pos0[b]), int(inp.q_pos[b, t]), cfg.W,
                                        cfg.scale)[0]
     return o
+
+
+# ---------------------------------------------------------------------------
+# Decode: a Full layer appends one token per sequence to the caches it owns and
+# publishes, and the layers that borrow them see the grown caches ([P1] section
+# "共享池里有四样东西": the slots hold the Full layer's main KV and index K, one
+# position each; [P1] compressor section: an entry exists once its group of m
+# tokens is complete).
+# ---------------------------------------------------------------------------
+
+def layer_append(rt: Runtime, cfg: LayerConfig, pending: list, x_tok, pos):
+    """One decode token per sequence for a Full layer.  x_tok [B, D]; pos [B]
+    absolute positions (< 0: no token for that sequence); pending[b] is the
+    partial-group state of `compress_step`.  A completed group's entry (main-KV
+    row and index-K row, computed as `compress` and `index_k` would) is written at
+    row g of the runtime's compress_kv / index_k, which grow as needed.  Returns
+    the ids of the entries written, per sequence (None where none)."""
+    kv = rt.get("compress_kv")
+    codes, scales = rt.get("index_k")
+    written = []
+    for b in range(len(pos)):
+        p = int(pos[b])
+        if p < 0:
+            written.append(None)
+            continue
+        pending[b], entry = compress_step(pending[b], x_tok[b], cfg.w_kv, cfg.w_gate, cfg.gamma, p, cfg.m,
+                                          cfg.eps, cfg.rope_base)
+        if entry is None:
+            written.append(None)
+            continue
+        g, latent_pre, row = entry
+        _, c, s = index_k(latent_pre[None], cfg.w_ik, np.array([g * cfg.m]), cfg.rope_base)
+        if cfg.kv_fp4:
+            row = kv_fp4_unpack(*kv_fp4_pack(row[None].astype(np.float32)))[0]
+        if g >= kv.shape[1]:
+            grow = g + 1 - kv.shape[1]
+            kv = np.concatenate([kv, np.zeros((kv.shape[0], grow, kv.shape[2]))], axis=1)
+            codes = np.concatenate([codes, np.zeros((codes.shape[0], grow, codes.shape[2]), codes.dtype)], axis=1)
+            scales = np.concatenate([scales, np.zeros((scales.shape[0], grow, scales.shape[2]), scales.dtype)],
+                                    axis=1)
+        kv[b, g], codes[b, g], scales[b, g] = row, c[0], s[0]
+        written.append(g)
+    rt.compress_kv, rt.index_k = kv, (codes, scales)
+    rt.writes += ["compress_kv", "index_k"]
+    return written
+
+
+def full_decode_step(rt: Runtime, cfg: LayerConfig, pending: list, x_tok, inp: LayerInputs):
+    """A Full layer at decode: append the new tokens (`layer_append`, positions
+    inp.q_pos[:, 0]), then select over its index K as it now stands and attend,
+    as the Full branch of `layer_forward` does after its compressor."""
+    assert cfg.mode == FULL and inp.q_pos.shape[1] == 1
+    layer_append(rt, cfg, pending, x_tok, inp.q_pos[:, 0])
+    topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k)
+    rt.topk_idxs = topk
+    rt.writes.append("topk_idxs")
+    if cands is not None:
+        rt.candidates, rt.candidates_s = cands, cfg.hsi_s
+        rt.writes.append("candidates")
+    return _attend(rt, cfg, inp)

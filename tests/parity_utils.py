@@ -8,7 +8,9 @@
 * FP4 codes / scale bytes: bit-exact, except that a code may differ where the
   oracle's u/s lies within 1e-3 relative of an E2M1 rounding midpoint, and a scale
   byte where amax/6 lies within 1e-3 relative of an E4M3 midpoint (then the whole
-  block is exempt).
+  block is exempt).  Codes 0x0 and 0x8 (zero with either sign) may stand for one
+  another only where |u/s| <= 1e-3: the sign of a value that close to zero is
+  decided by summation order, and both codes decode to zero.
 * Floating-point outputs: per row (token, head), max|gpu - ref| / max|ref|.
 """
 from __future__ import annotations
@@ -20,6 +22,7 @@ import numpy as np
 from oracle import csa2_oracle as O
 
 E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+ZERO_BAND = 1e-3   # |u / s| below which codes 0x0 and 0x8 (+0 and -0) are interchangeable
 _E4M3_GRID = O.e4m3_decode(np.arange(0x7F))
 E4M3_MIDS = (_E4M3_GRID[:-1] + _E4M3_GRID[1:]) / 2
 
@@ -100,9 +103,11 @@ def check_fp4(u, codes_gpu, scales_gpu, tag="", block=32):
         return out.reshape(rows, nb, block)
     cg, co = unpack(codes_gpu), unpack(codes_o)
     cdiff = (cg != co) & ~sdiff[:, :, None]
-    # a value within rounding of zero may carry either sign: codes 0x0 and 0x8 both
-    # decode to zero, so that pair is no difference in value
-    signed_zero = ((cg & 7) == 0) & ((co & 7) == 0)
+    # codes 0x0 and 0x8 both decode to zero; they may stand for one another only
+    # where the value itself is within rounding of zero, i.e. |u / s| <= 1e-3 (the
+    # same 1e-3 band as the midpoints, in units of the block scale), so that a
+    # wrong sign on a clearly nonzero sub-0.25 s value still fails
+    signed_zero = ((cg & 7) == 0) & ((co & 7) == 0) & (np.abs(ratio) <= ZERO_BAND)
     ok = (near_any(ratio[cdiff], E2M1_MIDS) | (s[:, :, None].repeat(block, 2)[cdiff] == 0)
           | signed_zero[cdiff])
     assert np.all(ok), f"{tag}: {np.count_nonzero(~ok)} codes differ away from an E2M1 midpoint"

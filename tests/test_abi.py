@@ -45,12 +45,6 @@ def test_runtime_slots_start_empty_and_reset():
     rt.close()
 
 
-def _fake(addr=0x1000):
-    class P:  # stands in for a tensor in pointer-only argument structs
-        pass
-    return addr
-
-
 def test_reuse_before_full_is_slot_empty():
     rt = K.Runtime()
     cfg = K.layer_cfg(K.REUSE, K.CSA2_BF16, m=2, k=512, W=128, H_I=32, H=64)
@@ -125,6 +119,20 @@ def test_compress_step_validation(field, value, status):
     a.workspace_bytes = 0
     assert K.lib().csa2_workspace_size(K.OP_COMPRESS_STEP, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
     assert n.value == a.B * 1024 * 4 * 4
+
+
+def test_compress_step_with_runtime_checks_the_entry_count():
+    # with a runtime the step republishes the caches with n_entries, which must fit
+    # the cache; an invalid call leaves the slots untouched (nothing is enqueued)
+    rt = K.Runtime()
+    a = K.CompressStepArgs(dtype=1, B=4, D=256, m=2, N_cap=100, eps=1e-6, rope_base=1e4, x=0x1000, pos=0x1000,
+                           w_kv=0x1000, w_gate=0x1000, gamma=0x1000, w_ik=0x1000, state=0x1000, kv_cache=0x1000,
+                           ik_codes=0x1000, ik_scales=0x1000, workspace=0x1000, workspace_bytes=1 << 20,
+                           n_entries=101)
+    assert K.STATUS[K.lib().csa2_compress_step(rt.handle, C.byref(a), None)] == "CSA2_ERR_SHAPE"
+    a.n_entries = -1
+    assert K.STATUS[K.lib().csa2_compress_step(rt.handle, C.byref(a), None)] == "CSA2_ERR_SHAPE"
+    assert rt.slot(K.SLOT_COMPRESS_KV).filled == 0 and rt.slot(K.SLOT_INDEX_K).filled == 0
 
 
 def test_workspace_must_be_16_byte_aligned():

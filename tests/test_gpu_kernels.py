@@ -411,3 +411,36 @@ def test_sparse_attn_vs_oracle(dtype, H, k, W):
             assert np.allclose(lg[b, t], lse_ref, rtol=1e-4, atol=1e-3)
     say(f"  worst row rel err {worst:.2e}")
     assert worst <= TOL[dtype]
+
+
+@pytest.mark.parametrize("H,T", [(64, 4), (64, 150), (16, 4), (64, 300)])
+def test_sparse_attn_window_only_decode(H, T):
+    """k = 0 (window rows only) on the few-query bf16 path: with row splits (T = 4)
+    and with one split per query (B * T = 300); 4 and 1 waves per workgroup; and
+    on the many-query path (B * T = 600).  Every wave must still load its query
+    fragments although no top-k id is read."""
+    B, W, L_w = 2, 128, 400
+    say(f"case: sparse_attn window only k=0 H={H} T={T}")
+    q = synth.gaussian((B, T, H, 512), 1.0, 41, "q", 0, torch.bfloat16, DEV)
+    kv = synth.gaussian((B, 8, 512), 1.0, 41, "kv_cache", 0, torch.bfloat16, DEV)
+    swa = synth.gaussian((B, L_w, 512), 1.0, 41, "swa_kv", 0, torch.bfloat16, DEV)
+    pos0 = np.array([0, 100], np.int32)
+    gen = np.random.default_rng(41)
+    pos = np.stack([gen.integers(int(pos0[b]), int(pos0[b]) + L_w, size=T) for b in range(B)]).astype(np.int32)
+    tk = torch.full((B, T, 1), 3, dtype=torch.int32, device=DEV)   # never read with k = 0
+    o = torch.empty_like(q)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=DEV)
+    K.csa2_sparse_attn(None, q, kv, tk, swa, torch.from_numpy(pos0).to(DEV), torch.from_numpy(pos).to(DEV), o,
+                       W=W, k=0, lse=lse)
+    torch.cuda.synchronize()
+    og, lg = npy(o), lse.cpu().numpy()
+    swn, qn = npy(swa), npy(q)
+    worst = 0.0
+    for b in range(B):
+        for t in sorted(set([0, 1, 2, T - 1] + list(range(0, T, 37)))):
+            ref, _, rows = O.sparse_attention(qn[b, t], np.zeros((0, 512)), np.zeros(0, np.int64), swn[b],
+                                              int(pos0[b]), int(pos[b, t]), W)
+            worst = max(worst, row_rel_err(og[b, t], ref))
+            assert np.allclose(lg[b, t], O.attention_lse(qn[b, t], rows), rtol=1e-4, atol=1e-3), (b, t)
+    say(f"  worst row rel err {worst:.2e}")
+    assert worst <= TOL[torch.bfloat16]

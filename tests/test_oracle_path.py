@@ -409,3 +409,56 @@ def test_modes_hsi_build_and_use():
         sel = rt.topk_idxs[0, t]
         assert set(sel[sel >= 0].tolist()) <= pool
         assert len(sel[sel >= 0]) == min(4, len(pool))
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_decode_append_grows_the_slots_like_a_longer_prefill(m):
+    # a Full prefill of P tokens, then S decode appends, leaves the runtime's main KV
+    # and index K equal to those of one Full prefill over all P + S tokens (the
+    # entries of complete groups; the trailing partial group is not an entry yet)
+    B, P, S, D = 2, 8, 2 * m + (1 if m > 1 else 0), 32
+    full, inputs = _tiny_layers(B=B, L=P + S, D=D, m=m, seed=30 + m)
+    fin = inputs()
+    whole = O.Runtime()
+    O.layer_forward(whole, full, O.LayerInputs(q=fin.q, swa_kv=fin.swa_kv, q_pos=fin.q_pos, swa_pos0=fin.swa_pos0,
+                                               q_idx=fin.q_idx, w=fin.w, x=fin.x[:, :(P + S) // m * m]))
+    rt = O.Runtime()
+    pre = O.LayerInputs(q=fin.q[:, :P], swa_kv=fin.swa_kv, q_pos=fin.q_pos[:, :P], swa_pos0=fin.swa_pos0,
+                        q_idx=fin.q_idx[:, :P], w=fin.w[:, :P], x=fin.x[:, :P])
+    O.layer_forward(rt, full, pre)
+    pending = [[] for _ in range(B)]
+    written = []
+    for t in range(P, P + S):
+        written.append(O.layer_append(rt, full, pending, fin.x[:, t], np.full(B, t)))
+    n = (P + S) // m
+    assert rt.compress_kv.shape[1] == n
+    assert np.allclose(rt.compress_kv, whole.compress_kv, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(rt.index_k[0], whole.index_k[0]) and np.array_equal(rt.index_k[1], whole.index_k[1])
+    assert [w[0] for w in written if w[0] is not None] == list(range(P // m, n))
+    assert len(pending[0]) == (P + S) % m
+
+
+def test_full_decode_step_sees_appended_entries_and_reindex_follows():
+    # after the appends, a Full decode query selects among all its visible entries
+    # (k covers them all, so the appended ones must be in the set), and a Reindex
+    # layer reading the slots sees the same grown index K
+    B, P, m, k = 1, 8, 2, 16
+    full, inputs = _tiny_layers(B=B, L=P + 4, D=32, m=m, seed=40)
+    full.k = k
+    fin = inputs()
+    rt = O.Runtime()
+    O.layer_forward(rt, full, O.LayerInputs(q=fin.q[:, :P], swa_kv=fin.swa_kv, q_pos=fin.q_pos[:, :P],
+                                            swa_pos0=fin.swa_pos0, q_idx=fin.q_idx[:, :P], w=fin.w[:, :P],
+                                            x=fin.x[:, :P]))
+    pending = [[]]
+    O.layer_append(rt, full, pending, fin.x[:, P], np.array([P]))
+    p = P + 1
+    step = O.LayerInputs(q=fin.q[:, p:p + 1], swa_kv=fin.swa_kv, q_pos=np.array([[p]]), swa_pos0=fin.swa_pos0,
+                         q_idx=fin.q_idx[:, p:p + 1], w=fin.w[:, p:p + 1])
+    o = O.full_decode_step(rt, full, pending, fin.x[:, p], step)
+    sel = rt.topk_idxs[0, 0]
+    assert list(sel[sel >= 0]) == list(range((p + 1) // m))          # 5 entries, the last one just appended
+    ref = O.sparse_attention(step.q[0, 0], rt.compress_kv[0], sel, fin.swa_kv[0], 0, p, full.W)[0]
+    assert np.allclose(o[0, 0], ref)
+    O.layer_forward(rt, O.LayerConfig(O.REINDEX, m=m, k=k, W=full.W), step)
+    assert np.array_equal(rt.topk_idxs[0, 0], sel)
