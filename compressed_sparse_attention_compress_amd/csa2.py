@@ -101,6 +101,7 @@ EXPORTS = {
     "csa2_compress": ([vp, C.POINTER(CompressArgs), vp], i32),
     "csa2_index_k": ([vp, C.POINTER(IndexKArgs), vp], i32),
     "csa2_score_topk": ([vp, C.POINTER(ScoreTopkArgs), vp], i32),
+    "csa2_score_topk_noalloc": ([vp, C.POINTER(ScoreTopkArgs), vp], i32),
     "csa2_sparse_attn": ([vp, C.POINTER(SparseAttnArgs), vp], i32),
     "csa2_compress_step": ([vp, C.POINTER(CompressStepArgs), vp], i32),
     "csa2_layer_forward": ([vp, C.POINTER(LayerCfg), C.POINTER(LayerIO), vp], i32),
@@ -241,6 +242,18 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
     a = score_topk_args(workspace=workspace, **kw)
     _check(lib().csa2_score_topk(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
+
+
+def csa2_score_topk_noalloc(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int,
+                            N_cap: Optional[int] = None, hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0,
+                            candidates=None, stream=None):
+    """csa2_score_topk with the library's fixed device scratch (no workspace, no
+    allocation): for callers that cannot allocate."""
+    if N_cap is None:
+        N_cap = codes.shape[1]
+    a = score_topk_args(q_idx=q_idx, w=w, codes=codes, scales=scales, q_pos=q_pos, topk=topk, n_entries=n_entries,
+                        m=m, k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates)
+    _check(lib().csa2_score_topk_noalloc(_rt(rt), C.byref(a), _stream(stream)))
 
 
 def sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: int, N_cap: int, scale: float = 0.0,

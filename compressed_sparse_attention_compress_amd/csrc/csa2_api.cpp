@@ -315,6 +315,25 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
   return ok();
 }
 
+}  // extern "C"
+
+namespace csa2 {
+
+csa2_status set_error(csa2_status s, const char* msg) { return fail(s, "%s", msg); }
+
+csa2_status score_topk_plan(const csa2_runtime* rt, const csa2_score_topk_args* in, size_t* bytes) {
+  REQ(in && bytes, CSA2_ERR_INVALID_ARG, "csa2_score_topk: args is NULL");
+  csa2_score_topk_args a = *in;
+  csa2_status s = resolve_score(rt, a);
+  if (s != CSA2_OK) return s;
+  *bytes = plan_score(a.dtype, a.B, a.T, score_scan(a), a.k, a.hsi, a.hsi_s, a.hsi_nb).total_bytes;
+  return ok();
+}
+
+}  // namespace csa2
+
+extern "C" {
+
 csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* in, csa2_stream stream) {
   REQ(in, CSA2_ERR_INVALID_ARG, "csa2_score_topk: args is NULL");
   csa2_score_topk_args a = *in;

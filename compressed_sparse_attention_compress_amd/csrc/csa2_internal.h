@@ -52,6 +52,16 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
                              int m, int k, int hsi, int hsi_s, int hsi_nb, void* workspace,
                              const ScorePlan& plan, hipStream_t stream);
 
+// ---- host API (csa2_api.cpp)
+// Validates a score/top-k call (resolving slots) and gives the workspace bytes it
+// needs; returns a csa2_status (int) and sets the thread's last error on failure.
+}  // namespace csa2
+#include "csa2.h"
+namespace csa2 {
+csa2_status score_topk_plan(const csa2_runtime* rt, const csa2_score_topk_args* a, size_t* bytes);
+// Sets the thread's last error message and returns s.
+csa2_status set_error(csa2_status s, const char* msg);
+
 // ---- sparse attention (k_attn.hip)
 struct AttnPlan {
   bool decode;      // few queries: workgroup per (query, split, head group)

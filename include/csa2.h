@@ -269,6 +269,21 @@ typedef struct csa2_score_topk_args {
 
 csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa2_stream stream);
 
+/* csa2_score_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments and results, but its scratch is a fixed device array of
+ * CSA2_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library, one per GPU, held until
+ * the process ends.  a->workspace must be NULL and a->workspace_bytes 0.  A call
+ * whose csa2_workspace_size(CSA2_OP_SCORE_TOPK) exceeds the array returns
+ * CSA2_ERR_WORKSPACE before anything is enqueued (the decode workloads, e.g. 64
+ * queries over 131072 entries, need about 8.4 MB; many-query prefill calls need
+ * more and take csa2_score_topk).  The call allocates and frees nothing.  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in the array has to be cleared between calls. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+csa2_status csa2_score_topk_noalloc(csa2_runtime* rt, const csa2_score_topk_args* a, csa2_stream stream);
+
 /* ------------------------------------------------------------------------ */
 /* (e) Sparse attention ([P1] section "一层全局注意力算四样东西": the layer's own
  * query reads the selected entries plus its 128-entry sliding window; [P2]

@@ -225,3 +225,14 @@ def test_kv_fp4_pack_zero_rows_is_noop():
     assert K.lib().csa2_kv_fp4_pack(None, 0, None, None, None) == 0
     assert K.STATUS[K.lib().csa2_kv_fp4_pack(None, 5, None, None, None)] == "CSA2_ERR_INVALID_ARG"
     assert K.STATUS[K.lib().csa2_kv_fp4_pack(0x1008, 5, 0x1000, 0x1000, None)] == "CSA2_ERR_INVALID_ARG"
+
+
+def test_noalloc_score_refuses_oversized_calls_and_workspaces():
+    # host checks come before any device call: 512 queries over 8192 entries need a
+    # 16 MiB key matrix + 256 B, more than the fixed scratch holds
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=512, H_I=32, N_cap=8192, n_entries=8192, m=1, k=512, q_idx=0x1000,
+                        w=0x1000, codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000)
+    assert K.STATUS[K.lib().csa2_score_topk_noalloc(None, C.byref(a), None)] == "CSA2_ERR_WORKSPACE"
+    assert b"scratch" in K.lib().csa2_last_error()
+    a.T, a.workspace, a.workspace_bytes = 1, 0x1000, 1 << 20
+    assert K.STATUS[K.lib().csa2_score_topk_noalloc(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"
