@@ -8,13 +8,17 @@ one batch (B=1, L=8192, hidden 4096, m=2, 32x128 FP4 indexer heads, top-512, win
 batched decode step (Reindex + Reuse over 64 sequences x 131072 m=2 entries), and
 a third ("decode_hsi_1m") the 1M-context decode step with the HSI candidate pool
 (4 sequences x 524288 entries), a fourth ("decode_append") the Full layer's
-decode append of one token per sequence, and a fifth ("decode_fp4kv") the batched
-decode step with the main KV stored as FP4.
+decode append of one token per sequence, a fifth ("decode_fp4kv") the batched
+decode step with the main KV stored as FP4, and two more the decoder macro-block
+prefill at L=32768, m=1 (Full, Reindex, Reuse, Reuse through csa2_layer_forward):
+"decoder_block" over all positions and "decoder_replay" with only the last R
+positions replayed through the decoder layers.
 
 Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
-on (torch's current stream).  The CPU oracle is timed on this host on the same
-workload (`cpu_baseline`): the whole prefill step, unsampled.
+on (torch's current stream).  The CPU oracle is timed on this host beside each
+record (`cpu_baseline`): the whole prefill step unsampled for the headline; a
+stated sample, extrapolated and labelled so, for the others.
 """
 from __future__ import annotations
 
@@ -189,7 +193,7 @@ class HsiDecodeBench:
         dev = "cuda"
         self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
         self.s_blk, self.n_b, self.copies = s_blk, n_b, copies
-        seed = 12
+        self.seed = seed = 12
         self.kv = torch.empty(B, n_entries, 512, dtype=torch.bfloat16, device=dev)
         codes = torch.empty(B, n_entries, 64, dtype=torch.uint8, device=dev)
         scales = torch.empty(B, n_entries, 4, dtype=torch.uint8, device=dev)
@@ -248,6 +252,85 @@ class HsiDecodeBench:
             "score_pool": {"bytes": 68.0 * B * pool + q_bytes + B * (self.n_b + self.k) * 4},
             "attn_2_layers": {"bytes": 2 * (rows * 1024.0 + 2.0 * B * self.H * 512 * 2)},
         }
+
+
+# --------------------------------------------------------------------------- C3
+
+class DecoderBench:
+    """Decoder macro-block prefill: one Full layer at m=1 compresses the encoder
+    output H20 of all L prompt tokens into the shared global KV and index K, then
+    the block's four layers (Full, Reindex, Reuse, Reuse) run through
+    csa2_layer_forward for the last R prompt positions, each layer with its own
+    queries and its window KV of the replayed positions.  R = L is the full
+    decoder prefill; R < L is the bounded replay (only the prompt's tail passes
+    through the decoder layers, their windows limited to that tail)."""
+
+    def __init__(self, torch, K, synth, L=32768, R=None, D=4096, H_I=32, k=512, W=128, H=64, seed=31):
+        self.t, self.K = torch, K
+        dev = "cuda"
+        R = L if R is None else R
+        self.L, self.R, self.D, self.H_I, self.k, self.W, self.H = L, R, D, H_I, k, W, H
+        self.modes = [K.FULL, K.REINDEX, K.REUSE, K.REUSE]
+        bf = torch.bfloat16
+        self.seed = seed
+        self.x = synth.gaussian((1, L, D), 1.0, seed, "x", 0, bf, dev)
+        self.w_kv = synth.linear_weight(512, D, seed, "w_kv", 0, bf, dev)
+        self.w_ik = synth.linear_weight(128, 512, seed, "w_ik", 0, bf, dev)
+        self.gamma = torch.ones(512, dtype=torch.float32, device=dev)
+        self.q_pos = torch.arange(L - R, L, dtype=torch.int32, device=dev)[None].contiguous()
+        self.swa_pos0 = torch.full((1,), L - R, dtype=torch.int32, device=dev)
+        self.layers = []
+        for l in range(4):
+            lay = {"q": synth.gaussian((1, R, H, 512), 1.0, seed, "q", l, bf, dev),
+                   "swa_kv": synth.gaussian((1, R, 512), 1.0, seed, "swa_kv", l, bf, dev),
+                   "o": torch.empty(1, R, H, 512, dtype=bf, device=dev)}
+            if self.modes[l] != K.REUSE:
+                lay["q_idx"] = synth.gaussian((1, R, H_I, 128), 1.0, seed, "q_idx", l, bf, dev)
+                lay["w"] = synth.gaussian((1, R, H_I), 1.0, seed, "w", l, torch.float32, dev)
+                lay["topk"] = torch.empty(1, R, k, dtype=torch.int32, device=dev)
+            self.layers.append(lay)
+        self.lat = torch.empty(1, L, 512, dtype=torch.float32, device=dev)
+        self.kv = torch.empty(1, L, 512, dtype=bf, device=dev)
+        self.codes = torch.empty(1, L, 64, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(1, L, 4, dtype=torch.uint8, device=dev)
+        self.rt = K.Runtime()
+        self.cfgs = [K.layer_cfg(mde, K.CSA2_BF16, m=1, k=k, W=W, H_I=H_I, H=H) for mde in self.modes]
+        need = max(K.layer_workspace_bytes(c, self._io(l)) for l, c in enumerate(self.cfgs))
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def _io(self, l, ws=None):
+        K, lay = self.K, self.layers[l]
+        kw = dict(B=1, T=self.R, q_pos=self.q_pos, q=lay["q"], swa_kv=lay["swa_kv"], swa_pos0=self.swa_pos0,
+                  o=lay["o"], N_cap=self.L, workspace=ws)
+        if self.modes[l] == K.FULL:
+            kw.update(D=self.D, x=self.x, w_kv=self.w_kv, w_gate=None, gamma=self.gamma, w_ik=self.w_ik,
+                      latent_pre=self.lat, kv_cache=self.kv, ik_codes=self.codes, ik_scales=self.scales,
+                      T_x=self.L)
+        if self.modes[l] != K.REUSE:
+            kw.update(q_idx=lay["q_idx"], w=lay["w"], topk=lay["topk"])
+        return K.layer_io(**kw)
+
+    def step(self, events=None):
+        for l, cfg in enumerate(self.cfgs):
+            if events is not None:
+                events[l].record()
+            self.K.csa2_layer_forward(self.rt, cfg, self._io(l, self.ws))
+        if events is not None:
+            events[4].record()
+
+    def compress_only(self):
+        self.K.csa2_compress(None, self.x, self.w_kv, None, self.gamma, self.lat, self.kv, m=1)
+
+    def work(self):
+        L, R, k, W, H = self.L, self.R, self.k, self.W, self.H
+        pos = range(L - R, L)
+        pairs = sum(p + 1 for p in pos)                       # m = 1: entry g visible at p >= g
+        rows = sum(min(k, p + 1) + min(W, p - (L - R) + 1) for p in pos)
+        return {"compress_flop": 2.0 * L * self.D * 512, "index_k_flop": 2.0 * L * 512 * 128,
+                "score_flop_per_layer": 2.0 * pairs * self.H_I * 128, "attn_flop_per_layer": 4.0 * rows * H * 512,
+                "flop": 2.0 * L * self.D * 512 + 2.0 * L * 512 * 128 + 2 * 2.0 * pairs * self.H_I * 128
+                        + 4 * 4.0 * rows * H * 512}
 
 
 # ------------------------------------------------------------ decode append
@@ -412,6 +495,125 @@ def cpu_baseline_prefill(bench, min_seconds=10.0):
             "measured_s": round(t_build + t_q, 2)}
 
 
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decoder(db, every=256):
+    """Oracle on this host for the decoder block: the compressor and index K over
+    all L prompt tokens in full, then score + top-k + attention of every
+    `every`-th replayed query through the four layers; the query part is
+    extrapolated to all R replayed queries (work per query is the same up to its
+    visible-entry count, which the sample spans evenly)."""
+    import numpy as np
+    from oracle import csa2_oracle as O
+    K = db.K
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    x, w_kv, gamma, w_ik = f64(db.x[0]), f64(db.w_kv), f64(db.gamma), f64(db.w_ik)
+    lays = [{n: f64(v[0]) for n, v in lay.items() if n in ("q", "q_idx", "w", "swa_kv")} for lay in db.layers]
+    t0 = time.perf_counter()
+    lat, kv, ids = O.compress(x, w_kv, None, gamma, 1, 0)
+    _, codes, scales = O.index_k(lat, w_ik, ids)
+    kd = O.fp4_unpack(codes, scales)
+    t1 = time.perf_counter()
+    sample = list(range(0, db.R, every))
+    for j in sample:
+        p = db.L - db.R + j
+        sel = None
+        for l, lay in enumerate(lays):
+            if db.modes[l] != K.REUSE:
+                sel = O.topk_select(O.index_scores(lay["q_idx"][j], lay["w"][j], kd, O.visible_entries(p, 1)),
+                                    db.k)
+            O.sparse_attention(lay["q"][j], kv, sel, lay["swa_kv"], db.L - db.R, p, db.W)
+    t2 = time.perf_counter()
+    total = (t1 - t0) + (t2 - t1) / len(sample) * db.R
+    return {"value": db.L / total, "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": (f"compressor + index K on all {db.L} tokens in full ({t1 - t0:.2f} s), then score + top-k + "
+                       f"attention through the 4 layers for every {every}th of the {db.R} replayed queries "
+                       f"({len(sample)} queries, {t2 - t1:.2f} s), extrapolated by the query count to "
+                       f"{total:.1f} s per step; numpy float64, BLAS threads = {_cores()}"),
+            "measured_s": round(t2 - t0, 2)}
+
+
+def cpu_baseline_decode(db, seqs=(0, 21, 42, 63)):
+    """Oracle on this host for the batched decode step on `seqs` of the B
+    sequences: index-K dequantisation, scores over all entries, top-k, then the
+    Reindex and the Reuse layer's attention; extrapolated by the sequence count.
+    The sequence's caches are drawn again from their seeds before the clock."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import csa2_oracle as O
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    p = int(db.q_pos[0, 0].item())
+    pos0 = int(db.swa_pos0[0].item())
+    spent = 0.0
+    for b in seqs:
+        codes, scales = O.fp4_pack(synth.cache_rows(db.N, 128, db.seed, "u", b, "cuda").cpu().numpy())
+        kv = f64(synth.cache_rows(db.N, 512, db.seed, "kv_cache", b, "cuda").to(torch.bfloat16))
+        if db.kv_fp4:
+            kv = O.kv_fp4_unpack(*O.kv_fp4_pack(kv.astype(np.float32)))
+        lay = [{n: f64(v[b]) for n, v in db.layers[l].items()} for l in range(2)]
+        t0 = time.perf_counter()
+        kd = O.fp4_unpack(codes, scales)
+        sel = O.topk_select(O.index_scores(lay[0]["q_idx"][0], lay[0]["w"][0], kd, db.N), db.k)
+        for l in range(2):
+            O.sparse_attention(lay[l]["q"][0], kv, sel, lay[l]["swa_kv"], pos0, p, db.W)
+        spent += time.perf_counter() - t0
+        del kv, kd
+    per_step = spent / len(seqs) * db.B
+    return {"value": per_step * 1e6, "unit": "us/step", "cores": _cores(), "kind": "oracle",
+            "sample": (f"{len(seqs)} of the {db.B} sequences (index-K dequantisation, scores over all {db.N} entries, "
+                       f"top-{db.k}, attention of the Reindex and the Reuse layer), {spent:.2f} s, extrapolated "
+                       f"by the sequence count; numpy float64, BLAS threads = {_cores()}"),
+            "measured_s": round(spent, 2)}
+
+
+def cpu_baseline_hsi(hb, seqs=(0,)):
+    """Oracle on this host for the 1M-context HSI decode step on `seqs` of the 4
+    sequences: the Full layer (scores over all entries, top-k, block maxima and
+    the pool), the Reindex layer inside the pool, and both layers' attention;
+    extrapolated by the sequence count."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import csa2_oracle as O
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    p = int(hb.q_pos[0, 0].item())
+    pos0 = int(hb.swa_pos0[0].item())
+    spent = 0.0
+    for b in seqs:
+        codes, scales = O.fp4_pack(synth.cache_rows(hb.N, 128, hb.seed, "u", b, "cuda").cpu().numpy())
+        kv = f64(synth.cache_rows(hb.N, 512, hb.seed, "kv_cache", b, "cuda").to(torch.bfloat16))
+        lay = [{n: f64(v[b]) for n, v in hb.layers[l].items()} for l in range(2)]
+        t0 = time.perf_counter()
+        kd = O.fp4_unpack(codes, scales)
+        sc = O.index_scores(lay[0]["q_idx"][0], lay[0]["w"][0], kd, hb.N)
+        sels = [O.topk_select(sc, hb.k)]
+        pool = O.pool_entries(O.hsi_pool(sc, hb.N, hb.s_blk, hb.n_b), hb.N, hb.s_blk)
+        sc2 = O.index_scores(lay[1]["q_idx"][0], lay[1]["w"][0], kd, hb.N)
+        sels.append(O.topk_select(sc2, hb.k, pool))
+        for l in range(2):
+            O.sparse_attention(lay[l]["q"][0], kv, sels[l], lay[l]["swa_kv"], pos0, p, hb.W)
+        spent += time.perf_counter() - t0
+        del kv, kd
+    per_step = spent / len(seqs) * hb.B
+    return {"value": per_step * 1e6, "unit": "us/step", "cores": _cores(), "kind": "oracle",
+            "sample": (f"{len(seqs)} of the {hb.B} sequences (Full layer: scores over all {hb.N} entries, top-{hb.k}, "
+                       f"block maxima and pool; Reindex layer inside the pool; both attentions), {spent:.2f} s, "
+                       f"extrapolated by the sequence count; numpy float64, BLAS threads = {_cores()}"),
+            "measured_s": round(spent, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +625,10 @@ def main():
     ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
     ap.add_argument("--no-append", action="store_true", help="skip the decode-append record")
     ap.add_argument("--no-fp4kv", action="store_true", help="skip the decode record with FP4 main KV")
+    ap.add_argument("--no-decoder", action="store_true",
+                    help="skip the decoder macro-block records (full prefill and bounded replay)")
+    ap.add_argument("--replay", type=int, default=2048,
+                    help="replayed tail length R of the bounded-replay decoder record")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches instead of a HIP graph replay of the step")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -510,6 +716,9 @@ def main():
             "attn_GBps": round(attn_gbs, 1),
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (dms * 1e-3), 4),
         }
+        if not args.no_cpu:
+            log("decode: cpu baseline (oracle, 4 of the sequences)")
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode(db)
         del db
         torch.cuda.empty_cache()
     if not args.no_decode and not args.no_fp4kv:
@@ -560,8 +769,50 @@ def main():
             "step_bytes": step_bytes,
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (hms * 1e-3), 4),
         }
+        if not args.no_cpu:
+            log("hsi decode: cpu baseline (oracle, 1 of the sequences)")
+            out["decode_hsi_1m"]["cpu_baseline"] = cpu_baseline_hsi(hb)
         del hb
         torch.cuda.empty_cache()
+    if not args.no_decoder:
+        for rec, R in (("decoder_block", None), ("decoder_replay", args.replay)):
+            log(f"{rec}: building inputs")
+            dcb = DecoderBench(torch, K, synth, R=R)
+            n_dec = max(3, args.steps // 2)
+            dec_eager, dec_st = time_steps(torch, dcb, 4, n_dec, 1)
+            dec_ms = time_graph(torch, dcb, n_dec, 1) if args.graph else dec_eager
+            dw = dcb.work()
+            # the projections' MFMA fraction, from the compressor call timed alone
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            dcb.compress_only()
+            ev[0].record()
+            for _ in range(5):
+                dcb.compress_only()
+            ev[1].record()
+            torch.cuda.synchronize()
+            c_ms = ev[0].elapsed_time(ev[1]) / 5
+            c_tf = dw["compress_flop"] / (c_ms * 1e-3) / 1e12
+            step_tf = dw["flop"] / (dec_ms * 1e-3) / 1e12
+            out[rec] = {
+                "workload": (f"decoder macro-block prefill: the Full layer (m=1) compresses H20 of all {dcb.L} "
+                             f"prompt tokens (hidden 4096) into the global KV and FP4 index K; Full, Reindex, Reuse, "
+                             f"Reuse through csa2_layer_forward for the last {dcb.R} positions (window KV of those "
+                             f"positions only), 32x128 indexer heads, top-512, SWA 128, 64 heads"
+                             + ("" if dcb.R == dcb.L else f"; bounded replay R={dcb.R}")),
+                "tokens_per_s": round(dcb.L / (dec_ms * 1e-3), 1), "ms_per_step": round(dec_ms, 4),
+                "ms_per_step_eager": round(dec_eager, 4),
+                "stages_ms": {n: round(t, 4) for n, t in zip(("full", "reindex", "reuse", "reuse2"), dec_st)},
+                "roofline": {"bound": "mfma", "kernel": "compress (projections)", "achieved": round(c_tf, 2),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(c_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                "step_tflops": round(step_tf, 2),
+                "step_frac_of_mfma_peak": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            }
+            if not args.no_cpu:
+                log(f"{rec}: cpu baseline (oracle)")
+                out[rec]["cpu_baseline"] = cpu_baseline_decoder(dcb)
+            del dcb
+            torch.cuda.empty_cache()
     if not args.no_append:
         log("decode append: building inputs")
         ab = AppendBench(torch, K, synth)

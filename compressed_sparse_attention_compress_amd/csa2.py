@@ -85,7 +85,8 @@ class LayerIO(C.Structure):
                 ("latent_pre", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
                 ("q_idx", vp), ("w", vp), ("topk", vp), ("candidates", vp),
                 ("q_pos", vp), ("q", vp), ("swa_kv", vp), ("L_w", i32), ("swa_pos0", vp),
-                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_scales", vp)]
+                ("o", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_scales", vp),
+                ("T_x", i32)]
 
 
 class SlotInfo(C.Structure):
@@ -346,7 +347,9 @@ def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, h
 
 def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,
              gamma=None, w_ik=None, latent_pre=None, kv_cache=None, ik_codes=None, ik_scales=None, q_idx=None,
-             w=None, topk=None, candidates=None, workspace=None, sink=None, kv_scales=None) -> LayerIO:
+             w=None, topk=None, candidates=None, workspace=None, sink=None, kv_scales=None, T_x=0) -> LayerIO:
+    """T_x: a Full layer's hidden-state tokens when they differ from the T queries
+    (decoder prefill with bounded replay: T_x = L prompt tokens, T = R replayed)."""
     return LayerIO(B=B, T=T, D=D, start_pos=start_pos, N_cap=N_cap, x=_ptr(x), w_kv=_ptr(w_kv),
                    w_gate=_ptr(w_gate), gamma=_ptr(gamma), w_ik=_ptr(w_ik), latent_pre=_ptr(latent_pre),
                    kv_cache=_ptr(kv_cache), ik_codes=_ptr(ik_codes), ik_scales=_ptr(ik_scales),
@@ -354,7 +357,7 @@ def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=N
                    q=_ptr(q), swa_kv=_ptr(swa_kv), L_w=swa_kv.shape[1], swa_pos0=_ptr(swa_pos0), o=_ptr(o),
                    workspace=_ptr(workspace),
                    workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
-                   sink=_ptr(sink), kv_scales=_ptr(kv_scales))
+                   sink=_ptr(sink), kv_scales=_ptr(kv_scales), T_x=T_x)
 
 
 def layer_workspace_bytes(cfg: LayerCfg, io: LayerIO) -> int:

@@ -411,19 +411,21 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
                                csa2_stream stream) {
   REQ(rt && cfg && io, CSA2_ERR_INVALID_ARG, "csa2_layer_forward: NULL argument");
   REQ(cfg->mode >= CSA2_FULL && cfg->mode <= CSA2_REUSE, CSA2_ERR_INVALID_ARG, "csa2_layer_forward: bad mode");
+  REQ(io->T_x >= 0, CSA2_ERR_SHAPE, "csa2_layer_forward: T_x must be >= 0");
+  const int T_x = io->T_x > 0 ? io->T_x : io->T;   // hidden-state tokens a Full layer compresses
   csa2_status s;
   int n_entries = 0;
   if (cfg->mode == CSA2_FULL) {
     REQ(cfg->hsi != CSA2_HSI_USE, CSA2_ERR_INVALID_ARG, "csa2_layer_forward: a Full layer cannot use a pool");
     csa2_compress_args ca{};
-    ca.dtype = cfg->dtype; ca.B = io->B; ca.T = io->T; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
+    ca.dtype = cfg->dtype; ca.B = io->B; ca.T = T_x; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
     ca.N_cap = io->N_cap; ca.eps = cfg->eps; ca.rope_base = cfg->rope_base; ca.x = io->x; ca.w_kv = io->w_kv;
     ca.w_gate = io->w_gate; ca.gamma = io->gamma; ca.latent_pre = io->latent_pre; ca.kv_cache = io->kv_cache;
     ca.kv_fmt = cfg->kv_fmt; ca.kv_scales = io->kv_scales;
     s = check_compress(&ca);
     if (s != CSA2_OK) return s;
     csa2_index_k_args ia{};
-    ia.dtype = cfg->dtype; ia.B = io->B; ia.N = io->T / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
+    ia.dtype = cfg->dtype; ia.B = io->B; ia.N = T_x / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
     ia.N_cap = io->N_cap; ia.rope_base = cfg->rope_base; ia.latent_pre = io->latent_pre; ia.w_ik = io->w_ik;
     ia.codes = io->ik_codes; ia.scales = io->ik_scales;
     s = check_index_k(&ia);
@@ -502,13 +504,13 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
   // ---- enqueue
   if (cfg->mode == CSA2_FULL) {
     csa2_compress_args ca{};
-    ca.dtype = cfg->dtype; ca.B = io->B; ca.T = io->T; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
+    ca.dtype = cfg->dtype; ca.B = io->B; ca.T = T_x; ca.D = io->D; ca.m = cfg->m; ca.start_pos = io->start_pos;
     ca.N_cap = io->N_cap; ca.eps = cfg->eps; ca.rope_base = cfg->rope_base; ca.x = io->x; ca.w_kv = io->w_kv;
     ca.w_gate = io->w_gate; ca.gamma = io->gamma; ca.latent_pre = io->latent_pre; ca.kv_cache = io->kv_cache;
     ca.kv_fmt = cfg->kv_fmt; ca.kv_scales = io->kv_scales;
     if ((s = csa2_compress(rt, &ca, stream)) != CSA2_OK) return s;
     csa2_index_k_args ia{};
-    ia.dtype = cfg->dtype; ia.B = io->B; ia.N = io->T / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
+    ia.dtype = cfg->dtype; ia.B = io->B; ia.N = T_x / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
     ia.N_cap = io->N_cap; ia.rope_base = cfg->rope_base; ia.latent_pre = io->latent_pre; ia.w_ik = io->w_ik;
     ia.codes = io->ik_codes; ia.scales = io->ik_scales;
     if ((s = csa2_index_k(rt, &ia, stream)) != CSA2_OK) return s;

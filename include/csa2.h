@@ -369,6 +369,14 @@ typedef struct csa2_layer_io {
   void* workspace; size_t workspace_bytes;
   const float* sink;        /* [H] float32 per-head attention sink, or NULL (see csa2_sparse_attn_args) */
   uint8_t* kv_scales;       /* Full with kv_fmt CSA2_KV_FP4: [B, N_cap, 32]; kv_cache then holds the codes */
+  int32_t T_x;              /* Full: hidden-state tokens compressed, x is [B, T_x, D] at positions start_pos ..
+                               start_pos + T_x - 1 (0: T_x = T).  The queries keep their own count T and
+                               positions q_pos.  A decoder prefill with bounded replay ([P2] "CED(Causal
+                               encoder-decoder)", decoder SWA bounded replay; [P3] section two, "为什么还要重放
+                               尾部"; [P4] "L'interaction avec le CED") compresses the encoder output of all
+                               L prompt tokens (T_x = L) while only the last R tokens pass through the
+                               decoder layers (T = R, q_pos = L-R .. L-1, window KV of the replayed
+                               segment only: swa_pos0 = L-R). */
 } csa2_layer_io;
 
 csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, const csa2_layer_io* io,

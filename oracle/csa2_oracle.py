@@ -621,3 +621,33 @@ def full_decode_step(rt: Runtime, cfg: LayerConfig, pending: list, x_tok, inp: L
         rt.candidates, rt.candidates_s = cands, cfg.hsi_s
         rt.writes.append("candidates")
     return _attend(rt, cfg, inp)
+
+
+# ---------------------------------------------------------------------------
+# Decoder prefill with bounded replay: [P2] "CED(Causal encoder-decoder)" (the
+# decoder's global KV is built from the encoder output; only the last positions
+# of the prompt go through the decoder layers, whose local window is limited to
+# that replayed segment; the truncation never touches the global KV), [P3]
+# section two ("为什么还要重放尾部": only a fixed tail passes through the decoder),
+# [P4] "L'interaction avec le CED" (the decoder's Full layer compresses H20, the
+# encoder output).  The replay length R is lost in extraction and is a parameter.
+# ---------------------------------------------------------------------------
+
+def decoder_replay(rt: Runtime, cfgs: list, layer_inputs: list, h20, R: int):
+    """Runs the decoder layers `cfgs` (cfgs[0] is the Full layer) over the last R of
+    the L prompt positions.  h20 [B, L, D] is the encoder output, compressed in
+    full by the Full layer into the shared global KV and index K; each
+    layer_inputs[l] gives q, q_idx, w for the R replayed positions ([B, R, ...])
+    and the layer's window KV rows for positions L-R .. L-1 ([B, R, 512]).
+    Returns the outputs of every layer, [B, R, H, 512] each."""
+    h20 = np.asarray(h20, dtype=np.float64)
+    B, L = h20.shape[:2]
+    assert 0 < R <= L
+    q_pos = np.tile(np.arange(L - R, L), (B, 1))
+    pos0 = np.full(B, L - R)
+    outs = []
+    for l, (cfg, li) in enumerate(zip(cfgs, layer_inputs)):
+        inp = LayerInputs(q=li.q, swa_kv=li.swa_kv, q_pos=q_pos, swa_pos0=pos0, q_idx=li.q_idx, w=li.w,
+                          x=h20 if l == 0 else None, start_pos=0)
+        outs.append(layer_forward(rt, cfg, inp))
+    return outs

@@ -183,6 +183,44 @@ def test_decoder_macro_block_full_size(K):
     assert n_exact >= n_all - 2 and n_att == 40
 
 
+def test_decoder_bounded_replay_full_size(K):
+    """L = 32768 prompt tokens, the last R = 2048 replayed through Full, Reindex,
+    Reuse, Reuse (the benchmark's DecoderBench itself); sampled replayed queries
+    against the oracle over the oracle's own global KV and index K."""
+    import bench
+    say("case: decoder bounded replay L=32768 R=2048 (benchmark launch configuration)")
+    db = bench.DecoderBench(torch, K, synth, R=2048)
+    db.step()
+    torch.cuda.synchronize()
+    L, R, k, W = db.L, db.R, db.k, db.W
+    lat_o, kv_o, ids = O.compress(f64(db.x[0]), f64(db.w_kv), None, f64(db.gamma), 1, 0)
+    u_o, codes_o, scales_o = O.index_k(lat_o, f64(db.w_ik), ids)
+    assert row_rel_err(f64(db.kv[0]), kv_o) <= TOL, "global KV rows"
+    cd, sd = db.codes[0].cpu().numpy(), db.scales[0].cpu().numpy()
+    check_fp4(u_o, cd, sd, "replay index K")
+    flips = _flips(cd, sd, codes_o, scales_o)
+    kd = O.fp4_unpack(codes_o, scales_o)
+    tks = [db.layers[l]["topk"][0].cpu().numpy() for l in (0, 1)]
+    worst, n_exact, n_att = 0.0, 0, 0
+    for j in [0, 1, 63, 126, 127, 128, 1000, R - 1]:
+        p = L - R + j
+        for li in (0, 1):
+            lay = db.layers[li]
+            sc = O.index_scores(f64(lay["q_idx"][0, j]), f64(lay["w"][0, j]), kd, p + 1)
+            ex = check_topk_row(sc, np.arange(p + 1), tks[li][j], k, f"replay layer{li} j{j}", flips)
+            n_exact += ex
+            sel = O.topk_select(sc, k) if ex else tks[li][j]
+            for lj in ((0,) if li == 0 else (1, 2, 3)):
+                ly = db.layers[lj]
+                ref, _, _ = O.sparse_attention(f64(ly["q"][0, j]), kv_o, sel, f64(ly["swa_kv"][0]), L - R, p, W)
+                err = row_rel_err(f64(ly["o"][0, j]), ref)
+                assert err <= TOL, f"replay layer{lj} j{j}: {err:.3e}"
+                worst = max(worst, err)
+                n_att += 1
+    say(f"  exact sets {n_exact}/16, {n_att} attention outputs compared, worst row rel err {worst:.2e}")
+    assert n_exact >= 14 and n_att == 32
+
+
 # -------------------------------------------------------------- decode C4
 
 def test_batched_decode_full_size(K):

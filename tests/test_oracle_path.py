@@ -462,3 +462,55 @@ def test_full_decode_step_sees_appended_entries_and_reindex_follows():
     assert np.allclose(o[0, 0], ref)
     O.layer_forward(rt, O.LayerConfig(O.REINDEX, m=m, k=k, W=full.W), step)
     assert np.array_equal(rt.topk_idxs[0, 0], sel)
+
+
+def _decoder_stack(B=1, L=48, D=32, H_I=2, H=2, W=6, k=5, seed=50):
+    # decoder macro-block: a Full layer at m = 1 (compressing H20), then Reindex, Reuse
+    r = rng(seed)
+    h20 = r.standard_normal((B, L, D))
+    w_kv, _, g = weights(D, seed, 1)
+    w_ik = r.standard_normal((128, 512)) / math.sqrt(512)
+    cfgs = [O.LayerConfig(O.FULL, m=1, k=k, W=W, w_kv=w_kv, w_gate=None, gamma=g, w_ik=w_ik),
+            O.LayerConfig(O.REINDEX, m=1, k=k, W=W), O.LayerConfig(O.REUSE, m=1, k=k, W=W)]
+    full_inputs = [O.LayerInputs(q=r.standard_normal((B, L, H, 512)), swa_kv=r.standard_normal((B, L, 512)),
+                                 q_pos=np.tile(np.arange(L), (B, 1)), swa_pos0=np.zeros(B, int),
+                                 q_idx=r.standard_normal((B, L, H_I, 128)), w=r.standard_normal((B, L, H_I)))
+                   for _ in cfgs]
+    return h20, cfgs, full_inputs
+
+
+def _tail(inp, L, R):
+    return O.LayerInputs(q=inp.q[:, L - R:], swa_kv=inp.swa_kv[:, L - R:], q_pos=inp.q_pos[:, L - R:],
+                         swa_pos0=inp.swa_pos0, q_idx=inp.q_idx[:, L - R:], w=inp.w[:, L - R:])
+
+
+def test_bounded_replay_keeps_the_global_kv_and_clips_only_the_window():
+    h20, cfgs, full_inputs = _decoder_stack()
+    L, W = h20.shape[1], cfgs[0].W
+    # the un-truncated decoder prefill: every position through every layer
+    rt_full = O.Runtime()
+    ref = []
+    for l, (cfg, inp) in enumerate(zip(cfgs, full_inputs)):
+        inp.x = h20 if l == 0 else None
+        ref.append(O.layer_forward(rt_full, cfg, inp))
+    for R in (L, 17):
+        rt = O.Runtime()
+        outs = O.decoder_replay(rt, cfgs, [_tail(i, L, R) for i in full_inputs], h20, R)
+        # the truncation never touches the global KV or the index K
+        assert np.array_equal(rt.compress_kv, rt_full.compress_kv)
+        assert np.array_equal(rt.index_k[0], rt_full.index_k[0])
+        for l in range(3):
+            assert outs[l].shape == (1, R, 2, 512)
+            for j in range(R):
+                p = L - R + j
+                if p >= L - R + W - 1:
+                    # the window lies inside the replayed segment: exactly the full prefill
+                    assert np.allclose(outs[l][0, j], ref[l][0, p], rtol=1e-12, atol=1e-12), (R, l, p)
+        if R < L:
+            # the first replayed position sees one window row instead of W
+            p = L - R
+            assert not np.allclose(outs[2][0, 0], ref[2][0, p])
+            tk = rt.topk_idxs[0, 0]
+            manual = O.sparse_attention(full_inputs[2].q[0, p], rt.compress_kv[0], tk,
+                                        full_inputs[2].swa_kv[0, L - R:], L - R, p, W)[0]
+            assert np.allclose(outs[2][0, 0], manual, rtol=1e-12, atol=1e-12)
