@@ -107,11 +107,12 @@ class PrefillBench:
 class DecodeBench:
     """Batched decode step, Reindex + Reuse: 64 sequences x 131072 m=2 entries."""
 
-    def __init__(self, torch, K, synth, B=64, n_entries=131072, m=2, H_I=32, k=512, W=128, H=64, kv_fp4=False):
+    def __init__(self, torch, K, synth, B=64, n_entries=131072, m=2, H_I=32, k=512, W=128, H=64, kv_fp4=False,
+                 swa_fp8=False):
         self.t, self.K = torch, K
         dev = "cuda"
         self.B, self.N, self.m, self.H_I, self.k, self.W, self.H = B, n_entries, m, H_I, k, W, H
-        self.kv_fp4 = kv_fp4
+        self.kv_fp4, self.swa_fp8 = kv_fp4, swa_fp8
         self.seed = seed = 11   # per-sequence cache rows: synth.cache_rows(n, d, seed, name, b)
         if kv_fp4:   # FP4 main KV: N(0,1) latent rows packed by the (bit-exact) FP4 packer
             self.kv = torch.empty(B, n_entries, 256, dtype=torch.uint8, device=dev)
@@ -138,11 +139,23 @@ class DecodeBench:
                        for l in range(2)]
         self.topk = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
         self.o = [torch.empty_like(self.layers[l]["q"]) for l in range(2)]
+        self.win = [self.layers[l]["swa_kv"] for l in range(2)]
+        if swa_fp8:
+            # each layer's window KV in an FP8 ring of W rows holding positions p-W+1..p;
+            # every step re-appends the newest token's row (what a decode step writes)
+            wpos = torch.arange(p - W + 1, p + 1, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+            self.win = []
+            self.new_rows = []
+            for l in range(2):
+                ring = torch.zeros(B, W, 512, dtype=torch.uint8, device=dev)
+                K.csa2_swa_append(self.layers[l]["swa_kv"], wpos, ring)
+                self.win.append(ring)
+                self.new_rows.append(self.layers[l]["swa_kv"][:, W - 1:].contiguous())
         nb = K.score_topk_workspace_bytes(q_idx=self.layers[0]["q_idx"], w=self.layers[0]["w"], codes=self.codes,
                                           scales=self.scales, q_pos=self.q_pos, topk=self.topk, n_entries=n_entries,
                                           m=m, k=k, N_cap=n_entries)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W, kv_fp4, n_entries)
+        na = K.sparse_attn_workspace_bytes(self.layers[0]["q"], k, W, kv_fp4, n_entries, swa_fp8, W)
         self.ws_attn = torch.empty(max(na, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -155,11 +168,15 @@ class DecodeBench:
                           n_entries=self.N, m=self.m, k=self.k, workspace=self.ws)
         if events is not None:
             events[1].record()
-        K.csa2_sparse_attn(None, r["q"], self.kv, self.topk, r["swa_kv"], self.swa_pos0, self.q_pos, self.o[0],
+        if self.swa_fp8:
+            K.csa2_swa_append(self.new_rows[0], self.q_pos, self.win[0])
+        K.csa2_sparse_attn(None, r["q"], self.kv, self.topk, self.win[0], self.swa_pos0, self.q_pos, self.o[0],
                            W=self.W, workspace=self.ws_attn, kv_scales=self.kv_scales)
         if events is not None:
             events[2].record()
-        K.csa2_sparse_attn(None, u["q"], self.kv, self.topk, u["swa_kv"], self.swa_pos0, self.q_pos, self.o[1],
+        if self.swa_fp8:
+            K.csa2_swa_append(self.new_rows[1], self.q_pos, self.win[1])
+        K.csa2_sparse_attn(None, u["q"], self.kv, self.topk, self.win[1], self.swa_pos0, self.q_pos, self.o[1],
                            W=self.W, workspace=self.ws_attn, kv_scales=self.kv_scales)
         if events is not None:
             events[3].record()
@@ -168,11 +185,13 @@ class DecodeBench:
         B, N = self.B, self.N
         rows = B * (min(self.k, N) + self.W)
         sel_row_bytes = 288.0 if self.kv_fp4 else 1024.0     # FP4 main KV row, or bf16 row
+        win_row_bytes = 512.0 if self.swa_fp8 else 1024.0     # FP8 ring row, or bf16 row
+        append_bytes = B * (1024.0 + 512.0) if self.swa_fp8 else 0.0   # newest row read, ring slot written
         return {
             "score_topk": {"bytes": 68.0 * B * N + B * self.H_I * (128 * 2 + 4) + B * self.k * 4,
                            "flop": 2.0 * B * N * self.H_I * 128},
-            "sparse_attn": {"bytes": B * min(self.k, N) * sel_row_bytes + B * self.W * 1024.0
-                            + 2.0 * B * self.H * 512 * 2,
+            "sparse_attn": {"bytes": B * min(self.k, N) * sel_row_bytes + B * self.W * win_row_bytes
+                            + 2.0 * B * self.H * 512 * 2 + append_bytes,
                             "flop": 4.0 * rows * self.H * 512},
         }
 
@@ -625,6 +644,8 @@ def main():
     ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
     ap.add_argument("--no-append", action="store_true", help="skip the decode-append record")
     ap.add_argument("--no-fp4kv", action="store_true", help="skip the decode record with FP4 main KV")
+    ap.add_argument("--no-fp8swa", action="store_true",
+                    help="skip the decode record with FP4 main KV and the FP8 window ring")
     ap.add_argument("--no-decoder", action="store_true",
                     help="skip the decoder macro-block records (full prefill and bounded replay)")
     ap.add_argument("--replay", type=int, default=2048,
@@ -744,6 +765,31 @@ def main():
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (fms * 1e-3), 4),
         }
         del fb
+        torch.cuda.empty_cache()
+    if not args.no_decode and not args.no_fp8swa:
+        log("decode (FP4 main KV, FP8 window ring): building caches")
+        wb = DecodeBench(torch, K, synth, B=args.decode_seqs, kv_fp4=True, swa_fp8=True)
+        log("decode (FP4 main KV, FP8 window ring): timing")
+        wms_eager, wst = time_steps(torch, wb, 3, max(args.steps, 20), args.warmup)
+        wms = time_graph(torch, wb, max(args.steps, 20), args.warmup) if args.graph else wms_eager
+        ww = wb.work()
+        attn_gbs = ww["sparse_attn"]["bytes"] / (wst[1] * 1e-3) / 1e9
+        step_bytes = ww["score_topk"]["bytes"] + 2 * ww["sparse_attn"]["bytes"]
+        out["decode_fp4kv_fp8swa"] = {
+            "workload": f"batched decode, Reindex + Reuse, FP4 main KV (288 B per entry) and each layer's SWA 128 "
+                        f"window KV in an FP8 ring (E4M3, 512 B per row; the step appends the newest row): "
+                        f"{wb.B} sequences x {wb.N} m=2 entries, FP4 index K, 32x128 indexer heads, top-512, "
+                        f"64 heads",
+            "us_per_step": round(wms * 1e3, 2), "us_per_step_eager": round(wms_eager * 1e3, 2),
+            "stages_us": {"score_topk": round(wst[0] * 1e3, 2), "append_attn_reindex": round(wst[1] * 1e3, 2),
+                          "append_attn_reuse": round(wst[2] * 1e3, 2)},
+            "roofline": {"bound": "hbm", "kernel": "swa_append + sparse_attn (FP4 KV, FP8 ring)",
+                         "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "attn_bytes_per_layer": ww["sparse_attn"]["bytes"],
+            "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (wms * 1e-3), 4),
+        }
+        del wb
         torch.cuda.empty_cache()
     if not args.no_hsi:
         log("hsi decode: building caches")

@@ -22,6 +22,7 @@ HSI_NONE, HSI_BUILD, HSI_USE = 0, 1, 2
 SLOT_COMPRESS_KV, SLOT_INDEX_K, SLOT_TOPK_IDXS, SLOT_CANDIDATES = 0, 1, 2, 3
 OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER, OP_COMPRESS_STEP = 0, 1, 2, 3
 KV_DENSE, KV_FP4 = 0, 1
+SWA_DENSE, SWA_FP8_RING = 0, 1
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_DTYPE",
           4: "CSA2_ERR_SLOT_EMPTY", 5: "CSA2_ERR_SLOT_MISMATCH", 6: "CSA2_ERR_WORKSPACE",
@@ -70,13 +71,18 @@ class SparseAttnArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H", i32), ("N_cap", i32), ("k", i32), ("L_w", i32),
                 ("W", i32), ("scale", C.c_float), ("q", vp), ("kv", vp), ("topk", vp), ("swa_kv", vp),
                 ("swa_pos0", vp), ("q_pos", vp), ("o", vp), ("lse", vp), ("workspace", vp),
-                ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_fmt", i32), ("kv_scales", vp)]
+                ("workspace_bytes", C.c_size_t), ("sink", vp), ("kv_fmt", i32), ("kv_scales", vp),
+                ("swa_fmt", i32)]
+
+
+class SwaAppendArgs(C.Structure):
+    _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("L_w", i32), ("rows", vp), ("pos", vp), ("ring", vp)]
 
 
 class LayerCfg(C.Structure):
     _fields_ = [("mode", i32), ("dtype", i32), ("m", i32), ("k", i32), ("W", i32), ("H_I", i32), ("H", i32),
                 ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("rope_base", C.c_float), ("eps", C.c_float),
-                ("scale", C.c_float), ("kv_fmt", i32)]
+                ("scale", C.c_float), ("kv_fmt", i32), ("swa_fmt", i32)]
 
 
 class LayerIO(C.Structure):
@@ -105,6 +111,7 @@ EXPORTS = {
     "csa2_score_topk_noalloc": ([vp, C.POINTER(ScoreTopkArgs), vp], i32),
     "csa2_sparse_attn": ([vp, C.POINTER(SparseAttnArgs), vp], i32),
     "csa2_compress_step": ([vp, C.POINTER(CompressStepArgs), vp], i32),
+    "csa2_swa_append": ([C.POINTER(SwaAppendArgs), vp], i32),
     "csa2_layer_forward": ([vp, C.POINTER(LayerCfg), C.POINTER(LayerIO), vp], i32),
     "csa2_workspace_size": ([i32, vp, C.POINTER(LayerCfg), C.POINTER(C.c_size_t)], i32),
     "csa2_fp4_pack": ([vp, C.c_int64, vp, vp, vp], i32),
@@ -265,12 +272,19 @@ def sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: int, N_
                           q_pos=_ptr(q_pos), o=_ptr(o), lse=_ptr(lse), workspace=_ptr(workspace),
                           workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
                           sink=_ptr(sink), kv_fmt=KV_DENSE if kv_scales is None else KV_FP4,
-                          kv_scales=_ptr(kv_scales))
+                          kv_scales=_ptr(kv_scales), swa_fmt=_swa_fmt(swa_kv))
 
 
-def sparse_attn_workspace_bytes(q, k: int, W: int, kv_fp4: bool = False, N_cap: int = 0) -> int:
+def _swa_fmt(swa_kv) -> int:
+    # uint8 window KV is the FP8 ring; the dense window has the layer dtype
+    return SWA_FP8_RING if swa_kv is not None and swa_kv.dtype == torch.uint8 else SWA_DENSE
+
+
+def sparse_attn_workspace_bytes(q, k: int, W: int, kv_fp4: bool = False, N_cap: int = 0, swa_fp8: bool = False,
+                                L_w: int = 0) -> int:
     B, T, H, _ = q.shape
-    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, k=k, W=W, N_cap=N_cap, kv_fmt=KV_FP4 if kv_fp4 else KV_DENSE)
+    a = SparseAttnArgs(dtype=_dtype(q), B=B, T=T, H=H, k=k, W=W, N_cap=N_cap, kv_fmt=KV_FP4 if kv_fp4 else KV_DENSE,
+                       swa_fmt=SWA_FP8_RING if swa_fp8 else SWA_DENSE, L_w=L_w)
     n = C.c_size_t()
     _check(lib().csa2_workspace_size(OP_SPARSE_ATTN, C.cast(C.byref(a), vp), None, C.byref(n)))
     return n.value
@@ -281,9 +295,11 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
                      sink=None, kv_scales=None):
     """Attend; kv/topk None -> the runtime's compress_kv / topk_idxs slots; sink
     [H] float32 per-head sink logits or None; kv_scales given: kv is FP4 main KV
-    (uint8 codes [B, N_cap, 256], scales [B, N_cap, 32]).  A workspace (row-split
-    partials for few-query calls, or the dequantised cache for FP4 KV outside
-    them) is allocated when needed and none is given."""
+    (uint8 codes [B, N_cap, 256], scales [B, N_cap, 32]); a uint8 swa_kv
+    [B, L_w, 512] is an FP8 window ring (see csa2_swa_append).  A workspace
+    (row-split partials for few-query calls, the dequantised cache for FP4 KV
+    outside them, the ring's dense rows) is allocated when needed and none is
+    given."""
     if k is None:
         k = topk.shape[-1]
     fp4 = kv_scales is not None
@@ -297,7 +313,7 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
     if kv is None and rt is not None and rt.slot(SLOT_COMPRESS_KV).filled:
         fp4 = rt.slot(SLOT_COMPRESS_KV).kv_fmt == KV_FP4
     if workspace is None:
-        nbytes = sparse_attn_workspace_bytes(q, k, W, fp4, N_cap)
+        nbytes = sparse_attn_workspace_bytes(q, k, W, fp4, N_cap, _swa_fmt(swa_kv) == SWA_FP8_RING, swa_kv.shape[1])
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     a = sparse_attn_args(q, kv, topk, swa_kv, swa_pos0, q_pos, o, W, k, N_cap, scale, lse, workspace, sink,
@@ -327,6 +343,15 @@ def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, i
     return workspace
 
 
+def csa2_swa_append(rows, pos, ring, stream=None):
+    """Quantise window rows [B, T, 512] (positions pos [B, T] int32, < 0 = none)
+    into the FP8 ring [B, L_w, 512] uint8, slot pos mod L_w."""
+    B, T = pos.shape
+    a = SwaAppendArgs(dtype=_dtype(rows), B=B, T=T, L_w=ring.shape[1], rows=_ptr(rows), pos=_ptr(pos),
+                      ring=_ptr(ring))
+    _check(lib().csa2_swa_append(C.byref(a), _stream(stream)))
+
+
 def csa2_fp4_pack(rows, codes, scales, stream=None):
     n = rows.shape[0] if rows.dim() == 2 else rows.numel() // 128
     _check(lib().csa2_fp4_pack(_ptr(rows), n, _ptr(codes), _ptr(scales), _stream(stream)))
@@ -340,9 +365,9 @@ def csa2_kv_fp4_pack(rows, codes, scales, stream=None):
 
 def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, hsi: int = HSI_NONE,
               hsi_s: int = 0, hsi_nb: int = 0, rope_base: float = 10000.0, eps: float = 1e-6,
-              scale: float = 0.0, kv_fmt: int = 0) -> LayerCfg:
+              scale: float = 0.0, kv_fmt: int = 0, swa_fmt: int = 0) -> LayerCfg:
     return LayerCfg(mode=mode, dtype=dtype, m=m, k=k, W=W, H_I=H_I, H=H, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb,
-                    rope_base=rope_base, eps=eps, scale=scale, kv_fmt=kv_fmt)
+                    rope_base=rope_base, eps=eps, scale=scale, kv_fmt=kv_fmt, swa_fmt=swa_fmt)
 
 
 def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,

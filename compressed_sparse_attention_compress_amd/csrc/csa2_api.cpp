@@ -209,7 +209,18 @@ csa2_status resolve_attn(const csa2_runtime* rt, csa2_sparse_attn_args& a) {
   REQ(a.N_cap >= 0, CSA2_ERR_SHAPE, "csa2_sparse_attn: bad N_cap");
   REQ(a.q && a.kv && a.topk && a.swa_kv && a.swa_pos0 && a.q_pos && a.o, CSA2_ERR_INVALID_ARG,
       "csa2_sparse_attn: NULL tensor");
+  REQ(a.swa_fmt == CSA2_SWA_DENSE || a.swa_fmt == CSA2_SWA_FP8_RING, CSA2_ERR_INVALID_ARG,
+      "csa2_sparse_attn: bad swa_fmt %d", a.swa_fmt);
+  REQ(a.swa_fmt != CSA2_SWA_FP8_RING || a.W <= a.L_w, CSA2_ERR_SHAPE,
+      "csa2_sparse_attn: an FP8 window ring of L_w = %d rows cannot serve a window of W = %d", a.L_w, a.W);
+  REQ(a.swa_fmt != CSA2_SWA_FP8_RING || ((uintptr_t)a.swa_kv & 15u) == 0, CSA2_ERR_INVALID_ARG,
+      "csa2_sparse_attn: the FP8 window ring must be 16-byte aligned");
   return CSA2_OK;
+}
+
+csa2::AttnPlan attn_plan(const csa2_sparse_attn_args& a) {
+  return csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W, a.kv_fmt == CSA2_KV_FP4, a.N_cap,
+                         a.swa_fmt == CSA2_SWA_FP8_RING, a.L_w);
 }
 
 }  // namespace
@@ -358,8 +369,7 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
   csa2_status s = resolve_attn(rt, a);
   if (s != CSA2_OK) return s;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / std::sqrt(512.0f);
-  const csa2::AttnPlan plan =
-      csa2::plan_attn(a.dtype, a.B, a.T, a.H, a.k, a.W, a.kv_fmt == CSA2_KV_FP4, a.N_cap);
+  const csa2::AttnPlan plan = attn_plan(a);
   REQ(plan.ws_bytes == 0 || (a.workspace != nullptr && a.workspace_bytes >= plan.ws_bytes), CSA2_ERR_WORKSPACE,
       "csa2_sparse_attn: workspace of %zu bytes needed (got %zu)", plan.ws_bytes, a.workspace_bytes);
   REQ(plan.ws_bytes == 0 || ((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE,
@@ -367,8 +377,21 @@ csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* in, 
   hipError_t e = csa2::launch_sparse_attn(a.dtype, a.q, a.kv, a.kv_fmt == CSA2_KV_FP4 ? a.kv_scales : nullptr,
                                           a.topk, a.swa_kv, a.swa_pos0, a.q_pos, a.o, a.lse,
                                           a.sink, a.B, a.T, a.H, a.N_cap, a.k, a.L_w, a.W, scale, a.workspace, plan,
-                                          st(stream));
+                                          st(stream), a.swa_fmt == CSA2_SWA_FP8_RING);
   if (e != hipSuccess) return hip_status(e, "csa2_sparse_attn launch");
+  return ok();
+}
+
+csa2_status csa2_swa_append(const csa2_swa_append_args* a, csa2_stream stream) {
+  REQ(a, CSA2_ERR_INVALID_ARG, "csa2_swa_append: args is NULL");
+  REQ(dtype_ok(a->dtype), CSA2_ERR_DTYPE, "csa2_swa_append: unsupported dtype %d", a->dtype);
+  REQ(a->B >= 0 && a->T >= 0 && a->L_w >= 1, CSA2_ERR_SHAPE, "csa2_swa_append: need B, T >= 0 and L_w >= 1");
+  if (a->B == 0 || a->T == 0) return ok();
+  REQ(a->rows && a->pos && a->ring, CSA2_ERR_INVALID_ARG, "csa2_swa_append: NULL tensor");
+  REQ(((uintptr_t)a->rows & 15u) == 0 && ((uintptr_t)a->ring & 7u) == 0, CSA2_ERR_INVALID_ARG,
+      "csa2_swa_append: rows must be 16-byte and the ring 8-byte aligned");
+  hipError_t e = csa2::launch_swa_append(a->dtype, a->rows, a->pos, a->ring, a->B, a->T, a->L_w, st(stream));
+  if (e != hipSuccess) return hip_status(e, "csa2_swa_append launch");
   return ok();
 }
 
@@ -382,7 +405,7 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   if (op == CSA2_OP_SPARSE_ATTN) {
     const csa2_sparse_attn_args* a = static_cast<const csa2_sparse_attn_args*>(args);
     // with kv NULL the slot decides the format; size for FP4 when the caller says so
-    *bytes = csa2::plan_attn(a->dtype, a->B, a->T, a->H, a->k, a->W, a->kv_fmt == CSA2_KV_FP4, a->N_cap).ws_bytes;
+    *bytes = attn_plan(*a).ws_bytes;
     return ok();
   }
   if (op == CSA2_OP_COMPRESS_STEP) {
@@ -393,8 +416,8 @@ csa2_status csa2_workspace_size(int32_t op, const void* args, const csa2_layer_c
   if (op == CSA2_OP_LAYER) {
     REQ(cfg, CSA2_ERR_INVALID_ARG, "csa2_workspace_size: layer op needs cfg");
     const csa2_layer_io* io = static_cast<const csa2_layer_io*>(args);
-    size_t need =
-        csa2::plan_attn(cfg->dtype, io->B, io->T, cfg->H, cfg->k, cfg->W, cfg->kv_fmt == CSA2_KV_FP4, io->N_cap).ws_bytes;
+    size_t need = csa2::plan_attn(cfg->dtype, io->B, io->T, cfg->H, cfg->k, cfg->W, cfg->kv_fmt == CSA2_KV_FP4,
+                                  io->N_cap, cfg->swa_fmt == CSA2_SWA_FP8_RING, io->L_w).ws_bytes;
     if (cfg->mode != CSA2_REUSE) {
       const int n_entries = io->N_cap;  // upper bound
       const int scan = cfg->hsi == CSA2_HSI_USE ? cfg->hsi_nb * cfg->hsi_s : n_entries;
@@ -463,6 +486,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
   aa.dtype = cfg->dtype; aa.B = io->B; aa.T = io->T; aa.H = cfg->H; aa.k = cfg->k; aa.L_w = io->L_w; aa.W = cfg->W;
   aa.scale = cfg->scale; aa.q = io->q; aa.swa_kv = io->swa_kv; aa.swa_pos0 = io->swa_pos0; aa.q_pos = io->q_pos;
   aa.o = io->o; aa.workspace = io->workspace; aa.workspace_bytes = io->workspace_bytes; aa.sink = io->sink;
+  aa.swa_fmt = cfg->swa_fmt;
   if (cfg->mode == CSA2_FULL) {
     aa.kv = io->kv_cache;
     aa.kv_fmt = cfg->kv_fmt;
@@ -494,8 +518,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     if (s != CSA2_OK) return s;
     // the attention workspace, for the main KV actually attended (a borrowed FP4
     // cache may be dequantised whole), before anything is enqueued
-    const csa2::AttnPlan ap = csa2::plan_attn(probe.dtype, probe.B, probe.T, probe.H, probe.k, probe.W,
-                                              probe.kv_fmt == CSA2_KV_FP4, probe.N_cap);
+    const csa2::AttnPlan ap = attn_plan(probe);
     REQ(ap.ws_bytes == 0 || (io->workspace != nullptr && io->workspace_bytes >= ap.ws_bytes), CSA2_ERR_WORKSPACE,
         "csa2_layer_forward: attention needs a workspace of %zu bytes (got %zu)", ap.ws_bytes, io->workspace_bytes);
     REQ(ap.ws_bytes == 0 || ((uintptr_t)io->workspace & 15u) == 0, CSA2_ERR_WORKSPACE,

@@ -37,6 +37,14 @@ hipError_t launch_kv_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes,
 hipError_t launch_kv_fp4_dequant(int dtype, const uint8_t* codes, const uint8_t* scales, int64_t n_rows, void* out,
                                  hipStream_t stream);
 
+// ---- window KV in FP8 (k_swa.hip)
+hipError_t launch_swa_append(int dtype, const void* rows, const int32_t* pos, uint8_t* ring, int B, int T_len,
+                             int L_w, hipStream_t stream);
+// ring -> dense rows [B, L_w, 512] of the dtype, row j = position (newest_b - L_w + 1 + j);
+// pos0_out[b] = max(swa_pos0[b], newest_b - L_w + 1)
+hipError_t launch_swa_window(int dtype, const uint8_t* ring, const int32_t* q_pos, const int32_t* swa_pos0,
+                             void* dense, int32_t* pos0_out, int B, int T_len, int L_w, hipStream_t stream);
+
 // ---- indexer score + top-k (k_score.hip)
 struct ScorePlan {
   bool tiled;       // two-phase path: query-tiled scoring into a key matrix, then one select per query
@@ -69,12 +77,16 @@ struct AttnPlan {
   int n_splits;     // row splits per query (decode only)
   int n_fp4;        // decode with FP4 KV: the first n_fp4 splits take the selected rows, the rest the window
   size_t ws_bytes;  // decode: split partials (bf16 rows, float32 log-sum-exp) when n_splits > 1;
-                    // FP4 KV outside decode: the dequantised cache rows [B, N_cap, 512]
+                    // FP4 KV outside decode: the dequantised cache rows [B, N_cap, 512];
+                    // then, with an FP8 window ring, its dense rows [B, L_w, 512] and B int32
+  size_t swa_off;   // byte offset of the dense window rows in the workspace (FP8 ring only)
 };
-AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap);
+AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap, bool swa_fp8 = false,
+                   int L_w = 0);
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const uint8_t* kv_scales, const int32_t* topk,
                               const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos,
                               void* o, float* lse, const float* sink, int B, int T, int H, int N_cap, int k,
-                              int L_w, int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream);
+                              int L_w, int W, float scale, void* workspace, const AttnPlan& plan, hipStream_t stream,
+                              bool swa_fp8 = false);
 
 }  // namespace csa2

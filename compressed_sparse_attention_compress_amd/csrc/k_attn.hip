@@ -914,7 +914,7 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
 
 }  // namespace
 
-AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap) {
+AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap, bool swa_fp8, int L_w) {
   AttnPlan p{};
   const long long Q = (long long)B * T;
   p.decode = (dtype == 1) && Q < 512;
@@ -945,14 +945,29 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, in
     p.ws_bytes = (size_t)Q * p.n_splits * H * (512 * 2 + 4) + 256;
   else if (kv_fp4 && !p.decode)
     p.ws_bytes = (size_t)B * N_cap * 512 * (dtype == 1 ? 2 : 4) + 256;
+  if (swa_fp8) {   // the ring's dense rows, then each sequence's first dense position
+    p.swa_off = (p.ws_bytes + 255) / 256 * 256;
+    p.ws_bytes = p.swa_off + (size_t)B * L_w * 512 * (dtype == 1 ? 2 : 4) + (size_t)B * 4 + 256;
+  }
   return p;
 }
 
 hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const uint8_t* kv_scales, const int32_t* topk,
                               const void* swa_kv, const int32_t* swa_pos0, const int32_t* q_pos, void* o, float* lse,
                               const float* sink, int B, int T, int H, int N_cap, int k, int L_w, int W, float scale,
-                              void* workspace, const AttnPlan& p, hipStream_t st) {
+                              void* workspace, const AttnPlan& p, hipStream_t st, bool swa_fp8) {
   if (B == 0 || T == 0) return hipSuccess;
+  if (swa_fp8) {
+    // the ring's rows of each sequence's last L_w positions, in position order, as
+    // dense rows of the dtype; the attention below reads them as a dense window
+    unsigned char* wb = static_cast<unsigned char*>(workspace) + p.swa_off;
+    int32_t* pos0_d = reinterpret_cast<int32_t*>(wb + (size_t)B * L_w * 512 * (dtype == 1 ? 2 : 4));
+    hipError_t e = launch_swa_window(dtype, static_cast<const uint8_t*>(swa_kv), q_pos, swa_pos0, wb, pos0_d, B, T,
+                                     L_w, st);
+    if (e != hipSuccess) return e;
+    swa_kv = wb;
+    swa_pos0 = pos0_d;
+  }
   const float sl2 = scale * 1.4426950408889634f;
   const int nw = (H + 15) / 16;
   if (p.kv_fp4 && !p.decode) {

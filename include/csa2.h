@@ -68,6 +68,22 @@ typedef enum csa2_dtype { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
  * when s is 0.  The rows quantised are the float32 post-RoPE latents.         */
 typedef enum csa2_kv_fmt { CSA2_KV_DENSE = 0, CSA2_KV_FP4 = 1 } csa2_kv_fmt;
 
+/* Storage of a layer's sliding-window KV.  DENSE: [B, L_w, 512] of the layer dtype,
+ * row j holding position swa_pos0[b] + j.  FP8_RING ([P3] section seven: the local
+ * window KV is more sensitive to quantisation and is kept in FP8): uint8
+ * [B, L_w, 512] E4M3FN bytes, one per dimension, no scale (round to nearest
+ * even, saturating at +-448), in a ring: the row of position u sits in slot
+ * u mod L_w (written by csa2_swa_append).  Attention with a ring needs W <= L_w
+ * and a 16-byte aligned ring; for each sequence the ring must hold the positions
+ * newest - L_w + 1 .. newest, newest being the largest q_pos of that sequence in
+ * the call, and swa_pos0[b] is the first position ever written (earlier positions
+ * are absent).  A query's window is clipped at newest - L_w + 1, so the query
+ * positions of one sequence in one call should lie within L_w - W of newest
+ * (decode: one query per sequence); a prefill attends its dense window rows and
+ * then appends the last L_w of them.  The rows are attended as their exact values
+ * (E4M3 values are exact in bf16). */
+typedef enum csa2_swa_fmt { CSA2_SWA_DENSE = 0, CSA2_SWA_FP8_RING = 1 } csa2_swa_fmt;
+
 /* Layer modes ([P1] section on the four slots and the mode excerpt; [P2] mode
  * tables; [P4] "Les trois modes"): Full computes main KV, index K and top-k;
  * Reindex borrows main KV and index K and selects anew; Reuse borrows main KV and
@@ -334,9 +350,34 @@ typedef struct csa2_sparse_attn_args {
   const float* sink;        /* [H] float32 per-head sink logits, or NULL (no sink) */
   int32_t kv_fmt;           /* csa2_kv_fmt of kv (ignored when kv is NULL) */
   const uint8_t* kv_scales; /* FP4 only: [B, N_cap, 32] */
+  int32_t swa_fmt;          /* csa2_swa_fmt of swa_kv; FP8_RING: the ring is read into the workspace
+                               (B * L_w * 512 elements of the dtype + B int32) before the attention */
 } csa2_sparse_attn_args;
 
 csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* a, csa2_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Window KV ring in FP8 ([P3] section seven; layout at csa2_swa_fmt): quantise
+ * each layer's new window rows into its ring.
+ *
+ *   rows  [B, T, 512] dtype              the window KV rows of positions pos
+ *   pos   [B, T] int32 (device)          absolute positions; < 0 = no row
+ *   ring  [B, L_w, 512] uint8 in/out     slot pos mod L_w of sequence b is overwritten
+ * Decode appends one row per sequence and step (T = 1); after a prefill the last
+ * L_w rows of each sequence are appended at once (two rows of one call must not
+ * share a slot, i.e. positions of one sequence in one call span fewer than L_w).
+ * Errors: CSA2_ERR_DTYPE; CSA2_ERR_SHAPE for B, T < 0 or L_w < 1;
+ * CSA2_ERR_INVALID_ARG for a NULL tensor (with B * T > 0), rows not 16-byte or the
+ * ring not 8-byte aligned.  Nothing is written on an error; B * T == 0 is a no-op. */
+typedef struct csa2_swa_append_args {
+  int32_t dtype;            /* csa2_dtype of rows */
+  int32_t B, T, L_w;
+  const void* rows;
+  const int32_t* pos;
+  uint8_t* ring;
+} csa2_swa_append_args;
+
+csa2_status csa2_swa_append(const csa2_swa_append_args* a, csa2_stream stream);
 
 /* ------------------------------------------------------------------------ */
 /* One layer in its configured mode ([P1] mode excerpt: a KV source compresses
@@ -352,6 +393,7 @@ typedef struct csa2_layer_cfg {
   int32_t hsi, hsi_s, hsi_nb;
   float rope_base, eps, scale;
   int32_t kv_fmt;           /* Full: storage of the main KV it writes (csa2_kv_fmt) */
+  int32_t swa_fmt;          /* storage of this layer's window KV io->swa_kv (csa2_swa_fmt) */
 } csa2_layer_cfg;
 
 typedef struct csa2_layer_io {

@@ -114,6 +114,14 @@ def e4m3_encode_nonneg(v: np.ndarray) -> np.ndarray:
     return idx.astype(np.uint8)
 
 
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest E4M3FN byte, ties to the even byte,
+    saturating at +-448; bit 7 is the sign (kept for a value rounding to zero)."""
+    v = np.asarray(v, dtype=np.float32)
+    mag = e4m3_encode_nonneg(np.abs(v))
+    return (mag | (np.signbit(v).astype(np.uint8) << 7)).astype(np.uint8)
+
+
 def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
     """Quantise rows of 128 values to FP4 index-K storage (``block`` = 32), or
     rows of 512 values to FP4 main-KV storage (``block`` = 16, see kv_fp4_pack).
@@ -651,3 +659,31 @@ def decoder_replay(rt: Runtime, cfgs: list, layer_inputs: list, h20, R: int):
                           x=h20 if l == 0 else None, start_pos=0)
         outs.append(layer_forward(rt, cfg, inp))
     return outs
+
+
+# ---------------------------------------------------------------------------
+# Window KV in FP8: [P3] section seven (the local sliding-window KV is more
+# sensitive to quantisation than the main KV and is kept in FP8).  Read here as
+# E4M3FN values with no scale (none is described), one byte per dimension, in a
+# per-layer ring of L_w rows: the row of position u sits in slot u mod L_w.
+# ---------------------------------------------------------------------------
+
+def swa_ring_append(ring, rows, pos):
+    """Quantise `rows` [n, 512] (positions `pos` [n]) into `ring` [L_w, 512] uint8
+    in place: slot u mod L_w takes the E4M3 bytes of position u's row."""
+    ring = np.asarray(ring)
+    L_w = ring.shape[0]
+    for r, u in zip(np.asarray(rows, dtype=np.float64), np.asarray(pos)):
+        if u >= 0:
+            ring[int(u) % L_w] = e4m3_encode(r.astype(np.float32))
+    return ring
+
+
+def swa_ring_rows(ring, first: int, last: int) -> np.ndarray:
+    """Dequantised window rows of positions first .. last (inclusive) read from
+    their ring slots, float64 [last - first + 1, 512]; the ring must hold them
+    (last - first < L_w)."""
+    ring = np.asarray(ring)
+    L_w = ring.shape[0]
+    assert last - first < L_w
+    return e4m3_decode(ring[[u % L_w for u in range(first, last + 1)]])

@@ -236,3 +236,49 @@ def test_noalloc_score_refuses_oversized_calls_and_workspaces():
     assert b"scratch" in K.lib().csa2_last_error()
     a.T, a.workspace, a.workspace_bytes = 1, 0x1000, 1 << 20
     assert K.STATUS[K.lib().csa2_score_topk_noalloc(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("swa_fmt", 2, "CSA2_ERR_INVALID_ARG"), ("W", 129, "CSA2_ERR_SHAPE"), ("swa_kv", 0x1008, "CSA2_ERR_INVALID_ARG"),
+])
+def test_attn_fp8_window_ring_validation(field, value, status):
+    # a ring serves windows of at most L_w rows and is read 16 bytes at a time
+    a = K.SparseAttnArgs(dtype=1, B=1, T=1, H=64, N_cap=100, k=512, L_w=128, W=128, q=0x1000, kv=0x1000,
+                         topk=0x1000, swa_kv=0x1000, swa_pos0=0x1000, q_pos=0x1000, o=0x1000,
+                         swa_fmt=K.SWA_FP8_RING)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_sparse_attn(None, C.byref(a), None)] == status
+
+
+def test_fp8_window_ring_workspace_sizes():
+    # the ring's dense rows (B * L_w * 512 elements) and B int32 follow the other
+    # workspace contents at a 256-byte boundary
+    def ws(dtype, B, T, ring, L_w=200):
+        a = K.SparseAttnArgs(dtype=dtype, B=B, T=T, H=64, k=512, W=128, N_cap=1000, L_w=L_w,
+                             swa_fmt=K.SWA_FP8_RING if ring else K.SWA_DENSE)
+        n = C.c_size_t()
+        assert K.lib().csa2_workspace_size(K.OP_SPARSE_ATTN, C.cast(C.byref(a), C.c_void_p), None, C.byref(n)) == 0
+        return n.value
+    assert ws(1, 300, 1, False) == 0 and ws(1, 300, 1, True) == 300 * 200 * 512 * 2 + 300 * 4 + 256
+    base = ws(1, 64, 1, False)
+    assert base > 0 and ws(1, 64, 1, True) == (base + 255) // 256 * 256 + 64 * 200 * 1024 + 64 * 4 + 256
+    assert ws(0, 2, 8, True, L_w=64) == 2 * 64 * 512 * 4 + 8 + 256
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, "CSA2_ERR_DTYPE"), ("L_w", 0, "CSA2_ERR_SHAPE"), ("T", -1, "CSA2_ERR_SHAPE"),
+    ("rows", None, "CSA2_ERR_INVALID_ARG"), ("pos", None, "CSA2_ERR_INVALID_ARG"),
+    ("ring", None, "CSA2_ERR_INVALID_ARG"), ("rows", 0x1008, "CSA2_ERR_INVALID_ARG"),
+    ("ring", 0x1004, "CSA2_ERR_INVALID_ARG"),
+])
+def test_swa_append_validation(field, value, status):
+    a = K.SwaAppendArgs(dtype=1, B=2, T=1, L_w=128, rows=0x1000, pos=0x1000, ring=0x1000)
+    setattr(a, field, value)
+    assert K.STATUS[K.lib().csa2_swa_append(C.byref(a), None)] == status
+
+
+def test_swa_append_empty_is_noop():
+    a = K.SwaAppendArgs(dtype=1, B=0, T=1, L_w=128)
+    assert K.lib().csa2_swa_append(C.byref(a), None) == 0
+    a = K.SwaAppendArgs(dtype=0, B=3, T=0, L_w=128)
+    assert K.lib().csa2_swa_append(C.byref(a), None) == 0

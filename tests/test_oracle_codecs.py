@@ -221,3 +221,37 @@ def test_kv_fp4_roundtrip_error_bound():
     # a finer block never has a larger scale than the 32-dim block around it
     _, s32 = O.fp4_pack(u, 32)
     assert np.all(O.e4m3_decode(scales).reshape(200, 16, 2).max(axis=2) == O.e4m3_decode(s32).reshape(200, 16))
+
+
+def test_e4m3_signed_encoder_matches_torch_and_round_trips():
+    # all finite E4M3FN values round-trip; values between them round to nearest even
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = O.e4m3_decode(codes).astype(np.float32)
+    back = O.e4m3_encode(vals)
+    # -0 keeps its sign bit; every other code returns itself
+    assert np.array_equal(back, codes)
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000) * 3, rng.standard_normal(2000) * 100,
+                        rng.standard_normal(2000) * 1e-3]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+    # saturation at 448 and the sign of a value rounding to zero
+    assert O.e4m3_encode(np.float32([1e4, -1e4, 448.0, -1e-5]))[:4].tolist() == [0x7E, 0xFE, 0x7E, 0x80]
+
+
+def test_swa_ring_slots_and_wraparound():
+    L_w = 8
+    ring = np.zeros((L_w, 512), dtype=np.uint8)
+    rows = np.arange(20 * 512, dtype=np.float64).reshape(20, 512) % 7 - 3
+    O.swa_ring_append(ring, rows[:12], np.arange(12))
+    # positions 4..11 are held (slots 4..7, then 0..3)
+    got = O.swa_ring_rows(ring, 4, 11)
+    assert np.array_equal(got, rows[4:12])   # small integers are exact in E4M3
+    O.swa_ring_append(ring, rows[12:15], np.array([12, -1, 14]))
+    assert np.array_equal(O.swa_ring_rows(ring, 14, 14), rows[14:15])
+    assert np.array_equal(O.swa_ring_rows(ring, 12, 12), rows[12:13])
+    assert np.array_equal(O.swa_ring_rows(ring, 7, 11), rows[7:12])  # position 13 was skipped: slot 5 keeps 5
+    assert np.array_equal(O.e4m3_decode(ring[5]), rows[5])
+    with pytest.raises(AssertionError):
+        O.swa_ring_rows(ring, 0, 8)
