@@ -48,7 +48,8 @@ hipError_t launch_swa_window(int dtype, const uint8_t* ring, const int32_t* q_po
 // ---- indexer score + top-k (k_score.hip)
 struct ScorePlan {
   bool tiled;       // two-phase path: query-tiled scoring into a key matrix, then one select per query
-  int chunk;        // entries per chunk (power of two)
+  bool stream;      // streaming path: filtered scoring over parts of `chunk` entries, then a merge
+  int chunk;        // entries per chunk (a power of two), or per part on the streaming path
   int n_chunks;     // chunks per query
   int k_chunk;      // candidates kept per chunk = min(k, chunk)
   size_t cand_bytes, lb_bytes, blk_bytes, key_bytes, total_bytes;

@@ -29,6 +29,11 @@
 // Kernel score_qtile_bf16 + select_rows (many queries over a cache of at most
 // 8192 entries): 4 queries per workgroup share each dequantised tile; keys go to
 // a key matrix, then one wave per query selects its k best.
+// Kernel score_stream (very many queries over caches longer than the tiled path
+// takes): one workgroup per (query, part of up to 65536 entries) keeps only the
+// entries scoring at least the k-th best seen so far and cuts them back to the k
+// best a few times per part, so a query costs a few selections instead of one per
+// chunk plus a merge.
 // Kernel topk_merge: one workgroup per query: the select over all chunk
 // candidates at or above the merge bound, indices sorted ascending and padded
 // with -1; with HSI BUILD also the n_b best blocks (newest block forced) as the
@@ -426,6 +431,144 @@ __device__ __forceinline__ float max_lane_groups(float x) {
 // bounds the k-th best key from below and the merge drops every candidate under it.
 __device__ __forceinline__ uint32_t rank_for_bound(int k, int nc) { return nc > 1 ? (uint32_t)((k + nc - 2) / (nc - 1)) : 0u; }
 
+// Indexer query fragments of query bt: row tile mt = heads 16mt.., k-step kb =
+// dims 32kb + 8lg ..  bf16: k-step j of lane group g holds dims 32g + 8j .. +7
+// (block g), fp16 as described above; fp32: k-step kb holds block kb (dims
+// 32kb + 8g .. +7).  wv[mt][i] is the weight of head 16mt + 4lg + i (times the
+// head's power of two for bf16).
+template <typename T>
+__device__ __forceinline__ void load_qfrags(const T* __restrict__ qb, const float* __restrict__ wrow, int H_I,
+                                            int lr, int lg, typename ScoreQ<T>::type (&qf)[2][4],
+                                            float (&wv)[2][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int h = mt * 16 + lr;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 raw[4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (h < H_I) raw[j] = load_frag(qb + (size_t)h * 128 + 32 * lg + 8 * j);
+        else zero_frag(raw[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)raw[j][i]));
+      }
+      amax = max_lane_groups(amax);
+      int ex = 0;
+      frexpf(amax, &ex);                          // amax < 2^ex
+      const int s = amax > 0.0f ? min(max(ex - 15, -96), 96) : 0;   // |q| 2^-s < 2^15
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[mt][j][i] = (f16)ldexpf((float)raw[j][i], -s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        const int sh = __shfl(s, 4 * lg + i, 64);
+        wv[mt][i] = hh < H_I ? ldexpf(wrow[hh], sh) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (h < H_I) qf[mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
+        else zero_frag(qf[mt][kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        wv[mt][i] = hh < H_I ? wrow[hh] : 0.0f;
+      }
+    }
+  }
+}
+
+// One super-tile of 64 consecutive entries in registers: lane (e = l % 16,
+// g = l / 16) holds, for tile tt, the 16 code bytes of quantisation block g of
+// entry 16tt + e and that entry's 4 scale bytes.
+struct StLoad {
+  uint4 c[SPT];
+  uint32_t s[SPT];
+};
+
+// Score of entry 64st + lane of a loaded super-tile, in every lane.  bf16: the
+// lane's dword j feeds k-step j, scaled by block g's scale inside the operand;
+// the weighted ReLU sums of the 4 tiles are head-summed over the 4 lane groups at
+// once with two rounds of permlane swaps.  fp32: four permlane swaps transpose the
+// 4 x 4 pattern (lane group x dword) so that dword kb of lane group g holds dims
+// 32kb + 8g .. +7 and k-step kb covers block kb, whose per-entry scale multiplies
+// the step's partial product.  ReLU is an integer max on the float's bits
+// (negative floats are negative integers).
+template <typename T>
+__device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type (&qf)[2][4],
+                                                 const float (&wv)[2][4], const StLoad& L, int lg) {
+  if constexpr (sizeof(T) == 2) {
+    float part[SPT];
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
+      float p2;
+      f16x2 mm;
+      split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
+      f32x4 acc[2];
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
+        acc[0] = mma16h(qf[0][j], kf, acc[0]);
+        acc[1] = mma16h(qf[1][j], kf, acc[1]);
+      }
+      float p = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          p = fmaf(wv[mt][ii], __int_as_float(max(__float_as_int(acc[mt][ii]), 0)), p);
+      part[tt] = p;
+    }
+    // after two rounds of swaps and adds lane group g holds tile g's sums
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float s13 = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+    const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  } else {
+    float mine = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
+      f32x4 acc[2];
+      auto a = __builtin_amdgcn_permlane32_swap(cw[0], cw[2], false, false);
+      auto b2 = __builtin_amdgcn_permlane32_swap(cw[1], cw[3], false, false);
+      auto c0 = __builtin_amdgcn_permlane16_swap(a[0], b2[0], false, false);
+      auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
+      cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
+      const uint32_t sw = L.s[tt];
+      const float scv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sw, 0), __builtin_amdgcn_cvt_f32_fp8((int)sw, 1),
+                            __builtin_amdgcn_cvt_f32_fp8((int)sw, 2), __builtin_amdgcn_cvt_f32_fp8((int)sw, 3)};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const auto kf = Fp4<T>::cvt(cw[kb]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const f32x4 tmp = mma16(qf[mt][kb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+          if (kb == 0) acc[mt] = tmp * scv[0];
+          else acc[mt] += tmp * scv[kb];
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) part += wv[mt][ii] * fmaxf(acc[mt][ii], 0.0f);
+      part = sum_lane_groups(part);   // entry 16tt + e, in all four lane groups
+      if (lg == tt) mine = part;
+    }
+    return mine;
+  }
+}
+
 template <typename T, bool POOL, bool BUILD>
 __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
@@ -457,65 +600,16 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   const int n_here = POOL ? C : min(C, n_t - base);
   const int Ce = min(C, (n_here + gran - 1) / gran * gran);
 
-  // indexer query fragments: row tile mt = heads 16mt.., k-step kb = dims 32kb + 8lg ..
-  // bf16: k-step j of lane group g holds dims 32g + 8j .. +7 (block g), fp16 as
-  // described above; fp32: k-step kb holds block kb (dims 32kb + 8g .. +7)
   typename ScoreQ<T>::type qf[2][4];
   float wv[2][4];
-  const T* qb = q_idx + (size_t)bt * H_I * 128;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int h = mt * 16 + lr;
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 raw[4];
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (h < H_I) raw[j] = load_frag(qb + (size_t)h * 128 + 32 * lg + 8 * j);
-        else zero_frag(raw[j]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)raw[j][i]));
-      }
-      amax = max_lane_groups(amax);
-      int ex = 0;
-      frexpf(amax, &ex);                          // amax < 2^ex
-      const int s = amax > 0.0f ? min(max(ex - 15, -96), 96) : 0;   // |q| 2^-s < 2^15
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[mt][j][i] = (f16)ldexpf((float)raw[j][i], -s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = mt * 16 + 4 * lg + i;
-        const int sh = __shfl(s, 4 * lg + i, 64);
-        wv[mt][i] = hh < H_I ? ldexpf(w[(size_t)bt * H_I + hh], sh) : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (h < H_I) qf[mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
-        else zero_frag(qf[mt][kb]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = mt * 16 + 4 * lg + i;
-        wv[mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
-      }
-    }
-  }
+  load_qfrags<T>(q_idx + (size_t)bt * H_I * 128, w + (size_t)bt * H_I, H_I, lr, lg, qf, wv);
   const int32_t* cq = POOL ? cands + (size_t)bt * hsi_nb : nullptr;
   const uint8_t* cb = codes + (size_t)b * N_cap * 64;
   const uint8_t* sb = scales + (size_t)b * N_cap * 4;
 
-  // ---- scoring.  Wave w takes super-tiles w, w+4, ... of 64 entries (4 tiles of
-  // 16), straight into registers: lane (e = l % 16, g = l / 16) of a tile loads the
-  // 16 code bytes of quantisation block g of entry e (a tile of consecutive entries
-  // is one contiguous 1 KB) and the entry's 4 scale bytes.  bf16: the lane's dword
-  // j feeds k-step j, scaled by block g's scale inside the operand.  fp32: four
-  // permlane swaps transpose the 4 x 4 pattern (lane group x dword) so that dword
-  // kb of lane group g holds dims 32kb + 8g .. +7 and k-step kb covers block kb,
-  // whose per-entry scale multiplies the step's partial product.  The next
-  // super-tile's loads are in flight while one is computed.
+  // ---- scoring.  Wave w takes super-tiles w, w+4, ... of 64 entries (StLoad,
+  // score_supertile); the next super-tile's loads are in flight while one is
+  // computed.
   const int n_st = Ce / 64;
   const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave
   auto entry_at = [&](int j, bool& valid) -> int {   // chunk position -> entry id
@@ -531,10 +625,6 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     const int ent = base + j;
     valid = ent < n_t;
     return valid ? ent : 0;
-  };
-  struct StLoad {
-    uint4 c[SPT];
-    uint32_t s[SPT];
   };
   // Flat selection reads consecutive entries through buffer resources over this
   // sequence's codes and scales: one offset per super-tile, immediate offsets per
@@ -574,86 +664,11 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     }
   };
   auto compute = [&](int i, const StLoad& L) {
-    const int st = wave + 4 * i;
-    if constexpr (sizeof(T) == 2) {
-      // per tile: 8 heads x 1 entry per lane; ReLU as an integer max on the float's
-      // bits (negative floats are negative integers)
-      float part[SPT];
-#pragma unroll
-      for (int tt = 0; tt < SPT; ++tt) {
-        const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
-        float p2;
-        f16x2 mm;
-        split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
-        f32x4 acc[2];
-        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
-          acc[0] = mma16h(qf[0][j], kf, acc[0]);
-          acc[1] = mma16h(qf[1][j], kf, acc[1]);
-        }
-        float p = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-            p = fmaf(wv[mt][ii], __int_as_float(max(__float_as_int(acc[mt][ii]), 0)), p);
-        part[tt] = p;
-      }
-      // head sums of the 4 tiles over the 4 lane groups at once: after two rounds
-      // of swaps and adds lane group g holds tile g's sums, i.e. entry st*64 + lane
-      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
-      const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
-      const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-      const float s13 = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
-      const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-      const float s = __uint_as_float(c[0]) + __uint_as_float(c[1]);
-      const int j = st * 64 + lane;
-      bool valid;
-      entry_at(j, valid);
-      keys[j] = valid ? score_key(s) : 0u;
-    } else {
-#pragma unroll
-    for (int tt = 0; tt < SPT; ++tt) {
-      uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
-      f32x4 acc[2];
-      {
-        auto a = __builtin_amdgcn_permlane32_swap(cw[0], cw[2], false, false);
-        auto b2 = __builtin_amdgcn_permlane32_swap(cw[1], cw[3], false, false);
-        auto c0 = __builtin_amdgcn_permlane16_swap(a[0], b2[0], false, false);
-        auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
-        cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
-        const uint32_t sw = L.s[tt];
-        const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-        const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-        const float sc2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
-        const float sc3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
-        const float scv[4] = {sc0, sc1, sc2, sc3};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const auto kf = Fp4<T>::cvt(cw[kb]);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const f32x4 tmp = mma16(qf[mt][kb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (kb == 0) acc[mt] = tmp * scv[0];
-            else acc[mt] += tmp * scv[kb];
-          }
-        }
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) part += wv[mt][ii] * fmaxf(acc[mt][ii], 0.0f);
-      part = sum_lane_groups(part);
-      const int j = st * 64 + tt * 16 + lr;
-      bool valid;
-      entry_at(j, valid);
-      if (lg == 0) keys[j] = valid ? score_key(part) : 0u;
-    }
-    }   // fp32
+    const float sc = score_supertile<T>(qf, wv, L, lg);
+    const int j = (wave + 4 * i) * 64 + lane;
+    bool valid;
+    entry_at(j, valid);
+    keys[j] = valid ? score_key(sc) : 0u;
   };
   // one loop per load form, so that each loop's wait counts see one kind of load
   auto scan = [&](auto load_st) {
@@ -960,6 +975,259 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
       cnt = emit_ordered<MG_THREADS>(bkey, nblk, s, sel, [&](int i, uint32_t slot) { out[slot] = i; });
     }
     for (int i = (int)cnt + threadIdx.x; i < hsi_nb; i += MG_THREADS) out[i] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming path (no HSI): one workgroup of 8 waves per (query, part of up to
+// ST_MAXR consecutive entries).  Scores are filtered as they are computed: an
+// entry is staged in LDS (key and id) only if its key is at least theta, the k-th
+// best key among the entries the workgroup has scored so far.  Every entry it
+// drops scores below the query's k-th best, so it cannot be chosen.  When the
+// staged set could overflow (and once after the first 4096 entries, to set
+// theta), it is cut back to its k best, which raises theta; so the block-wide
+// selection runs a few times per part instead of once per 4096 entries, and the
+// scan keeps the loads streaming.  The part's k best leave in id order: as the
+// query's top-k when one part covers its visible entries, else as a candidate
+// list for topk_merge with a lower bound of the part's rank-r0 key.
+constexpr int ST_THREADS = 512;    // two workgroups per CU
+constexpr int ST_NW = ST_THREADS / 64;
+constexpr int ST_ROUND = ST_NW * 64;   // entries scored per round: one super-tile per wave
+constexpr int ST_CAP = 4096;           // staged candidates
+constexpr int ST_MAXR = 65536;         // entries per part at most (an id bitmap of 2048 words)
+constexpr int ST_WPT = ST_MAXR / 32 / ST_THREADS;   // bitmap words per thread
+constexpr int ST_FIRST = 4096;         // entries scored before theta is first set
+
+struct StreamSmem {
+  SelSmem<ST_THREADS> sel;
+  uint32_t key[ST_CAP];
+  int32_t id[ST_CAP];
+  uint32_t bits[ST_MAXR / 32];
+  uint32_t wpre[ST_MAXR / 32];
+  uint32_t tkey[CSA2_MAX_TOPK];
+  int32_t tid[CSA2_MAX_TOPK];
+  uint32_t cnt, theta;
+};
+
+// Exclusive prefix counts of the set bits of words [0, nw) of S.bits into S.wpre.
+__device__ __forceinline__ void st_bit_prefix(StreamSmem& S, int nw) {
+  uint32_t pc[ST_WPT], tot = 0;
+#pragma unroll
+  for (int j = 0; j < ST_WPT; ++j) {
+    const int wi = threadIdx.x * ST_WPT + j;
+    pc[j] = wi < nw ? (uint32_t)__popc(S.bits[wi]) : 0u;
+    tot += pc[j];
+  }
+  uint32_t total;
+  uint32_t pre = block_prefix_excl<ST_THREADS>(tot, S.sel, total);
+#pragma unroll
+  for (int j = 0; j < ST_WPT; ++j) {
+    const int wi = threadIdx.x * ST_WPT + j;
+    if (wi < nw) S.wpre[wi] = pre;
+    pre += pc[j];
+  }
+  __syncthreads();
+}
+
+// Rank of id offset r among the set bits of S.bits (valid after st_bit_prefix).
+__device__ __forceinline__ uint32_t st_rank(const StreamSmem& S, int r) {
+  return S.wpre[r >> 5] + (uint32_t)__popc(S.bits[r >> 5] & ((1u << (r & 31)) - 1u));
+}
+
+// Chooses the `need` best of the c staged candidates (ties to the smaller id; ids
+// lie in [base, base + range)) and calls put(rank, key, id) for each, rank being
+// its position in id order; returns how many were chosen.  thresh receives a
+// value at or below the smallest chosen key; with r0 != 0, lb a lower bound of
+// the rank-r0 key.
+template <typename Put>
+__device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, int base, int range,
+                              uint32_t& thresh, uint32_t& lb, Put put) {
+  auto key_at = [&](int i) -> uint32_t { return S.key[i]; };
+  uint32_t mn, mx, nv;
+  key_stats<ST_THREADS>(key_at, c, S.sel, mn, mx, nv);
+  if (need > nv) need = nv;
+  const SelOut sel = (need == nv && r0 == 0) ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                             : select_threshold<ST_THREADS>(key_at, c, need, mn, mx, r0, S.sel, true);
+  thresh = sel.thresh;
+  lb = sel.lb;
+  const int nw = (range + 31) >> 5;
+  for (int i = threadIdx.x; i < nw; i += ST_THREADS) S.bits[i] = 0u;
+  __syncthreads();
+  if (sel.eq_take != 0xFFFFFFFFu) {
+    // a partial tie at the threshold: keep the eq_take smallest ids among the tied
+    for (int i = threadIdx.x; i < c; i += ST_THREADS)
+      if (S.key[i] == sel.thresh) {
+        const int r = S.id[i] - base;
+        atomicOr(&S.bits[r >> 5], 1u << (r & 31));
+      }
+    __syncthreads();
+    st_bit_prefix(S, nw);
+    for (int i = threadIdx.x; i < c; i += ST_THREADS)
+      if (S.key[i] == sel.thresh && st_rank(S, S.id[i] - base) >= sel.eq_take) S.key[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nw; i += ST_THREADS) S.bits[i] = 0u;
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < c; i += ST_THREADS) {
+    const uint32_t kk = S.key[i];
+    if (kk != 0u && kk >= sel.thresh) {
+      const int r = S.id[i] - base;
+      atomicOr(&S.bits[r >> 5], 1u << (r & 31));
+    }
+  }
+  __syncthreads();
+  st_bit_prefix(S, nw);
+  for (int i = threadIdx.x; i < c; i += ST_THREADS) {
+    const uint32_t kk = S.key[i];
+    if (kk != 0u && kk >= sel.thresh) put(st_rank(S, S.id[i] - base), kk, S.id[i]);
+  }
+  __syncthreads();
+  return need;
+}
+
+template <typename T>
+__global__ __launch_bounds__(ST_THREADS) void score_stream(
+    const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb, int32_t* __restrict__ topk, int T_len,
+    int H_I, int N_cap, int n_entries, int m, int R, int n_parts, int k, int k_chunk) {
+  __shared__ StreamSmem S;
+  const int part = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int bt = b * T_len + t;
+  const int n_t = visible(q_pos, bt, m, n_entries);
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int base = part * R;
+  const int np_q = (n_t + R - 1) / R;
+  const bool direct = np_q <= 1;   // one part covers the query: its top-k is written here
+  if (base >= n_t) {
+    if (direct && part == 0)   // nothing visible
+      for (int i = threadIdx.x; i < k; i += ST_THREADS) topk[(size_t)bt * k + i] = -1;
+    return;                    // a part beyond the visible range: never read by the merge
+  }
+  const int n_here = min(R, n_t - base);
+  const int n_rounds = (n_here + ST_ROUND - 1) / ST_ROUND;
+
+  typename ScoreQ<T>::type qf[2][4];
+  float wv[2][4];
+  load_qfrags<T>(q_idx + (size_t)bt * H_I * 128, w + (size_t)bt * H_I, H_I, lr, lg, qf, wv);
+  const uint8_t* cb = codes + (size_t)b * N_cap * 64;
+  const uint8_t* sb = scales + (size_t)b * N_cap * 4;
+  if (threadIdx.x == 0) {
+    S.cnt = 0u;
+    S.theta = 0u;
+  }
+  __syncthreads();
+
+  // Round i: wave w scores super-tile ST_NW i + w of the part.  Loads as in
+  // score_chunk: through buffer resources (reads past the N_cap entries, and the
+  // dead loads past the last round, return 0 with no memory access), else plain
+  // loads of entry 0 for the dead ones.
+  const bool use_buf = N_cap <= (1 << 25);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)cb, (short)0, use_buf ? N_cap * 64 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sb, (short)0, use_buf ? N_cap * 4 : 0, 0x00020000);
+  auto load_buf = [&](int i, StLoad& L) {
+    const bool live = i < n_rounds;
+    const int e = base + (i * ST_NW + wave) * 64 + lr;
+    const int oc = live ? e * 64 + 16 * lg : (int)0x80000000;
+    const int os = live ? e * 4 : (int)0x80000000;
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + tt * 1024, 0, 0);
+      L.c[tt] = make_uint4(v[0], v[1], v[2], v[3]);
+      L.s[tt] = __builtin_amdgcn_raw_buffer_load_b32(rs, os + tt * 64, 0, 0);
+    }
+  };
+  auto load_glob = [&](int i, StLoad& L) {
+    const bool live = i < n_rounds;
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const int e = base + (i * ST_NW + wave) * 64 + tt * 16 + lr;
+      const int ent = live && e < n_t ? e : 0;
+      L.c[tt] = *reinterpret_cast<const uint4*>(cb + (size_t)ent * 64 + 16 * lg);
+      L.s[tt] = *reinterpret_cast<const uint32_t*>(sb + (size_t)ent * 4);
+    }
+  };
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t theta = 0u;
+  auto round = [&](int i, const StLoad& L) {
+    const float sc = score_supertile<T>(qf, wv, L, lg);
+    const int j = (i * ST_NW + wave) * 64 + lane;   // position in the part
+    const uint32_t kk = j < n_here ? score_key(sc) : 0u;
+    const bool pass = kk != 0u && kk >= theta;
+    const uint64_t msk = __ballot(pass);
+    if (msk != 0ull) {
+      uint32_t slot0 = 0u;
+      if (lane == 0) slot0 = atomicAdd(&S.cnt, (uint32_t)__popcll(msk));
+      slot0 = __shfl(slot0, 0, 64);
+      if (pass) {
+        const uint32_t sl = slot0 + (uint32_t)__popcll(msk & lt);
+        S.key[sl] = kk;
+        S.id[sl] = base + j;
+      }
+    }
+    __syncthreads();
+    const uint32_t c = S.cnt;
+    __syncthreads();   // every thread has read the count before the next round adds to it
+    const int seen = min(n_here, (i + 1) * ST_ROUND);
+    if (i + 1 < n_rounds &&
+        (c > (uint32_t)(ST_CAP - ST_ROUND) || (theta == 0u && seen >= ST_FIRST && c >= (uint32_t)k))) {
+      uint32_t th, lb_unused;
+      const uint32_t got = st_choose(S, (int)c, (uint32_t)k, 0u, base, n_here, th, lb_unused,
+                                     [&](uint32_t r, uint32_t key, int32_t id) {
+                                       S.tkey[r] = key;
+                                       S.tid[r] = id;
+                                     });
+      for (uint32_t q = threadIdx.x; q < got; q += ST_THREADS) {
+        S.key[q] = S.tkey[q];
+        S.id[q] = S.tid[q];
+      }
+      if (threadIdx.x == 0) {
+        S.cnt = got;
+        S.theta = got >= (uint32_t)k ? th : 0u;
+      }
+      __syncthreads();
+    }
+    theta = S.theta;
+  };
+  auto scan = [&](auto load_st) {
+    StLoad L0, L1;
+    load_st(0, L0);
+    for (int i = 0; i < n_rounds; i += 2) {
+      load_st(i + 1, L1);
+      __builtin_amdgcn_sched_barrier(0);
+      round(i, L0);
+      load_st(i + 2, L0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < n_rounds) round(i + 1, L1);
+    }
+  };
+  if (use_buf) scan(load_buf);
+  else scan(load_glob);
+
+  // ---- the part's k best in id order
+  const int c = (int)S.cnt;
+  const uint32_t r0 = (direct || part == np_q - 1) ? 0u : rank_for_bound(k, np_q);
+  uint32_t th, lb;
+  if (direct) {
+    int32_t* out = topk + (size_t)bt * k;
+    const uint32_t got = st_choose(S, c, (uint32_t)k, 0u, base, n_here, th, lb,
+                                   [&](uint32_t r, uint32_t, int32_t id) { out[r] = id; });
+    for (int i = (int)got + threadIdx.x; i < k; i += ST_THREADS) out[i] = -1;
+  } else {
+    const size_t obase = ((size_t)bt * n_parts + part) * k_chunk;
+    const uint32_t got = st_choose(S, c, (uint32_t)k, r0, base, n_here, th, lb,
+                                   [&](uint32_t r, uint32_t key, int32_t id) {
+                                     cand_key[obase + r] = key;
+                                     cand_idx[obase + r] = id;
+                                   });
+    if (threadIdx.x == 0) chunk_lb[(size_t)bt * n_parts + part] = lb;
+    for (int i = (int)got + threadIdx.x; i < k_chunk; i += ST_THREADS) {
+      cand_key[obase + i] = 0u;
+      cand_idx[obase + i] = -1;
+    }
   }
 }
 
@@ -1420,6 +1688,29 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
 }
 
 template <typename T>
+hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
+                         const int32_t* q_pos, int32_t* topk, int B, int T_len, int H_I, int N_cap, int n_entries,
+                         int m, int k, void* ws, const ScorePlan& p, hipStream_t st) {
+  char* wsb = static_cast<char*>(ws);
+  const size_t n_slots = p.cand_bytes / 8;
+  uint32_t* cand_key = reinterpret_cast<uint32_t*>(wsb);
+  int32_t* cand_idx = reinterpret_cast<int32_t*>(wsb + n_slots * 4);
+  uint32_t* chunk_lb = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes);
+  dim3 g1(p.n_chunks, T_len, B);
+  hipLaunchKernelGGL(score_stream<T>, g1, dim3(ST_THREADS), 0, st, static_cast<const T*>(q_idx), w, codes, scales,
+                     q_pos, cand_key, cand_idx, chunk_lb, topk, T_len, H_I, N_cap, n_entries, m, p.chunk, p.n_chunks,
+                     k, p.k_chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single part
+  dim3 g2(T_len, B, 1);
+  hipLaunchKernelGGL((topk_merge<false, false>), g2, dim3(MG_THREADS), 0, st, cand_key, cand_idx, chunk_lb,
+                     (const uint32_t*)nullptr, q_pos, topk, (int32_t*)nullptr, T_len, n_entries, m, k, p.chunk,
+                     p.k_chunk, p.n_chunks, 0, 0, 0);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_mode(int hsi, const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
                        int n_entries, int m, int k, int hsi_s, int hsi_nb, void* ws, const ScorePlan& p,
@@ -1449,13 +1740,29 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
     p.total_bytes = p.key_bytes + 256;
     return p;
   }
+  const int k4 = (k + 3) & ~3;   // candidate lists in whole uint4s (the merge reads them so)
+  if (hsi == 0 && Q >= 8192) {
+    // streaming path (very many queries): parts of R entries (whole rounds, at most
+    // ST_MAXR), about 512 workgroups in all (two per CU); fewer selections per query
+    // than the chunked path, whose per-chunk selections dominate there
+    const long long want = n_scan <= 0 ? 1 : (Q * (long long)n_scan + 511) / 512;
+    long long R = (want + ST_ROUND - 1) / ST_ROUND * ST_ROUND;
+    if (R > ST_MAXR) R = ST_MAXR;
+    p.stream = true;
+    p.chunk = (int)R;
+    p.n_chunks = n_scan <= 0 ? 1 : (int)((n_scan + R - 1) / R);
+    p.k_chunk = k4;   // <= CSA2_MAX_TOPK <= R
+    p.cand_bytes = (size_t)Q * p.n_chunks * p.k_chunk * 8;
+    p.lb_bytes = ((size_t)Q * p.n_chunks * 4 + 255) / 256 * 256;
+    p.total_bytes = p.cand_bytes + p.lb_bytes + 256;
+    return p;
+  }
   int C = MAX_CHUNK;
   while (C > 256 && C / 2 >= n_scan) C /= 2;                       // no chunk much larger than the scan
   while (C > 1024 && Q * ((n_scan + C - 1) / C) < 1024) C /= 2;   // enough workgroups to fill the GPU
   if (hsi != 0 && C < hsi_s) C = hsi_s;                           // chunks hold whole blocks
   p.chunk = C;
   p.n_chunks = n_scan <= 0 ? 1 : (n_scan + C - 1) / C;
-  const int k4 = (k + 3) & ~3;   // candidate lists in whole uint4s (the merge reads them so)
   p.k_chunk = k4 < C ? k4 : C;
   p.cand_bytes = (size_t)Q * p.n_chunks * p.k_chunk * 8;
   p.lb_bytes = ((size_t)Q * p.n_chunks * 4 + 255) / 256 * 256;
@@ -1473,6 +1780,11 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
   if (plan.tiled)
     return launch_tiled(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k, plan.chunk,
                         workspace, plan, stream);
+  if (plan.stream)
+    return dtype == 1 ? launch_stream<bf16>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
+                                            workspace, plan, stream)
+                      : launch_stream<float>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
+                                             workspace, plan, stream);
   if (dtype == 1)
     return launch_mode<bf16>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
                              k, hsi_s, hsi_nb, workspace, plan, stream);

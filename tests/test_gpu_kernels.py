@@ -174,15 +174,20 @@ def test_score_topk_many_queries_vs_oracle(m, k, H_I):
 
 
 @pytest.mark.parametrize("dtype,T,n_fill", [(torch.bfloat16, 3, 5000), (torch.bfloat16, 300, 5000),
-                                            (torch.bfloat16, 300, 4000), (torch.float32, 3, 5000)])
+                                            (torch.bfloat16, 300, 4000), (torch.float32, 3, 5000),
+                                            (torch.bfloat16, 64, 40000), (torch.bfloat16, 8192, 10000),
+                                            (torch.float32, 8192, 10000), (torch.bfloat16, 8192, 70000)])
 def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill):
     """An index-K cache of 50 distinct rows repeated: every score value occurs ~100
     times, so the k-th best falls inside a group of equal scores and the selection
     must take that group's smallest positions (ties go to the smaller entry id).
     Equal rows give bit-identical scores on both sides, and the distinct values are
-    kept well apart, so the chosen set is unique and compared exactly: T = 3 runs
-    the chunked scorer and the merge, T = 300 the query-tiled scorer and the
-    per-query select (rows of up to 4096 keys held 64 per lane, longer rows 128)."""
+    kept well apart, so the chosen set is unique and compared exactly: T = 3 and
+    T = 64 run the chunked scorer and the merge, T = 300 the query-tiled scorer
+    and the per-query select (rows of up to 4096 keys held 64 per lane, longer
+    rows 128), T = 8192 the streaming scorer with its in-part cutbacks to the k
+    best (the boundary tie group cut there too), over one part and, with 70000
+    entries, two parts and the merge."""
     B, k, H_I, m = 1, 512, 32, 1
     say(f"case: score_topk exact ties dtype={dtype} T={T}")
     u = synth.gaussian((50, 128), 1.0, 31, "u", 0, torch.float32, "cpu").numpy()
@@ -200,7 +205,7 @@ def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill):
     torch.cuda.synchronize()
     tg = topk.cpu().numpy()
     checked = ties = 0
-    for t in sorted(set([0, 1, T - 1] + list(range(0, T, 37)))):
+    for t in sorted(set([0, 1, T - 1] + list(range(0, T, max(37, T // 12))))):
         sc = O.index_scores(npy(q_idx[0, t]), npy(w[0, t]), kd, n_fill)
         vals = np.unique(sc)
         gaps = np.diff(vals) / np.maximum(np.abs(vals[1:]), 1e-30)
