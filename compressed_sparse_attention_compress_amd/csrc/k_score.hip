@@ -600,16 +600,65 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   const int n_here = POOL ? C : min(C, n_t - base);
   const int Ce = min(C, (n_here + gran - 1) / gran * gran);
 
+  // indexer query fragments: row tile mt = heads 16mt.., k-step kb = dims 32kb + 8lg ..
+  // bf16: k-step j of lane group g holds dims 32g + 8j .. +7 (block g), fp16 as
+  // described above; fp32: k-step kb holds block kb (dims 32kb + 8g .. +7)
   typename ScoreQ<T>::type qf[2][4];
   float wv[2][4];
-  load_qfrags<T>(q_idx + (size_t)bt * H_I * 128, w + (size_t)bt * H_I, H_I, lr, lg, qf, wv);
+  const T* qb = q_idx + (size_t)bt * H_I * 128;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int h = mt * 16 + lr;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 raw[4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (h < H_I) raw[j] = load_frag(qb + (size_t)h * 128 + 32 * lg + 8 * j);
+        else zero_frag(raw[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)raw[j][i]));
+      }
+      amax = max_lane_groups(amax);
+      int ex = 0;
+      frexpf(amax, &ex);                          // amax < 2^ex
+      const int s = amax > 0.0f ? min(max(ex - 15, -96), 96) : 0;   // |q| 2^-s < 2^15
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[mt][j][i] = (f16)ldexpf((float)raw[j][i], -s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        const int sh = __shfl(s, 4 * lg + i, 64);
+        wv[mt][i] = hh < H_I ? ldexpf(w[(size_t)bt * H_I + hh], sh) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (h < H_I) qf[mt][kb] = load_frag(qb + (size_t)h * 128 + kb * 32 + 8 * lg);
+        else zero_frag(qf[mt][kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = mt * 16 + 4 * lg + i;
+        wv[mt][i] = hh < H_I ? w[(size_t)bt * H_I + hh] : 0.0f;
+      }
+    }
+  }
   const int32_t* cq = POOL ? cands + (size_t)bt * hsi_nb : nullptr;
   const uint8_t* cb = codes + (size_t)b * N_cap * 64;
   const uint8_t* sb = scales + (size_t)b * N_cap * 4;
 
-  // ---- scoring.  Wave w takes super-tiles w, w+4, ... of 64 entries (StLoad,
-  // score_supertile); the next super-tile's loads are in flight while one is
-  // computed.
+  // ---- scoring.  Wave w takes super-tiles w, w+4, ... of 64 entries (4 tiles of
+  // 16), straight into registers: lane (e = l % 16, g = l / 16) of a tile loads the
+  // 16 code bytes of quantisation block g of entry e (a tile of consecutive entries
+  // is one contiguous 1 KB) and the entry's 4 scale bytes.  bf16: the lane's dword
+  // j feeds k-step j, scaled by block g's scale inside the operand.  fp32: four
+  // permlane swaps transpose the 4 x 4 pattern (lane group x dword) so that dword
+  // kb of lane group g holds dims 32kb + 8g .. +7 and k-step kb covers block kb,
+  // whose per-entry scale multiplies the step's partial product.  The next
+  // super-tile's loads are in flight while one is computed.
   const int n_st = Ce / 64;
   const int st_w = (n_st - wave + 3) / 4;   // super-tiles of this wave
   auto entry_at = [&](int j, bool& valid) -> int {   // chunk position -> entry id
@@ -664,11 +713,86 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     }
   };
   auto compute = [&](int i, const StLoad& L) {
-    const float sc = score_supertile<T>(qf, wv, L, lg);
-    const int j = (wave + 4 * i) * 64 + lane;
-    bool valid;
-    entry_at(j, valid);
-    keys[j] = valid ? score_key(sc) : 0u;
+    const int st = wave + 4 * i;
+    if constexpr (sizeof(T) == 2) {
+      // per tile: 8 heads x 1 entry per lane; ReLU as an integer max on the float's
+      // bits (negative floats are negative integers)
+      float part[SPT];
+#pragma unroll
+      for (int tt = 0; tt < SPT; ++tt) {
+        const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
+        float p2;
+        f16x2 mm;
+        split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
+        f32x4 acc[2];
+        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
+          acc[0] = mma16h(qf[0][j], kf, acc[0]);
+          acc[1] = mma16h(qf[1][j], kf, acc[1]);
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            p = fmaf(wv[mt][ii], __int_as_float(max(__float_as_int(acc[mt][ii]), 0)), p);
+        part[tt] = p;
+      }
+      // head sums of the 4 tiles over the 4 lane groups at once: after two rounds
+      // of swaps and adds lane group g holds tile g's sums, i.e. entry st*64 + lane
+      const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      const float s13 = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+      const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+      const float s = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      const int j = st * 64 + lane;
+      bool valid;
+      entry_at(j, valid);
+      keys[j] = valid ? score_key(s) : 0u;
+    } else {
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
+      f32x4 acc[2];
+      {
+        auto a = __builtin_amdgcn_permlane32_swap(cw[0], cw[2], false, false);
+        auto b2 = __builtin_amdgcn_permlane32_swap(cw[1], cw[3], false, false);
+        auto c0 = __builtin_amdgcn_permlane16_swap(a[0], b2[0], false, false);
+        auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
+        cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
+        const uint32_t sw = L.s[tt];
+        const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+        const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
+        const float sc2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
+        const float sc3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+        const float scv[4] = {sc0, sc1, sc2, sc3};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const auto kf = Fp4<T>::cvt(cw[kb]);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const f32x4 tmp = mma16(qf[mt][kb], kf, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (kb == 0) acc[mt] = tmp * scv[0];
+            else acc[mt] += tmp * scv[kb];
+          }
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) part += wv[mt][ii] * fmaxf(acc[mt][ii], 0.0f);
+      part = sum_lane_groups(part);
+      const int j = st * 64 + tt * 16 + lr;
+      bool valid;
+      entry_at(j, valid);
+      if (lg == 0) keys[j] = valid ? score_key(part) : 0u;
+    }
+    }   // fp32
   };
   // one loop per load form, so that each loop's wait counts see one kind of load
   auto scan = [&](auto load_st) {
