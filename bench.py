@@ -785,7 +785,8 @@ def main():
                           "append_attn_reuse": round(wst[2] * 1e3, 2)},
             "roofline": {"bound": "hbm", "kernel": "swa_append + sparse_attn (FP4 KV, FP8 ring)",
                          "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                         "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for("sparse_attn_fp4kv_fp8swa", ["k_attn.hip", "k_swa.hip"])},
             "attn_bytes_per_layer": ww["sparse_attn"]["bytes"],
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (wms * 1e-3), 4),
         }
@@ -811,7 +812,7 @@ def main():
                           "attn_2_layers": round(hst[2] * 1e3, 2)},
             "roofline": {"bound": "hbm", "kernel": "score_full_build", "achieved": round(full_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(full_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None},
+                         "traffic": traffic_for("score_hsi_full", ["k_score.hip"])},
             "step_bytes": step_bytes,
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (hms * 1e-3), 4),
         }
@@ -850,7 +851,8 @@ def main():
                 "stages_ms": {n: round(t, 4) for n, t in zip(("full", "reindex", "reuse", "reuse2"), dec_st)},
                 "roofline": {"bound": "mfma", "kernel": "compress (projections)", "achieved": round(c_tf, 2),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(c_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                             "frac": round(c_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": traffic_for("compress_decoder", ["k_compress.hip"])},
                 "step_tflops": round(step_tf, 2),
                 "step_frac_of_mfma_peak": round(step_tf / MFMA_BF16_PEAK_TFLOPS, 4),
             }
@@ -874,7 +876,8 @@ def main():
             "us_per_token_step": round(per_tok * 1e3, 2), "us_per_token_step_eager": round(ams_eager / ab.m * 1e3, 2),
             "stages_us": {"group_first_token": round(ast[0] * 1e3, 2), "group_last_token": round(ast[1] * 1e3, 2)},
             "roofline": {"bound": "hbm", "kernel": "compress_step", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for("compress_step", ["k_compress.hip"])},
         }
         del ab
         torch.cuda.empty_cache()
