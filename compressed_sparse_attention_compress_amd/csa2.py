@@ -64,7 +64,7 @@ class ScoreTopkArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H_I", i32), ("N_cap", i32), ("n_entries", i32),
                 ("m", i32), ("k", i32), ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("q_idx", vp), ("w", vp),
                 ("codes", vp), ("scales", vp), ("q_pos", vp), ("topk", vp), ("candidates", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("scores", vp)]
 
 
 class SparseAttnArgs(C.Structure):
@@ -220,13 +220,15 @@ def csa2_index_k(rt, latent_pre, w_ik, codes, scales, m: int, entry0: int = 0, r
 
 
 def score_topk_args(q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int, N_cap: int,
-                    hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0, candidates=None, workspace=None):
+                    hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0, candidates=None, workspace=None,
+                    scores=None):
     B, T, H_I, _ = q_idx.shape
     return ScoreTopkArgs(dtype=_dtype(q_idx), B=B, T=T, H_I=H_I, N_cap=N_cap, n_entries=n_entries, m=m, k=k,
                          hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, q_idx=_ptr(q_idx), w=_ptr(w), codes=_ptr(codes),
                          scales=_ptr(scales), q_pos=_ptr(q_pos), topk=_ptr(topk), candidates=_ptr(candidates),
                          workspace=_ptr(workspace),
-                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+                         workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         scores=_ptr(scores))
 
 
 def score_topk_workspace_bytes(**kw) -> int:
@@ -238,8 +240,10 @@ def score_topk_workspace_bytes(**kw) -> int:
 
 def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int,
                     N_cap: Optional[int] = None, hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0,
-                    candidates=None, workspace=None, stream=None):
-    """Score and select; codes/scales None -> the runtime's index_k slot."""
+                    candidates=None, workspace=None, stream=None, scores=None):
+    """Score and select; codes/scales None -> the runtime's index_k slot.  scores:
+    optional float32 [B, T, n_scan] debug dump of the index scores (-inf where not
+    visible)."""
     if N_cap is None:
         N_cap = codes.shape[1]
     kw = dict(q_idx=q_idx, w=w, codes=codes, scales=scales, q_pos=q_pos, topk=topk, n_entries=n_entries, m=m,
@@ -247,7 +251,7 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
     if workspace is None:
         nbytes = score_topk_workspace_bytes(**kw)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q_idx.device)
-    a = score_topk_args(workspace=workspace, **kw)
+    a = score_topk_args(workspace=workspace, scores=scores, **kw)
     _check(lib().csa2_score_topk(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 

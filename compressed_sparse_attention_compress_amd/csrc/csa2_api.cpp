@@ -168,6 +168,7 @@ csa2_status resolve_score(const csa2_runtime* rt, csa2_score_topk_args& a) {
   }
   REQ(a.q_idx && a.w && a.q_pos && a.topk, CSA2_ERR_INVALID_ARG, "csa2_score_topk: NULL tensor");
   REQ(a.hsi == CSA2_HSI_NONE || a.candidates != nullptr, CSA2_ERR_INVALID_ARG, "csa2_score_topk: candidates is NULL");
+  REQ(((uintptr_t)a.scores & 3u) == 0, CSA2_ERR_INVALID_ARG, "csa2_score_topk: scores must be 4-byte aligned");
   return CSA2_OK;
 }
 
@@ -356,7 +357,7 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* in, cs
   REQ(((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE, "csa2_score_topk: workspace not 16-byte aligned");
   hipError_t e = csa2::launch_score_topk(a.dtype, a.q_idx, a.w, a.codes, a.scales, a.q_pos, a.topk, a.candidates, a.B,
                                          a.T, a.H_I, a.N_cap, a.n_entries, a.m, a.k, a.hsi, a.hsi_s, a.hsi_nb,
-                                         a.workspace, plan, st(stream));
+                                         a.workspace, plan, st(stream), a.scores);
   if (e != hipSuccess) return hip_status(e, "csa2_score_topk launch");
   publish(rt, CSA2_SLOT_TOPK_IDXS, a.topk, nullptr, 0, a.B, a.T, a.k, 0);
   if (a.hsi == CSA2_HSI_BUILD) publish(rt, CSA2_SLOT_CANDIDATES, a.candidates, nullptr, 0, a.B, a.T, a.hsi_nb, a.hsi_s);

@@ -59,7 +59,7 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
                              const uint8_t* scales, const int32_t* q_pos, int32_t* topk,
                              int32_t* candidates, int B, int T, int H_I, int N_cap, int n_entries,
                              int m, int k, int hsi, int hsi_s, int hsi_nb, void* workspace,
-                             const ScorePlan& plan, hipStream_t stream);
+                             const ScorePlan& plan, hipStream_t stream, float* scores_out = nullptr);
 
 // ---- host API (csa2_api.cpp)
 // Validates a score/top-k call (resolving slots) and gives the workspace bytes it

@@ -574,8 +574,8 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ cands,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb,
-    uint32_t* __restrict__ blkmax, int32_t* __restrict__ topk, int T_len, int H_I, int N_cap, int n_entries, int m,
-    int C, int k_chunk, int n_chunks, int k, int hsi_s, int hsi_nb, int nblk_max) {
+    uint32_t* __restrict__ blkmax, int32_t* __restrict__ topk, float* __restrict__ scores_out, int T_len, int H_I,
+    int N_cap, int n_entries, int m, int C, int k_chunk, int n_chunks, int k, int hsi_s, int hsi_nb, int nblk_max) {
   typedef typename Frag<T>::type FragT;
   __shared__ SelSmem<SC_THREADS> sm;
   __shared__ __attribute__((aligned(16))) uint32_t keys[MAX_CHUNK];
@@ -810,6 +810,11 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   if (use_buf) scan(load_buf);
   else scan(load_glob);
   __syncthreads();
+  if (scores_out != nullptr) {   // debug dump: the scores of this chunk's valid positions
+    float* srow = scores_out + (size_t)bt * (POOL ? hsi_nb * hsi_s : n_entries) + base;
+    for (int j = threadIdx.x; j < Ce; j += SC_THREADS)
+      if (keys[j] != 0u) srow[j] = key_score(keys[j]);
+  }
 
   if (BUILD) {
     // block maxima of this chunk (C is a multiple of hsi_s)
@@ -1213,8 +1218,9 @@ template <typename T>
 __global__ __launch_bounds__(ST_THREADS) void score_stream(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ cand_key,
-    int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb, int32_t* __restrict__ topk, int T_len,
-    int H_I, int N_cap, int n_entries, int m, int R, int n_parts, int k, int k_chunk) {
+    int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb, int32_t* __restrict__ topk,
+    float* __restrict__ scores_out, int T_len, int H_I, int N_cap, int n_entries, int m, int R, int n_parts, int k,
+    int k_chunk) {
   __shared__ StreamSmem S;
   const int part = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int bt = b * T_len + t;
@@ -1280,6 +1286,7 @@ __global__ __launch_bounds__(ST_THREADS) void score_stream(
     const float sc = score_supertile<T>(qf, wv, L, lg);
     const int j = (i * ST_NW + wave) * 64 + lane;   // position in the part
     const uint32_t kk = j < n_here ? score_key(sc) : 0u;
+    if (scores_out != nullptr && j < n_here) scores_out[(size_t)bt * n_entries + base + j] = key_score(kk);
     const bool pass = kk != 0u && kk >= theta;
     const uint64_t msk = __ballot(pass);
     if (msk != 0ull) {
@@ -1789,7 +1796,7 @@ template <typename T, bool POOL, bool BUILD>
 hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
                        int n_entries, int m, int k, int hsi_s, int hsi_nb, void* ws, const ScorePlan& p,
-                       hipStream_t st) {
+                       hipStream_t st, float* scores_out) {
   char* wsb = static_cast<char*>(ws);
   const size_t n_slots = p.cand_bytes / 8;
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(wsb);
@@ -1799,8 +1806,8 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   const int nblk_max = BUILD ? (n_entries + hsi_s - 1) / hsi_s : 0;
   dim3 g1(p.n_chunks, T_len, B);
   hipLaunchKernelGGL((score_chunk<T, POOL, BUILD>), g1, dim3(SC_THREADS), 0, st, static_cast<const T*>(q_idx), w,
-                     codes, scales, q_pos, cands, cand_key, cand_idx, chunk_lb, blkmax, topk, T_len, H_I, N_cap,
-                     n_entries, m, p.chunk, p.k_chunk, p.n_chunks, k, hsi_s, hsi_nb, nblk_max);
+                     codes, scales, q_pos, cands, cand_key, cand_idx, chunk_lb, blkmax, topk, scores_out, T_len, H_I,
+                     N_cap, n_entries, m, p.chunk, p.k_chunk, p.n_chunks, k, hsi_s, hsi_nb, nblk_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!BUILD && p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single chunk
@@ -1811,10 +1818,26 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   return hipGetLastError();
 }
 
+// Debug score dump helpers.
+__global__ __launch_bounds__(256) void fill_neg_inf(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = -INFINITY;
+}
+// Key matrix [Q, n_scan] of the tiled path -> scores (positions past a query's
+// visible range, which the scorer does not write, read -inf).
+__global__ __launch_bounds__(256) void keys_to_scores(const uint32_t* __restrict__ keys,
+                                                      const int32_t* __restrict__ q_pos, float* __restrict__ out,
+                                                      int T_len, int n_entries, int m, int n_scan) {
+  const int bt = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n_scan) return;
+  const int n_t = visible(q_pos, bt, m, n_entries);
+  out[(size_t)bt * n_scan + j] = j < n_t ? key_score(keys[(size_t)bt * n_scan + j]) : -INFINITY;
+}
+
 template <typename T>
 hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                          const int32_t* q_pos, int32_t* topk, int B, int T_len, int H_I, int N_cap, int n_entries,
-                         int m, int k, void* ws, const ScorePlan& p, hipStream_t st) {
+                         int m, int k, void* ws, const ScorePlan& p, hipStream_t st, float* scores_out) {
   char* wsb = static_cast<char*>(ws);
   const size_t n_slots = p.cand_bytes / 8;
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(wsb);
@@ -1822,8 +1845,8 @@ hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes
   uint32_t* chunk_lb = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes);
   dim3 g1(p.n_chunks, T_len, B);
   hipLaunchKernelGGL(score_stream<T>, g1, dim3(ST_THREADS), 0, st, static_cast<const T*>(q_idx), w, codes, scales,
-                     q_pos, cand_key, cand_idx, chunk_lb, topk, T_len, H_I, N_cap, n_entries, m, p.chunk, p.n_chunks,
-                     k, p.k_chunk);
+                     q_pos, cand_key, cand_idx, chunk_lb, topk, scores_out, T_len, H_I, N_cap, n_entries, m, p.chunk,
+                     p.n_chunks, k, p.k_chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single part
@@ -1838,15 +1861,15 @@ template <typename T>
 hipError_t launch_mode(int hsi, const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
                        int n_entries, int m, int k, int hsi_s, int hsi_nb, void* ws, const ScorePlan& p,
-                       hipStream_t st) {
+                       hipStream_t st, float* scores_out) {
   if (hsi == 1)
     return launch_impl<T, false, true>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
-                                       m, k, hsi_s, hsi_nb, ws, p, st);
+                                       m, k, hsi_s, hsi_nb, ws, p, st, scores_out);
   if (hsi == 2)
     return launch_impl<T, true, false>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
-                                       m, k, hsi_s, hsi_nb, ws, p, st);
+                                       m, k, hsi_s, hsi_nb, ws, p, st, scores_out);
   return launch_impl<T, false, false>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries, m,
-                                      k, hsi_s, hsi_nb, ws, p, st);
+                                      k, hsi_s, hsi_nb, ws, p, st, scores_out);
 }
 
 }  // namespace
@@ -1899,21 +1922,36 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
 hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
                              const uint8_t* scales, const int32_t* q_pos, int32_t* topk, int32_t* candidates, int B,
                              int T, int H_I, int N_cap, int n_entries, int m, int k, int hsi, int hsi_s, int hsi_nb,
-                             void* workspace, const ScorePlan& plan, hipStream_t stream) {
+                             void* workspace, const ScorePlan& plan, hipStream_t stream, float* scores_out) {
   if (B == 0 || T == 0) return hipSuccess;
-  if (plan.tiled)
-    return launch_tiled(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k, plan.chunk,
-                        workspace, plan, stream);
+  const int n_scan = hsi == 2 ? hsi_nb * hsi_s : n_entries;
+  if (plan.tiled) {
+    hipError_t e = launch_tiled(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k, plan.chunk,
+                                workspace, plan, stream);
+    if (e != hipSuccess || scores_out == nullptr) return e;
+    // the key matrix holds every visible (query, entry) key
+    hipLaunchKernelGGL(keys_to_scores, dim3((unsigned)((n_scan + 255) / 256), (unsigned)(B * T)), dim3(256), 0, stream,
+                       static_cast<const uint32_t*>(workspace), q_pos, scores_out, T, n_entries, m, n_scan);
+    return hipGetLastError();
+  }
+  if (scores_out != nullptr) {
+    // positions no scorer writes (invisible, past the cache, empty pool slots) read -inf
+    const size_t n = (size_t)B * T * n_scan;
+    hipLaunchKernelGGL(fill_neg_inf, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256), 0, stream,
+                       scores_out, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (plan.stream)
     return dtype == 1 ? launch_stream<bf16>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
-                                            workspace, plan, stream)
+                                            workspace, plan, stream, scores_out)
                       : launch_stream<float>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
-                                             workspace, plan, stream);
+                                             workspace, plan, stream, scores_out);
   if (dtype == 1)
     return launch_mode<bf16>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
-                             k, hsi_s, hsi_nb, workspace, plan, stream);
+                             k, hsi_s, hsi_nb, workspace, plan, stream, scores_out);
   return launch_mode<float>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m, k,
-                            hsi_s, hsi_nb, workspace, plan, stream);
+                            hsi_s, hsi_nb, workspace, plan, stream, scores_out);
 }
 
 }  // namespace csa2

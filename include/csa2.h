@@ -264,6 +264,13 @@ csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* 
  *                                        block ids ascending, then -1
  *   workspace  device scratch of at least csa2_workspace_size() bytes, 16-byte
  *              aligned (CSA2_ERR_WORKSPACE otherwise)
+ *   scores  [B, T, n_scan] float32 out or NULL: a debug dump of every scanned
+ *           position's index score (n_scan = n_entries, or hsi_nb * hsi_s for
+ *           HSI_USE, whose positions are the pool's: block j / hsi_s of the
+ *           candidates, entry j % hsi_s within it), -inf where the position is not
+ *           visible to the query or not a valid pool entry.  4-byte aligned
+ *           (CSA2_ERR_INVALID_ARG otherwise).  It adds a fill pass and the stores;
+ *           the selection does not read it.
  * Ties in score go to the smaller entry id; -0 counts as +0.
  * With rt != NULL the topk_idxs slot (and on BUILD the candidates slot) is set. */
 typedef struct csa2_score_topk_args {
@@ -281,6 +288,7 @@ typedef struct csa2_score_topk_args {
   int32_t* candidates;
   void* workspace;
   size_t workspace_bytes;
+  float* scores;            /* optional debug dump (see above), or NULL */
 } csa2_score_topk_args;
 
 csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa2_stream stream);

@@ -282,3 +282,10 @@ def test_swa_append_empty_is_noop():
     assert K.lib().csa2_swa_append(C.byref(a), None) == 0
     a = K.SwaAppendArgs(dtype=0, B=3, T=0, L_w=128)
     assert K.lib().csa2_swa_append(C.byref(a), None) == 0
+
+
+def test_score_dump_must_be_aligned():
+    a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=100, n_entries=100, m=1, k=8, q_idx=0x1000, w=0x1000,
+                        codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1000,
+                        workspace_bytes=1 << 30, scores=0x1002)
+    assert K.STATUS[K.lib().csa2_score_topk(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"

@@ -220,6 +220,45 @@ def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill):
     assert checked >= 2 and ties >= 1
 
 
+@pytest.mark.parametrize("dtype,T,n_fill,m", [(torch.bfloat16, 3, 5000, 2), (torch.float32, 3, 5000, 2),
+                                              (torch.bfloat16, 300, 3000, 1), (torch.bfloat16, 8192, 10000, 1)])
+def test_score_dump_vs_oracle(dtype, T, n_fill, m):
+    """The optional debug dump of csa2_score_topk on the chunked (T = 3), tiled
+    (T = 300) and streaming (T = 8192) paths: every visible entry's index score
+    against the oracle's, -inf past each query's visible range and the cache."""
+    B, N_cap, H_I, k = 1, n_fill + 100, 32, 64
+    say(f"case: score dump dtype={dtype} T={T} n={n_fill} m={m}")
+    codes, scales = _index_cache(B, N_cap, n_fill, 37)
+    q_idx = synth.gaussian((B, T, H_I, 128), 1.0, 37, "q_idx", 0, dtype, DEV)
+    w = synth.gaussian((B, T, H_I), 1.0, 37, "w", 0, torch.float32, DEV)
+    gen = np.random.default_rng(37)
+    pos = gen.integers(-2, n_fill * m + 50, size=(B, T)).astype(np.int32)
+    pos[0, 0] = n_fill * m - 1
+    topk = torch.empty(B, T, k, dtype=torch.int32, device=DEV)
+    scores = torch.full((B, T, n_fill), 7.0, dtype=torch.float32, device=DEV)
+    K.csa2_score_topk(None, q_idx, w, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                      torch.from_numpy(pos).to(DEV), topk, n_entries=n_fill, m=m, k=k, scores=scores)
+    torch.cuda.synchronize()
+    sg = scores.cpu().numpy()
+    kd = O.fp4_unpack(codes[0], scales[0])
+    for t in sorted(set([0, 1, T - 1] + list(range(0, T, max(1, T // 8))))):
+        nv = O.visible_entries(int(pos[0, t]), m) if pos[0, t] >= 0 else 0
+        nv = min(nv, n_fill)
+        ref = O.index_scores(npy(q_idx[0, t]), npy(w[0, t]), kd, nv)
+        got = sg[0, t]
+        assert np.all(np.isneginf(got[nv:])), f"t={t}: positions past {nv} not -inf"
+        if nv:
+            tol = 1e-4 * max(1.0, float(np.abs(ref).max()))
+            err = float(np.abs(got[:nv] - ref).max())
+            assert err <= tol, f"t={t}: {err:.3e} > {tol:.3e}"
+    # the selection is unchanged by the dump
+    topk2 = torch.empty_like(topk)
+    K.csa2_score_topk(None, q_idx, w, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                      torch.from_numpy(pos).to(DEV), topk2, n_entries=n_fill, m=m, k=k)
+    torch.cuda.synchronize()
+    assert torch.equal(topk, topk2)
+
+
 def test_score_topk_hsi_build_and_use():
     B, N_cap, m, k, s, nb = 2, 4096, 1, 64, 16, 20
     pos = np.array([[4095, 100, 10, 2000], [3000, 319, 4095, 17]])
@@ -258,10 +297,11 @@ def test_score_topk_hsi_build_and_use():
     wr = synth.gaussian((B, T, 32), 1.0, 24, "w", 1, torch.float32, DEV)
     pool_in = torch.from_numpy(pools.astype(np.int32)).to(DEV)
     topk2 = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    dump = torch.full((B, T, nb * s), 7.0, dtype=torch.float32, device=DEV)   # debug dump over pool positions
     K.csa2_score_topk(None, qr, wr, dc, ds, q_pos, topk2, n_entries=N_cap, m=m, k=k, hsi=K.HSI_USE, hsi_s=s,
-                      hsi_nb=nb, candidates=pool_in)
+                      hsi_nb=nb, candidates=pool_in, scores=dump)
     torch.cuda.synchronize()
-    t2 = topk2.cpu().numpy()
+    t2, dg = topk2.cpu().numpy(), dump.cpu().numpy()
     for b in range(B):
         kd = O.fp4_unpack(codes[b], scales[b])
         for t in range(T):
@@ -269,6 +309,14 @@ def test_score_topk_hsi_build_and_use():
             sc = O.index_scores(npy(qr[b, t]), npy(wr[b, t]), kd, nv)
             ent = O.pool_entries(pools[b, t], nv, s)
             check_topk_row(sc[ent], ent, t2[b, t], k, f"reindex-in-pool b{b} t{t}")
+            # dump position j: entry pool[j // s] * s + j % s, or -inf (empty slot, past n_t)
+            for j in range(nb * s):
+                blk = int(pools[b, t, j // s])
+                e = blk * s + j % s if blk >= 0 else -1
+                if 0 <= e < nv:
+                    assert abs(dg[b, t, j] - sc[e]) <= 1e-4 * max(1.0, float(np.abs(sc).max())), (b, t, j)
+                else:
+                    assert np.isneginf(dg[b, t, j]), (b, t, j)
     # slot published by BUILD
     info = rt.slot(K.SLOT_CANDIDATES)
     assert info.filled == 1 and info.extra == s and info.cols == nb and info.ptr == cand.data_ptr()
