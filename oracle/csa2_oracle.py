@@ -122,7 +122,27 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     return (mag | (np.signbit(v).astype(np.uint8) << 7)).astype(np.uint8)
 
 
-def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
+SCALE_E4M3, SCALE_UE8M0 = "e4m3", "ue8m0"
+
+
+def ue8m0_decode(b: np.ndarray) -> np.ndarray:
+    """Value of each UE8M0 byte: 2^(b - 127); byte 255 is NaN."""
+    b = np.asarray(b).astype(np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def ue8m0_encode_ceil(sigma: np.ndarray) -> np.ndarray:
+    """The UE8M0 byte of the smallest power of two at or above each float32
+    sigma >= 0 (clamped to 2^-127 .. 2^127); sigma == 0 gives byte 0."""
+    a = np.asarray(sigma, dtype=np.float32).astype(np.float64)
+    assert np.all(a >= 0.0)
+    mant, ex = np.frexp(a)                       # a = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(mant == 0.5, ex - 1, ex)        # exact powers of two keep their exponent
+    e = np.where(a == 0.0, -127, e)
+    return (np.clip(e, -127, 127) + 127).astype(np.uint8)
+
+
+def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK, scale_fmt: str = SCALE_E4M3):
     """Quantise rows of 128 values to FP4 index-K storage (``block`` = 32), or
     rows of 512 values to FP4 main-KV storage (``block`` = 16, see kv_fp4_pack).
 
@@ -131,6 +151,11 @@ def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
     scale byte = E4M3(sigma), s = its value; code_i = E2M1(u_i / s) (float32
     division), or 0 for the whole block when s == 0.  Code of dim 2j goes to the low
     nibble of byte j.  Returns (codes uint8 [rows, d/2], scales uint8 [rows, d/block]).
+
+    scale_fmt SCALE_UE8M0 (index K only; the pages give no scale format for index
+    K): the scale byte is the power of two X = 2^(b - 127) nearest at or above
+    sigma, so that |u / X| <= 6 up to sigma's own rounding; code_i = E2M1(u_i / X)
+    (exact division, nearest-even, saturating at 6).
     """
     u = np.asarray(u, dtype=np.float32)
     rows, d = u.shape
@@ -139,8 +164,13 @@ def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
     blocks = u.reshape(rows, nb, block)
     amax = np.max(np.abs(blocks), axis=2).astype(np.float32)
     sigma = (amax / np.float32(6.0)).astype(np.float32)
-    sbytes = e4m3_encode_nonneg(sigma)
-    s = e4m3_decode(sbytes).astype(np.float32)
+    if scale_fmt == SCALE_UE8M0:
+        sbytes = ue8m0_encode_ceil(sigma)
+        s = ue8m0_decode(sbytes).astype(np.float32)
+    else:
+        assert scale_fmt == SCALE_E4M3
+        sbytes = e4m3_encode_nonneg(sigma)
+        s = e4m3_decode(sbytes).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = (blocks / s[:, :, None]).astype(np.float32)
     codes = e2m1_encode(ratio)
@@ -149,7 +179,8 @@ def fp4_pack(u: np.ndarray, block: int = FP4_BLOCK):
     return packed, sbytes.reshape(rows, nb)
 
 
-def fp4_unpack(codes: np.ndarray, scales: np.ndarray, block: int = FP4_BLOCK) -> np.ndarray:
+def fp4_unpack(codes: np.ndarray, scales: np.ndarray, block: int = FP4_BLOCK,
+               scale_fmt: str = SCALE_E4M3) -> np.ndarray:
     """Dequantise FP4 storage: value(code) * value(scale of its block), float64
     [rows, 2 * codes.shape[1]]."""
     codes = np.asarray(codes, dtype=np.uint8)
@@ -160,7 +191,7 @@ def fp4_unpack(codes: np.ndarray, scales: np.ndarray, block: int = FP4_BLOCK) ->
     c[:, 0::2] = lo
     c[:, 1::2] = hi
     vals = e2m1_decode(c)
-    s = e4m3_decode(np.asarray(scales))
+    s = ue8m0_decode(np.asarray(scales)) if scale_fmt == SCALE_UE8M0 else e4m3_decode(np.asarray(scales))
     return vals * np.repeat(s, block, axis=1)
 
 
@@ -287,12 +318,12 @@ def compress_step(pending, x_tok, w_kv, w_gate, gamma, pos: int, m: int, eps: fl
 # with one scale per 32 dims, no Hadamard rotation.
 # ---------------------------------------------------------------------------
 
-def index_k(latent_pre, w_ik, entry_pos, rope_base: float = 10000.0):
+def index_k(latent_pre, w_ik, entry_pos, rope_base: float = 10000.0, scale_fmt: str = SCALE_E4M3):
     """latent_pre [N, 512], w_ik [128, 512] (output x input), entry_pos [N] (= g*m).
     Returns (u float64 [N, 128] before quantisation, codes [N, 64], scales [N, 4])."""
     u = np.asarray(latent_pre, dtype=np.float64) @ np.asarray(w_ik, dtype=np.float64).T
     u = rope_last(u, np.asarray(entry_pos), rope_base)
-    codes, scales = fp4_pack(u.astype(np.float32))
+    codes, scales = fp4_pack(u.astype(np.float32), FP4_BLOCK, scale_fmt)
     return u, codes, scales
 
 
@@ -454,6 +485,7 @@ class Runtime:
     """The four single-occupancy slots.  A slot holds a reference (not a copy)."""
     compress_kv: Optional[np.ndarray] = None   # [B, N, 512]
     index_k: Optional[tuple] = None            # (codes [B, N, 64], scales [B, N, 4])
+    index_k_fmt: str = SCALE_E4M3              # scale format of index_k
     topk_idxs: Optional[np.ndarray] = None     # [B, T, k]
     candidates: Optional[np.ndarray] = None    # [B, T, n_b] block ids (+ block size)
     candidates_s: int = 0
@@ -496,14 +528,15 @@ class LayerConfig:
     hsi_nb: int = 256
     scale: Optional[float] = None
     kv_fp4: bool = False   # Full: store the main KV as FP4 (attention reads it dequantised)
+    scale_fmt: str = SCALE_E4M3   # Full: scale format of the index K it writes
 
 
-def _score_and_select(rt: Runtime, cfg: LayerConfig, inp: LayerInputs, codes, scales):
+def _score_and_select(rt: Runtime, cfg: LayerConfig, inp: LayerInputs, codes, scales, scale_fmt=SCALE_E4M3):
     B, T = inp.q_pos.shape
     topk = np.full((B, T, cfg.k), -1, dtype=np.int64)
     cands = np.full((B, T, cfg.hsi_nb), -1, dtype=np.int64) if cfg.hsi == "build" else None
     for b in range(B):
-        kdeq = fp4_unpack(codes[b], scales[b])
+        kdeq = fp4_unpack(codes[b], scales[b], FP4_BLOCK, scale_fmt)
         for t in range(T):
             n_vis = visible_entries(inp.q_pos[b, t], cfg.m)
             sc = index_scores(inp.q_idx[b, t], inp.w[b, t], kdeq, n_vis)
@@ -527,7 +560,7 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
         for b in range(B):
             latent_pre, kv, ids = compress(inp.x[b], cfg.w_kv, cfg.w_gate, cfg.gamma, cfg.m,
                                            inp.start_pos, cfg.eps, cfg.rope_base)
-            _, codes, scales = index_k(latent_pre, cfg.w_ik, ids * cfg.m, cfg.rope_base)
+            _, codes, scales = index_k(latent_pre, cfg.w_ik, ids * cfg.m, cfg.rope_base, cfg.scale_fmt)
             if cfg.kv_fp4:
                 # [P3] section seven: the stored main KV is FP4; attention sees its
                 # dequantised values
@@ -535,8 +568,9 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
             kvs.append(kv), cs.append(codes), ss.append(scales), lat.append(latent_pre)
         rt.compress_kv = np.stack(kvs)
         rt.index_k = (np.stack(cs), np.stack(ss))
+        rt.index_k_fmt = cfg.scale_fmt
         rt.writes += ["compress_kv", "index_k"]
-        topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k)
+        topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k, rt.index_k_fmt)
         rt.topk_idxs = topk
         rt.writes.append("topk_idxs")
         if cands is not None:
@@ -547,7 +581,7 @@ def layer_forward(rt: Runtime, cfg: LayerConfig, inp: LayerInputs):
         kv_src = rt.get("compress_kv")
         if cfg.hsi == "build":
             raise ValueError("only a Full layer builds the candidate pool")
-        topk, _ = _score_and_select(rt, cfg, inp, codes, scales)
+        topk, _ = _score_and_select(rt, cfg, inp, codes, scales, rt.index_k_fmt)
         rt.topk_idxs = topk
         rt.writes.append("topk_idxs")
     elif cfg.mode == REUSE:
@@ -600,7 +634,7 @@ def layer_append(rt: Runtime, cfg: LayerConfig, pending: list, x_tok, pos):
             written.append(None)
             continue
         g, latent_pre, row = entry
-        _, c, s = index_k(latent_pre[None], cfg.w_ik, np.array([g * cfg.m]), cfg.rope_base)
+        _, c, s = index_k(latent_pre[None], cfg.w_ik, np.array([g * cfg.m]), cfg.rope_base, rt.index_k_fmt)
         if cfg.kv_fp4:
             row = kv_fp4_unpack(*kv_fp4_pack(row[None].astype(np.float32)))[0]
         if g >= kv.shape[1]:
@@ -622,7 +656,7 @@ def full_decode_step(rt: Runtime, cfg: LayerConfig, pending: list, x_tok, inp: L
     as the Full branch of `layer_forward` does after its compressor."""
     assert cfg.mode == FULL and inp.q_pos.shape[1] == 1
     layer_append(rt, cfg, pending, x_tok, inp.q_pos[:, 0])
-    topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k)
+    topk, cands = _score_and_select(rt, cfg, inp, *rt.index_k, rt.index_k_fmt)
     rt.topk_idxs = topk
     rt.writes.append("topk_idxs")
     if cands is not None:

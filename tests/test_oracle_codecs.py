@@ -255,3 +255,40 @@ def test_swa_ring_slots_and_wraparound():
     assert np.array_equal(O.e4m3_decode(ring[5]), rows[5])
     with pytest.raises(AssertionError):
         O.swa_ring_rows(ring, 0, 8)
+
+
+def test_ue8m0_decode_and_ceil_encoder():
+    # UE8M0: a bare biased exponent, 2^(b - 127), 255 is NaN
+    assert O.ue8m0_decode(np.array([127, 126, 128, 0, 254])).tolist() == [1.0, 0.5, 2.0, 2.0 ** -127, 2.0 ** 127]
+    assert np.isnan(O.ue8m0_decode(np.array([255]))[0])
+    # the encoder picks the smallest power of two at or above sigma
+    rng = np.random.default_rng(11)
+    sig = np.exp(rng.uniform(-60, 60, size=4000)).astype(np.float32)
+    x = O.ue8m0_decode(O.ue8m0_encode_ceil(sig))
+    assert np.all(x >= sig.astype(np.float64)) and np.all(x / 2 < sig.astype(np.float64))
+    p2 = np.float32([0.25, 1.0, 2.0 ** 20, 2.0 ** -100])
+    assert np.array_equal(O.ue8m0_decode(O.ue8m0_encode_ceil(p2)), p2.astype(np.float64))
+    assert O.ue8m0_encode_ceil(np.float32([0.0]))[0] == 0
+
+
+def test_fp4_pack_ue8m0_worked_block_and_bounds():
+    # amax 3.0: sigma 0.5 is a power of two, X = 0.5 (byte 126): 3.0 -> 6 (code 7), 1.0 -> 2 (code 4);
+    # amax 3.1: sigma 0.5167 -> X = 1 (byte 127): 3.1 -> 3 (code 5); a zero block gets byte 0
+    u = np.zeros((1, 128), np.float32)
+    u[0, 0], u[0, 1:32], u[0, 32] = 3.0, 1.0, 3.1
+    codes, scales = O.fp4_pack(u, 32, O.SCALE_UE8M0)
+    assert scales[0].tolist() == [126, 127, 0, 0]
+    assert codes[0, 0] == 0x47 and codes[0, 1] == 0x44 and codes[0, 16] == 0x05
+    # values on the grid round-trip exactly; anything else is within one scale unit
+    rng = np.random.default_rng(12)
+    vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6])
+    grid = rng.choice(vals, size=(64, 128)) * np.repeat(np.exp2(rng.integers(-20, 20, size=(64, 4))), 32, axis=1)
+    c, s = O.fp4_pack(grid.astype(np.float32), 32, O.SCALE_UE8M0)
+    assert np.array_equal(O.fp4_unpack(c, s, 32, O.SCALE_UE8M0), grid)
+    x = rng.standard_normal((200, 128)).astype(np.float32) * np.exp2(rng.integers(-8, 8, size=(200, 1)))
+    c, s = O.fp4_pack(x, 32, O.SCALE_UE8M0)
+    X = np.repeat(O.ue8m0_decode(s), 32, axis=1)
+    assert np.all(np.abs(O.fp4_unpack(c, s, 32, O.SCALE_UE8M0) - x) <= X)
+    # the same rows through the E4M3 codec keep their layout and size (68 B per entry)
+    c4, s4 = O.fp4_pack(x, 32)
+    assert c4.shape == c.shape and s4.shape == s.shape and c.shape[1] + s.shape[1] == 68
