@@ -23,6 +23,7 @@ SLOT_COMPRESS_KV, SLOT_INDEX_K, SLOT_TOPK_IDXS, SLOT_CANDIDATES = 0, 1, 2, 3
 OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_LAYER, OP_COMPRESS_STEP = 0, 1, 2, 3
 KV_DENSE, KV_FP4 = 0, 1
 SWA_DENSE, SWA_FP8_RING = 0, 1
+SCALE_E4M3, SCALE_UE8M0 = 0, 1   # index-K block scale formats (csa2_scale_fmt)
 
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_INVALID_ARG", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_DTYPE",
           4: "CSA2_ERR_SLOT_EMPTY", 5: "CSA2_ERR_SLOT_MISMATCH", 6: "CSA2_ERR_WORKSPACE",
@@ -52,19 +53,20 @@ class CompressStepArgs(C.Structure):
                 ("rope_base", C.c_float), ("x", vp), ("pos", vp), ("w_kv", vp), ("w_gate", vp), ("gamma", vp),
                 ("w_ik", vp), ("state", vp), ("kv_cache", vp), ("ik_codes", vp), ("ik_scales", vp),
                 ("latent_pre", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t), ("kv_fmt", i32),
-                ("kv_scales", vp), ("n_entries", i32)]
+                ("kv_scales", vp), ("n_entries", i32), ("scale_fmt", i32)]
 
 
 class IndexKArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("N", i32), ("m", i32), ("entry0", i32), ("N_cap", i32),
-                ("rope_base", C.c_float), ("latent_pre", vp), ("w_ik", vp), ("codes", vp), ("scales", vp)]
+                ("rope_base", C.c_float), ("latent_pre", vp), ("w_ik", vp), ("codes", vp), ("scales", vp),
+                ("scale_fmt", i32)]
 
 
 class ScoreTopkArgs(C.Structure):
     _fields_ = [("dtype", i32), ("B", i32), ("T", i32), ("H_I", i32), ("N_cap", i32), ("n_entries", i32),
                 ("m", i32), ("k", i32), ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("q_idx", vp), ("w", vp),
                 ("codes", vp), ("scales", vp), ("q_pos", vp), ("topk", vp), ("candidates", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("scores", vp)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("scores", vp), ("scale_fmt", i32)]
 
 
 class SparseAttnArgs(C.Structure):
@@ -82,7 +84,7 @@ class SwaAppendArgs(C.Structure):
 class LayerCfg(C.Structure):
     _fields_ = [("mode", i32), ("dtype", i32), ("m", i32), ("k", i32), ("W", i32), ("H_I", i32), ("H", i32),
                 ("hsi", i32), ("hsi_s", i32), ("hsi_nb", i32), ("rope_base", C.c_float), ("eps", C.c_float),
-                ("scale", C.c_float), ("kv_fmt", i32), ("swa_fmt", i32)]
+                ("scale", C.c_float), ("kv_fmt", i32), ("swa_fmt", i32), ("scale_fmt", i32)]
 
 
 class LayerIO(C.Structure):
@@ -212,23 +214,24 @@ def csa2_compress(rt, x, w_kv, w_gate, gamma, latent_pre, kv_cache, m: int, star
 
 
 def csa2_index_k(rt, latent_pre, w_ik, codes, scales, m: int, entry0: int = 0, rope_base: float = 10000.0,
-                 stream=None):
+                 stream=None, scale_fmt: int = SCALE_E4M3):
     B, N, _ = latent_pre.shape
     a = IndexKArgs(dtype=_dtype(w_ik), B=B, N=N, m=m, entry0=entry0, N_cap=codes.shape[1], rope_base=rope_base,
-                   latent_pre=_ptr(latent_pre), w_ik=_ptr(w_ik), codes=_ptr(codes), scales=_ptr(scales))
+                   latent_pre=_ptr(latent_pre), w_ik=_ptr(w_ik), codes=_ptr(codes), scales=_ptr(scales),
+                   scale_fmt=scale_fmt)
     _check(lib().csa2_index_k(_rt(rt), C.byref(a), _stream(stream)))
 
 
 def score_topk_args(q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int, N_cap: int,
                     hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0, candidates=None, workspace=None,
-                    scores=None):
+                    scores=None, scale_fmt: int = SCALE_E4M3):
     B, T, H_I, _ = q_idx.shape
     return ScoreTopkArgs(dtype=_dtype(q_idx), B=B, T=T, H_I=H_I, N_cap=N_cap, n_entries=n_entries, m=m, k=k,
                          hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, q_idx=_ptr(q_idx), w=_ptr(w), codes=_ptr(codes),
                          scales=_ptr(scales), q_pos=_ptr(q_pos), topk=_ptr(topk), candidates=_ptr(candidates),
                          workspace=_ptr(workspace),
                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
-                         scores=_ptr(scores))
+                         scores=_ptr(scores), scale_fmt=scale_fmt)
 
 
 def score_topk_workspace_bytes(**kw) -> int:
@@ -240,14 +243,14 @@ def score_topk_workspace_bytes(**kw) -> int:
 
 def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int,
                     N_cap: Optional[int] = None, hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0,
-                    candidates=None, workspace=None, stream=None, scores=None):
-    """Score and select; codes/scales None -> the runtime's index_k slot.  scores:
-    optional float32 [B, T, n_scan] debug dump of the index scores (-inf where not
-    visible)."""
+                    candidates=None, workspace=None, stream=None, scores=None, scale_fmt: int = SCALE_E4M3):
+    """Score and select; codes/scales None -> the runtime's index_k slot (whose
+    scale format then applies).  scores: optional float32 [B, T, n_scan] debug dump
+    of the index scores (-inf where not visible)."""
     if N_cap is None:
         N_cap = codes.shape[1]
     kw = dict(q_idx=q_idx, w=w, codes=codes, scales=scales, q_pos=q_pos, topk=topk, n_entries=n_entries, m=m,
-              k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates)
+              k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates, scale_fmt=scale_fmt)
     if workspace is None:
         nbytes = score_topk_workspace_bytes(**kw)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q_idx.device)
@@ -328,7 +331,7 @@ def csa2_sparse_attn(rt, q, kv, topk, swa_kv, swa_pos0, q_pos, o, W: int, k: Opt
 
 def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, ik_codes, ik_scales, m: int,
                        latent_pre=None, eps: float = 1e-6, rope_base: float = 10000.0, workspace=None, stream=None,
-                       kv_scales=None, n_entries: int = 0):
+                       kv_scales=None, n_entries: int = 0, scale_fmt: int = SCALE_E4M3):
     """Decode append: x [B, D] (one new token per sequence at positions pos [B]);
     state [B, 3, 512] float32 (None iff m == 1).  With a runtime, n_entries (the
     longest sequence's entry count after the step) is republished in the
@@ -342,7 +345,7 @@ def csa2_compress_step(rt, x, pos, w_kv, w_gate, gamma, w_ik, state, kv_cache, i
                          ik_scales=_ptr(ik_scales), latent_pre=_ptr(latent_pre), workspace=_ptr(workspace),
                          workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size(),
                          kv_fmt=KV_DENSE if kv_scales is None else KV_FP4, kv_scales=_ptr(kv_scales),
-                         n_entries=n_entries)
+                         n_entries=n_entries, scale_fmt=scale_fmt)
     _check(lib().csa2_compress_step(_rt(rt), C.byref(a), _stream(stream)))
     return workspace
 
@@ -369,9 +372,10 @@ def csa2_kv_fp4_pack(rows, codes, scales, stream=None):
 
 def layer_cfg(mode: int, dtype: int, m: int, k: int, W: int, H_I: int, H: int, hsi: int = HSI_NONE,
               hsi_s: int = 0, hsi_nb: int = 0, rope_base: float = 10000.0, eps: float = 1e-6,
-              scale: float = 0.0, kv_fmt: int = 0, swa_fmt: int = 0) -> LayerCfg:
+              scale: float = 0.0, kv_fmt: int = 0, swa_fmt: int = 0, scale_fmt: int = 0) -> LayerCfg:
     return LayerCfg(mode=mode, dtype=dtype, m=m, k=k, W=W, H_I=H_I, H=H, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb,
-                    rope_base=rope_base, eps=eps, scale=scale, kv_fmt=kv_fmt, swa_fmt=swa_fmt)
+                    rope_base=rope_base, eps=eps, scale=scale, kv_fmt=kv_fmt, swa_fmt=swa_fmt,
+                    scale_fmt=scale_fmt)
 
 
 def layer_io(B, T, q_pos, q, swa_kv, swa_pos0, o, N_cap=0, D=0, start_pos=0, x=None, w_kv=None, w_gate=None,

@@ -111,6 +111,8 @@ csa2_status check_compress_step(const csa2_compress_step_args* a) {
       "csa2_compress_step: bad kv_fmt %d", a->kv_fmt);
   REQ(a->kv_fmt != CSA2_KV_FP4 || a->kv_scales != nullptr, CSA2_ERR_INVALID_ARG,
       "csa2_compress_step: FP4 main KV needs kv_scales");
+  REQ(a->scale_fmt == CSA2_SCALE_E4M3 || a->scale_fmt == CSA2_SCALE_UE8M0, CSA2_ERR_INVALID_ARG,
+      "csa2_compress_step: bad scale_fmt %d", a->scale_fmt);
   const size_t need = (size_t)a->B * 1024 * 4 * 4;   // C and Z partials of 4 K quarters
   REQ(a->B == 0 || (a->workspace != nullptr && a->workspace_bytes >= need), CSA2_ERR_WORKSPACE,
       "csa2_compress_step: workspace of %zu bytes needed (got %zu)", need, a->workspace_bytes);
@@ -126,6 +128,8 @@ csa2_status check_index_k(const csa2_index_k_args* a) {
   REQ((long long)a->entry0 + a->N <= a->N_cap, CSA2_ERR_SHAPE, "csa2_index_k: cache too small");
   REQ(a->latent_pre && a->w_ik && a->codes && a->scales, CSA2_ERR_INVALID_ARG, "csa2_index_k: NULL tensor");
   REQ(a->rope_base > 0.f, CSA2_ERR_INVALID_ARG, "csa2_index_k: bad rope_base");
+  REQ(a->scale_fmt == CSA2_SCALE_E4M3 || a->scale_fmt == CSA2_SCALE_UE8M0, CSA2_ERR_INVALID_ARG,
+      "csa2_index_k: bad scale_fmt %d", a->scale_fmt);
   return CSA2_OK;
 }
 
@@ -154,7 +158,10 @@ csa2_status resolve_score(const csa2_runtime* rt, csa2_score_topk_args& a) {
         a.n_entries, s.cols);
     a.codes = static_cast<const uint8_t*>(s.ptr);
     a.scales = static_cast<const uint8_t*>(s.ptr2);
+    a.scale_fmt = s.kv_fmt;   // the index_k slot records its scale format
   }
+  REQ(a.scale_fmt == CSA2_SCALE_E4M3 || a.scale_fmt == CSA2_SCALE_UE8M0, CSA2_ERR_INVALID_ARG,
+      "csa2_score_topk: bad scale_fmt %d", a.scale_fmt);
   REQ(a.codes && a.scales, CSA2_ERR_INVALID_ARG, "csa2_score_topk: codes and scales must both be given or both NULL");
   REQ(a.n_entries >= 0 && a.n_entries <= a.N_cap, CSA2_ERR_SHAPE, "csa2_score_topk: n_entries must be in [0, N_cap]");
   if (a.hsi == CSA2_HSI_USE && a.candidates == nullptr) {
@@ -308,12 +315,12 @@ csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* 
                                             a->kv_cache, a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr,
                                             a->ik_codes, a->ik_scales, a->latent_pre,
                                             static_cast<float*>(a->workspace), a->B, a->D, a->m, a->N_cap, a->eps,
-                                            a->rope_base, st(stream));
+                                            a->rope_base, st(stream), a->scale_fmt);
   if (e != hipSuccess) return hip_status(e, "csa2_compress_step launch");
   // the Full layer's caches as they stand after this step, for the layers that borrow them
   publish(rt, CSA2_SLOT_COMPRESS_KV, a->kv_cache, a->kv_fmt == CSA2_KV_FP4 ? a->kv_scales : nullptr, a->dtype, a->B,
           a->N_cap, a->n_entries, a->m, a->kv_fmt);
-  publish(rt, CSA2_SLOT_INDEX_K, a->ik_codes, a->ik_scales, 0, a->B, a->N_cap, a->n_entries, a->m);
+  publish(rt, CSA2_SLOT_INDEX_K, a->ik_codes, a->ik_scales, 0, a->B, a->N_cap, a->n_entries, a->m, a->scale_fmt);
   return ok();
 }
 
@@ -321,9 +328,9 @@ csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stre
   csa2_status s = check_index_k(a);
   if (s != CSA2_OK) return s;
   hipError_t e = csa2::launch_index_k(a->dtype, a->latent_pre, a->w_ik, a->codes, a->scales, a->B, a->N, a->m,
-                                      a->entry0, a->N_cap, a->rope_base, st(stream));
+                                      a->entry0, a->N_cap, a->rope_base, st(stream), a->scale_fmt);
   if (e != hipSuccess) return hip_status(e, "csa2_index_k launch");
-  publish(rt, CSA2_SLOT_INDEX_K, a->codes, a->scales, 0, a->B, a->N_cap, a->entry0 + a->N, a->m);
+  publish(rt, CSA2_SLOT_INDEX_K, a->codes, a->scales, 0, a->B, a->N_cap, a->entry0 + a->N, a->m, a->scale_fmt);
   return ok();
 }
 
@@ -357,7 +364,7 @@ csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* in, cs
   REQ(((uintptr_t)a.workspace & 15u) == 0, CSA2_ERR_WORKSPACE, "csa2_score_topk: workspace not 16-byte aligned");
   hipError_t e = csa2::launch_score_topk(a.dtype, a.q_idx, a.w, a.codes, a.scales, a.q_pos, a.topk, a.candidates, a.B,
                                          a.T, a.H_I, a.N_cap, a.n_entries, a.m, a.k, a.hsi, a.hsi_s, a.hsi_nb,
-                                         a.workspace, plan, st(stream), a.scores);
+                                         a.workspace, plan, st(stream), a.scores, a.scale_fmt);
   if (e != hipSuccess) return hip_status(e, "csa2_score_topk launch");
   publish(rt, CSA2_SLOT_TOPK_IDXS, a.topk, nullptr, 0, a.B, a.T, a.k, 0);
   if (a.hsi == CSA2_HSI_BUILD) publish(rt, CSA2_SLOT_CANDIDATES, a.candidates, nullptr, 0, a.B, a.T, a.hsi_nb, a.hsi_s);
@@ -451,7 +458,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     csa2_index_k_args ia{};
     ia.dtype = cfg->dtype; ia.B = io->B; ia.N = T_x / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
     ia.N_cap = io->N_cap; ia.rope_base = cfg->rope_base; ia.latent_pre = io->latent_pre; ia.w_ik = io->w_ik;
-    ia.codes = io->ik_codes; ia.scales = io->ik_scales;
+    ia.codes = io->ik_codes; ia.scales = io->ik_scales; ia.scale_fmt = cfg->scale_fmt;
     s = check_index_k(&ia);
     if (s != CSA2_OK) return s;
     n_entries = ia.entry0 + ia.N;
@@ -473,6 +480,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     if (cfg->mode == CSA2_FULL) {
       sa.codes = io->ik_codes;
       sa.scales = io->ik_scales;
+      sa.scale_fmt = cfg->scale_fmt;
     } else {
       sa.N_cap = rt->slot[CSA2_SLOT_INDEX_K].rows;
     }
@@ -536,7 +544,7 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     csa2_index_k_args ia{};
     ia.dtype = cfg->dtype; ia.B = io->B; ia.N = T_x / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
     ia.N_cap = io->N_cap; ia.rope_base = cfg->rope_base; ia.latent_pre = io->latent_pre; ia.w_ik = io->w_ik;
-    ia.codes = io->ik_codes; ia.scales = io->ik_scales;
+    ia.codes = io->ik_codes; ia.scales = io->ik_scales; ia.scale_fmt = cfg->scale_fmt;
     if ((s = csa2_index_k(rt, &ia, stream)) != CSA2_OK) return s;
   }
   if (cfg->mode != CSA2_REUSE) {

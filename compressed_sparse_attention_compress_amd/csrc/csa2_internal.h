@@ -22,12 +22,12 @@ hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, co
                                 const void* w_gate, const float* gamma, const void* w_ik, float* state,
                                 void* kv_cache, uint8_t* kv_scales, uint8_t* codes, uint8_t* scales, float* latent_pre,
                                 float* cz, int B, int D, int m, int N_cap, float eps, float rope_base,
-                                hipStream_t stream);
+                                hipStream_t stream, int scale_fmt);
 
 // ---- index K and FP4 packing (k_index_k.hip)
 hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes,
                           uint8_t* scales, int B, int N, int m, int entry0, int N_cap,
-                          float rope_base, hipStream_t stream);
+                          float rope_base, hipStream_t stream, int scale_fmt);
 hipError_t launch_fp4_pack(const float* rows, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream);
 // FP4 main KV: 512-d float32 rows -> codes [n, 256] + E4M3 scales [n, 32], and back
@@ -59,7 +59,8 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
                              const uint8_t* scales, const int32_t* q_pos, int32_t* topk,
                              int32_t* candidates, int B, int T, int H_I, int N_cap, int n_entries,
                              int m, int k, int hsi, int hsi_s, int hsi_nb, void* workspace,
-                             const ScorePlan& plan, hipStream_t stream, float* scores_out = nullptr);
+                             const ScorePlan& plan, hipStream_t stream, float* scores_out = nullptr,
+                             int scale_fmt = 0);
 
 // ---- host API (csa2_api.cpp)
 // Validates a score/top-k call (resolving slots) and gives the workspace bytes it

@@ -110,6 +110,30 @@ __device__ __forceinline__ uint32_t fp4_code(float v, float s) {
   return (s == 0.0f) ? 0u : e2m1_encode(__fdiv_rn(v, s));
 }
 
+// UE8M0 (a bare biased exponent): value 2^(b - 127), byte 255 unused.
+__device__ __forceinline__ float ue8m0_decode(uint32_t b) {
+  return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);   // 2^-127 is subnormal
+}
+// Byte of the smallest power of two at or above sigma >= 0, clamped to 2^-127 ..
+// 2^127; sigma == 0 gives byte 0.
+__device__ __forceinline__ uint32_t ue8m0_encode_ceil(float sigma) {
+  if (!(sigma > 0.0f)) return 0u;
+  const uint32_t bits = __float_as_uint(sigma);
+  const int ex = (int)((bits >> 23) & 0xFFu);
+  const uint32_t mant = bits & 0x7FFFFFu;
+  // ceil(log2 sigma): normal 1.m x 2^(ex-127); subnormal mant x 2^-149
+  int e = ex != 0 ? ex - 127 + (mant != 0u ? 1 : 0) : (32 - __clz((int)(mant - 1u))) - 149;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return (uint32_t)(e + 127);
+}
+// One index-K block's scale byte and scale value in format sfmt (0 = E4M3, 1 = UE8M0).
+__device__ __forceinline__ uint32_t ik_scale_byte(float amax, int sfmt) {
+  return sfmt ? ue8m0_encode_ceil(__fdiv_rn(amax, 6.0f)) : fp4_scale_byte(amax);
+}
+__device__ __forceinline__ float ik_scale_value(uint32_t b, int sfmt) {
+  return sfmt ? ue8m0_decode(b) : e4m3_decode(b);
+}
+
 // ---------------------------------------------------------------- RoPE
 // Angle of rotary pair i (of n_rope/2) at position pos, computed in double so
 // that large positions (up to 2^20 and beyond) keep full float accuracy.

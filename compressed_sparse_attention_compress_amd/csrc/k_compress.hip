@@ -494,7 +494,7 @@ __device__ __forceinline__ float frag_elem(const f32x8& f, int i) { return f.v[i
 // pooled vector is normalised (RMSNorm), written before RoPE to latent_pre and
 // after RoPE on dims 448..511 (at position g*m) to the cache row g; then its
 // index-K row: 512 -> 128 (thread pair per output dim, halves of the dot product
-// added by a shuffle), RoPE on dims 64..127, FP4 codes with one E4M3 scale per
+// added by a shuffle), RoPE on dims 64..127, FP4 codes with one E4M3 (or UE8M0) scale per
 // 32 dims (wave q holds block q).
 template <typename T>
 __global__ __launch_bounds__(256) void compress_step_entry(const float* __restrict__ cz, const int32_t* __restrict__ pos_arr,
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
                                                            uint8_t* __restrict__ kv_scales,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                            float* __restrict__ latent_pre, int B, int m, int N_cap,
-                                                           float eps, double base) {
+                                                           float eps, double base, int sfmt) {
   typedef typename Frag<T>::type FragT;
   __shared__ float lat_s[512];
   __shared__ float red[4];
@@ -635,8 +635,8 @@ __global__ __launch_bounds__(256) void compress_step_entry(const float* __restri
     }
   }
   const float amax = wave_max_xor(fabsf(u), 63);   // block `wave` = outputs 32*wave .. +31
-  const uint32_t sb = fp4_scale_byte(amax);
-  const uint32_t code = fp4_code(u, e4m3_decode(sb));
+  const uint32_t sb = ik_scale_byte(amax, sfmt);
+  const uint32_t code = fp4_code(u, ik_scale_value(sb, sfmt));
   const uint32_t code_next = (uint32_t)__shfl_xor((int)code, 2, 64);   // output o + 1 for even o
   if (h == 0 && (o & 1) == 0) codes[((size_t)b * N_cap + g) * 64 + (o >> 1)] = (uint8_t)(code | (code_next << 4));
   if (lane == 0) scales[((size_t)b * N_cap + g) * 4 + wave] = (uint8_t)sb;
@@ -658,7 +658,7 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
 hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv, const void* w_gate,
                                 const float* gamma, const void* w_ik, float* state, void* kv_cache, uint8_t* kv_scales,
                                 uint8_t* codes, uint8_t* scales, float* latent_pre, float* cz, int B, int D, int m, int N_cap,
-                                float eps, float rope_base, hipStream_t stream) {
+                                float eps, float rope_base, hipStream_t stream, int sfmt) {
   if (B == 0) return hipSuccess;
   const dim3 g1((m > 1 ? 1024 : 512) / 16, STEP_KQ), g2(B), blk(256);
   if (dtype == 1) {
@@ -666,13 +666,13 @@ hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, co
                        static_cast<const bf16*>(w_kv), static_cast<const bf16*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<bf16>), g2, blk, 0, stream, cz, pos, gamma,
                        static_cast<const bf16*>(w_ik), state, static_cast<bf16*>(kv_cache), kv_scales, codes, scales,
-                       latent_pre, B, m, N_cap, eps, (double)rope_base);
+                       latent_pre, B, m, N_cap, eps, (double)rope_base, sfmt);
   } else {
     hipLaunchKernelGGL((compress_step_proj<float>), g1, blk, 0, stream, static_cast<const float*>(x),
                        static_cast<const float*>(w_kv), static_cast<const float*>(w_gate), cz, B, D);
     hipLaunchKernelGGL((compress_step_entry<float>), g2, blk, 0, stream, cz, pos, gamma,
                        static_cast<const float*>(w_ik), state, static_cast<float*>(kv_cache), kv_scales, codes, scales,
-                       latent_pre, B, m, N_cap, eps, (double)rope_base);
+                       latent_pre, B, m, N_cap, eps, (double)rope_base, sfmt);
   }
   return hipGetLastError();
 }

@@ -1,5 +1,5 @@
 // (b) Index K: 512 -> 128 projection of the pre-RoPE latent, RoPE on its last 64
-// dims at the entry position, FP4 (E2M1) codes with one E4M3 scale per 32 dims.
+// dims at the entry position, FP4 (E2M1) codes with one E4M3 (or UE8M0) scale per 32 dims.
 //
 // Method ([P1] "DeepSeek-V4.1 模型结构（2）…", section "indexer K 改由 main KV
 // 投影": the projection reads the main-KV entry before its RoPE, index K then gets
@@ -37,7 +37,8 @@ __device__ __forceinline__ void split_hi_lo(const f32x8& a, bf16x8& hi, bf16x8& 
 template <typename T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                      int N, int m, int entry0, int N_cap, double base) {
+                                                      int N, int m, int entry0, int N_cap, double base,
+                                                      int sfmt) {
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // quantisation block of this wave
   const int e0 = blockIdx.x * 16;
@@ -111,8 +112,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float v0 = acc[0][i], v1 = acc[1][i];
     float amax = fmaxf(fabsf(v0), fabsf(v1));
     amax = wave_max_xor(amax, 15);  // within the 16-lane group
-    const uint32_t sb = fp4_scale_byte(amax);
-    const float s = e4m3_decode(sb);
+    const uint32_t sb = ik_scale_byte(amax, sfmt);
+    const float s = ik_scale_value(sb, sfmt);
     const uint32_t c0 = fp4_code(v0, s), c1 = fp4_code(v1, s);
     const uint32_t o0 = __shfl_xor((int)c0, 1, 64), o1 = __shfl_xor((int)c1, 1, 64);
     if (e < N) {
@@ -213,15 +214,15 @@ hipError_t launch_kv_fp4_dequant(int dtype, const uint8_t* codes, const uint8_t*
 }
 
 hipError_t launch_index_k(int dtype, const float* latent_pre, const void* w_ik, uint8_t* codes, uint8_t* scales,
-                          int B, int N, int m, int entry0, int N_cap, float rope_base, hipStream_t stream) {
+                          int B, int N, int m, int entry0, int N_cap, float rope_base, hipStream_t stream, int sfmt) {
   if (N == 0 || B == 0) return hipSuccess;
   dim3 grid((N + 15) / 16, B), blk(256);
   if (dtype == 1)
     hipLaunchKernelGGL((index_k_kernel<bf16>), grid, blk, 0, stream, latent_pre, static_cast<const bf16*>(w_ik),
-                       codes, scales, N, m, entry0, N_cap, (double)rope_base);
+                       codes, scales, N, m, entry0, N_cap, (double)rope_base, sfmt);
   else
     hipLaunchKernelGGL((index_k_kernel<float>), grid, blk, 0, stream, latent_pre, static_cast<const float*>(w_ik),
-                       codes, scales, N, m, entry0, N_cap, (double)rope_base);
+                       codes, scales, N, m, entry0, N_cap, (double)rope_base, sfmt);
   return hipGetLastError();
 }
 

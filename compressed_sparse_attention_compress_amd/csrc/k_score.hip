@@ -417,6 +417,34 @@ __device__ __forceinline__ void split_e4m3(uint32_t byte, float& p2, f16x2& mm) 
   const f16 m = (f16)__uint_as_float((bits & 0x807FFFFFu) | 0x3F800000u);
   mm = f16x2{m, m};
 }
+// Scale of an index-K block for the fp16 operand.  E4M3 (SF 0): the exact split
+// above.  UE8M0 (SF 1): p2 = 2^(e - e_ref), mm = 1, with e_ref the entry's largest
+// block exponent byte; the entry's dot products are multiplied by 2^(e_ref - 127)
+// afterwards (entry_post), so every operand stays within fp16 (a block more than
+// ~2^24 below the entry's largest flushes to 0).
+__device__ __forceinline__ uint32_t max_byte4(uint32_t w) {
+  return max(max(w & 0xFFu, (w >> 8) & 0xFFu), max((w >> 16) & 0xFFu, w >> 24));
+}
+template <int SF>
+__device__ __forceinline__ void split_scale(uint32_t byte, uint32_t eref, float& p2, f16x2& mm) {
+  if constexpr (SF == 0) {
+    split_e4m3(byte, p2, mm);
+  } else {
+    const int d = (int)byte - (int)eref + 127;
+    p2 = d > 0 ? __uint_as_float((uint32_t)d << 23) : 0.0f;
+    mm = f16x2{(f16)1.0f, (f16)1.0f};
+  }
+}
+__device__ __forceinline__ float entry_post(uint32_t eref) {
+  return eref != 0u ? __uint_as_float(eref << 23) : 0.0f;
+}
+// A block scale as a float32 (the fp32 scoring path).
+template <int SF, int I>
+__device__ __forceinline__ float block_scale_f32(uint32_t w) {
+  if constexpr (SF == 0) return __builtin_amdgcn_cvt_f32_fp8((int)w, I);
+  else return ue8m0_decode((w >> (8 * I)) & 0xFFu);
+}
+
 // Max over lanes l, l^16, l^32, l^48 with the gfx950 permlane swaps.
 __device__ __forceinline__ float max_lane_groups(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -498,7 +526,7 @@ struct StLoad {
 // 32kb + 8g .. +7 and k-step kb covers block kb, whose per-entry scale multiplies
 // the step's partial product.  ReLU is an integer max on the float's bits
 // (negative floats are negative integers).
-template <typename T>
+template <typename T, int SF>
 __device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type (&qf)[2][4],
                                                  const float (&wv)[2][4], const StLoad& L, int lg) {
   if constexpr (sizeof(T) == 2) {
@@ -508,7 +536,8 @@ __device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type 
       const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
       float p2;
       f16x2 mm;
-      split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
+      const uint32_t eref = SF ? max_byte4(L.s[tt]) : 0u;
+      split_scale<SF>((L.s[tt] >> (8 * lg)) & 0xFFu, eref, p2, mm);
       f32x4 acc[2];
       acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -517,6 +546,11 @@ __device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type 
         const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
         acc[0] = mma16h(qf[0][j], kf, acc[0]);
         acc[1] = mma16h(qf[1][j], kf, acc[1]);
+      }
+      if constexpr (SF != 0) {
+        const float post = entry_post(eref);
+        acc[0] *= post;
+        acc[1] *= post;
       }
       float p = 0.f;
 #pragma unroll
@@ -545,8 +579,8 @@ __device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type 
       auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
       cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
       const uint32_t sw = L.s[tt];
-      const float scv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sw, 0), __builtin_amdgcn_cvt_f32_fp8((int)sw, 1),
-                            __builtin_amdgcn_cvt_f32_fp8((int)sw, 2), __builtin_amdgcn_cvt_f32_fp8((int)sw, 3)};
+      const float scv[4] = {block_scale_f32<SF, 0>(sw), block_scale_f32<SF, 1>(sw), block_scale_f32<SF, 2>(sw),
+                            block_scale_f32<SF, 3>(sw)};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const auto kf = Fp4<T>::cvt(cw[kb]);
@@ -569,7 +603,7 @@ __device__ __forceinline__ float score_supertile(const typename ScoreQ<T>::type 
   }
 }
 
-template <typename T, bool POOL, bool BUILD>
+template <typename T, bool POOL, bool BUILD, int SF>
 __global__ __launch_bounds__(SC_THREADS) void score_chunk(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ cands,
@@ -723,7 +757,8 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
         const uint32_t cw[4] = {L.c[tt].x, L.c[tt].y, L.c[tt].z, L.c[tt].w};
         float p2;
         f16x2 mm;
-        split_e4m3((L.s[tt] >> (8 * lg)) & 0xFFu, p2, mm);
+        const uint32_t eref = SF ? max_byte4(L.s[tt]) : 0u;
+        split_scale<SF>((L.s[tt] >> (8 * lg)) & 0xFFu, eref, p2, mm);
         f32x4 acc[2];
         acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -732,6 +767,11 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
           const f16x8 kf = fp4x8_scaled_f16(cw[j], p2, mm);
           acc[0] = mma16h(qf[0][j], kf, acc[0]);
           acc[1] = mma16h(qf[1][j], kf, acc[1]);
+        }
+        if constexpr (SF != 0) {
+          const float post = entry_post(eref);
+          acc[0] *= post;
+          acc[1] *= post;
         }
         float p = 0.f;
 #pragma unroll
@@ -765,10 +805,10 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
         auto c1 = __builtin_amdgcn_permlane16_swap(a[1], b2[1], false, false);
         cw[0] = c0[0]; cw[1] = c0[1]; cw[2] = c1[0]; cw[3] = c1[1];
         const uint32_t sw = L.s[tt];
-        const float sc0 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
-        const float sc1 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1);
-        const float sc2 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2);
-        const float sc3 = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+        const float sc0 = block_scale_f32<SF, 0>(sw);
+        const float sc1 = block_scale_f32<SF, 1>(sw);
+        const float sc2 = block_scale_f32<SF, 2>(sw);
+        const float sc3 = block_scale_f32<SF, 3>(sw);
         const float scv[4] = {sc0, sc1, sc2, sc3};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -1214,7 +1254,7 @@ __device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, 
   return need;
 }
 
-template <typename T>
+template <typename T, int SF>
 __global__ __launch_bounds__(ST_THREADS) void score_stream(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ cand_key,
@@ -1283,7 +1323,7 @@ __global__ __launch_bounds__(ST_THREADS) void score_stream(
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t theta = 0u;
   auto round = [&](int i, const StLoad& L) {
-    const float sc = score_supertile<T>(qf, wv, L, lg);
+    const float sc = score_supertile<T, SF>(qf, wv, L, lg);
     const int j = (i * ST_NW + wave) * 64 + lane;   // position in the part
     const uint32_t kk = j < n_here ? score_key(sc) : 0u;
     if (scores_out != nullptr && j < n_here) scores_out[(size_t)bt * n_entries + base + j] = key_score(kk);
@@ -1377,6 +1417,7 @@ constexpr int QT_CE = 4096;           // entries per workgroup (64 super-tiles o
 constexpr int SEL_MAX = 8192;         // keys per query row held in registers by select_rows
 
 
+template <int SF>
 __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     const bf16* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ keys,
@@ -1463,6 +1504,7 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
     for (int tt = 0; tt < SPT; ++tt) {
       const unsigned char* tb = src + tt * 1024;
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
+      const uint32_t eref = SF ? max_byte4(sw) : 0u;
       f32x4 acc[QT][2];
 #pragma unroll
       for (int qi = 0; qi < QT; ++qi) {
@@ -1474,12 +1516,20 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
         const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
         float p2;
         f16x2 mm;
-        split_e4m3((sw >> (8 * kb)) & 0xFFu, p2, mm);
+        split_scale<SF>((sw >> (8 * kb)) & 0xFFu, eref, p2, mm);
         const f16x8 kf = fp4x8_scaled_f16(cw, p2, mm);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
           acc[qi][0] = mma16h(qf[qi][0][kb], kf, acc[qi][0]);
           acc[qi][1] = mma16h(qf[qi][1][kb], kf, acc[qi][1]);
+        }
+      }
+      if constexpr (SF != 0) {
+        const float post = entry_post(eref);
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) {
+          acc[qi][0] *= post;
+          acc[qi][1] *= post;
         }
       }
       // per query: weighted ReLU (integer max on the float bits) summed over the
@@ -1774,12 +1824,13 @@ __global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __rest
   for (int i = (int)want + lane; i < k; i += 64) out[i] = -1;
 }
 
+template <int SF>
 hipError_t launch_tiled(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                         const int32_t* q_pos, int32_t* topk, int B, int T_len, int H_I, int N_cap, int n_entries,
                         int m, int k, int n_scan, void* ws, const ScorePlan& p, hipStream_t st) {
   uint32_t* keys = static_cast<uint32_t*>(ws);
   dim3 g1((n_scan + QT_CE - 1) / QT_CE, (T_len + QT - 1) / QT, B);
-  hipLaunchKernelGGL(score_qtile_bf16, g1, dim3(SC_THREADS), 0, st, static_cast<const bf16*>(q_idx), w, codes,
+  hipLaunchKernelGGL(score_qtile_bf16<SF>, g1, dim3(SC_THREADS), 0, st, static_cast<const bf16*>(q_idx), w, codes,
                      scales, q_pos, keys, T_len, H_I, N_cap, n_entries, m, n_scan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1792,7 +1843,7 @@ hipError_t launch_tiled(const void* q_idx, const float* w, const uint8_t* codes,
   return hipGetLastError();
 }
 
-template <typename T, bool POOL, bool BUILD>
+template <typename T, bool POOL, bool BUILD, int SF>
 hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
                        int n_entries, int m, int k, int hsi_s, int hsi_nb, void* ws, const ScorePlan& p,
@@ -1805,7 +1856,7 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   uint32_t* blkmax = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes + p.lb_bytes);
   const int nblk_max = BUILD ? (n_entries + hsi_s - 1) / hsi_s : 0;
   dim3 g1(p.n_chunks, T_len, B);
-  hipLaunchKernelGGL((score_chunk<T, POOL, BUILD>), g1, dim3(SC_THREADS), 0, st, static_cast<const T*>(q_idx), w,
+  hipLaunchKernelGGL((score_chunk<T, POOL, BUILD, SF>), g1, dim3(SC_THREADS), 0, st, static_cast<const T*>(q_idx), w,
                      codes, scales, q_pos, cands, cand_key, cand_idx, chunk_lb, blkmax, topk, scores_out, T_len, H_I,
                      N_cap, n_entries, m, p.chunk, p.k_chunk, p.n_chunks, k, hsi_s, hsi_nb, nblk_max);
   hipError_t e = hipGetLastError();
@@ -1834,7 +1885,7 @@ __global__ __launch_bounds__(256) void keys_to_scores(const uint32_t* __restrict
   out[(size_t)bt * n_scan + j] = j < n_t ? key_score(keys[(size_t)bt * n_scan + j]) : -INFINITY;
 }
 
-template <typename T>
+template <typename T, int SF>
 hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                          const int32_t* q_pos, int32_t* topk, int B, int T_len, int H_I, int N_cap, int n_entries,
                          int m, int k, void* ws, const ScorePlan& p, hipStream_t st, float* scores_out) {
@@ -1844,7 +1895,7 @@ hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes
   int32_t* cand_idx = reinterpret_cast<int32_t*>(wsb + n_slots * 4);
   uint32_t* chunk_lb = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes);
   dim3 g1(p.n_chunks, T_len, B);
-  hipLaunchKernelGGL(score_stream<T>, g1, dim3(ST_THREADS), 0, st, static_cast<const T*>(q_idx), w, codes, scales,
+  hipLaunchKernelGGL((score_stream<T, SF>), g1, dim3(ST_THREADS), 0, st, static_cast<const T*>(q_idx), w, codes, scales,
                      q_pos, cand_key, cand_idx, chunk_lb, topk, scores_out, T_len, H_I, N_cap, n_entries, m, p.chunk,
                      p.n_chunks, k, p.k_chunk);
   hipError_t e = hipGetLastError();
@@ -1857,18 +1908,18 @@ hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int SF>
 hipError_t launch_mode(int hsi, const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
                        const int32_t* q_pos, int32_t* topk, int32_t* cands, int B, int T_len, int H_I, int N_cap,
                        int n_entries, int m, int k, int hsi_s, int hsi_nb, void* ws, const ScorePlan& p,
                        hipStream_t st, float* scores_out) {
   if (hsi == 1)
-    return launch_impl<T, false, true>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
+    return launch_impl<T, false, true, SF>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
                                        m, k, hsi_s, hsi_nb, ws, p, st, scores_out);
   if (hsi == 2)
-    return launch_impl<T, true, false>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
+    return launch_impl<T, true, false, SF>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries,
                                        m, k, hsi_s, hsi_nb, ws, p, st, scores_out);
-  return launch_impl<T, false, false>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries, m,
+  return launch_impl<T, false, false, SF>(q_idx, w, codes, scales, q_pos, topk, cands, B, T_len, H_I, N_cap, n_entries, m,
                                       k, hsi_s, hsi_nb, ws, p, st, scores_out);
 }
 
@@ -1919,15 +1970,17 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
   return p;
 }
 
-hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
-                             const uint8_t* scales, const int32_t* q_pos, int32_t* topk, int32_t* candidates, int B,
-                             int T, int H_I, int N_cap, int n_entries, int m, int k, int hsi, int hsi_s, int hsi_nb,
-                             void* workspace, const ScorePlan& plan, hipStream_t stream, float* scores_out) {
-  if (B == 0 || T == 0) return hipSuccess;
+namespace {
+
+template <int SF>
+hipError_t launch_fmt(int dtype, const void* q_idx, const float* w, const uint8_t* codes, const uint8_t* scales,
+                      const int32_t* q_pos, int32_t* topk, int32_t* candidates, int B, int T, int H_I, int N_cap,
+                      int n_entries, int m, int k, int hsi, int hsi_s, int hsi_nb, void* workspace,
+                      const ScorePlan& plan, hipStream_t stream, float* scores_out) {
   const int n_scan = hsi == 2 ? hsi_nb * hsi_s : n_entries;
   if (plan.tiled) {
-    hipError_t e = launch_tiled(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k, plan.chunk,
-                                workspace, plan, stream);
+    hipError_t e = launch_tiled<SF>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
+                                    plan.chunk, workspace, plan, stream);
     if (e != hipSuccess || scores_out == nullptr) return e;
     // the key matrix holds every visible (query, entry) key
     hipLaunchKernelGGL(keys_to_scores, dim3((unsigned)((n_scan + 255) / 256), (unsigned)(B * T)), dim3(256), 0, stream,
@@ -1943,15 +1996,30 @@ hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const
     if (e != hipSuccess) return e;
   }
   if (plan.stream)
-    return dtype == 1 ? launch_stream<bf16>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
-                                            workspace, plan, stream, scores_out)
-                      : launch_stream<float>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m, k,
-                                             workspace, plan, stream, scores_out);
+    return dtype == 1 ? launch_stream<bf16, SF>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries, m,
+                                                k, workspace, plan, stream, scores_out)
+                      : launch_stream<float, SF>(q_idx, w, codes, scales, q_pos, topk, B, T, H_I, N_cap, n_entries,
+                                                 m, k, workspace, plan, stream, scores_out);
   if (dtype == 1)
-    return launch_mode<bf16>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
-                             k, hsi_s, hsi_nb, workspace, plan, stream, scores_out);
-  return launch_mode<float>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m, k,
-                            hsi_s, hsi_nb, workspace, plan, stream, scores_out);
+    return launch_mode<bf16, SF>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries,
+                                 m, k, hsi_s, hsi_nb, workspace, plan, stream, scores_out);
+  return launch_mode<float, SF>(hsi, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries,
+                                m, k, hsi_s, hsi_nb, workspace, plan, stream, scores_out);
+}
+
+}  // namespace
+
+hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,
+                             const uint8_t* scales, const int32_t* q_pos, int32_t* topk, int32_t* candidates, int B,
+                             int T, int H_I, int N_cap, int n_entries, int m, int k, int hsi, int hsi_s, int hsi_nb,
+                             void* workspace, const ScorePlan& plan, hipStream_t stream, float* scores_out,
+                             int scale_fmt) {
+  if (B == 0 || T == 0) return hipSuccess;
+  return scale_fmt == 1
+             ? launch_fmt<1>(dtype, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
+                             k, hsi, hsi_s, hsi_nb, workspace, plan, stream, scores_out)
+             : launch_fmt<0>(dtype, q_idx, w, codes, scales, q_pos, topk, candidates, B, T, H_I, N_cap, n_entries, m,
+                             k, hsi, hsi_s, hsi_nb, workspace, plan, stream, scores_out);
 }
 
 }  // namespace csa2

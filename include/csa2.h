@@ -123,7 +123,8 @@ typedef struct csa2_slot_info {
   int32_t B, rows, cols;/* COMPRESS_KV: B, N_cap, n_entries; INDEX_K: B, N_cap, n_entries;
                            TOPK_IDXS: B, T, k; CANDIDATES: B, T, n_b */
   int32_t extra;        /* CANDIDATES: block size s; COMPRESS_KV/INDEX_K: m */
-  int32_t kv_fmt;       /* COMPRESS_KV: csa2_kv_fmt (FP4: ptr = codes, ptr2 = scales) */
+  int32_t kv_fmt;       /* COMPRESS_KV: csa2_kv_fmt (FP4: ptr = codes, ptr2 = scales);
+                           INDEX_K: csa2_scale_fmt of the scales */
 } csa2_slot_info;
 
 csa2_status csa2_runtime_slot(const csa2_runtime* rt, csa2_slot slot, csa2_slot_info* out);
@@ -165,6 +166,16 @@ typedef struct csa2_compress_args {
 csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* Scale format of the index K ([P1] indexer-K section: FP4 with one scale per 32
+ * dims; the pages name no format for it).  E4M3: scale = E4M3FN(amax / 6)
+ * (float32 divide, nearest-even, saturating at 448), codes E2M1(u / s), all zero
+ * when s is 0.  UE8M0: the byte b of the smallest power of two X = 2^(b - 127) at
+ * or above amax / 6 (b clamped to 0 .. 254, 0 also for an all-zero block), codes
+ * E2M1(u / X).  Both: E2M1 nearest-even, saturating at 6, sign kept; 68 B per
+ * entry.  The FP4 main KV always uses E4M3. */
+typedef enum csa2_scale_fmt { CSA2_SCALE_E4M3 = 0, CSA2_SCALE_UE8M0 = 1 } csa2_scale_fmt;
+
+/* ------------------------------------------------------------------------ */
 /* (b) Index K ([P1] section "indexer K 改由 main KV 投影": projected 512 -> 128
  * from the main-KV entry before its RoPE, RoPE on its own last 64 dims at the
  * entry position, stored FP4 with one scale per 32 dims, no Hadamard rotation).
@@ -174,7 +185,9 @@ csa2_status csa2_compress(csa2_runtime* rt, const csa2_compress_args* a, csa2_st
  *   codes      [B, N_cap, 64]  uint8 out  rows entry0 .. entry0 + N - 1 written
  *   scales     [B, N_cap, 4]   uint8 out
  *   entry position for RoPE = (entry0 + i) * m
- * With rt != NULL the index_k slot is set to (codes, scales), n_entries = entry0 + N. */
+ *   scale_fmt  csa2_scale_fmt of the scales written (CSA2_ERR_INVALID_ARG otherwise)
+ * With rt != NULL the index_k slot is set to (codes, scales, scale_fmt),
+ * n_entries = entry0 + N. */
 typedef struct csa2_index_k_args {
   int32_t dtype;            /* csa2_dtype of w_ik */
   int32_t B, N, m;
@@ -185,6 +198,7 @@ typedef struct csa2_index_k_args {
   const void* w_ik;
   uint8_t* codes;
   uint8_t* scales;
+  int32_t scale_fmt;        /* csa2_scale_fmt */
 } csa2_index_k_args;
 
 csa2_status csa2_index_k(csa2_runtime* rt, const csa2_index_k_args* a, csa2_stream stream);
@@ -243,6 +257,7 @@ typedef struct csa2_compress_step_args {
   int32_t kv_fmt;           /* csa2_kv_fmt */
   uint8_t* kv_scales;       /* FP4 only: [B, N_cap, 32] */
   int32_t n_entries;        /* host; see above (read only with rt != NULL) */
+  int32_t scale_fmt;        /* csa2_scale_fmt of the index-K rows written */
 } csa2_compress_step_args;
 
 csa2_status csa2_compress_step(csa2_runtime* rt, const csa2_compress_step_args* a, csa2_stream stream);
@@ -289,6 +304,7 @@ typedef struct csa2_score_topk_args {
   void* workspace;
   size_t workspace_bytes;
   float* scores;            /* optional debug dump (see above), or NULL */
+  int32_t scale_fmt;        /* csa2_scale_fmt of explicit codes/scales; borrowed ones carry the slot's */
 } csa2_score_topk_args;
 
 csa2_status csa2_score_topk(csa2_runtime* rt, const csa2_score_topk_args* a, csa2_stream stream);
@@ -402,6 +418,7 @@ typedef struct csa2_layer_cfg {
   float rope_base, eps, scale;
   int32_t kv_fmt;           /* Full: storage of the main KV it writes (csa2_kv_fmt) */
   int32_t swa_fmt;          /* storage of this layer's window KV io->swa_kv (csa2_swa_fmt) */
+  int32_t scale_fmt;        /* Full: csa2_scale_fmt of the index K it writes (others read the slot's) */
 } csa2_layer_cfg;
 
 typedef struct csa2_layer_io {

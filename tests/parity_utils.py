@@ -80,19 +80,27 @@ def check_topk_row(scores, cand_ids, gpu_row, k, tag="", exempt=None):
     return exact
 
 
-def check_fp4(u, codes_gpu, scales_gpu, tag="", block=32):
+def check_fp4(u, codes_gpu, scales_gpu, tag="", block=32, scale_fmt=O.SCALE_E4M3):
     """u: oracle float64 values before quantisation [rows, d] (index K: d = 128,
     block 32; main KV: d = 512, block 16).  Returns (#code mismatches, #scale
-    mismatches), all of them inside the rounding bands."""
+    mismatches), all of them inside the rounding bands.  UE8M0 scales (index K)
+    round sigma up to a power of two, so their band is sigma within 1e-3 relative
+    of a power of two."""
     u32 = np.asarray(u, dtype=np.float64).astype(np.float32)
-    codes_o, scales_o = O.fp4_pack(u32, block)
+    codes_o, scales_o = O.fp4_pack(u32, block, scale_fmt)
     rows, d = u32.shape
     nb = d // block
     blocks = u32.reshape(rows, nb, block)
     sigma = (np.max(np.abs(blocks), axis=2).astype(np.float32) / np.float32(6)).astype(np.float64)
     sdiff = scales_gpu != scales_o
-    assert np.all(near_any(sigma[sdiff], E4M3_MIDS)), f"{tag}: scale bytes differ away from an E4M3 midpoint"
-    s = O.e4m3_decode(scales_o)
+    if scale_fmt == O.SCALE_UE8M0:
+        sd = sigma[sdiff]
+        p2 = np.exp2(np.round(np.log2(np.maximum(sd, 1e-300))))   # nearest power of two
+        assert np.all(np.abs(sd - p2) <= 1e-3 * sd), f"{tag}: UE8M0 scale bytes differ away from a power of two"
+        s = O.ue8m0_decode(scales_o)
+    else:
+        assert np.all(near_any(sigma[sdiff], E4M3_MIDS)), f"{tag}: scale bytes differ away from an E4M3 midpoint"
+        s = O.e4m3_decode(scales_o)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = blocks / s[:, :, None]
     def unpack(c):

@@ -107,7 +107,8 @@ def test_score_workspace_too_small():
     ("m", 3, "CSA2_ERR_INVALID_ARG"), ("state", None, "CSA2_ERR_INVALID_ARG"),
     ("w_gate", None, "CSA2_ERR_INVALID_ARG"), ("D", 100, "CSA2_ERR_SHAPE"), ("dtype", 9, "CSA2_ERR_DTYPE"),
     ("workspace_bytes", 1024, "CSA2_ERR_WORKSPACE"), ("workspace", 0x1008, "CSA2_ERR_WORKSPACE"),
-    ("pos", None, "CSA2_ERR_INVALID_ARG"),
+    ("pos", None, "CSA2_ERR_INVALID_ARG"), ("scale_fmt", 2, "CSA2_ERR_INVALID_ARG"),
+    ("scale_fmt", -1, "CSA2_ERR_INVALID_ARG"),
 ])
 def test_compress_step_validation(field, value, status):
     a = K.CompressStepArgs(dtype=1, B=4, D=256, m=2, N_cap=100, eps=1e-6, rope_base=1e4, x=0x1000, pos=0x1000,
@@ -150,6 +151,7 @@ def test_workspace_must_be_16_byte_aligned():
 @pytest.mark.parametrize("field,value,status", [
     ("H_I", 33, "CSA2_ERR_SHAPE"), ("k", 0, "CSA2_ERR_SHAPE"), ("k", 2000, "CSA2_ERR_SHAPE"),
     ("n_entries", 5000, "CSA2_ERR_SHAPE"), ("hsi", 5, "CSA2_ERR_INVALID_ARG"),
+    ("scale_fmt", 2, "CSA2_ERR_INVALID_ARG"),
 ])
 def test_score_validation(field, value, status):
     a = K.ScoreTopkArgs(dtype=1, B=1, T=1, H_I=32, N_cap=4096, n_entries=4096, m=1, k=512, q_idx=0x1000,
@@ -289,3 +291,23 @@ def test_score_dump_must_be_aligned():
                         codes=0x1000, scales=0x1000, q_pos=0x1000, topk=0x1000, workspace=0x1000,
                         workspace_bytes=1 << 30, scores=0x1002)
     assert K.STATUS[K.lib().csa2_score_topk(None, C.byref(a), None)] == "CSA2_ERR_INVALID_ARG"
+
+
+@pytest.mark.parametrize("fmt,status", [(0, "CSA2_OK"), (1, "CSA2_OK"), (2, "CSA2_ERR_INVALID_ARG"),
+                                        (-3, "CSA2_ERR_INVALID_ARG")])
+def test_index_k_scale_format_validation(fmt, status):
+    # N = 0 enqueues nothing, so a valid format returns OK without a GPU
+    a = K.IndexKArgs(dtype=1, B=2, N=0, m=1, entry0=0, N_cap=10, rope_base=1e4, latent_pre=0x1000, w_ik=0x1000,
+                     codes=0x1000, scales=0x1000, scale_fmt=fmt)
+    assert K.STATUS[K.lib().csa2_index_k(None, C.byref(a), None)] == status
+
+
+def test_layer_rejects_a_bad_scale_format_before_enqueueing():
+    rt = K.Runtime()
+    cfg = K.layer_cfg(K.FULL, K.CSA2_BF16, m=1, k=64, W=16, H_I=32, H=16, scale_fmt=7)
+    io = K.LayerIO(B=1, T=16, D=256, N_cap=16, x=0x1000, w_kv=0x1000, gamma=0x1000, w_ik=0x1000,
+                   latent_pre=0x1000, kv_cache=0x1000, ik_codes=0x1000, ik_scales=0x1000, q_idx=0x1000, w=0x1000,
+                   topk=0x1000, q_pos=0x1000, q=0x1000, swa_kv=0x1000, L_w=16, swa_pos0=0x1000, o=0x1000,
+                   workspace=0x1000, workspace_bytes=1 << 30)
+    assert K.STATUS[K.lib().csa2_layer_forward(rt.handle, C.byref(cfg), C.byref(io), None)] == "CSA2_ERR_INVALID_ARG"
+    assert rt.slot(K.SLOT_INDEX_K).filled == 0 and rt.slot(K.SLOT_COMPRESS_KV).filled == 0

@@ -30,8 +30,9 @@ class GpuLayerStack:
     """Device buffers of one Full layer's caches plus per-layer call helpers."""
 
     def __init__(self, shape: synth.LayerShape, dtype, hsi=K.HSI_NONE if torch.cuda.is_available() else 0,
-                 hsi_s=0, hsi_nb=0, kv_fp4=False):
+                 hsi_s=0, hsi_nb=0, kv_fp4=False, scale_fmt=0):
         s = shape
+        self.scale_fmt = scale_fmt   # csa2_scale_fmt of the index K a Full layer writes
         self.s, self.dtype = s, dtype
         self.N = s.L // s.m
         self.rt = K.Runtime()
@@ -53,7 +54,7 @@ class GpuLayerStack:
         hsi = self.hsi if hsi is None else hsi
         cfg = K.layer_cfg(mode, K.CSA2_BF16 if self.dtype == torch.bfloat16 else K.CSA2_F32, m=s.m, k=s.k, W=s.W,
                           H_I=s.H_I, H=s.H, hsi=hsi, hsi_s=self.hsi_s, hsi_nb=self.hsi_nb,
-                          kv_fmt=K.KV_FP4 if self.kv_fp4 else K.KV_DENSE)
+                          kv_fmt=K.KV_FP4 if self.kv_fp4 else K.KV_DENSE, scale_fmt=self.scale_fmt)
         topk = torch.full((s.B, s.L, s.k), -9, dtype=torch.int32, device=DEV)
         o = torch.empty_like(inp["q"])
         kw = dict(B=s.B, T=s.L, q_pos=inp["q_pos"], q=inp["q"], swa_kv=inp["swa_kv"], swa_pos0=inp["swa_pos0"], o=o,
@@ -101,12 +102,16 @@ def _compare_layer(tag, o_gpu, topk_gpu, rt_o: O.Runtime, o_ref, scores_fn, tol,
     return exact
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_full_reindex_reuse_tiny(dtype):
+@pytest.mark.parametrize("dtype,sfmt", [(torch.float32, "e4m3"), (torch.bfloat16, "e4m3"),
+                                       (torch.bfloat16, "ue8m0"), (torch.float32, "ue8m0")])
+def test_full_reindex_reuse_tiny(dtype, sfmt):
+    """sfmt: scale format of the Full layer's index K; the Reindex layer reads it
+    from the index_k slot with the codes."""
     shape = synth.TINY if dtype == torch.float32 else synth.LayerShape(B=2, L=640, D=512, m=2, H_I=32, k=64, W=32, H=16)
     tol = 1e-3 if dtype == torch.float32 else 2e-2
-    say(f"case: layers Full/Reindex/Reuse dtype={dtype} shape={shape}")
-    g = GpuLayerStack(shape, dtype)
+    say(f"case: layers Full/Reindex/Reuse dtype={dtype} shape={shape} index-K scales {sfmt}")
+    gfmt = K.SCALE_UE8M0 if sfmt == O.SCALE_UE8M0 else K.SCALE_E4M3
+    g = GpuLayerStack(shape, dtype, scale_fmt=gfmt)
     full_in = synth.full_layer_inputs(shape, 0, dtype, DEV, layer=0)
     re_in = synth.full_layer_inputs(shape, 0, dtype, DEV, layer=1, with_x=False)
     ru_in = synth.full_layer_inputs(shape, 0, dtype, DEV, layer=2, with_x=False)
@@ -114,7 +119,7 @@ def test_full_reindex_reuse_tiny(dtype):
     rt_o = O.Runtime()
     cfg_full = O.LayerConfig(O.FULL, m=shape.m, k=shape.k, W=shape.W, w_kv=npy(full_in["w_kv"]),
                              w_gate=None if full_in["w_gate"] is None else npy(full_in["w_gate"]),
-                             gamma=npy(full_in["gamma"]), w_ik=npy(full_in["w_ik"]))
+                             gamma=npy(full_in["gamma"]), w_ik=npy(full_in["w_ik"]), scale_fmt=sfmt)
     # ---- Full
     o_full, t_full = g.run(K.FULL, full_in)
     o_ref = O.layer_forward(rt_o, cfg_full, _np_inputs(full_in, True))
@@ -123,9 +128,11 @@ def test_full_reindex_reuse_tiny(dtype):
         lat_o, kv_o, ids = O.compress(npy(full_in["x"][b]), cfg_full.w_kv, cfg_full.w_gate, cfg_full.gamma, shape.m)
         assert row_rel_err(npy(g.kv[b]), kv_o) <= tol
         u, _, _ = O.index_k(lat_o, cfg_full.w_ik, ids * shape.m)
-        nc, ns = check_fp4(u, g.codes[b].cpu().numpy(), g.scales[b].cpu().numpy(), f"full codes b{b}")
+        nc, ns = check_fp4(u, g.codes[b].cpu().numpy(), g.scales[b].cpu().numpy(), f"full codes b{b}",
+                           scale_fmt=sfmt)
         say(f"  full b={b}: FP4 code mismatches in band {nc}, scale {ns}")
-    kd = [O.fp4_unpack(codes_o[b], scales_o[b]) for b in range(shape.B)]
+    assert g.rt.slot(K.SLOT_INDEX_K).kv_fmt == gfmt   # the slot records the scale format
+    kd = [O.fp4_unpack(codes_o[b], scales_o[b], scale_fmt=sfmt) for b in range(shape.B)]
     # entries whose GPU codes differ from the oracle's (each inside a rounding band, checked above)
     cg, sg = g.codes.cpu().numpy(), g.scales.cpu().numpy()
     flips = [np.where((cg[b] != codes_o[b]).any(1) | (sg[b] != scales_o[b]).any(1))[0] for b in range(shape.B)]

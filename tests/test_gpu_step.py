@@ -31,13 +31,16 @@ def npy(t):
     return t.detach().float().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,m", [(torch.bfloat16, 2), (torch.bfloat16, 1), (torch.bfloat16, 4),
-                                     (torch.float32, 2)])
-def test_compress_step_continues_the_prefill(dtype, m):
+@pytest.mark.parametrize("dtype,m,sfmt", [(torch.bfloat16, 2, "e4m3"), (torch.bfloat16, 1, "e4m3"),
+                                          (torch.bfloat16, 4, "e4m3"), (torch.float32, 2, "e4m3"),
+                                          (torch.bfloat16, 2, "ue8m0"), (torch.float32, 1, "ue8m0")])
+def test_compress_step_continues_the_prefill(dtype, m, sfmt):
+    """sfmt: scale format of the index-K rows (the prefill's and the steps')."""
     B, D = 3, (512 if dtype == torch.bfloat16 else 256)
     P, S = 8 * m, 6 * m + 1                 # prefill tokens, then S append steps
     L = P + S
-    say(f"case: compress_step dtype={dtype} m={m} B={B} D={D} prefill {P} + {S} steps")
+    gfmt = K.SCALE_UE8M0 if sfmt == O.SCALE_UE8M0 else K.SCALE_E4M3
+    say(f"case: compress_step dtype={dtype} m={m} B={B} D={D} prefill {P} + {S} steps, index-K scales {sfmt}")
     x = synth.gaussian((B, L, D), 1.0, 61, "x", 0, dtype, DEV)
     w_kv = synth.linear_weight(512, D, 61, "w_kv", 0, dtype, DEV)
     w_gate = synth.linear_weight(512, D, 61, "w_gate", 0, dtype, DEV) if m > 1 else None
@@ -49,7 +52,7 @@ def test_compress_step_continues_the_prefill(dtype, m):
     scales = torch.zeros(B, N_cap, 4, dtype=torch.uint8, device=DEV)
     lat = torch.empty(B, P // m, 512, dtype=torch.float32, device=DEV)
     K.csa2_compress(None, x[:, :P].contiguous(), w_kv, w_gate, gamma, lat, kv, m=m, start_pos=0)
-    K.csa2_index_k(None, lat, w_ik, codes, scales, m=m)
+    K.csa2_index_k(None, lat, w_ik, codes, scales, m=m, scale_fmt=gfmt)
     state = torch.full((B, 3, 512), float("nan"), dtype=torch.float32, device=DEV) if m > 1 else None
     lat_step = torch.zeros(B, 512, dtype=torch.float32, device=DEV)
     ws = None
@@ -59,7 +62,8 @@ def test_compress_step_continues_the_prefill(dtype, m):
         pos = [t, t, t - 1 if s > 0 else -1]   # sequence 2 lags one step
         xs = torch.stack([x[b, max(pos[b], 0)] for b in range(B)]).contiguous()
         ws = K.csa2_compress_step(None, xs, torch.tensor(pos, dtype=torch.int32, device=DEV), w_kv, w_gate, gamma,
-                                  w_ik, state, kv, codes, scales, m=m, latent_pre=lat_step, workspace=ws)
+                                  w_ik, state, kv, codes, scales, m=m, latent_pre=lat_step, workspace=ws,
+                                  scale_fmt=gfmt)
         for b in range(B):
             if pos[b] >= 0:
                 done[b] = pos[b]
@@ -73,7 +77,8 @@ def test_compress_step_continues_the_prefill(dtype, m):
         u, _, _ = O.index_k(lp, npy(w_ik), ids * m)
         g0 = P // m                            # rows written by the steps
         worst = max(worst, row_rel_err(kvg[b, g0:n_done], kvo[g0:]))
-        nc, ns = check_fp4(u[g0:], cg[b, g0:n_done], sg[b, g0:n_done], f"step b{b}")
+        check_fp4(u[:g0], cg[b, :g0], sg[b, :g0], f"prefill b{b}", scale_fmt=sfmt)
+        nc, ns = check_fp4(u[g0:], cg[b, g0:n_done], sg[b, g0:n_done], f"step b{b}", scale_fmt=sfmt)
         assert np.all(kvg[b, n_done:] == 0) and np.all(cg[b, n_done:] == 0), f"b{b}: rows past the last group"
         say(f"  b{b}: {n_done - g0} appended rows, fp4 code/scale differences at rounding midpoints {nc}/{ns}")
     assert worst <= TOL[dtype], worst

@@ -65,6 +65,26 @@ def test_scale_byte_flip_away_from_midpoint_rejected():
         check_fp4(u, codes, bad)
 
 
+def test_ue8m0_scale_flip_only_at_a_power_of_two():
+    # amax = 6 * 2^3 exactly: sigma = 8 is a power of two, so a GPU whose sigma
+    # came out a hair above it may pick the next byte (scale 16), with codes to match
+    u = _block_with([1.0]) * 8.0
+    codes, scales = O.fp4_pack(u.astype(np.float32), 32, O.SCALE_UE8M0)
+    assert scales[0, 0] == 127 + 3
+    up = scales.copy()
+    up[0, 0] += 1
+    codes_up, _ = O.fp4_pack(u.astype(np.float32) / 2.0, 32, O.SCALE_UE8M0)   # the codes under scale 16
+    assert check_fp4(u, codes_up, up, scale_fmt=O.SCALE_UE8M0)[1] == 1
+    # amax = 6 * 5: sigma = 5 is no power of two, the byte is fixed
+    u = _block_with([1.0]) * 5.0
+    codes, scales = O.fp4_pack(u.astype(np.float32), 32, O.SCALE_UE8M0)
+    bad = scales.copy()
+    bad[0, 0] += 1
+    with pytest.raises(AssertionError):
+        check_fp4(u, codes, bad, scale_fmt=O.SCALE_UE8M0)
+    assert check_fp4(u, codes, scales, scale_fmt=O.SCALE_UE8M0) == (0, 0)
+
+
 def test_topk_band_rule():
     scores = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.5])
     ids = np.arange(6)
