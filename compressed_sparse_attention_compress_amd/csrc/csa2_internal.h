@@ -52,7 +52,9 @@ struct ScorePlan {
   int chunk;        // entries per chunk (a power of two), or per part on the streaming path
   int n_chunks;     // chunks per query
   int k_chunk;      // candidates kept per chunk = min(k, chunk)
-  size_t cand_bytes, lb_bytes, blk_bytes, key_bytes, total_bytes;
+  int pf_cpg;       // chunks per pre-filter group before the merge (0: no pre-filter)
+  int pf_groups;    // pre-filter groups per query
+  size_t cand_bytes, lb_bytes, blk_bytes, seg_bytes, key_bytes, total_bytes;
 };
 ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hsi_s, int hsi_nb);
 hipError_t launch_score_topk(int dtype, const void* q_idx, const float* w, const uint8_t* codes,

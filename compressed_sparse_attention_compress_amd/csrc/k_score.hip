@@ -918,6 +918,99 @@ __global__ __launch_bounds__(SC_THREADS) void score_chunk(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pre-filter before the merge (queries with many chunks): one workgroup per
+// (query, group of pf_cpg chunks) drops the group's candidates below the merge
+// bound (the smallest rank-r0 key over the query's full chunks, which no chosen
+// key is below) and compacts the rest, in order, to the front of the group's
+// own candidate range, with their count in seg_cnt.  The merge then stages only
+// the survivors instead of streaming every chunk's list through one workgroup.
+constexpr int PF_THREADS = 256;
+constexpr int PF_PER = 16;                          // candidates per thread
+constexpr int PF_ITEMS = PF_THREADS * PF_PER;       // candidates per group at most
+constexpr long long PF_MIN_ITEMS = 32768;           // pre-filter above this many candidates per query
+constexpr int PF_MAX_GROUPS = 512;                  // groups per query at most (offsets in the merge's LDS)
+
+template <bool POOL>
+__global__ __launch_bounds__(PF_THREADS) void topk_prefilter(uint32_t* __restrict__ cand_key,
+                                                             int32_t* __restrict__ cand_idx,
+                                                             const uint32_t* __restrict__ chunk_lb,
+                                                             const int32_t* __restrict__ q_pos,
+                                                             uint32_t* __restrict__ seg_cnt, int T_len, int n_entries,
+                                                             int m, int C, int k_chunk, int n_chunks, int cpg,
+                                                             int n_groups, int single_direct) {
+  __shared__ uint32_t s_bound;
+  __shared__ uint32_t wsum[PF_THREADS / 64];
+  const int g = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int bt = b * T_len + t;
+  const int n_t = visible(q_pos, bt, m, n_entries);
+  const int nc = POOL ? n_chunks : (n_t + C - 1) / C;
+  const int c0 = g * cpg, c1 = min(nc, c0 + cpg);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // no chunk of this query here, or a single chunk that wrote the query's top-k
+  // itself (the merge reads every group's count, and skips such a query)
+  if (c0 >= c1 || (single_direct && nc <= 1)) {
+    if (threadIdx.x == 0) seg_cnt[(size_t)bt * n_groups + g] = 0u;
+    return;
+  }
+  // the merge bound, as the merge computes it
+  uint32_t tl = 0xFFFFFFFFu;
+  for (int cc = threadIdx.x; cc < nc - 1; cc += PF_THREADS) tl = min(tl, chunk_lb[(size_t)bt * n_chunks + cc]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) tl = min(tl, (uint32_t)__shfl_xor((int)tl, off, 64));
+  if (threadIdx.x == 0) s_bound = 0xFFFFFFFFu;
+  __syncthreads();
+  if (lane == 0) atomicMin(&s_bound, tl);
+  __syncthreads();
+  const uint32_t bound = nc > 1 ? s_bound : 0u;
+  // thread i holds candidates [PF_PER i, PF_PER i + PF_PER) of the group (k_chunk % 4 == 0)
+  const size_t base = ((size_t)bt * n_chunks + c0) * k_chunk;
+  const int n_items = (c1 - c0) * k_chunk;
+  const int i0 = threadIdx.x * PF_PER;
+  uint4 kv[PF_PER / 4];
+  int4 iv[PF_PER / 4];
+#pragma unroll
+  for (int j = 0; j < PF_PER / 4; ++j) {
+    const bool in = i0 + 4 * j < n_items;
+    kv[j] = in ? *reinterpret_cast<const uint4*>(cand_key + base + i0 + 4 * j) : make_uint4(0, 0, 0, 0);
+    iv[j] = in ? *reinterpret_cast<const int4*>(cand_idx + base + i0 + 4 * j) : make_int4(-1, -1, -1, -1);
+  }
+  uint32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < PF_PER / 4; ++j) {
+    own += (kv[j].x != 0u && kv[j].x >= bound) + (kv[j].y != 0u && kv[j].y >= bound) +
+           (kv[j].z != 0u && kv[j].z >= bound) + (kv[j].w != 0u && kv[j].w >= bound);
+  }
+  // exclusive prefix of the per-thread counts (thread order is candidate order)
+  uint32_t x = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(x, off, 64);
+    if (lane >= off) x += u;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();   // also: every read of the group's range is done before any write below
+  uint32_t slot = x - own, total = 0;
+#pragma unroll
+  for (int w = 0; w < PF_THREADS / 64; ++w) {
+    slot += w < wave ? wsum[w] : 0u;
+    total += wsum[w];
+  }
+#pragma unroll
+  for (int j = 0; j < PF_PER / 4; ++j) {
+    const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+    const int32_t ii[4] = {iv[j].x, iv[j].y, iv[j].z, iv[j].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (kk[u] != 0u && kk[u] >= bound) {
+        cand_key[base + slot] = kk[u];
+        cand_idx[base + slot] = ii[u];
+        ++slot;
+      }
+  }
+  if (threadIdx.x == 0) seg_cnt[(size_t)bt * n_groups + g] = total;
+}
+
 constexpr int MG_THREADS = 512;
 constexpr int MG_TILE = 4096;    // candidate keys read into LDS per round (LDS-tile form)
 constexpr int MG_CAP = 4096;     // staged candidates kept in LDS (LDS-tile form)
@@ -936,7 +1029,8 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
                                                          const int32_t* __restrict__ q_pos, int32_t* __restrict__ topk,
                                                          int32_t* __restrict__ cands_out, int T_len, int n_entries,
                                                          int m, int k, int C, int k_chunk, int n_chunks, int hsi_s,
-                                                         int hsi_nb, int nblk_max) {
+                                                         int hsi_nb, int nblk_max, const uint32_t* __restrict__ seg_cnt,
+                                                         int pf_cpg, int pf_groups) {
   __shared__ SelSmem<MG_THREADS> sel;
   // one 80 KB area: [tile | staged keys | staged candidate positions]; the block
   // selection of HSI BUILD (a workgroup of its own) uses all of it
@@ -978,7 +1072,41 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
     constexpr int MG_NW = MG_THREADS / 64;
     constexpr int MG_REG = 8;   // uint4 loads per lane: 32 candidates
     constexpr int MG_ROUND = MG_THREADS * 4 * MG_REG;   // 16384 candidates per register round
-    const bool in_regs = (k_chunk & 3) == 0;
+    const bool pf = pf_cpg > 0;   // pre-filtered: group g's survivors at the front of its range
+    const bool in_regs = !pf && (k_chunk & 3) == 0;
+    const int seg_len = pf_cpg * k_chunk;   // candidate range of one pre-filter group
+    uint32_t* seg_off = tile;               // group offsets among the survivors (pre-filtered)
+    const int ng = pf ? (nc + pf_cpg - 1) / pf_cpg : 0;
+    if (pf) {
+      // survivors per group -> offsets (ng <= MG_TILE); a wave copies group g's
+      // survivors for g = wave, wave + 8, ... (entry order: group-major)
+      const uint32_t* cnt_row = seg_cnt + (size_t)bt * pf_groups;
+      for (int g = threadIdx.x; g < ng; g += MG_THREADS) seg_off[g] = cnt_row[g];
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        for (int g = 0; g < ng; ++g) {
+          const uint32_t c = seg_off[g];
+          seg_off[g] = acc;
+          acc += c;
+        }
+        s_bound = acc;
+      }
+      __syncthreads();
+      staged = s_bound;
+      if (staged <= cap) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        for (int g = wave; g < ng; g += MG_NW) {
+          const uint32_t o = seg_off[g];
+          const uint32_t n = (g + 1 < ng ? seg_off[g + 1] : staged) - o;
+          for (uint32_t i = lane; i < n; i += 64) {
+            skey[o + i] = kb[(size_t)g * seg_len + i];
+            sidx[o + i] = g * seg_len + (int)i;
+          }
+        }
+      }
+      __syncthreads();
+    }
     if (in_regs && n_items > 0) {
       // rounds of up to 16384 candidates at once: wave w holds items
       // [w * 2048, w * 2048 + 2048) of the round, lane l the 4 consecutive items
@@ -1053,7 +1181,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
         __syncthreads();
       }
     }
-    for (int r = 0; r < (in_regs ? 0 : n_items); r += MG_TILE) {
+    for (int r = 0; r < (in_regs || pf ? 0 : n_items); r += MG_TILE) {
       const int len = min(MG_TILE, n_items - r);
       for (int i0 = 0; i0 < len; i0 += 4 * MG_THREADS) {   // all loads of a round in flight together
         uint32_t kk[4];
@@ -1095,6 +1223,20 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
       else
         cnt = emit_ordered<MG_THREADS>(key_at, (int)staged, s, sel,
                                        [&](int i, uint32_t slot) { out[slot] = ib[sidx[i]]; });
+    } else if (pf) {
+      // more survivors than LDS holds: select straight from the groups' ranges
+      auto key_at = [&](int i) -> uint32_t {
+        const int g = i / seg_len, r = i - g * seg_len;
+        const uint32_t o = seg_off[g];
+        const uint32_t n = (g + 1 < ng ? seg_off[g + 1] : staged) - o;
+        return (uint32_t)r < n ? kb[i] : 0u;
+      };
+      uint32_t mn, mx, nv;
+      key_stats<MG_THREADS>(key_at, n_items, sel, mn, mx, nv);
+      const uint32_t need = nv < (uint32_t)k ? nv : (uint32_t)k;
+      const SelOut s = need == nv ? SelOut{mn, 0xFFFFFFFFu, 0u}
+                                  : select_threshold<MG_THREADS>(key_at, n_items, need, mn, mx, 0u, sel);
+      cnt = emit_ordered<MG_THREADS>(key_at, n_items, s, sel, [&](int i, uint32_t slot) { out[slot] = ib[i]; });
     } else {
       // more candidates than LDS holds: select straight from the workspace
       auto key_at = [&](int i) -> uint32_t { const uint32_t kk = kb[i]; return kk >= bound ? kk : 0u; };
@@ -1854,6 +1996,7 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   int32_t* cand_idx = reinterpret_cast<int32_t*>(wsb + n_slots * 4);
   uint32_t* chunk_lb = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes);
   uint32_t* blkmax = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes + p.lb_bytes);
+  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(wsb + p.cand_bytes + p.lb_bytes + (p.blk_bytes + 255) / 256 * 256);
   const int nblk_max = BUILD ? (n_entries + hsi_s - 1) / hsi_s : 0;
   dim3 g1(p.n_chunks, T_len, B);
   hipLaunchKernelGGL((score_chunk<T, POOL, BUILD, SF>), g1, dim3(SC_THREADS), 0, st, static_cast<const T*>(q_idx), w,
@@ -1862,10 +2005,17 @@ hipError_t launch_impl(const void* q_idx, const float* w, const uint8_t* codes, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!BUILD && p.n_chunks <= 1) return hipSuccess;   // every query was finished by its single chunk
+  if (p.pf_cpg > 0) {
+    hipLaunchKernelGGL((topk_prefilter<POOL>), dim3(p.pf_groups, T_len, B), dim3(PF_THREADS), 0, st, cand_key,
+                       cand_idx, chunk_lb, q_pos, seg_cnt, T_len, n_entries, m, p.chunk, p.k_chunk, p.n_chunks,
+                       p.pf_cpg, p.pf_groups, BUILD ? 0 : 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 g2(T_len, B, BUILD ? 2 : 1);
   hipLaunchKernelGGL((topk_merge<POOL, BUILD>), g2, dim3(MG_THREADS), 0, st, cand_key, cand_idx, chunk_lb, blkmax,
                      q_pos, topk, cands, T_len, n_entries, m, k, p.chunk, p.k_chunk, p.n_chunks, hsi_s, hsi_nb,
-                     nblk_max);
+                     nblk_max, (const uint32_t*)seg_cnt, p.pf_cpg, p.pf_groups);
   return hipGetLastError();
 }
 
@@ -1904,7 +2054,7 @@ hipError_t launch_stream(const void* q_idx, const float* w, const uint8_t* codes
   dim3 g2(T_len, B, 1);
   hipLaunchKernelGGL((topk_merge<false, false>), g2, dim3(MG_THREADS), 0, st, cand_key, cand_idx, chunk_lb,
                      (const uint32_t*)nullptr, q_pos, topk, (int32_t*)nullptr, T_len, n_entries, m, k, p.chunk,
-                     p.k_chunk, p.n_chunks, 0, 0, 0);
+                     p.k_chunk, p.n_chunks, 0, 0, 0, (const uint32_t*)nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -1957,7 +2107,9 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
   }
   int C = MAX_CHUNK;
   while (C > 256 && C / 2 >= n_scan) C /= 2;                       // no chunk much larger than the scan
-  while (C > 1024 && Q * ((n_scan + C - 1) / C) < 1024) C /= 2;   // enough workgroups to fill the GPU
+  // enough workgroups to fill the GPU; a pool scan (a small gathered set, so the
+  // merge input stays small) goes down to 256-entry chunks
+  while (C > (hsi == 2 ? 256 : 1024) && Q * ((n_scan + C - 1) / C) < 1024) C /= 2;
   if (hsi != 0 && C < hsi_s) C = hsi_s;                           // chunks hold whole blocks
   p.chunk = C;
   p.n_chunks = n_scan <= 0 ? 1 : (n_scan + C - 1) / C;
@@ -1966,7 +2118,16 @@ ScorePlan plan_score(int dtype, int B, int T, int n_scan, int k, int hsi, int hs
   p.lb_bytes = ((size_t)Q * p.n_chunks * 4 + 255) / 256 * 256;
   const long long nblk = (hsi == 1) ? ((long long)n_scan + hsi_s - 1) / hsi_s : 0;
   p.blk_bytes = (size_t)(Q * nblk * 4);
-  p.total_bytes = p.cand_bytes + p.lb_bytes + p.blk_bytes + 256;
+  // pre-filter the candidate lists when the merge would stream many of them
+  // through its one workgroup per query: groups of PF_ITEMS candidates
+  const long long n_items = (long long)p.n_chunks * p.k_chunk;
+  const int cpg = PF_ITEMS / p.k_chunk;
+  if (n_items > PF_MIN_ITEMS && (p.k_chunk & 3) == 0 && cpg >= 1 && (p.n_chunks + cpg - 1) / cpg <= PF_MAX_GROUPS) {
+    p.pf_cpg = cpg;
+    p.pf_groups = (p.n_chunks + cpg - 1) / cpg;
+    p.seg_bytes = ((size_t)Q * p.pf_groups * 4 + 255) / 256 * 256;
+  }
+  p.total_bytes = p.cand_bytes + p.lb_bytes + (p.blk_bytes + 255) / 256 * 256 + p.seg_bytes + 256;
   return p;
 }
 

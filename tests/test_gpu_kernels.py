@@ -173,26 +173,31 @@ def test_score_topk_many_queries_vs_oracle(m, k, H_I):
     assert exact >= n - 1
 
 
-@pytest.mark.parametrize("dtype,T,n_fill", [(torch.bfloat16, 3, 5000), (torch.bfloat16, 300, 5000),
-                                            (torch.bfloat16, 300, 4000), (torch.float32, 3, 5000),
-                                            (torch.bfloat16, 64, 40000), (torch.bfloat16, 8192, 10000),
-                                            (torch.float32, 8192, 10000), (torch.bfloat16, 8192, 70000)])
-def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill):
-    """An index-K cache of 50 distinct rows repeated: every score value occurs ~100
-    times, so the k-th best falls inside a group of equal scores and the selection
-    must take that group's smallest positions (ties go to the smaller entry id).
-    Equal rows give bit-identical scores on both sides, and the distinct values are
-    kept well apart, so the chosen set is unique and compared exactly: T = 3 and
-    T = 64 run the chunked scorer and the merge, T = 300 the query-tiled scorer
+@pytest.mark.parametrize("dtype,T,n_fill,n_rows", [(torch.bfloat16, 3, 5000, 50), (torch.bfloat16, 300, 5000, 50),
+                                                   (torch.bfloat16, 300, 4000, 50), (torch.float32, 3, 5000, 50),
+                                                   (torch.bfloat16, 64, 40000, 50), (torch.bfloat16, 8192, 10000, 50),
+                                                   (torch.float32, 8192, 10000, 50),
+                                                   (torch.bfloat16, 8192, 70000, 50),
+                                                   (torch.bfloat16, 4, 65536, 50), (torch.bfloat16, 3, 200000, 8)])
+def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill, n_rows):
+    """An index-K cache of n_rows distinct rows repeated: every score value occurs
+    n_fill / n_rows times, so the k-th best falls inside a group of equal scores and
+    the selection must take that group's smallest positions (ties go to the smaller
+    entry id).  Equal rows give bit-identical scores on both sides, and the distinct
+    values are kept well apart, so the chosen set is unique and compared exactly:
+    T = 3 .. 64 run the chunked scorer and the merge (with 20 and more chunks per
+    query the candidate lists are pre-filtered in groups first; with 8 rows over
+    200000 entries more than the merge's LDS holds survive the pre-filter, and it
+    selects straight from the groups' ranges), T = 300 the query-tiled scorer
     and the per-query select (rows of up to 4096 keys held 64 per lane, longer
     rows 128), T = 8192 the streaming scorer with its in-part cutbacks to the k
     best (the boundary tie group cut there too), over one part and, with 70000
     entries, two parts and the merge."""
     B, k, H_I, m = 1, 512, 32, 1
-    say(f"case: score_topk exact ties dtype={dtype} T={T}")
-    u = synth.gaussian((50, 128), 1.0, 31, "u", 0, torch.float32, "cpu").numpy()
+    say(f"case: score_topk exact ties dtype={dtype} T={T} n={n_fill} rows={n_rows}")
+    u = synth.gaussian((n_rows, 128), 1.0, 31, "u", 0, torch.float32, "cpu").numpy()
     base_c, base_s = O.fp4_pack(u)
-    rep = np.random.default_rng(31).integers(0, 50, size=n_fill)
+    rep = np.random.default_rng(31).integers(0, n_rows, size=n_fill)
     codes = base_c[rep][None].copy()
     scales = base_s[rep][None].copy()
     kd = O.fp4_unpack(codes[0], scales[0])
