@@ -178,19 +178,19 @@ def test_score_topk_many_queries_vs_oracle(m, k, H_I):
                                                    (torch.bfloat16, 64, 40000, 50), (torch.bfloat16, 8192, 10000, 50),
                                                    (torch.float32, 8192, 10000, 50),
                                                    (torch.bfloat16, 8192, 70000, 50),
-                                                   (torch.bfloat16, 4, 65536, 50), (torch.bfloat16, 3, 200000, 8)])
+                                                   (torch.bfloat16, 4, 100000, 50), (torch.bfloat16, 3, 200000, 8)])
 def test_score_topk_exact_ties_vs_oracle(dtype, T, n_fill, n_rows):
     """An index-K cache of n_rows distinct rows repeated: every score value occurs
     n_fill / n_rows times, so the k-th best falls inside a group of equal scores and
     the selection must take that group's smallest positions (ties go to the smaller
     entry id).  Equal rows give bit-identical scores on both sides, and the distinct
     values are kept well apart, so the chosen set is unique and compared exactly:
-    T = 3 .. 64 run the chunked scorer and the merge (with 20 and more chunks per
-    query the candidate lists are pre-filtered in groups first; with 8 rows over
-    200000 entries more than the merge's LDS holds survive the pre-filter, and it
-    selects straight from the groups' ranges), T = 300 the query-tiled scorer
-    and the per-query select (rows of up to 4096 keys held 64 per lane, longer
-    rows 128), T = 8192 the streaming scorer with its in-part cutbacks to the k
+    T = 3 .. 64 run the chunked scorer and the merge (with 100000 entries and more
+    the candidate lists, over 32768 per query, are pre-filtered in groups first;
+    with 8 rows over 200000 entries more than the merge's LDS holds survive the
+    pre-filter, and it selects straight from the groups' ranges), T = 300 the
+    query-tiled scorer and the per-query select (rows of up to 4096 keys held 64
+    per lane, longer rows 128), T = 8192 the streaming scorer with its in-part cutbacks to the k
     best (the boundary tie group cut there too), over one part and, with 70000
     entries, two parts and the merge."""
     B, k, H_I, m = 1, 512, 32, 1
