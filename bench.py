@@ -18,7 +18,8 @@ Every input is seeded synthetic data already resident in HBM when timing starts.
 Per-kernel times come from HIP events recorded on the stream the library launches
 on (torch's current stream).  The CPU oracle is timed on this host beside each
 record (`cpu_baseline`): the whole prefill step unsampled for the headline; a
-stated sample, extrapolated and labelled so, for the others.
+stated sample, extrapolated and labelled so, for the decode and decoder records;
+all sequences for the decode append.
 """
 from __future__ import annotations
 
@@ -563,7 +564,11 @@ def cpu_baseline_decode(db, seqs=(0, 21, 42, 63)):
     """Oracle on this host for the batched decode step on `seqs` of the B
     sequences: index-K dequantisation, scores over all entries, top-k, then the
     Reindex and the Reuse layer's attention; extrapolated by the sequence count.
-    The sequence's caches are drawn again from their seeds before the clock."""
+    The sequence's caches are drawn again from their seeds before the clock.
+    With FP4 main KV the selected rows are dequantised inside the clock; with the
+    FP8 window ring each layer appends the newest row and reads its window from
+    the ring inside the clock (the ring holding the earlier rows is built
+    before it)."""
     import numpy as np
     import torch
     import synth
@@ -573,25 +578,83 @@ def cpu_baseline_decode(db, seqs=(0, 21, 42, 63)):
         return x.detach().float().cpu().numpy().astype(np.float64)
     p = int(db.q_pos[0, 0].item())
     pos0 = int(db.swa_pos0[0].item())
+    W = db.W
     spent = 0.0
     for b in seqs:
         codes, scales = O.fp4_pack(synth.cache_rows(db.N, 128, db.seed, "u", b, "cuda").cpu().numpy())
-        kv = f64(synth.cache_rows(db.N, 512, db.seed, "kv_cache", b, "cuda").to(torch.bfloat16))
-        if db.kv_fp4:
-            kv = O.kv_fp4_unpack(*O.kv_fp4_pack(kv.astype(np.float32)))
         lay = [{n: f64(v[b]) for n, v in db.layers[l].items()} for l in range(2)]
+        if db.kv_fp4:
+            # FP4 rows of the entries the step selects (packing all N rows here would
+            # take ~10 s a sequence; the step reads only these)
+            sel0 = O.topk_select(O.index_scores(lay[0]["q_idx"][0], lay[0]["w"][0], O.fp4_unpack(codes, scales),
+                                                db.N), db.k)
+            ids0 = np.sort(sel0[sel0 >= 0])
+            rows = synth.cache_rows(db.N, 512, db.seed, "kv_cache", b, "cuda")[torch.from_numpy(ids0).cuda()]
+            kvc, kvs = O.kv_fp4_pack(rows.cpu().numpy())
+        else:
+            kv = f64(synth.cache_rows(db.N, 512, db.seed, "kv_cache", b, "cuda").to(torch.bfloat16))
+        rings = []
+        if db.swa_fp8:
+            for l in range(2):
+                ring = np.zeros((W, 512), dtype=np.uint8)
+                O.swa_ring_append(ring, lay[l]["swa_kv"], np.arange(p - W + 1, p + 1))
+                rings.append(ring)
         t0 = time.perf_counter()
         kd = O.fp4_unpack(codes, scales)
         sel = O.topk_select(O.index_scores(lay[0]["q_idx"][0], lay[0]["w"][0], kd, db.N), db.k)
+        if db.kv_fp4:
+            j = np.searchsorted(ids0, sel[sel >= 0])
+            kv_a, sel_a = O.kv_fp4_unpack(kvc[j], kvs[j]), np.arange(j.size)
+        else:
+            kv_a, sel_a = kv, sel
         for l in range(2):
-            O.sparse_attention(lay[l]["q"][0], kv, sel, lay[l]["swa_kv"], pos0, p, db.W)
+            if db.swa_fp8:
+                O.swa_ring_append(rings[l], lay[l]["swa_kv"][W - 1:], [p])
+                win, w0 = O.swa_ring_rows(rings[l], p - W + 1, p), p - W + 1
+            else:
+                win, w0 = lay[l]["swa_kv"], pos0
+            O.sparse_attention(lay[l]["q"][0], kv_a, sel_a, win, w0, p, W)
         spent += time.perf_counter() - t0
-        del kv, kd
+        del kv_a, kd
     per_step = spent / len(seqs) * db.B
+    extra = (" (FP4 main KV: the selected rows dequantised" + ("; FP8 window ring: append + window read per layer)"
+                                                                if db.swa_fp8 else ")")) if db.kv_fp4 else ""
     return {"value": per_step * 1e6, "unit": "us/step", "cores": _cores(), "kind": "oracle",
             "sample": (f"{len(seqs)} of the {db.B} sequences (index-K dequantisation, scores over all {db.N} entries, "
-                       f"top-{db.k}, attention of the Reindex and the Reuse layer), {spent:.2f} s, extrapolated "
-                       f"by the sequence count; numpy float64, BLAS threads = {_cores()}"),
+                       f"top-{db.k}, attention of the Reindex and the Reuse layer{extra}), {spent:.2f} s, "
+                       f"extrapolated by the sequence count; numpy float64, BLAS threads = {_cores()}"),
+            "measured_s": round(spent, 2)}
+
+
+def cpu_baseline_append(ab):
+    """Oracle on this host for the decode append record: `compress_step` and, at
+    a group's last token, `index_k`, for every sequence over the m steps of one
+    group (the record's step); all B sequences, no sampling."""
+    import numpy as np
+    from oracle import csa2_oracle as O
+
+    def f64(x):
+        return x.detach().float().cpu().numpy().astype(np.float64)
+    xs = [f64(x) for x in ab.x]
+    w_kv, w_gate, w_ik, gamma = f64(ab.w_kv), f64(ab.w_gate), f64(ab.w_ik), f64(ab.gamma)
+    pos = [int(p[0].item()) for p in ab.pos]
+    reps, spent = 0, 0.0
+    while reps == 0 or spent < 2.0:
+        t0 = time.perf_counter()
+        for b in range(ab.B):
+            pending = []
+            for i in range(ab.m):
+                pending, ent = O.compress_step(pending, xs[i][b], w_kv, w_gate, gamma, pos[i], ab.m)
+                if ent is not None:
+                    g, lat, _ = ent
+                    O.index_k(lat[None], w_ik, np.array([g * ab.m]))
+        spent += time.perf_counter() - t0
+        reps += 1
+    per_step = spent / reps / ab.m
+    return {"value": per_step * 1e6, "unit": "us/token step", "cores": _cores(), "kind": "oracle",
+            "sample": (f"all {ab.B} sequences, the {ab.m} steps of one group (C and Z projections, pool; at the "
+                       f"group's last token RMSNorm, RoPE and the index-K row), {reps} run(s), {spent:.2f} s; "
+                       f"numpy float64, BLAS threads = {_cores()}"),
             "measured_s": round(spent, 2)}
 
 
@@ -764,6 +827,9 @@ def main():
             "attn_bytes_per_layer": fw["sparse_attn"]["bytes"],
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (fms * 1e-3), 4),
         }
+        if not args.no_cpu:
+            log("decode (FP4 main KV): cpu baseline (oracle, 4 of the sequences)")
+            out["decode_fp4kv"]["cpu_baseline"] = cpu_baseline_decode(fb)
         del fb
         torch.cuda.empty_cache()
     if not args.no_decode and not args.no_fp8swa:
@@ -790,6 +856,9 @@ def main():
             "attn_bytes_per_layer": ww["sparse_attn"]["bytes"],
             "step_frac_of_hbm_roofline": round(step_bytes / HBM_PEAK_GBS / 1e9 / (wms * 1e-3), 4),
         }
+        if not args.no_cpu:
+            log("decode (FP4 main KV, FP8 window ring): cpu baseline (oracle, 4 of the sequences)")
+            out["decode_fp4kv_fp8swa"]["cpu_baseline"] = cpu_baseline_decode(wb)
         del wb
         torch.cuda.empty_cache()
     if not args.no_hsi:
@@ -879,6 +948,9 @@ def main():
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": traffic_for("compress_step", ["k_compress.hip"])},
         }
+        if not args.no_cpu:
+            log("decode append: cpu baseline (oracle, all sequences)")
+            out["decode_append"]["cpu_baseline"] = cpu_baseline_append(ab)
         del ab
         torch.cuda.empty_cache()
     if not args.no_cpu:
