@@ -1293,10 +1293,11 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
 // Streaming path (no HSI): one workgroup of 8 waves per (query, part of up to
 // ST_MAXR consecutive entries).  Scores are filtered as they are computed: an
 // entry is staged in LDS (key and id) only if its key is at least theta, the k-th
-// best key among the entries the workgroup has scored so far.  Every entry it
-// drops scores below the query's k-th best, so it cannot be chosen.  When the
-// staged set could overflow (and once after the first 4096 entries, to set
-// theta), it is cut back to its k best, which raises theta; so the block-wide
+// best key among the entries the workgroup had scored at its last cutback.  Every
+// entry it drops scores below the query's k-th best, so it cannot be chosen.  The
+// staged count is checked every ST_CHECK rounds; when the next ST_CHECK rounds
+// could overflow the staging (and once after the first 4096 entries, to set
+// theta), the staged set is cut back to its k best, which raises theta; so the block-wide
 // selection runs a few times per part instead of once per 4096 entries, and the
 // scan keeps the loads streaming.  The part's k best leave in id order: as the
 // query's top-k when one part covers its visible entries, else as a candidate
@@ -1308,6 +1309,8 @@ constexpr int ST_CAP = 4096;           // staged candidates
 constexpr int ST_MAXR = 65536;         // entries per part at most (an id bitmap of 2048 words)
 constexpr int ST_WPT = ST_MAXR / 32 / ST_THREADS;   // bitmap words per thread
 constexpr int ST_FIRST = 4096;         // entries scored before theta is first set
+constexpr int ST_CHECK = 4;            // rounds between checks of the staged count
+static_assert(ST_CAP - ST_CHECK * ST_ROUND >= CSA2_MAX_TOPK, "a cutback must leave room for ST_CHECK rounds");
 
 struct StreamSmem {
   SelSmem<ST_THREADS> sel;
@@ -1481,12 +1484,16 @@ __global__ __launch_bounds__(ST_THREADS) void score_stream(
         S.id[sl] = base + j;
       }
     }
+    // the staged count is checked (two barriers) every ST_CHECK rounds and after the
+    // last; a cutback leaves room for ST_CHECK more rounds, so the staging between
+    // two checks cannot overflow
+    if (i % ST_CHECK != ST_CHECK - 1 && i + 1 < n_rounds) return;
     __syncthreads();
     const uint32_t c = S.cnt;
     __syncthreads();   // every thread has read the count before the next round adds to it
     const int seen = min(n_here, (i + 1) * ST_ROUND);
-    if (i + 1 < n_rounds &&
-        (c > (uint32_t)(ST_CAP - ST_ROUND) || (theta == 0u && seen >= ST_FIRST && c >= (uint32_t)k))) {
+    if (i + 1 < n_rounds && (c > (uint32_t)(ST_CAP - ST_CHECK * ST_ROUND) ||
+                             (theta == 0u && seen >= ST_FIRST && c >= (uint32_t)k))) {
       uint32_t th, lb_unused;
       const uint32_t got = st_choose(S, (int)c, (uint32_t)k, 0u, base, n_here, th, lb_unused,
                                      [&](uint32_t r, uint32_t key, int32_t id) {
