@@ -1302,7 +1302,7 @@ __global__ __launch_bounds__(MG_THREADS) void topk_merge(const uint32_t* __restr
 // scan keeps the loads streaming.  The part's k best leave in id order: as the
 // query's top-k when one part covers its visible entries, else as a candidate
 // list for topk_merge with a lower bound of the part's rank-r0 key.
-constexpr int ST_THREADS = 512;    // two workgroups per CU
+constexpr int ST_THREADS = 512;    // two workgroups per CU (bf16; see the launch bounds)
 constexpr int ST_NW = ST_THREADS / 64;
 constexpr int ST_ROUND = ST_NW * 64;   // entries scored per round: one super-tile per wave
 constexpr int ST_CAP = 4096;           // staged candidates
@@ -1323,20 +1323,32 @@ struct StreamSmem {
   uint32_t cnt, theta;
 };
 
-// Exclusive prefix counts of the set bits of words [0, nw) of S.bits into S.wpre.
-__device__ __forceinline__ void st_bit_prefix(StreamSmem& S, int nw) {
-  uint32_t pc[ST_WPT], tot = 0;
+// The staging one selection works on: keys and ids of the staged candidates,
+// the id bitmap and its word prefix counts, and the block-wide selection memory.
+struct StView {
+  SelSmem<ST_THREADS>* sel;
+  uint32_t* key;
+  int32_t* id;
+  uint32_t* bits;
+  uint32_t* wpre;
+};
+
+// Exclusive prefix counts of the set bits of words [0, nw) of S.bits into S.wpre
+// (WPT bitmap words per thread).
+template <int WPT>
+__device__ __forceinline__ void st_bit_prefix(const StView& S, int nw) {
+  uint32_t pc[WPT], tot = 0;
 #pragma unroll
-  for (int j = 0; j < ST_WPT; ++j) {
-    const int wi = threadIdx.x * ST_WPT + j;
+  for (int j = 0; j < WPT; ++j) {
+    const int wi = threadIdx.x * WPT + j;
     pc[j] = wi < nw ? (uint32_t)__popc(S.bits[wi]) : 0u;
     tot += pc[j];
   }
   uint32_t total;
-  uint32_t pre = block_prefix_excl<ST_THREADS>(tot, S.sel, total);
+  uint32_t pre = block_prefix_excl<ST_THREADS>(tot, *S.sel, total);
 #pragma unroll
-  for (int j = 0; j < ST_WPT; ++j) {
-    const int wi = threadIdx.x * ST_WPT + j;
+  for (int j = 0; j < WPT; ++j) {
+    const int wi = threadIdx.x * WPT + j;
     if (wi < nw) S.wpre[wi] = pre;
     pre += pc[j];
   }
@@ -1344,24 +1356,24 @@ __device__ __forceinline__ void st_bit_prefix(StreamSmem& S, int nw) {
 }
 
 // Rank of id offset r among the set bits of S.bits (valid after st_bit_prefix).
-__device__ __forceinline__ uint32_t st_rank(const StreamSmem& S, int r) {
+__device__ __forceinline__ uint32_t st_rank(const StView& S, int r) {
   return S.wpre[r >> 5] + (uint32_t)__popc(S.bits[r >> 5] & ((1u << (r & 31)) - 1u));
 }
 
 // Chooses the `need` best of the c staged candidates (ties to the smaller id; ids
-// lie in [base, base + range)) and calls put(rank, key, id) for each, rank being
-// its position in id order; returns how many were chosen.  thresh receives a
-// value at or below the smallest chosen key; with r0 != 0, lb a lower bound of
-// the rank-r0 key.
-template <typename Put>
-__device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, int base, int range,
+// lie in [base, base + range), range <= 32 WPT ST_THREADS) and calls put(rank,
+// key, id) for each, rank being its position in id order; returns how many were
+// chosen.  thresh receives a value at or below the smallest chosen key; with
+// r0 != 0, lb a lower bound of the rank-r0 key.
+template <int WPT, typename Put>
+__device__ uint32_t st_choose(const StView& S, int c, uint32_t need, uint32_t r0, int base, int range,
                               uint32_t& thresh, uint32_t& lb, Put put) {
   auto key_at = [&](int i) -> uint32_t { return S.key[i]; };
   uint32_t mn, mx, nv;
-  key_stats<ST_THREADS>(key_at, c, S.sel, mn, mx, nv);
+  key_stats<ST_THREADS>(key_at, c, *S.sel, mn, mx, nv);
   if (need > nv) need = nv;
   const SelOut sel = (need == nv && r0 == 0) ? SelOut{mn, 0xFFFFFFFFu, 0u}
-                                             : select_threshold<ST_THREADS>(key_at, c, need, mn, mx, r0, S.sel, true);
+                                             : select_threshold<ST_THREADS>(key_at, c, need, mn, mx, r0, *S.sel, true);
   thresh = sel.thresh;
   lb = sel.lb;
   const int nw = (range + 31) >> 5;
@@ -1375,7 +1387,7 @@ __device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, 
         atomicOr(&S.bits[r >> 5], 1u << (r & 31));
       }
     __syncthreads();
-    st_bit_prefix(S, nw);
+    st_bit_prefix<WPT>(S, nw);
     for (int i = threadIdx.x; i < c; i += ST_THREADS)
       if (S.key[i] == sel.thresh && st_rank(S, S.id[i] - base) >= sel.eq_take) S.key[i] = 0u;
     __syncthreads();
@@ -1390,7 +1402,7 @@ __device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, 
     }
   }
   __syncthreads();
-  st_bit_prefix(S, nw);
+  st_bit_prefix<WPT>(S, nw);
   for (int i = threadIdx.x; i < c; i += ST_THREADS) {
     const uint32_t kk = S.key[i];
     if (kk != 0u && kk >= sel.thresh) put(st_rank(S, S.id[i] - base), kk, S.id[i]);
@@ -1399,14 +1411,17 @@ __device__ uint32_t st_choose(StreamSmem& S, int c, uint32_t need, uint32_t r0, 
   return need;
 }
 
+// bf16: at most 128 VGPRs, so that two workgroups (16 waves) share a CU; the
+// compiler's own choice (145) left room for one, and the scan ran 27% slower
 template <typename T, int SF>
-__global__ __launch_bounds__(ST_THREADS) void score_stream(
+__global__ __launch_bounds__(ST_THREADS, sizeof(T) == 2 ? 4 : 2) void score_stream(
     const T* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const int32_t* __restrict__ q_pos, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_idx, uint32_t* __restrict__ chunk_lb, int32_t* __restrict__ topk,
     float* __restrict__ scores_out, int T_len, int H_I, int N_cap, int n_entries, int m, int R, int n_parts, int k,
     int k_chunk) {
   __shared__ StreamSmem S;
+  const StView V{&S.sel, S.key, S.id, S.bits, S.wpre};
   const int part = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int bt = b * T_len + t;
   const int n_t = visible(q_pos, bt, m, n_entries);
@@ -1495,7 +1510,7 @@ __global__ __launch_bounds__(ST_THREADS) void score_stream(
     if (i + 1 < n_rounds && (c > (uint32_t)(ST_CAP - ST_CHECK * ST_ROUND) ||
                              (theta == 0u && seen >= ST_FIRST && c >= (uint32_t)k))) {
       uint32_t th, lb_unused;
-      const uint32_t got = st_choose(S, (int)c, (uint32_t)k, 0u, base, n_here, th, lb_unused,
+      const uint32_t got = st_choose<ST_WPT>(V, (int)c, (uint32_t)k, 0u, base, n_here, th, lb_unused,
                                      [&](uint32_t r, uint32_t key, int32_t id) {
                                        S.tkey[r] = key;
                                        S.tid[r] = id;
@@ -1533,12 +1548,12 @@ __global__ __launch_bounds__(ST_THREADS) void score_stream(
   uint32_t th, lb;
   if (direct) {
     int32_t* out = topk + (size_t)bt * k;
-    const uint32_t got = st_choose(S, c, (uint32_t)k, 0u, base, n_here, th, lb,
+    const uint32_t got = st_choose<ST_WPT>(V, c, (uint32_t)k, 0u, base, n_here, th, lb,
                                    [&](uint32_t r, uint32_t, int32_t id) { out[r] = id; });
     for (int i = (int)got + threadIdx.x; i < k; i += ST_THREADS) out[i] = -1;
   } else {
     const size_t obase = ((size_t)bt * n_parts + part) * k_chunk;
-    const uint32_t got = st_choose(S, c, (uint32_t)k, r0, base, n_here, th, lb,
+    const uint32_t got = st_choose<ST_WPT>(V, c, (uint32_t)k, r0, base, n_here, th, lb,
                                    [&](uint32_t r, uint32_t key, int32_t id) {
                                      cand_key[obase + r] = key;
                                      cand_idx[obase + r] = id;
@@ -1795,8 +1810,10 @@ __device__ __forceinline__ int wave_boundary_bin(const uint32_t* hist, uint32_t 
   return __shfl(hit, src, 64);
 }
 
+// Rows of up to 4096 keys: at most 128 VGPRs, so that four workgroups share a CU
+// (the compiler's own choice, 175, left room for two: 10% slower).
 template <int KPT>
-__global__ __launch_bounds__(SC_THREADS) void select_rows(const uint32_t* __restrict__ keys,
+__global__ __launch_bounds__(SC_THREADS, KPT <= 64 ? 4 : 1) void select_rows(const uint32_t* __restrict__ keys,
                                                           const int32_t* __restrict__ q_pos,
                                                           int32_t* __restrict__ topk, int T_len, int n_entries,
                                                           int m, int n_scan, int k) {
