@@ -781,36 +781,45 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const bf16* __restrict_
   const float* ls_q = part_lse + qi * n_splits * H + h;                    // split s at s * H
   const bf16* po_q = part_o + (qi * n_splits * H + h) * 512 + d0;          // split s at s * H * 512
   const float s2 = sink_log2(sink, h, H);   // the head's sink logit, counted once here
+  // online merge, eight splits at a time: their log-sum-exps and partial rows are
+  // loaded together, then the running maximum (which starts at the sink) is raised
+  // to theirs and the sums rescaled, so a call costs one load round per eight
+  // splits (an empty split's row is read but not used: its log-sum-exp is -inf)
   float mx = s2;
-#pragma unroll 8
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, ls_q[(size_t)s * H]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, den = 0.f;
-  // four splits' partials in flight at a time (an empty split's row is read but
-  // not used: its log-sum-exp is -inf)
-  auto add = [&](float ls, const uint4& a) {   // a: 8 bf16 dims
-    if (ls == -INFINITY) return;
-    const float wgt = exp2f(ls - mx);
-    den += wgt;
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  constexpr int CB = 8;
+  for (int s = 0; s < n_splits; s += CB) {
+    float ls[CB];
+    uint4 a[CB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wgt * __uint_as_float(w[i] << 16);
-      acc[2 * i + 1] += wgt * __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int u = 0; u < CB; ++u) {
+      const bool in = s + u < n_splits;
+      ls[u] = in ? ls_q[(size_t)(s + u) * H] : -INFINITY;
+      a[u] = in ? *reinterpret_cast<const uint4*>(po_q + (size_t)(s + u) * H * 512) : make_uint4(0, 0, 0, 0);
     }
-  };
-  int s = 0;
-  for (; s + 4 <= n_splits; s += 4) {
-    float ls[4];
-    uint4 a[4];
+    float cm = ls[0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ls[u] = ls_q[(size_t)(s + u) * H];
-      a[u] = *reinterpret_cast<const uint4*>(po_q + (size_t)(s + u) * H * 512);
+    for (int u = 1; u < CB; ++u) cm = fmaxf(cm, ls[u]);
+    if (cm > mx) {   // mx = -inf (nothing yet) gives the factor 0 on the zero sums
+      const float f = exp2f(mx - cm);
+      den *= f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= f;
+      mx = cm;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) add(ls[u], a[u]);
+    for (int u = 0; u < CB; ++u) {
+      if (ls[u] == -INFINITY) continue;
+      const float wgt = exp2f(ls[u] - mx);
+      den += wgt;
+      const uint32_t w[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wgt * __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] += wgt * __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
   }
-  for (; s < n_splits; ++s) add(ls_q[(size_t)s * H], *reinterpret_cast<const uint4*>(po_q + (size_t)s * H * 512));
   if (s2 != -INFINITY) den += exp2f(s2 - mx);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   bf16* orow = o + (qi * H + h) * 512 + d0;
