@@ -7,7 +7,9 @@ outputs (entries, queries, rows) is recomputed one by one by the CPU oracle.
 * decoder macro-block, m=1, L=32768: Full (from one hidden tensor), Reindex, Reuse,
   Reuse;
 * batched decode, 64 sequences x 131072 m=2 entries, Reindex + Reuse (the
-  benchmark's DecodeBench itself), with bf16 and with FP4 main KV;
+  benchmark's DecodeBench itself), with bf16 and with FP4 main KV, and with a
+  planted top-512 set (entries scoring far above the rest) that must be selected
+  exactly;
 * 1M-context decode with the HSI candidate pool: 4 sequences x 524288 entries,
   Full layer (flat top-512 + 256 blocks of 64) then Reindex within the pool.
 
@@ -258,6 +260,69 @@ def test_batched_decode_full_size(K):
             worst = max(worst, err)
     say(f"  exact sets {n_exact}/{len(sample)}, attention compared for all, worst row rel err {worst:.2e}")
     assert n_exact >= len(sample) - 1
+
+
+def test_batched_decode_planted_full_size(K):
+    """The batched decode workload (64 x 131072 entries) with 512 entries of 8 of
+    the sequences planted: their pre-quantisation index-K rows point along the
+    layer's positively weighted indexer heads, so they outscore every other entry
+    by far more than the band rule's 1e-3 (checked on the oracle's scores).  The
+    GPU's top-512 of those sequences must then be exactly the planted set, and
+    their attention outputs match the oracle's over it."""
+    import bench
+    say("case: batched decode 64 x 131072 entries with planted top-512 sets")
+    db = bench.DecodeBench(torch, K, synth)
+    gen = np.random.default_rng(97)
+    seqs = [0, 9, 18, 27, 36, 45, 54, 63]
+    r = db.layers[0]
+    planted = {}
+    for b in seqs:
+        ids = np.sort(gen.choice(db.N, db.k, replace=False))
+        qi, wv = f64(r["q_idx"][b, 0]), f64(r["w"][b, 0])
+        v = (np.maximum(wv, 0.0)[:, None] * qi).sum(0)
+        v /= np.linalg.norm(v)
+        rows = (v[None, :] * (8.0 + 4.0 * gen.random((db.k, 1)))
+                + 0.05 * gen.standard_normal((db.k, 128))).astype(np.float32)
+        c_o, s_o = O.fp4_pack(rows)
+        c_g = torch.empty(db.k, 64, dtype=torch.uint8, device=DEV)
+        s_g = torch.empty(db.k, 4, dtype=torch.uint8, device=DEV)
+        K.csa2_fp4_pack(torch.from_numpy(rows).to(DEV), c_g, s_g)
+        torch.cuda.synchronize()
+        assert np.array_equal(c_g.cpu().numpy(), c_o) and np.array_equal(s_g.cpu().numpy(), s_o), "planted FP4 rows"
+        idx = torch.from_numpy(ids).to(DEV)
+        db.codes[b][idx] = c_g
+        db.scales[b][idx] = s_g
+        planted[b] = (ids, c_o, s_o)
+    db.step()
+    torch.cuda.synchronize()
+    topk = db.topk.cpu().numpy()
+    p = int(db.q_pos[0, 0].item())
+    pos0 = int(db.swa_pos0[0].item())
+    worst = 0.0
+    for b in seqs:
+        ids, c_o, s_o = planted[b]
+        u = synth.cache_rows(db.N, 128, db.seed, "u", b, DEV).cpu().numpy()
+        codes_o, scales_o = O.fp4_pack(u)
+        codes_o[ids], scales_o[ids] = c_o, s_o
+        kd = O.fp4_unpack(codes_o, scales_o)
+        sc = O.index_scores(f64(r["q_idx"][b, 0]), f64(r["w"][b, 0]), kd, db.N)
+        del kd, u
+        others = np.delete(sc, ids)
+        margin = sc[ids].min() / max(others.max(), 1e-30) - 1.0
+        assert sc[ids].min() > 0 and margin > 1e-2, f"b{b}: planting left a margin of {margin:.2e} only"
+        assert np.array_equal(topk[b, 0], ids), f"b{b}: the top-k is not the planted set"
+        kv_b = synth.cache_rows(db.N, 512, db.seed, "kv_cache", b, DEV).to(torch.bfloat16)
+        rows = f64(kv_b[torch.from_numpy(ids.astype(np.int64)).to(DEV)])
+        del kv_b
+        for li in range(2):
+            lay = db.layers[li]
+            ref, _, _ = O.sparse_attention(f64(lay["q"][b, 0]), rows, np.arange(rows.shape[0]), f64(lay["swa_kv"][b]),
+                                           pos0, p, db.W)
+            err = row_rel_err(f64(db.o[li][b, 0]), ref)
+            assert err <= TOL, f"planted decode b{b} layer{li}: {err:.3e}"
+            worst = max(worst, err)
+        say(f"  b{b}: planted set selected exactly (score margin {margin:.2f})")
+    say(f"  {len(seqs)} sequences, worst attention row rel err {worst:.2e}")
 
 
 def test_batched_decode_fp4_kv_full_size(K):
