@@ -261,13 +261,14 @@ def csa2_score_topk(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m:
 
 def csa2_score_topk_noalloc(rt, q_idx, w, codes, scales, q_pos, topk, n_entries: int, m: int, k: int,
                             N_cap: Optional[int] = None, hsi: int = HSI_NONE, hsi_s: int = 0, hsi_nb: int = 0,
-                            candidates=None, stream=None):
+                            candidates=None, stream=None, scale_fmt: int = SCALE_E4M3):
     """csa2_score_topk with the library's fixed device scratch (no workspace, no
     allocation): for callers that cannot allocate."""
     if N_cap is None:
         N_cap = codes.shape[1]
     a = score_topk_args(q_idx=q_idx, w=w, codes=codes, scales=scales, q_pos=q_pos, topk=topk, n_entries=n_entries,
-                        m=m, k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates)
+                        m=m, k=k, N_cap=N_cap, hsi=hsi, hsi_s=hsi_s, hsi_nb=hsi_nb, candidates=candidates,
+                        scale_fmt=scale_fmt)
     _check(lib().csa2_score_topk_noalloc(_rt(rt), C.byref(a), _stream(stream)))
 
 

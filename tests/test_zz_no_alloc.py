@@ -1,9 +1,10 @@
 """The no-alloc score/top-k entry point (csa2_score_topk_noalloc, fixed device
 scratch inside the library) against csa2_score_topk with a caller workspace, on
-two calls in a row through the C ABI, the second with a smaller input (and the
-HSI pool build, which uses more of the scratch's regions): top-k ids and pool
-blocks must be bit-identical.  Also: a call too large for the scratch is refused
-before anything is enqueued."""
+calls in a row through the C ABI, each with a smaller input than the one before:
+a flat scan, then an HSI pool build with the merge pre-filter (which use more of
+the scratch's regions), then a flat scan over UE8M0-scaled index K: top-k ids
+and pool blocks must be bit-identical.  Also: a call too large for the scratch is
+refused before anything is enqueued."""
 import ctypes as C
 
 import pytest
@@ -25,23 +26,31 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _inputs(B, N, seed, H_I=32):
+def _inputs(B, N, seed, H_I=32, ue8m0=False):
     codes = torch.empty(B, N, 64, dtype=torch.uint8, device=DEV)
     scales = torch.empty(B, N, 4, dtype=torch.uint8, device=DEV)
     for b in range(B):
-        K.csa2_fp4_pack(synth.cache_rows(N, 128, seed, "u", b, DEV), codes[b], scales[b])
+        u = synth.cache_rows(N, 128, seed, "u", b, DEV)
+        if ue8m0:   # UE8M0 block scales, packed by the oracle's encoder
+            from oracle import csa2_oracle as O
+            c, sc = O.fp4_pack(u.cpu().numpy(), 32, O.SCALE_UE8M0)
+            codes[b], scales[b] = torch.from_numpy(c).to(DEV), torch.from_numpy(sc).to(DEV)
+        else:
+            K.csa2_fp4_pack(u, codes[b], scales[b])
     q = synth.decode_query_inputs(B, 8, H_I, 8, seed=seed, dtype=torch.bfloat16, device=DEV)
     return codes, scales, q["q_idx"], q["w"]
 
 
 def test_noalloc_matches_workspace_entry_on_two_calls():
     m, k = 2, 512
-    calls = [dict(B=16, N=65536, hsi=K.HSI_NONE, s=0, nb=0, seed=81),
-             dict(B=4, N=20000, hsi=K.HSI_BUILD, s=64, nb=32, seed=82)]
+    sf_ue = K.SCALE_UE8M0
+    calls = [dict(B=16, N=65536, hsi=K.HSI_NONE, s=0, nb=0, seed=81, sf=K.SCALE_E4M3),
+             dict(B=4, N=100000, hsi=K.HSI_BUILD, s=64, nb=32, seed=82, sf=K.SCALE_E4M3),
+             dict(B=2, N=30000, hsi=K.HSI_NONE, s=0, nb=0, seed=83, sf=sf_ue)]
     refs, outs = [], []
     data = []
     for c in calls:
-        codes, scales, q_idx, w = _inputs(c["B"], c["N"], c["seed"])
+        codes, scales, q_idx, w = _inputs(c["B"], c["N"], c["seed"], ue8m0=c["sf"] == sf_ue)
         q_pos = torch.full((c["B"], 1), c["N"] * m - 1 - 3, dtype=torch.int32, device=DEV)
         data.append((codes, scales, q_idx, w, q_pos))
     # reference: the workspace entry point
@@ -49,14 +58,15 @@ def test_noalloc_matches_workspace_entry_on_two_calls():
         tk = torch.full((c["B"], 1, k), -7, dtype=torch.int32, device=DEV)
         cand = torch.full((c["B"], 1, max(c["nb"], 1)), -7, dtype=torch.int32, device=DEV)
         K.csa2_score_topk(None, q_idx, w, codes, scales, q_pos, tk, n_entries=c["N"], m=m, k=k, hsi=c["hsi"],
-                          hsi_s=c["s"], hsi_nb=c["nb"], candidates=cand if c["hsi"] else None)
+                          hsi_s=c["s"], hsi_nb=c["nb"], candidates=cand if c["hsi"] else None, scale_fmt=c["sf"])
         refs.append((tk, cand))
     # the no-alloc entry point: two calls in a row, the second smaller
     for c, (codes, scales, q_idx, w, q_pos) in zip(calls, data):
         tk = torch.full((c["B"], 1, k), -5, dtype=torch.int32, device=DEV)
         cand = torch.full((c["B"], 1, max(c["nb"], 1)), -5, dtype=torch.int32, device=DEV)
         K.csa2_score_topk_noalloc(None, q_idx, w, codes, scales, q_pos, tk, n_entries=c["N"], m=m, k=k,
-                                  hsi=c["hsi"], hsi_s=c["s"], hsi_nb=c["nb"], candidates=cand if c["hsi"] else None)
+                                  hsi=c["hsi"], hsi_s=c["s"], hsi_nb=c["nb"], candidates=cand if c["hsi"] else None,
+                                  scale_fmt=c["sf"])
         outs.append((tk, cand))
     torch.cuda.synchronize()
     for i, c in enumerate(calls):
