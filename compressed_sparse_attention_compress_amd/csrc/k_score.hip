@@ -10,7 +10,7 @@
 // Ties go to the smaller entry id; -0 and +0 are equal.
 //
 // Dequantisation (every bf16 path): a key element is an E2M1 value times an E4M3
-// block scale, exact in fp16.  v_cvt_scalef32_pk_f16_fp4 expands the codes and
+// block scale, exact in fp16 (UE8M0 scales: see below).  v_cvt_scalef32_pk_f16_fp4 expands the codes and
 // applies the power of two of the scale, one v_pk_mul_f16 applies its sign and
 // significand, so the block scale sits inside the MFMA operand and the four
 // 32-dim blocks of a key chain into one v_mfma_f32_16x16x32_f16 accumulator.  The
@@ -34,10 +34,15 @@
 // entries scoring at least the k-th best seen so far and cuts them back to the k
 // best a few times per part, so a query costs a few selections instead of one per
 // chunk plus a merge.
+// Kernel topk_prefilter (queries with many chunks): workgroups over groups of
+// chunks drop the candidates below the merge bound before the merge stages them.
 // Kernel topk_merge: one workgroup per query: the select over all chunk
 // candidates at or above the merge bound, indices sorted ascending and padded
 // with -1; with HSI BUILD also the n_b best blocks (newest block forced) as the
 // pool.
+// Index-K scales are E4M3 or UE8M0 (a template argument of every scorer); with
+// UE8M0 the fp16 operand takes each block's power of two relative to the entry's
+// largest, which multiplies the entry's dot products afterwards.
 #include "csa2_internal.h"
 #include "device_common.h"
 #include "lds_dma.h"
