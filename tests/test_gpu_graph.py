@@ -59,3 +59,11 @@ def test_prefill_step_graph_replay(K):
     say("case: prefill step (compress, index K, score/top-k, attention) as a HIP graph, L=1024, hidden 512")
     pb = bench.PrefillBench(torch, K, synth, L=1024, D=512)
     _replays_match(pb.step, [pb.lat, pb.kv, pb.codes, pb.scales, pb.topk, pb.o])
+
+
+def test_hsi_decode_step_graph_replay(K):
+    import bench
+    say("case: HSI decode step (Full scan + pool build with the merge pre-filter, pool scan, two attention calls) "
+        "as a HIP graph, 4 x 131072 entries")
+    hb = bench.HsiDecodeBench(torch, K, synth, B=4, n_entries=131072, copies=1)
+    _replays_match(hb.step, [hb.tk[0], hb.tk[1], hb.cand, hb.o[0], hb.o[1]])
