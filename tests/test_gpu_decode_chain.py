@@ -35,14 +35,20 @@ def npy(t):
     return t.detach().float().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,kv_fp4", [(torch.bfloat16, False), (torch.float32, False), (torch.bfloat16, True)])
-def test_decode_chain_through_the_runtime(dtype, kv_fp4):
+@pytest.mark.parametrize("dtype,kv_fp4,sfmt", [(torch.bfloat16, False, "e4m3"), (torch.float32, False, "e4m3"),
+                                               (torch.bfloat16, True, "e4m3"), (torch.bfloat16, False, "ue8m0")])
+def test_decode_chain_through_the_runtime(dtype, kv_fp4, sfmt):
+    """sfmt: scale format of the index K the prefill and the appends write; the
+    Full layer's own selection, the Reindex layer and the oracle read it from the
+    index_k slot."""
     B, m, P, S = 2, 2, 16, 5
     D = 512 if dtype == torch.bfloat16 else 256
     H_I, H, k, W = 4, 8, 8, 8
     L = P + S
     N_cap = L // m + 3
-    say(f"case: decode chain dtype={dtype} fp4kv={kv_fp4} B={B} m={m} prefill {P} + {S} appends, k={k}")
+    say(f"case: decode chain dtype={dtype} fp4kv={kv_fp4} index-K scales {sfmt} B={B} m={m} prefill {P} + {S} "
+        f"appends, k={k}")
+    gfmt = K.SCALE_UE8M0 if sfmt == O.SCALE_UE8M0 else K.SCALE_E4M3
     shape = synth.LayerShape(B=B, L=L, D=D, m=m, H_I=H_I, k=k, W=W, H=H)
     inp = [synth.full_layer_inputs(shape, 91, dtype, DEV, layer=l, with_x=(l == 0)) for l in range(3)]
     f = inp[0]
@@ -60,7 +66,7 @@ def test_decode_chain_through_the_runtime(dtype, kv_fp4):
         kv_sc = None
     codes = torch.zeros(B, N_cap, 64, dtype=torch.uint8, device=DEV)
     scales = torch.zeros(B, N_cap, 4, dtype=torch.uint8, device=DEV)
-    cfg_full = K.layer_cfg(K.FULL, cd, m=m, k=k, W=W, H_I=H_I, H=H, kv_fmt=fmt)
+    cfg_full = K.layer_cfg(K.FULL, cd, m=m, k=k, W=W, H_I=H_I, H=H, kv_fmt=fmt, scale_fmt=gfmt)
     o_pre = torch.empty_like(f["q"][:, :P]).contiguous()
     tk_pre = torch.empty(B, P, k, dtype=torch.int32, device=DEV)
     kw = dict(B=B, T=P, q_pos=f["q_pos"][:, :P].contiguous(), q=f["q"][:, :P].contiguous(), swa_kv=f["swa_kv"],
@@ -87,7 +93,7 @@ def test_decode_chain_through_the_runtime(dtype, kv_fp4):
         xs = torch.stack([f["x"][b, max(pos[b], 0)] for b in range(B)]).contiguous()
         step_ws = K.csa2_compress_step(rt, xs, torch.tensor(pos, dtype=torch.int32, device=DEV), f["w_kv"],
                                        f["w_gate"], f["gamma"], f["w_ik"], state, kv, codes, scales, m=m,
-                                       workspace=step_ws, kv_scales=kv_sc, n_entries=n_ent)
+                                       workspace=step_ws, kv_scales=kv_sc, n_entries=n_ent, scale_fmt=gfmt)
         assert rt.slot(K.SLOT_COMPRESS_KV).cols == n_ent and rt.slot(K.SLOT_INDEX_K).cols == n_ent
     n_ent = rt.slot(K.SLOT_INDEX_K).cols
     p_last = [done[0], done[1]]
@@ -123,7 +129,7 @@ def test_decode_chain_through_the_runtime(dtype, kv_fp4):
     # ---- oracle: the same chain
     ort = O.Runtime()
     ocfg = O.LayerConfig(O.FULL, m=m, k=k, W=W, w_kv=npy(f["w_kv"]), w_gate=npy(f["w_gate"]), gamma=npy(f["gamma"]),
-                         w_ik=npy(f["w_ik"]), kv_fp4=kv_fp4)
+                         w_ik=npy(f["w_ik"]), kv_fp4=kv_fp4, scale_fmt=sfmt)
     O.layer_forward(ort, ocfg, O.LayerInputs(q=npy(f["q"][:, :P]), swa_kv=npy(f["swa_kv"]),
                                              q_pos=npy(f["q_pos"][:, :P]), swa_pos0=npy(f["swa_pos0"]),
                                              q_idx=npy(f["q_idx"][:, :P]), w=npy(f["w"][:, :P]),
@@ -148,7 +154,8 @@ def test_decode_chain_through_the_runtime(dtype, kv_fp4):
     # every selection is a valid top-k of the oracle's scores over the grown index K,
     # and on these seeded inputs equal to the oracle's; at least one selection holds
     # an appended entry (else the test could not tell a stale entry count)
-    kd = [O.fp4_unpack(ort.index_k[0][b], ort.index_k[1][b]) for b in range(B)]
+    assert ort.index_k_fmt == sfmt and rt.slot(K.SLOT_INDEX_K).kv_fmt == gfmt
+    kd = [O.fp4_unpack(ort.index_k[0][b], ort.index_k[1][b], scale_fmt=sfmt) for b in range(B)]
     appended_seen = False
     for l in range(3):
         src = 0 if l == 0 else 1
