@@ -223,6 +223,9 @@ csa2_status resolve_attn(const csa2_runtime* rt, csa2_sparse_attn_args& a) {
       "csa2_sparse_attn: an FP8 window ring of L_w = %d rows cannot serve a window of W = %d", a.L_w, a.W);
   REQ(a.swa_fmt != CSA2_SWA_FP8_RING || ((uintptr_t)a.swa_kv & 15u) == 0, CSA2_ERR_INVALID_ARG,
       "csa2_sparse_attn: the FP8 window ring must be 16-byte aligned");
+  REQ((((uintptr_t)a.q | (uintptr_t)a.o) & 15u) == 0 && (a.kv_fmt == CSA2_KV_FP4 || ((uintptr_t)a.kv & 15u) == 0) &&
+          (a.swa_fmt == CSA2_SWA_FP8_RING || ((uintptr_t)a.swa_kv & 15u) == 0),
+      CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: q, o and dense kv and window rows must be 16-byte aligned");
   return CSA2_OK;
 }
 

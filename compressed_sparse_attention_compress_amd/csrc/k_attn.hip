@@ -822,9 +822,10 @@ __global__ __launch_bounds__(256) void attn_combine_bf16(const bf16* __restrict_
   }
   if (s2 != -INFINITY) den += exp2f(s2 - mx);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  bf16* orow = o + (qi * H + h) * 512 + d0;
+  bf16x8 ov;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) orow[i] = (bf16)(acc[i] * inv);
+  for (int i = 0; i < 8; ++i) ov[i] = (bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8*>(o + (qi * H + h) * 512 + d0) = ov;
   if (lse != nullptr && d0 == 0) lse[qi * H + h] = den > 0.f ? (mx + log2f(den)) * 0.69314718055994531f : -INFINITY;
 }
 

@@ -332,6 +332,7 @@ csa2_status csa2_score_topk_noalloc(csa2_runtime* rt, const csa2_score_topk_args
  *
  *   q        [B, T, H, 512] dtype        RoPE already applied
  *   kv       [B, N_cap, 512] dtype       NULL -> runtime compress_kv slot
+ *            (q, o, dense kv and dense swa_kv 16-byte aligned, else CSA2_ERR_INVALID_ARG)
  *   topk     [B, T, k] int32             NULL -> runtime topk_idxs slot; -1 = empty,
  *                                        ids outside [0, N_cap) are skipped
  *   swa_kv   [B, L_w, 512] dtype         the layer's window KV, row j = position swa_pos0[b] + j

@@ -174,6 +174,9 @@ def test_hsi_use_needs_candidates():
 @pytest.mark.parametrize("field,value,status", [
     ("H", 65, "CSA2_ERR_SHAPE"), ("W", 0, "CSA2_ERR_SHAPE"), ("k", 1100, "CSA2_ERR_SHAPE"),
     ("q", None, "CSA2_ERR_INVALID_ARG"), ("kv", None, "CSA2_ERR_INVALID_ARG"),
+    # rows and queries are read, and outputs written, 16 bytes at a time
+    ("q", 0x1008, "CSA2_ERR_INVALID_ARG"), ("o", 0x1004, "CSA2_ERR_INVALID_ARG"),
+    ("kv", 0x1002, "CSA2_ERR_INVALID_ARG"), ("swa_kv", 0x1008, "CSA2_ERR_INVALID_ARG"),
 ])
 def test_attn_validation(field, value, status):
     a = K.SparseAttnArgs(dtype=1, B=1, T=1, H=64, N_cap=100, k=512, L_w=128, W=128, q=0x1000, kv=0x1000,
