@@ -17,6 +17,8 @@
 // 2 or 4 tokens entirely in registers.  Output: the pooled entry in float32.
 // Kernel 2 (compress_finalize): one wave per entry: RMSNorm in float32, write the
 // pre-RoPE latent (float32, in place) and the cache row with RoPE applied.
+// m == 1 with a bf16 cache (compress_m1_bf16): one kernel; a workgroup holds 128
+// whole 512-channel rows and finishes them in its epilogue.
 #include "csa2_internal.h"
 #include "device_common.h"
 #include "lds_dma.h"
@@ -315,6 +317,167 @@ __global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __res
   }
 }
 
+// m == 1 with bf16 operands and a bf16 cache: one workgroup owns 128 tokens and
+// all 512 channels, so RMSNorm, the pre-RoPE latent, RoPE and the cache row come
+// out of the accumulators in the epilogue (no finalize pass, no second read of
+// the latent, and every token row of x is read from memory once).  8 waves of
+// 64 tokens x 128 channels on v_mfma_f32_16x16x32_bf16.  Operands go straight
+// from global memory into two 80 KB LDS stages of 64-wide k-steps (16 KB of
+// tokens, 64 KB of weights), one barrier per k-step, the loads of step k + 1
+// issued right after it.  LDS rows are 128 B with the swizzle of the gated
+// kernel above (unit u of row r in slot u ^ (r & 7)).  The epilogue reuses the
+// stages: the rotary table, the per-wave sums of squares, and a row-major
+// staging area through which 32 token rows at a time leave as whole rows.
+constexpr int F_BM = 128;                          // tokens per workgroup
+constexpr int F_ROWB = 128;                        // bytes of a row per stage (64 bf16)
+constexpr int F_A_BYTES = F_BM * F_ROWB;           // 16 KB of tokens
+constexpr int F_STAGE = F_A_BYTES + 512 * F_ROWB;  // + 64 KB of weights
+constexpr int F_NS = 2;                            // stages (160 KB)
+constexpr int F_LROW = 512 * 4 + 16;               // epilogue row stride (bytes): fp32 row + pad
+
+__global__ __launch_bounds__(512) void compress_m1_bf16(const bf16* __restrict__ x, const bf16* __restrict__ w_kv,
+                                                        const float* __restrict__ gamma, float* __restrict__ lat,
+                                                        bf16* __restrict__ kv_cache, int T_len, int D, int entry0,
+                                                        int N_cap, float eps, double base) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[F_NS * F_STAGE];
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int b = blockIdx.y;
+  const int row0 = blockIdx.x * F_BM;
+  const bf16* xb = x + (size_t)b * T_len * D;
+
+  // DMA instruction j (0..79) of a stage fills stage rows 8j .. 8j+7 (1 KB): rows
+  // 0..127 are tokens, rows 128..639 weight rows (channels).  Wave w issues
+  // instructions w, w + 8, .., w + 72; lane i writes slot i % 8 of row 8j + i / 8.
+  const unsigned char* gsrc[10];
+#pragma unroll
+  for (int q = 0; q < 10; ++q) {
+    const int j = wave + 8 * q;
+    const int r = 8 * j + (lane >> 3);
+    const int unit = (lane & 7) ^ (r & 7);
+    const bf16* rowp = r < F_BM ? xb + (size_t)min(row0 + r, T_len - 1) * D   // rows past the end: discarded
+                                : w_kv + (size_t)(r - F_BM) * D;
+    gsrc[q] = reinterpret_cast<const unsigned char*>(rowp) + unit * 16;
+  }
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt & (F_NS - 1)) * F_STAGE;
+#pragma unroll
+    for (int q = 0; q < 10; ++q) dma16_asm(gsrc[q] + (size_t)kt * F_ROWB, (const lds_u8*)(st + (wave + 8 * q) * 1024));
+  };
+  // fragment rows: tile row r has r & 7 == lr & 7
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int slot = (ks * 4 + lg) ^ (lr & 7);
+    aoff[ks] = (wm * 64 + lr) * F_ROWB + slot * 16;
+    boff[ks] = F_A_BYTES + (wn * 128 + lr) * F_ROWB + slot * 16;
+  }
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = D / 64;
+  issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    WAIT_VMCNT(0);   // this wave's loads of step kt are in
+    COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();   // every wave's loads of step kt are in; every wave is past step kt - 1
+    COMPILER_FENCE();
+    if (kt + 1 < nk) issue(kt + 1);   // into the stage of step kt - 1
+    const unsigned char* cur = smem + (kt & (F_NS - 1)) * F_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[4], bb[8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(cur + aoff[ks] + mt * 16 * F_ROWB);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) bb[nt] = *reinterpret_cast<const bf16x8*>(cur + boff[ks] + nt * 16 * F_ROWB);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mma16(a[mt], bb[nt], acc[mt][nt]);
+    }
+  }
+  __syncthreads();   // the ring is free: the epilogue reuses its LDS
+
+  // lane holds token wm*64 + mt*16 + 4*lg + i, channel wn*128 + nt*16 + lr
+  float* ssq = reinterpret_cast<float*>(smem);                    // [4 wn][128 tokens]
+  float2* rot = reinterpret_cast<float2*>(smem + 2048);           // [128 tokens][32 pairs]
+  unsigned char* lbuf = smem + 2048 + F_BM * 32 * 8;              // [32 rows][F_LROW]
+  for (int i = threadIdx.x; i < F_BM * 32; i += 512) {
+    const int r = i >> 5;
+    float c = 1.f, sn = 0.f;
+    if (row0 + r < T_len) rope_cos_sin((int64_t)(entry0 + row0 + r), i & 31, 64, base, c, sn);
+    rot[i] = make_float2(c, sn);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sq = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) sq += acc[mt][nt][i] * acc[mt][nt][i];
+      sq = wave_sum_xor(sq, 15);
+      if (lr == 0) ssq[wn * F_BM + wm * 64 + mt * 16 + 4 * lg + i] = sq;
+    }
+  float g[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) g[nt] = gamma[wn * 128 + nt * 16 + lr];
+  __syncthreads();
+  float rinv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = wm * 64 + mt * 16 + 4 * lg + i;
+      const float ss = ssq[t] + ssq[F_BM + t] + ssq[2 * F_BM + t] + ssq[3 * F_BM + t];
+      rinv[mt][i] = 1.0f / sqrtf(ss * (1.0f / 512.0f) + eps);
+    }
+  const int n_entries = T_len;
+  // four passes of 32 token rows (16 per wm) staged row-major, then written out
+  // 16 B (latent) and 8 B (cache row) per thread
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* lrow = reinterpret_cast<float*>(lbuf + (wm * 16 + 4 * lg + i) * F_LROW) + wn * 128 + lr;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) lrow[nt * 16] = acc[p][nt][i] * rinv[p][i] * g[nt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int piece = threadIdx.x + 512 * u;
+      const int lrw = piece >> 7, c4 = piece & 127;
+      const int tl = (lrw >> 4) * 64 + p * 16 + (lrw & 15);
+      const int tok = row0 + tl;
+      if (tok < T_len) {
+        float4 v = *reinterpret_cast<const float4*>(lbuf + lrw * F_LROW + c4 * 16);
+        reinterpret_cast<float4*>(lat + ((size_t)b * n_entries + tok) * 512)[c4] = v;
+        if (c4 >= 112) {   // dims 448..511: pairs 2c4 - 224 and 2c4 - 223
+          const float2 r0 = rot[tl * 32 + 2 * c4 - 224], r1 = rot[tl * 32 + 2 * c4 - 223];
+          const float x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
+          v.x = x0 * r0.x - x1 * r0.y;
+          v.y = x0 * r0.y + x1 * r0.x;
+          v.z = x2 * r1.x - x3 * r1.y;
+          v.w = x2 * r1.y + x3 * r1.x;
+        }
+        bf16x2 p0, p1;
+        p0[0] = (bf16)v.x; p0[1] = (bf16)v.y;
+        p1[0] = (bf16)v.z; p1[1] = (bf16)v.w;
+        uint2 w2;
+        __builtin_memcpy(&w2.x, &p0, 4);
+        __builtin_memcpy(&w2.y, &p1, 4);
+        *reinterpret_cast<uint2*>(kv_cache + ((size_t)b * N_cap + entry0 + tok) * 512 + 4 * c4) = w2;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // One wave per entry: RMSNorm, RoPE on dims 448..511, write latent (fp32, in
 // place over the pooled values) and the cache row.  The 4 x 32 rotary angles of
 // the workgroup's entries are evaluated once, one per thread, into LDS.
@@ -396,6 +559,11 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
   const T* wk = static_cast<const T*>(w_kv);
   const T* wg = static_cast<const T*>(w_gate);
   if constexpr (sizeof(T) == 2) {
+    if (m == 1 && kv_scales == nullptr) {   // whole rows per workgroup: the epilogue finishes the entries
+      hipLaunchKernelGGL(compress_m1_bf16, dim3((T_len + F_BM - 1) / F_BM, B), dim3(512), 0, st, xx, wk, gamma, lat,
+                         static_cast<bf16*>(kv), T_len, D, start_pos, N_cap, eps, (double)base);
+      return hipGetLastError();
+    }
     dim3 gb((T_len + G_BM - 1) / G_BM, m > 1 ? 512 / 64 : 512 / 128, B);
     if (m == 1) hipLaunchKernelGGL((compress_gemm_pool_bf16<1>), gb, dim3(512), 0, st, xx, wk, wg, lat, T_len, D);
     else if (m == 2) hipLaunchKernelGGL((compress_gemm_pool_bf16<2>), gb, dim3(512), 0, st, xx, wk, wg, lat, T_len, D);
