@@ -543,12 +543,24 @@ csa2_status csa2_layer_forward(csa2_runtime* rt, const csa2_layer_cfg* cfg, cons
     ca.N_cap = io->N_cap; ca.eps = cfg->eps; ca.rope_base = cfg->rope_base; ca.x = io->x; ca.w_kv = io->w_kv;
     ca.w_gate = io->w_gate; ca.gamma = io->gamma; ca.latent_pre = io->latent_pre; ca.kv_cache = io->kv_cache;
     ca.kv_fmt = cfg->kv_fmt; ca.kv_scales = io->kv_scales;
-    if ((s = csa2_compress(rt, &ca, stream)) != CSA2_OK) return s;
     csa2_index_k_args ia{};
     ia.dtype = cfg->dtype; ia.B = io->B; ia.N = T_x / cfg->m; ia.m = cfg->m; ia.entry0 = io->start_pos / cfg->m;
     ia.N_cap = io->N_cap; ia.rope_base = cfg->rope_base; ia.latent_pre = io->latent_pre; ia.w_ik = io->w_ik;
     ia.codes = io->ik_codes; ia.scales = io->ik_scales; ia.scale_fmt = cfg->scale_fmt;
-    if ((s = csa2_index_k(rt, &ia, stream)) != CSA2_OK) return s;
+    if (csa2::compress_makes_index_k(cfg->dtype, cfg->m, cfg->kv_fmt == CSA2_KV_FP4)) {
+      // one kernel writes the cache rows, the pre-RoPE latent and the index K
+      // (both argument sets were checked above)
+      hipError_t e = csa2::launch_compress_index_k(ca.x, ca.w_kv, ca.gamma, ca.latent_pre, ca.kv_cache, ia.w_ik,
+                                                   ia.codes, ia.scales, ca.B, ca.T, ca.D, ca.start_pos, ca.N_cap,
+                                                   ca.eps, ca.rope_base, st(stream), ia.scale_fmt);
+      if (e != hipSuccess) return hip_status(e, "csa2_layer_forward: compress launch");
+      publish(rt, CSA2_SLOT_COMPRESS_KV, ca.kv_cache, nullptr, ca.dtype, ca.B, ca.N_cap, ca.start_pos + ca.T, 1,
+              ca.kv_fmt);
+      publish(rt, CSA2_SLOT_INDEX_K, ia.codes, ia.scales, 0, ia.B, ia.N_cap, ia.entry0 + ia.N, 1, ia.scale_fmt);
+    } else {
+      if ((s = csa2_compress(rt, &ca, stream)) != CSA2_OK) return s;
+      if ((s = csa2_index_k(rt, &ia, stream)) != CSA2_OK) return s;
+    }
   }
   if (cfg->mode != CSA2_REUSE) {
     if ((s = csa2_score_topk(rt, &sa, stream)) != CSA2_OK) return s;

@@ -16,6 +16,14 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
                            int D, int m, int start_pos, int N_cap, float eps, float rope_base,
                            hipStream_t stream);
 
+// Full layer with m == 1, bf16 and a bf16 cache: the compressor kernel also writes
+// the index-K codes and scales (what launch_index_k would write from latent_pre)
+bool compress_makes_index_k(int dtype, int m, bool kv_fp4);
+hipError_t launch_compress_index_k(const void* x, const void* w_kv, const float* gamma, float* latent_pre,
+                                   void* kv_cache, const void* w_ik, uint8_t* codes, uint8_t* scales, int B, int T,
+                                   int D, int start_pos, int N_cap, float eps, float rope_base, hipStream_t stream,
+                                   int scale_fmt);
+
 // decode append: C and Z of one token per sequence into cz [B, 1024] (float32), then
 // the group pool / entry / index-K row per sequence
 hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv,

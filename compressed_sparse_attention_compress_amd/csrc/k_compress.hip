@@ -328,6 +328,10 @@ __global__ __launch_bounds__(512) void compress_gemm_pool_bf16(const bf16* __res
 // kernel above (unit u of row r in slot u ^ (r & 7)).  The epilogue reuses the
 // stages: the rotary table, the per-wave sums of squares, and a row-major
 // staging area through which 32 token rows at a time leave as whole rows.
+// With w_ik given (the Full layer's own call) the epilogue also makes the index-K
+// rows from the staged pre-RoPE latent (the same float32 hi + lo bf16 split, MFMA
+// order, RoPE and FP4 block rule as index_k_kernel), so no second pass reads the
+// latent back.
 constexpr int F_BM = 128;                          // tokens per workgroup
 constexpr int F_ROWB = 128;                        // bytes of a row per stage (64 bf16)
 constexpr int F_A_BYTES = F_BM * F_ROWB;           // 16 KB of tokens
@@ -337,8 +341,10 @@ constexpr int F_LROW = 512 * 4 + 16;               // epilogue row stride (bytes
 
 __global__ __launch_bounds__(512) void compress_m1_bf16(const bf16* __restrict__ x, const bf16* __restrict__ w_kv,
                                                         const float* __restrict__ gamma, float* __restrict__ lat,
-                                                        bf16* __restrict__ kv_cache, int T_len, int D, int entry0,
-                                                        int N_cap, float eps, double base) {
+                                                        bf16* __restrict__ kv_cache, const bf16* __restrict__ w_ik,
+                                                        uint8_t* __restrict__ ik_codes, uint8_t* __restrict__ ik_scales,
+                                                        int sfmt, int T_len, int D, int entry0, int N_cap, float eps,
+                                                        double base) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[F_NS * F_STAGE];
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -474,6 +480,74 @@ __global__ __launch_bounds__(512) void compress_m1_bf16(const bf16* __restrict__
         *reinterpret_cast<uint2*>(kv_cache + ((size_t)b * N_cap + entry0 + tok) * 512 + 4 * c4) = w2;
       }
     }
+    if (w_ik != nullptr) {
+      // index K of the 32 staged rows: wave (rt, q) = rows 16rt .. 16rt+15, dims
+      // 32q .. 32q+31 (quantisation block q) as two column tiles
+      const int q = wave & 3, rt = wave >> 2;
+      const unsigned char* arow = lbuf + (16 * rt + lr) * F_LROW + 32 * lg;
+      f32x4 u[2];
+      u[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < 16; k0 += 4) {   // four k-steps of weights in flight per round
+        bf16x8 bw[4][2];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            bw[v][j] = *reinterpret_cast<const bf16x8*>(w_ik + (size_t)((2 * q + j) * 16 + lr) * 512 + (k0 + v) * 32 +
+                                                        8 * lg);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 a0 = *reinterpret_cast<const float4*>(arow + (k0 + v) * 128);
+          const float4 a1 = *reinterpret_cast<const float4*>(arow + (k0 + v) * 128 + 16);
+          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bf16 h = (bf16)av[e];
+            hi[e] = h;
+            lo[e] = (bf16)(av[e] - (float)h);
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            u[j] = mma16(hi, bw[v][j], u[j]);
+            u[j] = mma16(lo, bw[v][j], u[j]);
+          }
+        }
+      }
+      // lane: rows 16rt + 4lg + i, dims 32q + 16j + lr.  RoPE on dims 64..127 (blocks
+      // 2 and 3): pair (64 + 2p, 65 + 2p) lives in lanes l, l ^ 1
+      if (q >= 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int pair = (2 * q + j - 4) * 8 + (lr >> 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float2 cs = rot[(rt * 64 + p * 16 + 4 * lg + i) * 32 + pair];
+            const float mine = u[j][i], other = __shfl_xor(mine, 1, 64);
+            u[j][i] = (lr & 1) ? (other * cs.y + mine * cs.x) : (mine * cs.x - other * cs.y);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = row0 + rt * 64 + p * 16 + 4 * lg + i;
+        const float v0 = u[0][i], v1 = u[1][i];
+        const float amax = wave_max_xor(fmaxf(fabsf(v0), fabsf(v1)), 15);   // the block: 16 lanes x 2
+        const uint32_t sb = ik_scale_byte(amax, sfmt);
+        const float sc = ik_scale_value(sb, sfmt);
+        const uint32_t c0 = fp4_code(v0, sc), c1 = fp4_code(v1, sc);
+        const uint32_t o0 = __shfl_xor((int)c0, 1, 64), o1 = __shfl_xor((int)c1, 1, 64);
+        if (tok < T_len) {
+          uint8_t* crow = ik_codes + ((size_t)b * N_cap + entry0 + tok) * 64 + 16 * q;
+          if ((lr & 1) == 0) {
+            crow[lr >> 1] = (uint8_t)(c0 | (o0 << 4));
+            crow[8 + (lr >> 1)] = (uint8_t)(c1 | (o1 << 4));
+          }
+          if (lr == 0) ik_scales[((size_t)b * N_cap + entry0 + tok) * 4 + q] = (uint8_t)sb;
+        }
+      }
+    }
     __syncthreads();
   }
 }
@@ -550,7 +624,8 @@ __global__ __launch_bounds__(256) void compress_finalize(float* __restrict__ lat
 template <typename T>
 hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const float* gamma, float* lat,
                     void* kv, uint8_t* kv_scales, int B, int T_len, int D, int m, int start_pos, int N_cap, float eps,
-                    float base, hipStream_t st) {
+                    float base, hipStream_t st, const void* w_ik = nullptr, uint8_t* ik_codes = nullptr,
+                    uint8_t* ik_scales = nullptr, int sfmt = 0) {
   const int n_entries = T_len / m;
   if (n_entries == 0 || B == 0) return hipSuccess;
   dim3 blk(256);
@@ -561,7 +636,8 @@ hipError_t launch_t(const void* x, const void* w_kv, const void* w_gate, const f
   if constexpr (sizeof(T) == 2) {
     if (m == 1 && kv_scales == nullptr) {   // whole rows per workgroup: the epilogue finishes the entries
       hipLaunchKernelGGL(compress_m1_bf16, dim3((T_len + F_BM - 1) / F_BM, B), dim3(512), 0, st, xx, wk, gamma, lat,
-                         static_cast<bf16*>(kv), T_len, D, start_pos, N_cap, eps, (double)base);
+                         static_cast<bf16*>(kv), static_cast<const bf16*>(w_ik), ik_codes, ik_scales, sfmt, T_len, D,
+                         start_pos, N_cap, eps, (double)base);
       return hipGetLastError();
     }
     dim3 gb((T_len + G_BM - 1) / G_BM, m > 1 ? 512 / 64 : 512 / 128, B);
@@ -822,6 +898,16 @@ hipError_t launch_compress(int dtype, const void* x, const void* w_kv, const voi
                          rope_base, stream);
 }
 
+
+bool compress_makes_index_k(int dtype, int m, bool kv_fp4) { return dtype == 1 && m == 1 && !kv_fp4; }
+
+hipError_t launch_compress_index_k(const void* x, const void* w_kv, const float* gamma, float* latent_pre,
+                                   void* kv_cache, const void* w_ik, uint8_t* codes, uint8_t* scales, int B, int T,
+                                   int D, int start_pos, int N_cap, float eps, float rope_base, hipStream_t stream,
+                                   int scale_fmt) {
+  return launch_t<bf16>(x, w_kv, nullptr, gamma, latent_pre, kv_cache, nullptr, B, T, D, 1, start_pos, N_cap, eps,
+                        rope_base, stream, w_ik, codes, scales, scale_fmt);
+}
 
 hipError_t launch_compress_step(int dtype, const void* x, const int32_t* pos, const void* w_kv, const void* w_gate,
                                 const float* gamma, const void* w_ik, float* state, void* kv_cache, uint8_t* kv_scales,

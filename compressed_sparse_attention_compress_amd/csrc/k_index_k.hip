@@ -35,7 +35,7 @@ __device__ __forceinline__ void split_hi_lo(const f32x8& a, bf16x8& hi, bf16x8& 
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
+__global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ lat, const T* __restrict__ w_ik,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                       int N, int m, int entry0, int N_cap, double base,
                                                       int sfmt) {
