@@ -1669,10 +1669,18 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
   auto compute = [&](int i, const unsigned char* ring) {
     const int st = wave + 4 * i;
     const unsigned char* src = ring + wave * ST_BYTES;
+    // the super-tile's code and scale words, read from LDS together up front
+    uint32_t cwa[SPT][4], swa[SPT];
 #pragma unroll
     for (int tt = 0; tt < SPT; ++tt) {
-      const unsigned char* tb = src + tt * 1024;
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
+      swa[tt] = *reinterpret_cast<const uint32_t*>(src + SPT * 1024 + (tt * 16 + lr) * 4);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        cwa[tt][kb] = *reinterpret_cast<const uint32_t*>(src + tt * 1024 + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
+    }
+#pragma unroll
+    for (int tt = 0; tt < SPT; ++tt) {
+      const uint32_t sw = swa[tt];
       const uint32_t eref = SF ? max_byte4(sw) : 0u;
       f32x4 acc[QT][2];
 #pragma unroll
@@ -1682,7 +1690,7 @@ __global__ __launch_bounds__(SC_THREADS, 2) void score_qtile_bf16(
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(tb + ((4 * lr + ((kb + (lr >> 2)) & 3)) << 4) + 4 * lg);
+        const uint32_t cw = cwa[tt][kb];
         float p2;
         f16x2 mm;
         split_scale<SF>((sw >> (8 * kb)) & 0xFFu, eref, p2, mm);
