@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # fp32 (vector and MFMA)
 
 METRIC = "CSA2 layer prefill tokens/s + decode µs/step; % HBM/MFMA roofline"
 
@@ -101,6 +102,52 @@ class PrefillBench:
             "score_topk": {"flop": 2.0 * s.B * pairs * s.H_I * 128, "pairs": s.B * pairs},
             "sparse_attn": {"flop": 4.0 * s.B * rows * H * 512, "rows": s.B * rows},
         }
+
+
+# --------------------------------------------------------------------------- C1
+
+class TinyLayerBench:
+    """Tiny Full layer, fp32 (B=1, L=512, hidden 256, m=2, 4 indexer heads, top-32,
+    SWA 16, 8 heads): one csa2_layer_forward call (compressor, index K, score +
+    top-k, attention); a latency figure, the oracle timed beside it."""
+
+    def __init__(self, torch, K, synth):
+        self.t, self.K = torch, K
+        self.shape = s = synth.TINY
+        dev = "cuda"
+        self.inp = synth.full_layer_inputs(s, 0, torch.float32, dev, layer=0)
+        self.N = s.L // s.m
+        self.lat = torch.empty(s.B, self.N, 512, dtype=torch.float32, device=dev)
+        self.kv = torch.empty(s.B, self.N, 512, dtype=torch.float32, device=dev)
+        self.codes = torch.empty(s.B, self.N, 64, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(s.B, self.N, 4, dtype=torch.uint8, device=dev)
+        self.topk = torch.empty(s.B, s.L, s.k, dtype=torch.int32, device=dev)
+        self.o = torch.empty_like(self.inp["q"])
+        self.rt = K.Runtime()
+        self.cfg = K.layer_cfg(K.FULL, K.CSA2_F32, m=s.m, k=s.k, W=s.W, H_I=s.H_I, H=s.H)
+        i = self.inp
+        self.kw = dict(B=s.B, T=s.L, q_pos=i["q_pos"], q=i["q"], swa_kv=i["swa_kv"], swa_pos0=i["swa_pos0"], o=self.o,
+                       N_cap=self.N, D=s.D, x=i["x"], w_kv=i["w_kv"], w_gate=i["w_gate"], gamma=i["gamma"],
+                       w_ik=i["w_ik"], latent_pre=self.lat, kv_cache=self.kv, ik_codes=self.codes,
+                       ik_scales=self.scales, q_idx=i["q_idx"], w=i["w"], topk=self.topk)
+        nb = K.layer_workspace_bytes(self.cfg, K.layer_io(**self.kw))
+        self.ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        self.io = K.layer_io(workspace=self.ws, **self.kw)
+        torch.cuda.synchronize()
+
+    def step(self, events=None):
+        if events is not None:
+            events[0].record()
+        self.K.csa2_layer_forward(self.rt, self.cfg, self.io)
+        if events is not None:
+            events[1].record()
+
+    def work(self):
+        s = self.shape
+        n_t = [(t + 1) // s.m for t in range(s.L)]
+        rows = sum(min(s.k, n) + min(s.W, t + 1) for t, n in enumerate(n_t))
+        return (2.0 * s.B * s.L * s.D * 512 * (1 if s.m == 1 else 2) + 2.0 * s.B * self.N * 512 * 128
+                + 2.0 * s.B * sum(n_t) * s.H_I * 128 + 4.0 * s.B * rows * s.H * 512)
 
 
 # --------------------------------------------------------------------------- C4
@@ -515,6 +562,32 @@ def cpu_baseline_prefill(bench, min_seconds=10.0):
             "measured_s": round(t_build + t_q, 2)}
 
 
+def cpu_baseline_tiny(tb, min_seconds=2.0):
+    """The oracle's whole Full layer (compressor, index K, score + top-k and
+    attention for all 512 queries) on the same inputs, repeated for at least
+    `min_seconds`."""
+    import numpy as np
+    from oracle import csa2_oracle as O
+    s, i = tb.shape, tb.inp
+
+    def f64(x):
+        return None if x is None else x.detach().float().cpu().numpy().astype(np.float64)
+    cfg = O.LayerConfig(O.FULL, m=s.m, k=s.k, W=s.W, w_kv=f64(i["w_kv"]), w_gate=f64(i["w_gate"]),
+                        gamma=f64(i["gamma"]), w_ik=f64(i["w_ik"]))
+    li = O.LayerInputs(q=f64(i["q"]), swa_kv=f64(i["swa_kv"]), q_pos=i["q_pos"].cpu().numpy(),
+                       swa_pos0=i["swa_pos0"].cpu().numpy(), q_idx=f64(i["q_idx"]), w=f64(i["w"]), x=f64(i["x"]))
+    runs, t = 0, 0.0
+    while runs == 0 or t < min_seconds:
+        t0 = time.perf_counter()
+        O.layer_forward(O.Runtime(), cfg, li)
+        t += time.perf_counter() - t0
+        runs += 1
+    per = t / runs
+    return {"value": round(per * 1e6, 1), "unit": "us per layer call", "cores": _cores(), "kind": "oracle",
+            "sample": f"the whole tiny Full layer, unsampled; {runs} runs, mean {per:.3f} s; numpy float64",
+            "measured_s": round(t, 2)}
+
+
 def _cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -706,6 +779,7 @@ def main():
     ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--no-hsi", action="store_true", help="skip the 1M-context HSI decode record")
     ap.add_argument("--no-append", action="store_true", help="skip the decode-append record")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 layer latency record")
     ap.add_argument("--no-fp4kv", action="store_true", help="skip the decode record with FP4 main KV")
     ap.add_argument("--no-fp8swa", action="store_true",
                     help="skip the decode record with FP4 main KV and the FP8 window ring")
@@ -953,6 +1027,26 @@ def main():
             out["decode_append"]["cpu_baseline"] = cpu_baseline_append(ab)
         del ab
         torch.cuda.empty_cache()
+    if not args.no_tiny:
+        log("tiny layer: timing")
+        tb = TinyLayerBench(torch, K, synth)
+        n_tiny = max(args.steps, 50)
+        tms_eager, _ = time_steps(torch, tb, 1, n_tiny, args.warmup)
+        tms = time_graph(torch, tb, n_tiny, args.warmup) if args.graph else tms_eager
+        tflops = tb.work() / (tms * 1e-3) / 1e12
+        out["tiny_layer"] = {
+            "workload": "tiny Full layer, fp32: B=1, L=512, hidden 256, m=2 (256 entries), latent 512, indexer 4x128 "
+                        "FP4, top-32, SWA 16, 8 heads x 512; one csa2_layer_forward call (compressor, index K, "
+                        "score + top-k, attention)",
+            "us_per_call": round(tms * 1e3, 2), "us_per_call_eager": round(tms_eager * 1e3, 2),
+            "roofline": {"bound": "latency", "kernel": "layer (fp32)", "achieved": round(tflops, 3),
+                         "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_PEAK_TFLOPS, 5),
+                         "traffic": None},
+        }
+        if not args.no_cpu:
+            log("tiny layer: cpu baseline (oracle, whole layer)")
+            out["tiny_layer"]["cpu_baseline"] = cpu_baseline_tiny(tb)
+        del tb
     if not args.no_cpu:
         log("cpu baseline: the oracle on the whole prefill step")
         pb2 = PrefillBench(torch, K, synth)
