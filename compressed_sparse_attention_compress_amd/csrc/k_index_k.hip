@@ -43,16 +43,7 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
   const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // quantisation block of this wave
   const int e0 = blockIdx.x * 16;
   const int b = blockIdx.y;
-  // rotary angles of the 16 entries x 32 pairs, two per thread, into LDS
   __shared__ float2 rot[16][32];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = threadIdx.x + 256 * r, ee = idx >> 5, pair = idx & 31;
-    float c = 1.f, s = 0.f;
-    if (e0 + ee < N) rope_cos_sin((int64_t)(entry0 + e0 + ee) * m, pair, 64, base, c, s);
-    rot[ee][pair] = make_float2(c, s);
-  }
-  __syncthreads();
   const float* lb = lat + (size_t)b * N * 512;
   const int arow = e0 + lr;
   // rows past N read row N - 1: they only feed outputs of entries that are not stored
@@ -62,9 +53,9 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
   acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // eight k-steps per round: all their loads are issued before the first MFMA
-  for (int k0 = 0; k0 < 16; k0 += 8) {
-    f32x8 a[8];
-    typename Frag<T>::type bw[8][2];
+  f32x8 a[8];
+  typename Frag<T>::type bw[8][2];
+  auto load_round = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       a[u] = load_frag(arow_p + (k0 + u) * 32 + 8 * lg);
@@ -72,6 +63,8 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
       for (int j = 0; j < 2; ++j)
         bw[u][j] = load_frag(w_ik + (size_t)((2 * q + j) * 16 + lr) * 512 + (k0 + u) * 32 + 8 * lg);
     }
+  };
+  auto mma_round = [&]() {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if constexpr (sizeof(T) == 2) {
@@ -87,7 +80,21 @@ __global__ __launch_bounds__(256) void index_k_kernel(const float* __restrict__ 
         for (int j = 0; j < 2; ++j) acc[j] = mma16(a[u], bw[u][j], acc[j]);
       }
     }
+  };
+  load_round(0);
+  // rotary angles of the 16 entries x 32 pairs, two per thread, into LDS, while
+  // the first round's loads are in flight (read after the barrier below)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = threadIdx.x + 256 * r, ee = idx >> 5, pair = idx & 31;
+    float c = 1.f, s = 0.f;
+    if (e0 + ee < N) rope_cos_sin((int64_t)(entry0 + e0 + ee) * m, pair, 64, base, c, s);
+    rot[ee][pair] = make_float2(c, s);
   }
+  mma_round();
+  load_round(8);
+  mma_round();
+  __syncthreads();   // the rotary table is complete
 
   // RoPE on dims 64..127 (blocks 2 and 3): pair (64+2p, 65+2p) lives in lanes l, l^1
   if (q >= 2) {
