@@ -410,7 +410,10 @@ csa2_status csa2_swa_append(const csa2_swa_append_args* a, csa2_stream stream);
  * that is neither reuses both).  Full: compress -> index_k -> score_topk ->
  * sparse_attn.  Reindex: score_topk on the index_k slot -> sparse_attn on the
  * compress_kv slot.  Reuse: sparse_attn on the compress_kv and topk_idxs slots.
- * Fields a mode does not use are ignored.                                    */
+ * Fields a mode does not use are ignored.  A Full layer with m = 1, bf16 and a
+ * bf16 cache runs compress and index_k as one kernel; its outputs (cache rows,
+ * latent_pre, index-K codes and scales, slot contents) are bit for bit those of
+ * csa2_compress followed by csa2_index_k.                                    */
 typedef struct csa2_layer_cfg {
   int32_t mode;             /* csa2_mode */
   int32_t dtype;            /* csa2_dtype */
