@@ -30,6 +30,8 @@ def _need_gpu():
     (1, 1000, 512, 40, 60, 1),
     (1, 128, 4096, 0, 0, 0),
     (3, 77, 256, 5, 3, 1),
+    (1, 1, 64, 0, 0, 0),       # one token, one 64-wide k-step
+    (2, 129, 64, 7, 0, 1),     # a second tile holding a single token
 ])
 def test_fused_full_layer_equals_two_calls(B, T_x, D, start, extra, sfmt):
     say(f"case: fused m=1 Full layer B={B} T_x={T_x} D={D} start={start} scale_fmt={sfmt}")
