@@ -54,7 +54,7 @@ def test_kv_fp4_pack_bitexact():
     assert np.array_equal(codes.cpu().numpy(), c_o)
 
 
-@pytest.mark.parametrize("dtype,m", [(torch.bfloat16, 2), (torch.float32, 1), (torch.bfloat16, 4)])
+@pytest.mark.parametrize("dtype,m", [(torch.bfloat16, 2), (torch.float32, 1), (torch.bfloat16, 4), (torch.bfloat16, 1)])
 def test_compress_writes_fp4_kv(dtype, m):
     B, T, D = 2, 96 * m, 256
     N_cap = T // m + 5
