@@ -87,11 +87,12 @@ struct AttnPlan {
   bool decode;      // few queries: workgroup per (query, split, head group)
   bool kv_fp4;      // main KV stored as FP4
   int n_splits;     // row splits per query (decode only)
-  int n_fp4;        // decode with FP4 KV: the first n_fp4 splits take the selected rows, the rest the window
+  int n_fp4;        // decode with FP4 KV or an FP8 window ring: the first n_fp4 splits take the selected rows, the rest the window
   size_t ws_bytes;  // decode: split partials (bf16 rows, float32 log-sum-exp) when n_splits > 1;
                     // FP4 KV outside decode: the dequantised cache rows [B, N_cap, 512];
                     // then, with an FP8 window ring, its dense rows [B, L_w, 512] and B int32
-  size_t swa_off;   // byte offset of the dense window rows in the workspace (FP8 ring only)
+  bool ring_direct; // FP8 window ring read by the decode kernel itself (window rows in splits of their own)
+  size_t swa_off;   // byte offset of the dense window rows in the workspace (FP8 ring, when not ring_direct)
 };
 AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, int N_cap, bool swa_fp8 = false,
                    int L_w = 0);

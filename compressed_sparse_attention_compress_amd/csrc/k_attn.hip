@@ -27,6 +27,8 @@
 //   heads 16w..16w+15), rows gathered once into a 4-stage ring of 32-row chunks
 //   with three chunks in flight.  Row splits, when used, write partials (bf16
 //   normalised output, float32 log-sum-exp) that attn_combine merges.
+#include <type_traits>
+
 #include "csa2_internal.h"
 #include "device_common.h"
 #include "lds_dma.h"
@@ -67,13 +69,15 @@ __device__ __forceinline__ v4s tr_read(const lds_u8* p) {
 __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 3) | ((r & 3) << 1) | ((r >> 3) & 1); }
 
 // Row list of one query: valid selected ids (order kept), then window rows
-// encoded as -(j+1) for swa row j.  Returns the number of rows.  Needs a
-// __syncthreads() before use by other waves (done by the callers).
-// after_issue() runs once in every wave: in wave 0 right after the first 512
-// ids are requested (so loads it issues queue behind them), elsewhere at once.
+// encoded as -(j+1) for swa row j: dense row j = position pos0 + j, or with
+// `ring` the ring slot of that position (position u sits in slot u mod L_w).
+// Returns the number of rows.  Needs a __syncthreads() before use by other waves
+// (done by the callers).  after_issue() runs once in every wave: in wave 0 right
+// after the first 512 ids are requested (so loads it issues queue behind them),
+// elsewhere at once.
 template <typename F>
 __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const int32_t* tk, int k, int N_cap, int p,
-                                             int pos0, int L_w, int W, F&& after_issue) {
+                                             int pos0, int L_w, int W, F&& after_issue, bool ring = false) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave == 0) {
     int cnt = 0;
@@ -107,7 +111,8 @@ __device__ __forceinline__ int build_rowlist(int* rowlist, int* n_sel_s, const i
   int hi = p;
   if (hi > pos0 + L_w - 1) hi = pos0 + L_w - 1;
   const int n_win = hi >= lo ? hi - lo + 1 : 0;
-  for (int j = threadIdx.x; j < n_win; j += blockDim.x) rowlist[n_sel + j] = -(lo - pos0 + j) - 1;
+  for (int j = threadIdx.x; j < n_win; j += blockDim.x)
+    rowlist[n_sel + j] = -(ring ? (lo + j) % L_w : lo - pos0 + j) - 1;
   __syncthreads();
   return n_sel + n_win;
 }
@@ -472,19 +477,30 @@ constexpr int RAW4 = DRC * 288;         // FP4 chunk: 32 x 256 B of codes, then 
 // single bf16 chunk buffer (same swizzled layout as a gathered bf16 chunk), and
 // a second barrier hands that buffer to the MFMA steps.  E2M1 x E4M3 values are
 // exact in bf16, so the MFMA inputs are exactly the dequantised cache.
-template <int NW, bool FP4>
+//
+// FP8 window ring (W8 = true): `swa` is the layer's ring of L_w E4M3 rows (512 B,
+// position u in slot u mod L_w) and the window rows go to splits of their own
+// (the last n_splits - n_fp4).  The ring's first position is p0 = max(swa_pos0,
+// newest - L_w + 1), newest = the sequence's largest query position in the call
+// (what a dense copy of the ring would start at).  A window chunk lands raw (32 x
+// 512 B, two rows per DMA instruction) in a 4-stage ring of 16 KiB stages and is
+// widened to bf16 (E4M3 values are exact in bf16) into the two chunk buffers the
+// same way as an FP4 chunk.
+template <int NW, bool FP4, bool W8>
 __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     const bf16* __restrict__ q, const void* __restrict__ kv, const uint8_t* __restrict__ kv_scales,
-    const int32_t* __restrict__ topk, const bf16* __restrict__ swa, const int32_t* __restrict__ swa_pos0,
+    const int32_t* __restrict__ topk, const void* __restrict__ swa, const int32_t* __restrict__ swa_pos0,
     const int32_t* __restrict__ q_pos, bf16* __restrict__ o, float* __restrict__ lse, const float* __restrict__ sink,
     bf16* __restrict__ part_o, float* __restrict__ part_lse, int T_len, int H, int N_cap, int k, int L_w, int W,
     float scale_log2, int n_splits, int n_fp4) {
   constexpr int RPW = DRC / NW;   // gathers per wave per chunk
   constexpr int DPW4 = 8 / NW + 4 / NW;   // DMA instructions per wave per FP4 chunk
+  constexpr int DPW8 = 16 / NW;           // DMA instructions per wave per FP8 window chunk
   __shared__ __attribute__((aligned(16))) unsigned char ring[DNS * DRC * PRS];
   __shared__ int rowlist[MAX_ROWS];
   __shared__ int n_sel_s;
   static_assert(!FP4 || 2 * DRC * PRS + DNS * RAW4 <= DNS * DRC * PRS, "FP4 buffers fit in the ring");
+  static_assert(!W8 || 2 * DRC * PRS + DNS * DRC * 512 <= DNS * DRC * PRS, "FP8 window buffers fit in the ring");
 
   const int qi = blockIdx.x / n_splits, split = blockIdx.x % n_splits;
   const int b = qi / T_len;
@@ -496,27 +512,36 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   const int head = wave * 16 + lr;
   bf16x8 qf[16];
   const bf16* qrow = q + ((size_t)bt * H + head) * 512;
-  const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], swa_pos0[b],
-                                   L_w, W, [&]() {
+  int pos0 = swa_pos0[b];
+  if constexpr (W8) {   // the ring's first position: from the sequence's newest query
+    int nw = -2147483647 - 1;
+    for (int t = lane; t < T_len; t += 64) nw = max(nw, q_pos[(size_t)b * T_len + t]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nw = max(nw, __shfl_xor(nw, off, 64));
+    pos0 = max(pos0, __builtin_amdgcn_readfirstlane(nw) - L_w + 1);   // every lane holds the maximum
+  }
+  const int n_rows = build_rowlist(rowlist, &n_sel_s, topk + (size_t)bt * k, k, N_cap, q_pos[bt], pos0, L_w, W,
+                                   [&]() {
 #pragma unroll
                                      for (int ks = 0; ks < 16; ++ks) {
                                        if (head < H) qf[ks] = load_frag(qrow + ks * 32 + 8 * lg);
                                        else zero_frag(qf[ks]);
                                      }
-                                   });
+                                   },
+                                   W8);
   // rows [rb, rb + nr) of the row list belong to this workgroup's kind of split
   int rb = 0, nr = n_rows, sp = split, nsp = n_splits;
-  bool fp4_rows = false;
-  if constexpr (FP4) {
+  bool fp4_rows = false, fp8_rows = false;
+  if constexpr (FP4 || W8) {
     const int n_sel = n_sel_s;
     if (split < n_fp4) {
-      nr = n_sel; nsp = n_fp4; fp4_rows = true;
+      nr = n_sel; nsp = n_fp4; fp4_rows = FP4;
     } else {
-      rb = n_sel; nr = n_rows - n_sel; sp = split - n_fp4; nsp = n_splits - n_fp4;
+      rb = n_sel; nr = n_rows - n_sel; sp = split - n_fp4; nsp = n_splits - n_fp4; fp8_rows = W8;
     }
   }
   const bf16* kvb = static_cast<const bf16*>(kv) + (size_t)b * N_cap * 512;   // bf16 rows (not read by FP4 splits)
-  const bf16* swb = swa + (size_t)b * L_w * 512;
+  const bf16* swb = static_cast<const bf16*>(swa) + (size_t)b * L_w * 512;    // dense bf16 window (not with W8)
   f32x4 oacc[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -537,7 +562,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   for (int d8 = 0; d8 < 8; ++d8) toff[d8] = (((2 * d8 + th) ^ tsw) << 4) + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
 
   // one 32-row chunk c in LDS (bf16, swizzled): scores, online softmax, PV
-  auto attend = [&](const unsigned char* cur, int c) {
+  auto attend = [&](const unsigned char* cur, int c) __attribute__((always_inline)) {
     // ---- S^T = R Q^T: 32 rows (two row tiles) x this wave's 16 heads
     f32x4 s[2];
     s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -611,7 +636,41 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     COMPILER_FENCE();
   };
 
-  if (!fp4_rows) {
+  // two dequantised chunks (chunk c in buffer c & 1), then a raw ring of 4 stages.
+  // Chunk c + 1 is dequantised while chunk c is attended, so one barrier per
+  // chunk: it finds raw chunk c + 1 landed, chunk c dequantised by every wave and
+  // chunk c - 1 (whose buffer chunk c + 1 takes) no longer read.  DPW = DMA
+  // instructions per wave per raw chunk.
+  auto dqb = [&](int c) -> unsigned char* { return ring + (c & 1) * (DRC * PRS); };
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  auto bf16_pair = [](float lo, float hi) -> uint32_t {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  };
+  auto dq_loop = [&](auto dpw_c, auto issue_raw, auto dequant) {
+    constexpr int DPW = decltype(dpw_c)::value;
+    for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue_raw(c);
+    if (c0 < c1) {
+      if (c1 - c0 >= 3) WAIT_VMCNT(2 * DPW);
+      else if (c1 - c0 == 2) WAIT_VMCNT(DPW);
+      else WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();   // raw chunk c0 is in LDS
+      COMPILER_FENCE();
+      dequant(c0);
+    }
+    for (int c = c0; c < c1; ++c) {
+      const int younger = min(c1 - 2 - c, DNS - 3);   // chunks issued after c + 1
+      if (younger >= 1) WAIT_VMCNT(DPW);
+      else WAIT_VMCNT(0);
+      WAIT_LGKM0();
+      __builtin_amdgcn_s_barrier();
+      COMPILER_FENCE();
+      if (c + DNS - 1 < c1) issue_raw(c + DNS - 1);
+      if (c + 1 < c1) dequant(c + 1);
+      attend(dqb(c), c);
+    }
+  };
+
+  if (!fp4_rows && !fp8_rows) {
     auto stage = [&](int c) -> unsigned char* { return ring + (c & (DNS - 1)) * (DRC * PRS); };
     auto issue = [&](int c) {
       unsigned char* buf = stage(c);
@@ -635,11 +694,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
       if (c + DNS - 1 < c1) issue(c + DNS - 1);
       attend(stage(c), c);
     }
-  } else if constexpr (FP4) {
+  } else if (fp4_rows) {
+   if constexpr (FP4) {
     const uint8_t* codes_b = static_cast<const uint8_t*>(kv) + (size_t)b * N_cap * 256;
     const uint8_t* scales_b = kv_scales + (size_t)b * N_cap * 32;
-    // two dequantised chunks (chunk c in buffer c & 1), then the raw ring
-    auto dqb = [&](int c) -> unsigned char* { return ring + (c & 1) * (DRC * PRS); };
     auto raw = [&](int c) -> unsigned char* { return ring + 2 * DRC * PRS + (c & (DNS - 1)) * RAW4; };
     auto issue4 = [&](int c) {
       unsigned char* st = raw(c);
@@ -662,12 +720,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     // (E2M1 magnitude k -> byte via an 8-entry v_perm table, sign to bit 7), the
     // hardware FP8 conversion yields float32, the block scale multiplies, and the
     // upper halves are the exact bf16 values.
-    typedef float v2f __attribute__((ext_vector_type(2)));
     auto to_e4m3 = [](uint32_t nib4) -> uint32_t {   // 4 nibbles, one per byte
       return __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, nib4 & 0x07070707u) | ((nib4 & 0x08080808u) << 4);
-    };
-    auto bf16_pair = [](float lo, float hi) -> uint32_t {
-      return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
     };
     // 16 threads per row, thread l of a row takes units l, l + 16, l + 32, l + 48
     // (16-B units of the bf16 row = 8 dims = one code word): the 16 stores of a row
@@ -696,29 +750,45 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
         }
       }
     };
-    // Chunk c + 1 is dequantised while chunk c is attended, so one barrier per
-    // chunk: it finds raw chunk c + 1 landed, chunk c dequantised by every wave and
-    // chunk c - 1 (whose buffer chunk c + 1 takes) no longer read.
-    for (int c = c0; c < c0 + DNS - 1 && c < c1; ++c) issue4(c);
-    if (c0 < c1) {
-      if (c1 - c0 >= 3) WAIT_VMCNT(2 * DPW4);
-      else if (c1 - c0 == 2) WAIT_VMCNT(DPW4);
-      else WAIT_VMCNT(0);
-      __builtin_amdgcn_s_barrier();   // raw chunk c0 is in LDS
-      COMPILER_FENCE();
-      dequant(c0);
-    }
-    for (int c = c0; c < c1; ++c) {
-      const int younger = min(c1 - 2 - c, DNS - 3);   // chunks issued after c + 1
-      if (younger >= 1) WAIT_VMCNT(DPW4);
-      else WAIT_VMCNT(0);
-      WAIT_LGKM0();
-      __builtin_amdgcn_s_barrier();
-      COMPILER_FENCE();
-      if (c + DNS - 1 < c1) issue4(c + DNS - 1);
-      if (c + 1 < c1) dequant(c + 1);
-      attend(dqb(c), c);
-    }
+    dq_loop(std::integral_constant<int, DPW4>{}, issue4, dequant);
+   }
+  } else {
+   if constexpr (W8) {
+    const uint8_t* ring8 = static_cast<const uint8_t*>(swa) + (size_t)b * L_w * 512;
+    auto raw = [&](int c) -> unsigned char* { return ring + 2 * DRC * PRS + (c & (DNS - 1)) * (DRC * 512); };
+    auto issue8 = [&](int c) {   // one instruction moves 2 rows x 512 B; window rows are -(slot + 1)
+      unsigned char* st = raw(c);
+#pragma unroll
+      for (int jj = 0; jj < 16 / NW; ++jj) {
+        const int j = wave + NW * jj;
+        const int r = c * DRC + 2 * j + (lane >> 5);
+        const int rid = rl[r < nr ? r : 0];
+        dma16_asm(ring8 + (size_t)(-rid - 1) * 512 + (lane & 31) * 16, (const lds_u8*)(st + j * 1024));
+      }
+    };
+    // 16 threads per row, thread l of a row widening units l, l + 16, l + 32, l + 48
+    // (8 dims each) into their swizzled slots, as for an FP4 chunk
+    auto widen = [&](int c) {
+      const unsigned char* st = raw(c);
+      for (int x = threadIdx.x; x < DRC * 16; x += 64 * NW) {
+        const int rr = x >> 4, l = x & 15;
+        const unsigned char* srow = st + rr * 512;
+        unsigned char* drow = dqb(c) + rr * PRS;
+        const int sz = swz(rr & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int unit = 16 * j + l;
+          const uint2 w = *reinterpret_cast<const uint2*>(srow + unit * 8);
+          const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+          const v2f b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+          const uint4 h = make_uint4(bf16_pair(a0.x, a0.y), bf16_pair(a1.x, a1.y), bf16_pair(b0.x, b0.y),
+                                     bf16_pair(b1.x, b1.y));
+          *reinterpret_cast<uint4*>(drow + ((unit ^ sz) << 4)) = h;
+        }
+      }
+    };
+    dq_loop(std::integral_constant<int, DPW8>{}, issue8, widen);
+   }
   }
 
   // ---- this split's normalised output and log-sum-exp (base 2) per head; the
@@ -939,9 +1009,12 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, in
     int ns = (int)((256 + Q - 1) / Q);
     if (ns > max_chunks) ns = max_chunks;
     if (ns < 1) ns = 1;
-    if (kv_fp4) {
-      // selected rows (FP4) and window rows (bf16) go to different splits, in
-      // proportion to their chunk counts; at least one of each
+    // An FP8 window ring is read by the kernel itself when the query has two or more
+    // splits anyway (with one, it is widened into a dense window first)
+    p.ring_direct = swa_fp8 && (kv_fp4 || ns >= 2);
+    if (kv_fp4 || p.ring_direct) {
+      // selected rows (FP4 or bf16) and window rows (bf16, or FP8 from the ring) go
+      // to different splits, in proportion to their chunk counts; at least one of each
       const int c4 = (k + DRC - 1) / DRC, cw = (W + DRC - 1) / DRC;
       if (ns < 2) ns = 2;
       int nw = (int)(((long long)ns * cw + (c4 + cw) / 2) / (c4 + cw));
@@ -955,7 +1028,7 @@ AttnPlan plan_attn(int dtype, int B, int T, int H, int k, int W, bool kv_fp4, in
     p.ws_bytes = (size_t)Q * p.n_splits * H * (512 * 2 + 4) + 256;
   else if (kv_fp4 && !p.decode)
     p.ws_bytes = (size_t)B * N_cap * 512 * (dtype == 1 ? 2 : 4) + 256;
-  if (swa_fp8) {   // the ring's dense rows, then each sequence's first dense position
+  if (swa_fp8 && !p.ring_direct) {   // the ring's dense rows, then each sequence's first dense position
     p.swa_off = (p.ws_bytes + 255) / 256 * 256;
     p.ws_bytes = p.swa_off + (size_t)B * L_w * 512 * (dtype == 1 ? 2 : 4) + (size_t)B * 4 + 256;
   }
@@ -967,7 +1040,7 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const ui
                               const float* sink, int B, int T, int H, int N_cap, int k, int L_w, int W, float scale,
                               void* workspace, const AttnPlan& p, hipStream_t st, bool swa_fp8) {
   if (B == 0 || T == 0) return hipSuccess;
-  if (swa_fp8) {
+  if (swa_fp8 && !p.ring_direct) {
     // the ring's rows of each sequence's last L_w positions, in position order, as
     // dense rows of the dtype; the attention below reads them as a dense window
     unsigned char* wb = static_cast<unsigned char*>(workspace) + p.swa_off;
@@ -995,9 +1068,9 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const ui
   }
   const bf16* qq = static_cast<const bf16*>(q);
   const bf16* kk = static_cast<const bf16*>(kv);
-  const bf16* ss = static_cast<const bf16*>(swa_kv);
   bf16* oo = static_cast<bf16*>(o);
   if (!p.decode) {
+    const bf16* ss = static_cast<const bf16*>(swa_kv);
     // head pairs of 32 heads; two waves (dim halves) each
     const int tbl = std::max(1, std::min(128, (T + 7) / 8));   // tokens per run dealt to one XCD
     const dim3 grid(8 * tbl * ((T + 8 * tbl - 1) / (8 * tbl)), B);
@@ -1013,19 +1086,24 @@ hipError_t launch_sparse_attn(int dtype, const void* q, const void* kv, const ui
   const int groups = Q * p.n_splits;
   bf16* part_o = static_cast<bf16*>(workspace);
   float* part_lse = reinterpret_cast<float*>(part_o + (size_t)Q * p.n_splits * H * 512);
-#define CSA2_DECODE(NWV, F4)                                                                                   \
-  hipLaunchKernelGGL((attn_decode_bf16<NWV, F4>), dim3(groups), dim3(64 * NWV), 0, st, qq, kv, kv_scales, topk, \
-                     ss, swa_pos0, q_pos, oo, lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2,           \
+#define CSA2_DECODE(NWV, F4, W8)                                                                                   \
+  hipLaunchKernelGGL((attn_decode_bf16<NWV, F4, W8>), dim3(groups), dim3(64 * NWV), 0, st, qq, kv, kv_scales, topk, \
+                     swa_kv, swa_pos0, q_pos, oo, lse, sink, part_o, part_lse, T, H, N_cap, k, L_w, W, sl2,           \
                      p.n_splits, p.n_fp4)
+#define CSA2_DECODE_NW(F4, W8)              \
+  do {                                      \
+    if (H > 32) CSA2_DECODE(4, F4, W8);     \
+    else if (H > 16) CSA2_DECODE(2, F4, W8); \
+    else CSA2_DECODE(1, F4, W8);            \
+  } while (0)
   if (p.kv_fp4) {
-    if (H > 32) CSA2_DECODE(4, true);
-    else if (H > 16) CSA2_DECODE(2, true);
-    else CSA2_DECODE(1, true);
+    if (p.ring_direct) CSA2_DECODE_NW(true, true);
+    else CSA2_DECODE_NW(true, false);
   } else {
-    if (H > 32) CSA2_DECODE(4, false);
-    else if (H > 16) CSA2_DECODE(2, false);
-    else CSA2_DECODE(1, false);
+    if (p.ring_direct) CSA2_DECODE_NW(false, true);
+    else CSA2_DECODE_NW(false, false);
   }
+#undef CSA2_DECODE_NW
 #undef CSA2_DECODE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;

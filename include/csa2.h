@@ -375,8 +375,12 @@ typedef struct csa2_sparse_attn_args {
   const float* sink;        /* [H] float32 per-head sink logits, or NULL (no sink) */
   int32_t kv_fmt;           /* csa2_kv_fmt of kv (ignored when kv is NULL) */
   const uint8_t* kv_scales; /* FP4 only: [B, N_cap, 32] */
-  int32_t swa_fmt;          /* csa2_swa_fmt of swa_kv; FP8_RING: the ring is read into the workspace
-                               (B * L_w * 512 elements of the dtype + B int32) before the attention */
+  int32_t swa_fmt;          /* csa2_swa_fmt of swa_kv; FP8_RING: bf16 calls of fewer than 512 queries
+                               whose rows take two or more splits (FP4 KV, or fewer than 256 queries
+                               with more than 32 rows: k + W > 32)
+                               read the ring inside the attention kernel; every other call first
+                               reads it into the workspace (B * L_w * 512 elements of the dtype +
+                               B int32).  csa2_workspace_size gives the bytes either way. */
 } csa2_sparse_attn_args;
 
 csa2_status csa2_sparse_attn(csa2_runtime* rt, const csa2_sparse_attn_args* a, csa2_stream stream);

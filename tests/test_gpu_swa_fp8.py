@@ -131,9 +131,27 @@ def _dense_from_ring(oring, pos0, L_w, dtype):
     return torch.from_numpy(dense).to(dtype).to(DEV)
 
 
+def _ring_vs_dense(o_ring, o_dense, lse_ring=None, lse_dense=None, exact=True):
+    """The ring call against the same call over the ring's rows as a dense window.
+    Where both run the same kernel over the same splits the results are equal bit
+    for bit.  The bf16 decode kernel gives a ring's window rows splits of their own
+    (read and widened from the ring), while a dense window shares splits with bf16
+    selected rows: the same rows, but partials merged in another grouping, so the
+    two agree to the bf16 partials' rounding."""
+    if exact:
+        assert torch.equal(o_ring, o_dense), "ring vs dense window of its rows"
+        if lse_ring is not None:
+            assert torch.equal(lse_ring, lse_dense), "ring vs dense window: lse"
+        return
+    err = row_rel_err(npy(o_ring), npy(o_dense))
+    assert err <= 1e-2, f"ring vs dense window of its rows: {err:.2e}"
+    if lse_ring is not None:
+        assert torch.allclose(lse_ring, lse_dense, rtol=1e-5, atol=1e-5), "ring vs dense window: lse"
+
+
 @pytest.mark.parametrize("dtype,kv_fp4,L_w,W,H", [
     (torch.bfloat16, False, 128, 128, 64), (torch.bfloat16, True, 160, 128, 64), (torch.float32, False, 128, 64, 8),
-    (torch.bfloat16, False, 96, 64, 16),
+    (torch.bfloat16, False, 96, 64, 16), (torch.bfloat16, True, 96, 64, 32), (torch.bfloat16, True, 128, 100, 16),
 ])
 def test_ring_attention_decode(dtype, kv_fp4, L_w, W, H):
     B, k, N_cap = 3, 32, 80
@@ -169,7 +187,7 @@ def test_ring_attention_decode(dtype, kv_fp4, L_w, W, H):
     K.csa2_sparse_attn(None, q, kv, tk, dense, torch.tensor(pos0, dtype=torch.int32, device=DEV), q_pos, o_dense,
                        W=W, lse=lse_dense, kv_scales=kv_scales)
     torch.cuda.synchronize()
-    assert torch.equal(o_ring, o_dense) and torch.equal(lse_ring, lse_dense), "ring vs dense window of its rows"
+    _ring_vs_dense(o_ring, o_dense, lse_ring, lse_dense, exact=kv_fp4 or dtype == torch.float32)
     og, qn = npy(o_ring), npy(q)
     worst = 0.0
     for b in range(B):
@@ -183,10 +201,13 @@ def test_ring_attention_decode(dtype, kv_fp4, L_w, W, H):
     assert worst <= TOL[dtype]
 
 
-def test_ring_attention_many_queries():
-    """Many queries per sequence (the many-query kernel), all within L_w - W of
-    the newest position so that every window lies inside the ring."""
-    dtype, B, T, H, k, W, L_w, N_cap = torch.bfloat16, 2, 300, 16, 16, 128, 448, 64
+@pytest.mark.parametrize("T,L_w", [(300, 448), (8, 160)])
+def test_ring_attention_many_queries(T, L_w):
+    """Several queries per sequence, all within L_w - W of the newest position so
+    that every window lies inside the ring: 600 queries take the many-query
+    kernel, 16 the decode kernel, which finds the ring's first position from each
+    sequence's newest query itself."""
+    dtype, B, H, k, W, N_cap = torch.bfloat16, 2, 16, 16, 128, 64
     last = [700, 400]
     n_pre = [600, 300]
     say(f"case: ring attention many queries B={B} T={T} H={H} L_w={L_w} W={W}")
@@ -209,7 +230,7 @@ def test_ring_attention_many_queries():
     K.csa2_sparse_attn(None, q, kv, tk, dense, torch.tensor(pos0, dtype=torch.int32, device=DEV), q_pos, o_dense,
                        W=W)
     torch.cuda.synchronize()
-    assert torch.equal(o_ring, o_dense), "ring vs dense window of its rows"
+    _ring_vs_dense(o_ring, o_dense, exact=B * T >= 512)
     og, qn, kvn = npy(o_ring), npy(q), npy(kv)
     worst = 0.0
     for b in range(B):
@@ -267,14 +288,14 @@ def test_ring_through_reuse_layer(dtype):
         o = torch.empty_like(g["q"])
         kw = dict(B=B, T=P, q_pos=g["q_pos"], q=g["q"], swa_kv=swa, swa_pos0=g["swa_pos0"], o=o, N_cap=N_cap)
         need = K.layer_workspace_bytes(cfg, K.layer_io(**kw))
-        if fmt == K.SWA_FP8_RING:
-            assert need >= B * L_w * 512 * (2 if dtype == torch.bfloat16 else 4)
+        if fmt == K.SWA_FP8_RING and dtype == torch.float32:   # widened into a dense window first
+            assert need >= B * L_w * 512 * 4
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
         K.csa2_layer_forward(rt, cfg, K.layer_io(workspace=ws, **kw))
         outs[fmt] = o
     torch.cuda.synchronize()
     assert np.array_equal(ring.cpu().numpy(), oring)
-    assert torch.equal(outs[K.SWA_FP8_RING], outs[K.SWA_DENSE]), "ring vs dense window of its rows"
+    _ring_vs_dense(outs[K.SWA_FP8_RING], outs[K.SWA_DENSE], exact=dtype == torch.float32)
 
     def cpu(t):
         return npy(t)
