@@ -314,3 +314,49 @@ def test_ring_through_reuse_layer(dtype):
     err = row_rel_err(npy(outs[K.SWA_FP8_RING]), ref)
     say(f"  row rel err {err:.2e}")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("kv_fp4,H", [(False, 64), (True, 16)])
+def test_ring_attention_window_only(kv_fp4, H):
+    """k = 0 with the window in a ring, on the decode kernel that reads the ring
+    itself: the selected-row split has no rows (an empty partial the merge must
+    ignore) and the window rows come from the FP8 splits; compared with the
+    oracle's window-only attention and with the same call over a dense copy."""
+    dtype, B, W, L_w, N_cap = torch.bfloat16, 3, 128, 160, 40
+    last = [300, 140, 60]
+    n_pre = [250, 100, 30]
+    say(f"case: ring attention window only k=0 fp4kv={kv_fp4} H={H}")
+    rows = window_rows(B, max(last) + 1, 29, dtype, with_specials=False)
+    ring, oring = _ring_for(rows, n_pre, last, L_w, dtype)
+    q = synth.gaussian((B, 1, H, 512), 1.0, 29, "q", 0, dtype, DEV)
+    kvf = synth.gaussian((B, N_cap, 512), 1.0, 29, "kv_cache", 0, torch.float32, DEV)
+    if kv_fp4:
+        kv = torch.empty(B, N_cap, 256, dtype=torch.uint8, device=DEV)
+        kv_scales = torch.empty(B, N_cap, 32, dtype=torch.uint8, device=DEV)
+        K.csa2_kv_fp4_pack(kvf.contiguous(), kv, kv_scales)
+    else:
+        kv, kv_scales = kvf.to(dtype), None
+    tk = torch.full((B, 1, 1), 3, dtype=torch.int32, device=DEV)   # never read with k = 0
+    q_pos = torch.tensor(last, dtype=torch.int32, device=DEV)[:, None].contiguous()
+    swa_pos0 = torch.zeros(B, dtype=torch.int32, device=DEV)
+    o_ring = torch.empty_like(q)
+    lse_ring = torch.empty(B, 1, H, dtype=torch.float32, device=DEV)
+    K.csa2_sparse_attn(None, q, kv, tk, ring, swa_pos0, q_pos, o_ring, W=W, k=0, lse=lse_ring, kv_scales=kv_scales)
+    pos0 = [max(0, last[b] - L_w + 1) for b in range(B)]
+    dense = _dense_from_ring(oring, pos0, L_w, dtype)
+    o_dense = torch.empty_like(q)
+    lse_dense = torch.empty_like(lse_ring)
+    K.csa2_sparse_attn(None, q, kv, tk, dense, torch.tensor(pos0, dtype=torch.int32, device=DEV), q_pos, o_dense,
+                       W=W, k=0, lse=lse_dense, kv_scales=kv_scales)
+    torch.cuda.synchronize()
+    _ring_vs_dense(o_ring, o_dense, lse_ring, lse_dense, exact=kv_fp4)
+    og, lg, qn = npy(o_ring), lse_ring.cpu().numpy(), npy(q)
+    worst = 0.0
+    for b in range(B):
+        win = O.swa_ring_rows(oring[b], pos0[b], last[b])
+        ref, _, used = O.sparse_attention(qn[b, 0], np.zeros((0, 512)), np.zeros(0, np.int64), win, pos0[b],
+                                          last[b], W)
+        worst = max(worst, row_rel_err(og[b, 0], ref))
+        assert np.allclose(lg[b, 0], O.attention_lse(qn[b, 0], used), rtol=1e-4, atol=1e-3), b
+    say(f"  worst row rel err {worst:.2e}")
+    assert worst <= TOL[dtype]
