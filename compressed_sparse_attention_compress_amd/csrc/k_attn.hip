@@ -562,7 +562,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
   for (int d8 = 0; d8 < 8; ++d8) toff[d8] = (((2 * d8 + th) ^ tsw) << 4) + (4 * lg + (lr >> 2)) * PRS + 8 * (lr & 1);
 
   // one 32-row chunk c in LDS (bf16, swizzled): scores, online softmax, PV
-  auto attend = [&](const unsigned char* cur, int c) __attribute__((always_inline)) {
+  // mid(0) and mid(1) run between S's MFMAs (the FP4 and FP8 splits widen the next
+  // chunk there, so its VALU work overlaps the MFMAs in flight)
+  auto attend = [&](const unsigned char* cur, int c, auto&& mid) __attribute__((always_inline)) {
     // ---- S^T = R Q^T: 32 rows (two row tiles) x this wave's 16 heads
     f32x4 s[2];
     s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -578,6 +580,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
       __builtin_amdgcn_sched_barrier(0);
       s[f >> 4] = mma16(a0, qf[f & 15], s[f >> 4]);
       __builtin_amdgcn_sched_barrier(0);
+      if (f == 7) mid(0);
+      if (f == 23) mid(1);
       a0 = a1;
       if (f + 2 < 32) a1 = a2;
     }
@@ -655,7 +659,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
       else WAIT_VMCNT(0);
       __builtin_amdgcn_s_barrier();   // raw chunk c0 is in LDS
       COMPILER_FENCE();
-      dequant(c0);
+      dequant(c0, 0);
+      dequant(c0, 1);
     }
     for (int c = c0; c < c1; ++c) {
       const int younger = min(c1 - 2 - c, DNS - 3);   // chunks issued after c + 1
@@ -665,8 +670,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
       __builtin_amdgcn_s_barrier();
       COMPILER_FENCE();
       if (c + DNS - 1 < c1) issue_raw(c + DNS - 1);
-      if (c + 1 < c1) dequant(c + 1);
-      attend(dqb(c), c);
+      attend(dqb(c), c, [&](int h) {
+        if (c + 1 < c1) dequant(c + 1, h);
+      });
     }
   };
 
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
       __builtin_amdgcn_s_barrier();   // chunk c is in LDS; every wave is done with chunk c - 1
       COMPILER_FENCE();
       if (c + DNS - 1 < c1) issue(c + DNS - 1);
-      attend(stage(c), c);
+      attend(stage(c), c, [](int) {});
     }
   } else if (fp4_rows) {
    if constexpr (FP4) {
@@ -727,9 +733,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     // (16-B units of the bf16 row = 8 dims = one code word): the 16 stores of a row
     // land on 16 distinct slots of the swizzled row, so they are free of bank
     // conflicts (rows of 8 threads x 8 consecutive units conflicted 4 ways).
-    auto dequant = [&](int c) {
+    auto dequant = [&](int c, int h) {   // half h of the chunk's rows
       const unsigned char* st = raw(c);
-      for (int x = threadIdx.x; x < DRC * 16; x += 64 * NW) {
+      for (int x = threadIdx.x + h * (DRC * 8); x < (h + 1) * (DRC * 8); x += 64 * NW) {
         const int rr = x >> 4, l = x & 15;
         const uint32_t* crow = reinterpret_cast<const uint32_t*>(st + rr * 256);
         const unsigned char* srow = st + DRC * 256 + rr * 32;
@@ -768,9 +774,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_decode_bf16(
     };
     // 16 threads per row, thread l of a row widening units l, l + 16, l + 32, l + 48
     // (8 dims each) into their swizzled slots, as for an FP4 chunk
-    auto widen = [&](int c) {
+    auto widen = [&](int c, int h) {   // half h of the chunk's rows
       const unsigned char* st = raw(c);
-      for (int x = threadIdx.x; x < DRC * 16; x += 64 * NW) {
+      for (int x = threadIdx.x + h * (DRC * 8); x < (h + 1) * (DRC * 8); x += 64 * NW) {
         const int rr = x >> 4, l = x & 15;
         const unsigned char* srow = st + rr * 512;
         unsigned char* drow = dqb(c) + rr * PRS;
